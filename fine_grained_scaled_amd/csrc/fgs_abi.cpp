@@ -1,0 +1,225 @@
+// fgs_abi.cpp -- the extern "C" entry points of libfgs: argument validation
+// (before any HIP call), error reporting, and dispatch to the launchers.
+// The operations themselves are documented in include/fgs.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fgs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return FGS_OK;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(FGS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxRowBlocks = 65535;   // grid.y limit of the 128x128 quant kernels
+
+int check_bf16_source(const void* x, int64_t rows, int64_t cols, int64_t ldx)
+{
+    if (rows < 0 || cols < 0) return fail(FGS_ERR_INVALID_ARG, "rows (%lld) and cols (%lld) must be >= 0",
+                                          (long long)rows, (long long)cols);
+    if (rows == 0 || cols == 0) return FGS_OK;
+    if (!x) return fail(FGS_ERR_INVALID_ARG, "x is NULL");
+    if (ldx < cols) return fail(FGS_ERR_INVALID_ARG, "ldx (%lld) < cols (%lld)", (long long)ldx, (long long)cols);
+    if (cols % 8 || ldx % 8) return fail(FGS_ERR_UNSUPPORTED, "cols and ldx must be multiples of 8 (16-byte rows)");
+    if (!aligned(x, 16)) return fail(FGS_ERR_UNSUPPORTED, "x must be 16-byte aligned");
+    if ((rows + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "rows too large (%lld)", (long long)rows);
+    return FGS_OK;
+}
+
+int check_operand(const fgs_operand* op, const char* name, int64_t rows, int64_t K)
+{
+    if (!op) return fail(FGS_ERR_INVALID_ARG, "%s is NULL", name);
+    if (rows == 0) return FGS_OK;
+    if (!op->data) return fail(FGS_ERR_INVALID_ARG, "%s.data is NULL", name);
+    if (!op->scales) return fail(FGS_ERR_INVALID_ARG, "%s.scales is NULL", name);
+    if (op->ld < K) return fail(FGS_ERR_INVALID_ARG, "%s.ld (%lld) < K (%lld)", name, (long long)op->ld, (long long)K);
+    const int64_t ld_bytes = op->elem == FGS_ELEM_E2M1 ? op->ld / 2 : op->ld;
+    if (op->elem == FGS_ELEM_E2M1 && (op->ld & 1)) return fail(FGS_ERR_UNSUPPORTED, "%s.ld must be even for E2M1", name);
+    if (ld_bytes % 16) return fail(FGS_ERR_UNSUPPORTED, "%s row stride must be a multiple of 16 bytes", name);
+    if (!aligned(op->data, 16)) return fail(FGS_ERR_UNSUPPORTED, "%s.data must be 16-byte aligned", name);
+    if (!aligned(op->scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "%s.scales must be 4-byte aligned", name);
+    return FGS_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* fgs_last_error(void) { return g_last_error.c_str(); }
+
+const char* fgs_version(void) { return "fgs 0.1.0 (gfx950)"; }
+
+size_t fgs_workspace_bytes(int64_t rows, int64_t cols)
+{
+    (void)rows;
+    (void)cols;
+    return 256;
+}
+
+int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                           uint8_t* q, float* scales, uint8_t* qT, float* scalesT,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (mode != FGS_SCALE_TENSOR && mode != FGS_SCALE_TILE_1x128 && mode != FGS_SCALE_BLOCK_128x128)
+        return fail(FGS_ERR_INVALID_ARG, "mode %d is not TENSOR, TILE_1x128 or BLOCK_128x128", mode);
+    int st = check_bf16_source(x, rows, cols, ldx);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
+    if (q) {
+        if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
+        if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0 (cols = %lld)", (long long)cols);
+        if (!aligned(q, 16) || !aligned(scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte and scales 4-byte aligned");
+    }
+    if (qT) {
+        if (!scalesT && mode != FGS_SCALE_TENSOR) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
+        if (rows % 128) return fail(FGS_ERR_UNSUPPORTED, "column-wise output needs rows %% 128 == 0 (rows = %lld)", (long long)rows);
+        if (!aligned(qT, 16) || (scalesT && !aligned(scalesT, 4))) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
+    }
+    if (mode == FGS_SCALE_TENSOR) {
+        if (!workspace || workspace_bytes < 4) return fail(FGS_ERR_INVALID_ARG, "TENSOR mode needs a workspace of >= 4 bytes");
+        if (!aligned(workspace, 4)) return fail(FGS_ERR_UNSUPPORTED, "workspace must be 4-byte aligned");
+    }
+    fgs::QuantE4M3Args a{x, rows, cols, ldx, mode, q, scales, qT, scalesT, workspace};
+    return hip_status(fgs::launch_quant_e4m3(a, static_cast<hipStream_t>(stream)), "quantize_blockwise launch");
+}
+
+int fgs_quantize_mx(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                    uint8_t* q, uint8_t* scales, uint8_t* qT, uint8_t* scalesT, void* stream)
+{
+    int st = check_bf16_source(x, rows, cols, ldx);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
+    if (q) {
+        if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
+        if (cols % 32) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 32 == 0");
+        if (!aligned(q, 16)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+    }
+    if (qT) {
+        if (!scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
+        if (rows % 128) return fail(FGS_ERR_UNSUPPORTED, "column-wise output needs rows %% 128 == 0");
+        if (!aligned(qT, 16)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte aligned");
+    }
+    fgs::QuantMXArgs a{x, rows, cols, ldx, q, scales, qT, scalesT};
+    return hip_status(fgs::launch_quant_mx(a, static_cast<hipStream_t>(stream)), "quantize_mx launch");
+}
+
+int fgs_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                       int rht_mask, uint64_t rht_seed, int round, uint64_t sr_seed,
+                       uint8_t* q, uint8_t* scales, uint8_t* qT, uint8_t* scalesT,
+                       float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (rht_mask < 0 || rht_mask > 3) return fail(FGS_ERR_INVALID_ARG, "rht_mask must be in 0..3");
+    if (round != FGS_ROUND_RNE && round != FGS_ROUND_STOCHASTIC) return fail(FGS_ERR_INVALID_ARG, "round must be RNE or STOCHASTIC");
+    int st = check_bf16_source(x, rows, cols, ldx);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
+    if (!tensor_scale || !aligned(tensor_scale, 4)) return fail(FGS_ERR_INVALID_ARG, "tensor_scale must be a 4-byte aligned device pointer");
+    if (!workspace || workspace_bytes < 8 || !aligned(workspace, 4)) return fail(FGS_ERR_INVALID_ARG, "NVFP4 needs a workspace of >= 8 bytes");
+    if (q) {
+        if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
+        if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0");
+        if (!aligned(q, 16)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+    }
+    if (qT) {
+        if (!scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
+        if (rows % 128) return fail(FGS_ERR_UNSUPPORTED, "column-wise output needs rows %% 128 == 0");
+        if (!aligned(qT, 16)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte aligned");
+    }
+    fgs::QuantNVFP4Args a{x, rows, cols, ldx, rht_mask, rht_seed, round == FGS_ROUND_STOCHASTIC, sr_seed,
+                          q, scales, qT, scalesT, tensor_scale, workspace};
+    return hip_status(fgs::launch_quant_nvfp4(a, static_cast<hipStream_t>(stream)), "quantize_nvfp4 launch");
+}
+
+static int check_gemm_common(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                             void* C, int64_t ldc, int out_dtype)
+{
+    if (M < 0 || N < 0 || K < 0) return fail(FGS_ERR_INVALID_ARG, "M, N, K must be >= 0");
+    if (out_dtype != FGS_OUT_FP32 && out_dtype != FGS_OUT_BF16) return fail(FGS_ERR_INVALID_ARG, "out_dtype %d invalid", out_dtype);
+    if (!A || !B) return fail(FGS_ERR_INVALID_ARG, "A and B must not be NULL");
+    if (M == 0 || N == 0) return FGS_OK;
+    if (K == 0 || K % 128) return fail(FGS_ERR_UNSUPPORTED, "K must be a positive multiple of 128 (K = %lld)", (long long)K);
+    if (!C) return fail(FGS_ERR_INVALID_ARG, "C is NULL");
+    if (ldc < N) return fail(FGS_ERR_INVALID_ARG, "ldc (%lld) < N (%lld)", (long long)ldc, (long long)N);
+    if (!aligned(C, out_dtype == FGS_OUT_FP32 ? 4 : 2)) return fail(FGS_ERR_UNSUPPORTED, "C misaligned");
+    if (A->elem != B->elem) return fail(FGS_ERR_UNSUPPORTED, "A and B element formats differ");
+    if (A->elem != FGS_ELEM_E4M3 && A->elem != FGS_ELEM_E2M1) return fail(FGS_ERR_INVALID_ARG, "unknown element format %d", A->elem);
+    int st = check_operand(A, "A", M, K);
+    if (st != FGS_OK) return st;
+    return check_operand(B, "B", N, K);
+}
+
+static bool is_fp32_mode(int m)
+{
+    return m == FGS_SCALE_TENSOR || m == FGS_SCALE_TILE_1x128 || m == FGS_SCALE_BLOCK_128x128;
+}
+
+int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                          void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    int st = check_gemm_common(A, B, M, N, K, C, ldc, out_dtype);
+    if (st != FGS_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
+    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (A->elem == FGS_ELEM_E4M3 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
+        if (A->scale_mode == FGS_SCALE_BLOCK_128x128)
+            return fail(FGS_ERR_UNSUPPORTED, "A with 128x128 block scales is not supported (use TILE_1x128 or TENSOR)");
+        return hip_status(fgs::launch_gemm_fp8(a, s), "gemm_block_scaled launch");
+    }
+    if (A->elem == FGS_ELEM_E4M3 && A->scale_mode == FGS_SCALE_MX32_E8M0 && B->scale_mode == FGS_SCALE_MX32_E8M0)
+        return hip_status(fgs::launch_gemm_mx(a, s), "gemm_block_scaled (MX) launch");
+    if (A->elem == FGS_ELEM_E2M1 && A->scale_mode == FGS_SCALE_NV16_E4M3 && B->scale_mode == FGS_SCALE_NV16_E4M3) {
+        if (!A->tensor_scale || !B->tensor_scale) return fail(FGS_ERR_INVALID_ARG, "NVFP4 operands need tensor_scale");
+        return hip_status(fgs::launch_gemm_nvfp4(a, s), "gemm_block_scaled (NVFP4) launch");
+    }
+    return fail(FGS_ERR_UNSUPPORTED, "unsupported operand combination (elem %d, A scale %d, B scale %d)",
+                A->elem, A->scale_mode, B->scale_mode);
+}
+
+int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                  int32_t G, int64_t total_M, int64_t N, int64_t K,
+                                  void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
+    int st = check_gemm_common(A, B, total_M, N, K, C, ldc, out_dtype);
+    if (st != FGS_OK) return st;
+    if (total_M == 0 || N == 0 || G == 0) return ok();
+    if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
+    if (A->elem != FGS_ELEM_E4M3 || A->scale_mode != FGS_SCALE_TILE_1x128 || B->scale_mode != FGS_SCALE_BLOCK_128x128)
+        return fail(FGS_ERR_UNSUPPORTED, "grouped GEMM supports E4M3 A TILE_1x128 x B BLOCK_128x128");
+    if (total_M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
+    const int64_t tiles = ((total_M + 127) / 128 + G) * ((N + 127) / 128);
+    if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
+    fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G};
+    return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_gemm_block_scaled launch");
+}
+
+} // extern "C"

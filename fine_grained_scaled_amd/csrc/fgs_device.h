@@ -1,0 +1,146 @@
+// fgs_device.h -- device helpers of the gfx950 kernels (internal header of
+// libfgs; never included by host-only code outside csrc/).
+//
+// Arithmetic rules the kernels must reproduce bit for bit:
+//  * FP32-scaled E4M3 ("Can you explain the role of FP8 precision in
+//    DeepSeek-V3 training", sections "Fine-grained quantization", "Online
+//    quantization"): s = fl32(amax / 448), code = E4M3_RNE_SAT(fl32(x / s)).
+//  * Everything is IEEE binary32 with round-to-nearest-even; the library is
+//    compiled with -ffp-contract=off so every fused multiply-add below is
+//    written out on purpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgs {
+
+// ------------------------------------------------------------------------
+// bit casts
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
+
+// BF16 pair packed in a 32-bit word -> its two FP32 values (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------------------
+// cross-lane max of non-negative integers (amax carried as |BF16| bits,
+// where the integer order equals the value order and NaN > Inf > finite,
+// so the maximum propagates NaN exactly and independently of order).
+// ------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)v, CTRL, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+// quad_perm [1,0,3,2] = xor 1; [2,3,0,1] = xor 2; row_half_mirror; row_mirror
+constexpr int DPP_XOR1 = 0xB1;
+constexpr int DPP_XOR2 = 0x4E;
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// max over aligned groups of 2 / 4 / 16 lanes (every lane gets the result)
+__device__ __forceinline__ uint32_t max_lanes2(uint32_t v) { return dpp_max<DPP_XOR1>(v); }
+__device__ __forceinline__ uint32_t max_lanes4(uint32_t v)
+{
+    return dpp_max<DPP_XOR2>(dpp_max<DPP_XOR1>(v));
+}
+__device__ __forceinline__ uint32_t max_lanes16(uint32_t v)
+{
+    v = max_lanes4(v);
+    v = dpp_max<DPP_HALF_MIRROR>(v);
+    return dpp_max<DPP_MIRROR>(v);
+}
+// max across lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave)
+__device__ __forceinline__ uint32_t max_xor16(uint32_t v)
+{
+    uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
+    return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v)
+{
+    uint32_t o = (uint32_t)__shfl_xor((int)v, 32);
+    return v > o ? v : o;
+}
+
+// ------------------------------------------------------------------------
+// E4M3 (OCP E4M3FN) round-to-nearest-even with saturation, for a
+// non-negative finite FP32 value; returns the 7-bit magnitude code.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code_abs(float a)
+{
+    // below 2^-6 the E4M3 grid is uniform with step 2^-9: round a * 2^9
+    // (exact scaling) to the nearest even integer, 0..8 (8 = 2^-6, code 0x08)
+    uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+    // normal range: drop 20 of the 23 mantissa bits with RNE, then rebias the
+    // exponent from 127 to 7 (a carry out of the mantissa bumps the exponent)
+    uint32_t b = as_u32(a);
+    uint32_t nrm = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t c = (a < 0.015625f) ? sub : nrm;
+    return c < 0x7Eu ? c : 0x7Eu;
+}
+
+// ------------------------------------------------------------------------
+// Correctly rounded fl32(x / s) from a per-block reciprocal r = RN(1/s):
+// q0 = x*r, residual x - q0*s (exact with FMA), one correction step.  Equal
+// to IEEE division for every BF16 x with |x| <= amax and s = fl32(amax/448)
+// of a BF16 amax >= 2^-64 (checked exhaustively on the host, all 5.3e8
+// pairs); blocks with a smaller amax are pre-scaled by 2^64 on both sides,
+// which leaves the quotient unchanged.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float div_by_scale(float x, float s, float r)
+{
+    float q0 = x * r;
+    float res = __builtin_fmaf(-q0, s, x);
+    return __builtin_fmaf(res, r, q0);
+}
+
+// fl32(amax / 448) for a BF16-valued amax, by multiplication and one FMA
+// correction (bit-equal to IEEE division for every BF16 amax).
+__device__ __forceinline__ float scale_from_amax_448(float amax)
+{
+    const float inv448 = 1.0f / 448.0f;   // RN(1/448), folded at compile time
+    float s0 = amax * inv448;
+    float e = __builtin_fmaf(-s0, 448.0f, amax);
+    return __builtin_fmaf(e, inv448, s0);
+}
+
+// Per-block quantization constants of the FP32-scaled E4M3 rule.
+struct E4M3Block {
+    float s;      // the block scale written out
+    float k;      // 1 or 2^64 (pre-scale of tiny blocks)
+    float sp;     // s * k
+    float r;      // RN(1 / sp)
+    bool nan;     // amax non-finite: scale NaN, all codes 0x7F
+};
+
+__device__ __forceinline__ E4M3Block e4m3_block_from_amax_bits(uint32_t amax_bits16)
+{
+    E4M3Block b;
+    float amax = as_f32(amax_bits16 << 16);
+    b.nan = amax_bits16 >= 0x7F80u;
+    if (b.nan) {
+        b.s = __builtin_nanf("");
+        b.k = 1.0f; b.sp = 1.0f; b.r = 1.0f;
+        return b;
+    }
+    b.s = (amax_bits16 == 0) ? 1.0f : scale_from_amax_448(amax);
+    b.k = (amax < 0x1p-64f) ? 0x1p64f : 1.0f;
+    b.sp = b.s * b.k;
+    b.r = 1.0f / b.sp;   // IEEE division (hipcc keeps FP32 division correctly rounded)
+    return b;
+}
+
+// code of one BF16 element (raw 16-bit pattern in the low half of h)
+__device__ __forceinline__ uint32_t e4m3_quant_bf16(uint32_t h, const E4M3Block& b)
+{
+    if (b.nan) return 0x7Fu;
+    float a = as_f32((h & 0x7FFFu) << 16) * b.k;
+    uint32_t c = e4m3_code_abs(div_by_scale(a, b.sp, b.r));
+    return c | ((h >> 8) & 0x80u);
+}
+
+} // namespace fgs

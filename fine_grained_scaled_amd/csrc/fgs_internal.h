@@ -1,0 +1,65 @@
+// fgs_internal.h -- launcher interfaces between the C ABI layer and the
+// gfx950 kernels of libfgs (validated arguments only reach these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fgs.h"
+
+namespace fgs {
+
+struct QuantE4M3Args {
+    const void* x;
+    int64_t rows, cols, ldx;
+    int mode;
+    uint8_t* q;
+    float* scales;
+    uint8_t* qT;
+    float* scalesT;
+    void* workspace;   // >= 4 bytes for TENSOR mode
+};
+hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream);
+
+struct QuantMXArgs {
+    const void* x;
+    int64_t rows, cols, ldx;
+    uint8_t* q;
+    uint8_t* scales;
+    uint8_t* qT;
+    uint8_t* scalesT;
+};
+hipError_t launch_quant_mx(const QuantMXArgs& a, hipStream_t stream);
+
+struct QuantNVFP4Args {
+    const void* x;
+    int64_t rows, cols, ldx;
+    int rht_mask;
+    uint64_t rht_seed;
+    int stochastic;
+    uint64_t sr_seed;
+    uint8_t* q;
+    uint8_t* scales;
+    uint8_t* qT;
+    uint8_t* scalesT;
+    float* tensor_scale;
+    void* workspace;   // >= 8 bytes
+};
+hipError_t launch_quant_nvfp4(const QuantNVFP4Args& a, hipStream_t stream);
+
+struct GemmArgs {
+    fgs_operand A, B;
+    int64_t M, N, K;
+    void* C;
+    int64_t ldc;
+    int out_bf16;
+    // grouped variant
+    const int32_t* group_offsets;   // nullptr for the dense GEMM
+    int32_t G;
+};
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t stream);
+
+} // namespace fgs

@@ -1,0 +1,263 @@
+// quant_e4m3.hip -- online FP32-scaled E4M3 quantization on gfx950.
+//
+// "Can you explain the role of FP8 precision in DeepSeek-V3 training",
+// sections "Fine-grained quantization" (activations in 1x128 tiles, weights
+// in 128x128 blocks, each with its own scale) and "Online quantization"
+// (the scale is derived from the current tile/block amax); "Accelerating FP8
+// training performance with the NVIDIA NeMo framework" (per-tensor current
+// scaling).  The rule: scale = fl32(amax / 448), code = E4M3_RNE_SAT(x / s).
+//
+// One workgroup (256 threads, 4 waves) owns a 128 x 128 block of the BF16
+// source.  Thread t (wave w, lane l) holds an 8 x 8 sub-block:
+//   column group cg = l & 15         -> source columns c0 + 8*cg .. +7
+//   row group    rg = 4*w + (l >> 4) -> source rows    r0 + 8*rg .. +7
+// Each of its eight 16-byte loads reads row r0 + 8*rg + u; the 16 lanes of a
+// DPP row read one 256-byte contiguous row segment.  From the one read the
+// kernel emits the row-wise codes (1x128 tiles = one row of the block, or
+// the block / tensor scale) and the column-wise codes (128x1 tiles along the
+// source rows, the wgrad operand, or the transposed block/tensor codes),
+// the latter transposed through LDS so every store is a full 128-byte row.
+#include "fgs_device.h"
+#include "fgs_internal.h"
+
+namespace fgs {
+
+namespace {
+
+constexpr int TB = 128;        // block edge
+constexpr int TPAD = 16;       // LDS row padding of the transposed code tile
+
+__device__ __forceinline__ uint32_t abs_max8(const uint4& v)
+{
+    uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+    uint32_t c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
+    uint32_t m0 = max(a & 0xFFFFu, a >> 16), m1 = max(b & 0xFFFFu, b >> 16);
+    uint32_t m2 = max(c & 0xFFFFu, c >> 16), m3 = max(d & 0xFFFFu, d >> 16);
+    return max(max(m0, m1), max(m2, m3));
+}
+
+// |BF16| bits of element j (0..7) of an 8-element vector
+__device__ __forceinline__ uint32_t abs_elem(const uint4& v, int j)
+{
+    uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
+    return ((j & 1) ? (w >> 16) : w) & 0x7FFFu;
+}
+
+__device__ __forceinline__ uint32_t raw_elem(const uint4& v, int j)
+{
+    uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
+    return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+__device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
+{
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = e4m3_quant_bf16(raw_elem(v, j), b);
+    uint2 o;
+    o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    return o;
+}
+
+template <int MODE>   // FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
+__global__ __launch_bounds__(256) void quant_e4m3_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    uint8_t* __restrict__ q, float* __restrict__ scales,
+    uint8_t* __restrict__ qT, float* __restrict__ scalesT,
+    const uint32_t* __restrict__ tensor_amax)
+{
+    __shared__ uint32_t red[4][TB];
+    __shared__ __align__(16) uint8_t tbuf[TB][TB + TPAD];
+
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = l & 15, rg = 4 * w + (l >> 4);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    const int64_t col = c0 + 8 * cg;
+    const bool col_ok = col < cols;
+
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t row = r0 + 8 * rg + u;
+        if (col_ok && row < rows)
+            v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+        else
+            v[u] = make_uint4(0, 0, 0, 0);
+    }
+
+    // ---------------- shared (block / tensor) scale --------------------
+    E4M3Block shared_b;
+    if constexpr (MODE == FGS_SCALE_BLOCK_128x128) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = max(m, abs_max8(v[u]));
+        m = max_xor32(max_xor16(max_lanes16(m)));
+        if (l == 0) red[w][0] = m;
+        __syncthreads();
+        m = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
+        shared_b = e4m3_block_from_amax_bits(m);
+        if (t == 0) {
+            if (q) scales[blockIdx.y * ((cols + TB - 1) / TB) + blockIdx.x] = shared_b.s;
+            if (qT) scalesT[blockIdx.x * ((rows + TB - 1) / TB) + blockIdx.y] = shared_b.s;
+        }
+    } else if constexpr (MODE == FGS_SCALE_TENSOR) {
+        shared_b = e4m3_block_from_amax_bits(tensor_amax[0]);
+        if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+            if (scales) scales[0] = shared_b.s;
+            if (scalesT) scalesT[0] = shared_b.s;
+        }
+    }
+
+    // ---------------- row-wise output ---------------------------------
+    if (q) {
+        float srow[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            E4M3Block b;
+            if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+                b = e4m3_block_from_amax_bits(max_lanes16(abs_max8(v[u])));
+                srow[u] = b.s;
+            } else {
+                b = shared_b;
+            }
+            const int64_t row = r0 + 8 * rg + u;
+            uint2 codes = quant8(v[u], b);
+            if (col_ok && row < rows)
+                *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+        }
+        if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+            if (cg == 0) {
+                float* dst = scales + blockIdx.x * rows + r0 + 8 * rg;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (r0 + 8 * rg + u < rows) dst[u] = srow[u];
+            }
+        }
+    }
+
+    // ---------------- column-wise (transposed) output ------------------
+    if (qT) {
+        E4M3Block bcol[8];
+        if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+            uint32_t cm[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) m = max(m, abs_elem(v[u], j));
+                cm[j] = max_xor32(max_xor16(m));
+            }
+            if ((l >> 4) == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) red[w][8 * cg + j] = cm[j];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = 8 * cg + j;
+                uint32_t m = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
+                bcol[j] = e4m3_block_from_amax_bits(m);
+            }
+            if (w == 0 && (l >> 4) == 0 && col_ok) {
+                float* dst = scalesT + blockIdx.y * cols + col;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dst[j] = bcol[j].s;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bcol[j] = shared_b;
+        }
+        // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = e4m3_quant_bf16(raw_elem(v[u], j), bcol[j]);
+            uint2 o;
+            o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = o;
+        }
+        __syncthreads();
+        // 8 lanes write one 128-byte row of qT
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int trow = 32 * i + (t >> 3), chunk = t & 7;
+            const int64_t orow = c0 + trow;
+            if (orow < cols) {
+                uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
+                *reinterpret_cast<uint4*>(qT + orow * rows + r0 + 16 * chunk) = d;
+            }
+        }
+    }
+}
+
+// Tensor amax (|BF16| bits) of a 128 x 128-block grid, one atomic per workgroup.
+__global__ __launch_bounds__(256) void amax_bf16_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    int64_t nbr, int64_t nbc, uint32_t* __restrict__ out)
+{
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = l & 15, rg = 4 * w + (l >> 4);
+    uint32_t m = 0;
+    for (int64_t blk = blockIdx.x; blk < nbr * nbc; blk += gridDim.x) {
+        const int64_t r0 = (blk / nbc) * TB, c0 = (blk % nbc) * TB;
+        const int64_t col = c0 + 8 * cg;
+        if (col >= cols) continue;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t row = r0 + 8 * rg + u;
+            if (row < rows) m = max(m, abs_max8(*reinterpret_cast<const uint4*>(x + row * ldx + col)));
+        }
+    }
+    m = max_xor32(max_xor16(max_lanes16(m)));
+    if (l == 0) red[w] = m;
+    __syncthreads();
+    if (t == 0) {
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(out, m);
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v)
+{
+    if ((int)threadIdx.x < n) p[threadIdx.x] = v;
+}
+
+} // namespace
+
+hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
+{
+    const int64_t nbr = (a.rows + TB - 1) / TB, nbc = (a.cols + TB - 1) / TB;
+    if (nbr == 0 || nbc == 0) return hipSuccess;
+    dim3 grid((unsigned)nbc, (unsigned)nbr), block(256);
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    switch (a.mode) {
+    case FGS_SCALE_TILE_1x128:
+        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_TILE_1x128>, grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr);
+        break;
+    case FGS_SCALE_BLOCK_128x128:
+        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128>, grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr);
+        break;
+    case FGS_SCALE_TENSOR: {
+        uint32_t* amax = static_cast<uint32_t*>(a.workspace);
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, amax, 1, 0u);
+        const int64_t nblk = nbr * nbc;
+        const unsigned g = (unsigned)(nblk < 1024 ? nblk : 1024);
+        hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
+        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_TENSOR>, grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax);
+        break;
+    }
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+} // namespace fgs

@@ -1,0 +1,204 @@
+"""Python binding of libfgs: argument marshalling only.
+
+Every step of the path runs in the HIP kernels behind the C ABI; this module
+checks tensor placement and dtypes, allocates outputs with torch, and passes
+raw device pointers plus torch's current HIP stream.  There is no CPU
+fallback: without the built library or a GPU every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (ELEM_E2M1, ELEM_E4M3, OUT_BF16, OUT_FP32, ROUND_RNE, ROUND_STOCHASTIC,
+                   SCALE_BLOCK_128x128, SCALE_MX32_E8M0, SCALE_NV16_E4M3, SCALE_TENSOR,
+                   SCALE_TILE_1x128, FgsOperand, check)
+
+MODES = {"tensor": SCALE_TENSOR, "tile": SCALE_TILE_1x128, "block": SCALE_BLOCK_128x128}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("fine_grained_scaled_amd operates on GPU tensors only")
+
+
+def _bf16_matrix(x: torch.Tensor):
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    _need_gpu(x)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along columns")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def _workspace(device) -> torch.Tensor:
+    n = _lib.load().fgs_workspace_bytes(0, 0)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Operand:
+    """A quantized GEMM operand of `rows` x `K`, K-contiguous."""
+    data: torch.Tensor
+    scales: torch.Tensor
+    scale_mode: int
+    elem: int = ELEM_E4M3
+    tensor_scale: Optional[torch.Tensor] = None
+    ld: Optional[int] = None
+
+    def c_struct(self) -> FgsOperand:
+        ld = self.ld
+        if ld is None:
+            ld = self.data.stride(-2) * (2 if self.elem == ELEM_E2M1 else 1)
+        return FgsOperand(self.data.data_ptr(), ld, self.elem, self.scale_mode,
+                          self.scales.data_ptr(),
+                          self.tensor_scale.data_ptr() if self.tensor_scale is not None else 0)
+
+
+@dataclass
+class Quantized:
+    q: Optional[torch.Tensor]
+    scales: Optional[torch.Tensor]
+    qT: Optional[torch.Tensor]
+    scalesT: Optional[torch.Tensor]
+    scale_mode: int
+    elem: int = ELEM_E4M3
+    tensor_scale: Optional[torch.Tensor] = None   # NVFP4: [2] (row-wise, column-wise)
+
+    def rowwise(self) -> Operand:
+        ts = self.tensor_scale[0:1] if self.tensor_scale is not None else None
+        return Operand(self.q, self.scales, self.scale_mode, self.elem, ts)
+
+    def colwise(self) -> Operand:
+        ts = self.tensor_scale[1:2] if self.tensor_scale is not None else None
+        scales = self.scalesT
+        if scales is None and self.scale_mode == SCALE_TENSOR:
+            scales = self.scales
+        return Operand(self.qT, scales, self.scale_mode, self.elem, ts)
+
+
+def quantize_blockwise(x: torch.Tensor, mode: str = "tile", rowwise: bool = True,
+                       colwise: bool = False) -> Quantized:
+    """Online FP32-scaled E4M3 quantization (1x128 tiles, 128x128 blocks or
+    one per-tensor scale); row-wise and/or transposed (column-wise) outputs."""
+    rows, cols, ldx = _bf16_matrix(x)
+    m = MODES[mode]
+    dev = x.device
+    q = s = qT = sT = None
+    if rowwise:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        if m == SCALE_TILE_1x128:
+            s = torch.empty(((cols + 127) // 128, rows), dtype=torch.float32, device=dev)
+        elif m == SCALE_BLOCK_128x128:
+            s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=dev)
+        else:
+            s = torch.empty(1, dtype=torch.float32, device=dev)
+    if colwise:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        if m == SCALE_TILE_1x128:
+            sT = torch.empty(((rows + 127) // 128, cols), dtype=torch.float32, device=dev)
+        elif m == SCALE_BLOCK_128x128:
+            sT = torch.empty(((cols + 127) // 128, (rows + 127) // 128), dtype=torch.float32, device=dev)
+        else:
+            sT = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = _workspace(dev) if m == SCALE_TENSOR else None
+    check(_lib.load().fgs_quantize_blockwise(
+        _ptr(x), rows, cols, ldx, m, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
+    return Quantized(q, s, qT, sT, m)
+
+
+def quantize_mx(x: torch.Tensor, rowwise: bool = True, colwise: bool = False) -> Quantized:
+    """MXFP8: E4M3 codes with an E8M0 power-of-two scale per 32 elements."""
+    rows, cols, ldx = _bf16_matrix(x)
+    dev = x.device
+    q = s = qT = sT = None
+    if rowwise:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows, (cols + 31) // 32), dtype=torch.uint8, device=dev)
+    if colwise:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        sT = torch.empty((cols, (rows + 31) // 32), dtype=torch.uint8, device=dev)
+    check(_lib.load().fgs_quantize_mx(_ptr(x), rows, cols, ldx, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), _stream()))
+    return Quantized(q, s, qT, sT, SCALE_MX32_E8M0)
+
+
+def quantize_nvfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
+                   rht_mask: int = 0, rht_seed: int = 0, stochastic: bool = False,
+                   sr_seed: int = 0) -> Quantized:
+    """NVFP4: packed E2M1 codes, E4M3 scale per 16 elements, FP32 tensor
+    scale; optional random Hadamard transform and stochastic rounding."""
+    rows, cols, ldx = _bf16_matrix(x)
+    dev = x.device
+    q = s = qT = sT = None
+    if rowwise:
+        q = torch.empty((rows, (cols + 1) // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows, (cols + 15) // 16), dtype=torch.uint8, device=dev)
+    if colwise:
+        qT = torch.empty((cols, (rows + 1) // 2), dtype=torch.uint8, device=dev)
+        sT = torch.empty((cols, (rows + 15) // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(2, dtype=torch.float32, device=dev)
+    ws = _workspace(dev)
+    check(_lib.load().fgs_quantize_nvfp4(
+        _ptr(x), rows, cols, ldx, rht_mask, rht_seed & (2**64 - 1),
+        ROUND_STOCHASTIC if stochastic else ROUND_RNE, sr_seed & (2**64 - 1),
+        _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), _ptr(ts), _ptr(ws), ws.numel(), _stream()))
+    return Quantized(q, s, qT, sT, SCALE_NV16_E4M3, ELEM_E2M1, ts)
+
+
+def _out_code(out_dtype):
+    if out_dtype == torch.float32:
+        return OUT_FP32
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
+                      out: Optional[torch.Tensor] = None, K: Optional[int] = None) -> torch.Tensor:
+    """C[M x N] = sum_k A^[m, k] * B^[n, k] over scaled low-precision operands."""
+    _need_gpu(A.data, B.data, A.scales, B.scales)
+    M, N = A.data.shape[0], B.data.shape[0]
+    if K is None:
+        K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.data.device)
+    a, b = A.c_struct(), B.c_struct()
+    check(_lib.load().fgs_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), M, N, K,
+                                            _ptr(out), out.stride(0), code, _stream()))
+    return out
+
+
+def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, N: int,
+                              out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                              K: Optional[int] = None) -> torch.Tensor:
+    """MoE expert GEMMs: rows offsets[g]..offsets[g+1] of A times B_g^T.
+    B.data is [G*N x K] (groups contiguous); group_offsets is int32 [G+1] on the GPU."""
+    _need_gpu(A.data, B.data, group_offsets)
+    if group_offsets.dtype != torch.int32:
+        raise TypeError("group_offsets must be int32")
+    total_M = A.data.shape[0]
+    G = group_offsets.numel() - 1
+    if K is None:
+        K = A.data.shape[1]
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((total_M, N), dtype=out_dtype, device=A.data.device)
+    a, b = A.c_struct(), B.c_struct()
+    check(_lib.load().fgs_grouped_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
+                                                    G, total_M, N, K, _ptr(out), out.stride(0), code, _stream()))
+    return out

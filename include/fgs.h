@@ -1,0 +1,204 @@
+/*
+ * fgs.h -- C ABI of libfgs: fine-grained scaled low-precision quantization
+ * and block-scaled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow three web pages on fine-grained scaled training:
+ *  [DSV3]  "Can you explain the role of FP8 precision in DeepSeek-V3
+ *          training" (codingmall.com): "Mixed precision framework" (GEMMs in
+ *          FP8), "Fine-grained quantization" (activations in 1x128 tiles,
+ *          weights in 128x128 blocks, each scaled independently), "Online
+ *          quantization" (scales from the current tile/block, no history),
+ *          "Increasing accumulation precision" (partial sums promoted to
+ *          FP32 registers at intervals), "Unified E4M3 format" (E4M3 in the
+ *          forward and backward passes).
+ *  [NEMO]  "Accelerating FP8 training performance with the NVIDIA NeMo
+ *          framework" (hyper.ai): per-tensor and block-wise scaling recipes,
+ *          MXFP8 with one scale per block of 32 values.
+ *  [NVFP4] "NVIDIA developed a method to train neural networks at 4-bit"
+ *          (news.hamidun.com), "How it works": the 4-bit NVFP4 format, random
+ *          16x16 Hadamard transforms of gradient inputs, stochastic rounding.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and the call returns at once.
+ *  - Matrices are row-major.  BF16 inputs are raw 16-bit patterns.  Every
+ *    GEMM operand is K-contiguous ("NT"): C[m][n] = sum_k A[m][k] * B[n][k].
+ *  - Element codes: E4M3 = OCP E4M3FN byte (0x7E = 448, 0x7F/0xFF NaN);
+ *    E2M1 = OCP FP4 nibble, two per byte, element 2j in the low nibble.
+ *  - Quantization is online: every scale comes from the amax of the data
+ *    being quantized in this call.  FP32-scaled blocks use
+ *    scale = fl32(amax / 448) and code = E4M3_RNE_SAT(fl32(x / scale));
+ *    an all-zero block gets scale 1 and signed-zero codes; a block holding
+ *    NaN/Inf gets scale NaN and NaN codes.
+ *  - Status: FGS_OK, or a negative fgs_status.  Argument errors are detected
+ *    before any HIP call and leave outputs untouched; fgs_last_error() then
+ *    returns a message (thread-local).  A kernel launch failure returns
+ *    FGS_ERR_HIP; a fault inside a kernel surfaces at the caller's next
+ *    synchronisation.
+ *  - Pointers must be 16-byte aligned; row strides are in elements.
+ */
+#ifndef FGS_H
+#define FGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FGS_OK = 0,
+    FGS_ERR_INVALID_ARG = -1,
+    FGS_ERR_UNSUPPORTED = -2,
+    FGS_ERR_HIP = -3
+} fgs_status;
+
+/* Element formats of a quantized operand. */
+typedef enum {
+    FGS_ELEM_E4M3 = 0, /* one byte per element */
+    FGS_ELEM_E2M1 = 1  /* two elements per byte */
+} fgs_elem;
+
+/*
+ * Scale granularities.  For an operand of R rows and contraction length K
+ * (K-contiguous codes, row stride ld):
+ *  FGS_SCALE_TENSOR        FP32 [1]                     [NEMO] per-tensor
+ *  FGS_SCALE_TILE_1x128    FP32 [K/128][R]  (tile-column-major, so one
+ *                          K-block's scales are contiguous)  [DSV3] 1x128
+ *  FGS_SCALE_BLOCK_128x128 FP32 [ceil(R/128)][K/128]         [DSV3] 128x128
+ *  FGS_SCALE_MX32_E8M0     u8   [R][K/32]  2^(c-127)          [NEMO] MXFP8
+ *  FGS_SCALE_NV16_E4M3     u8   [R][K/16]  E4M3 codes, times an FP32 tensor
+ *                          scale                              [NVFP4]
+ */
+typedef enum {
+    FGS_SCALE_TENSOR = 0,
+    FGS_SCALE_TILE_1x128 = 1,
+    FGS_SCALE_BLOCK_128x128 = 2,
+    FGS_SCALE_MX32_E8M0 = 3,
+    FGS_SCALE_NV16_E4M3 = 4
+} fgs_scale;
+
+typedef enum { FGS_ROUND_RNE = 0, FGS_ROUND_STOCHASTIC = 1 } fgs_round;
+typedef enum { FGS_OUT_FP32 = 0, FGS_OUT_BF16 = 1 } fgs_out;
+
+/* One quantized GEMM operand: R rows x K, K-contiguous. */
+typedef struct {
+    const void *data;          /* codes (device)                                  */
+    int64_t ld;                /* row stride in ELEMENTS (E2M1: elements, even)   */
+    int32_t elem;              /* fgs_elem                                        */
+    int32_t scale_mode;        /* fgs_scale                                       */
+    const void *scales;        /* device; layout per fgs_scale                    */
+    const float *tensor_scale; /* device FP32 [1]; NV16 only, else NULL           */
+} fgs_operand;
+
+/*
+ * fgs_quantize_blockwise -- online FP32-scaled E4M3 quantization.
+ *   [DSV3] "Fine-grained quantization", "Online quantization";
+ *   [NEMO] per-tensor current scaling.
+ * x        BF16 [rows x cols], row stride ldx (elements, multiple of 8).
+ * mode     FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR.
+ * Row-wise output (quantized along cols; NULL q skips it; needs cols % 128 == 0):
+ *   q       E4M3 [rows x cols] (dense), scales per mode for R = rows, K = cols.
+ * Column-wise output (the transpose, quantized along rows; NULL qT skips it;
+ *   needs rows % 128 == 0):
+ *   qT      E4M3 [cols x rows] (dense), scalesT per mode for R = cols, K = rows.
+ *   TILE re-quantizes each 128-row column segment from the BF16 source
+ *   (the wgrad operand); BLOCK and TENSOR transpose the row-wise codes and
+ *   scale grid (the 128x128 grid and a single scale are transpose-invariant).
+ * Both outputs come from one read of x.  TENSOR mode needs a workspace of
+ *   fgs_workspace_bytes() bytes (device, 4-byte aligned) for the tensor amax;
+ *   TILE/BLOCK ignore it.
+ * rows and cols may be 0 (nothing is enqueued).
+ */
+int fgs_quantize_blockwise(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                           int mode, uint8_t *q, float *scales,
+                           uint8_t *qT, float *scalesT,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fgs_quantize_mx -- MXFP8: E4M3 codes with one E8M0 scale 2^e per 32
+ *   contiguous elements, e the smallest integer with amax <= 448 * 2^e
+ *   (clamped to [-127, 127]); code = E4M3_RNE_SAT(x * 2^-e).   [NEMO] MXFP8.
+ * Row-wise (needs cols % 32 == 0): q [rows x cols], scales u8 [rows][cols/32].
+ * Column-wise (needs rows % 128 == 0): qT [cols x rows], scalesT u8
+ *   [cols][rows/32] (blocks of 32 along the source rows).
+ */
+int fgs_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                    uint8_t *q, uint8_t *scales, uint8_t *qT, uint8_t *scalesT,
+                    void *stream);
+
+/*
+ * fgs_quantize_nvfp4 -- NVFP4: E2M1 codes, one E4M3 scale per 16 contiguous
+ *   elements, one FP32 tensor scale per output.   [NVFP4] "How it works".
+ *   s_t = fl32(amax_t / 2688); s_b = E4M3(fl32(amax_b / fl32(6 s_t)));
+ *   code = E2M1(sat6(fl32(x / fl32(dec(s_b) * s_t)))), RNE or stochastic.
+ * rht_mask bit 0: apply the random 16x16 Hadamard transform (signs from
+ *   rht_seed) along the quantized dimension of the row-wise output; bit 1:
+ *   same for the column-wise output.  The transform precedes the amax.
+ * round    FGS_ROUND_RNE or FGS_ROUND_STOCHASTIC (applies to both outputs);
+ *   the SR word of an element hashes sr_seed with its linear index
+ *   row * cols + col in x.
+ * Row-wise (needs cols % 128 == 0): q [rows x cols/2], scales u8 [rows][cols/16].
+ * Column-wise (needs rows % 128 == 0): qT [cols x rows/2], scalesT u8
+ *   [cols][rows/16].
+ * tensor_scale  device FP32 [2]: [0] row-wise s_t, [1] column-wise s_t.
+ * workspace     fgs_workspace_bytes() bytes of device memory.
+ */
+int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                       int rht_mask, uint64_t rht_seed, int round, uint64_t sr_seed,
+                       uint8_t *q, uint8_t *scales, uint8_t *qT, uint8_t *scalesT,
+                       float *tensor_scale, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * fgs_gemm_block_scaled -- C[M x N] = sum_k A^[m,k] * B^[n,k] with scaled
+ *   low-precision operands.   [DSV3] "Mixed precision framework",
+ *   "Increasing accumulation precision"; [NEMO]; [NVFP4].
+ * A: M x K operand, B: N x K operand (fgs_operand).  Supported pairs:
+ *   E4M3 with A in {TILE_1x128, TENSOR} and B in {BLOCK_128x128, TILE_1x128,
+ *     TENSOR}: MFMA partial sums over one 128-deep K block are scaled by
+ *     sA * sB and added into FP32 accumulators once per block (promotion);
+ *   E4M3 with MX32_E8M0 on both: hardware-scaled MFMA, FP32 accumulation;
+ *   E2M1 with NV16_E4M3 on both: operands decoded exactly to FP16, FP16
+ *     MFMA with FP32 accumulation, tensor scales applied at the end.
+ * K must be a multiple of 128.  M, N >= 0 arbitrary.
+ * C: FP32 or BF16 (RNE) [M x N], row stride ldc >= N (elements).
+ */
+int fgs_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
+                          int64_t M, int64_t N, int64_t K,
+                          void *C, int64_t ldc, int out_dtype, void *stream);
+
+/*
+ * fgs_grouped_gemm_block_scaled -- MoE expert GEMMs: for each group g,
+ *   rows group_offsets[g] .. group_offsets[g+1]-1 of A times B_g^T.
+ *   [DSV3] "Mixed precision framework" (expert GEMMs in FP8, gating kept in
+ *   higher precision and outside this call).
+ * A: total_M x K, E4M3 TILE_1x128 (scales [K/128][total_M]).
+ * B: G x N x K E4M3 codes (group g at g*N*ld), BLOCK_128x128 scales
+ *   [G][ceil(N/128)][K/128] (group g at g*ceil(N/128)*(K/128)).
+ * group_offsets: DEVICE int32 [G+1], non-decreasing, offsets[0] = 0,
+ *   offsets[G] = total_M.  Read on the device (no host synchronisation);
+ *   offsets outside [0, total_M] make the affected groups write nothing.
+ * C: [total_M x N] FP32 or BF16.  Rows not covered by any group are not written.
+ */
+int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
+                                  const int32_t *group_offsets, int32_t G,
+                                  int64_t total_M, int64_t N, int64_t K,
+                                  void *C, int64_t ldc, int out_dtype, void *stream);
+
+/* Device workspace needed by TENSOR-mode and NVFP4 quantization (bytes). */
+size_t fgs_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Message for the last error on this thread ("" if none); never NULL. */
+const char *fgs_last_error(void);
+
+/* Library version string. */
+const char *fgs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGS_H */

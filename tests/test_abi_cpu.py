@@ -1,0 +1,126 @@
+"""The C ABI library loads, exports every entry point declared in
+include/fgs.h, and rejects invalid arguments with the documented status
+codes before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fine_grained_scaled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fgs.h")).read()
+    return sorted(set(re.findall(r"\b(fgs_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from fine_grained_scaled_amd import _build
+        _build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_workspace(lib):
+    assert b"gfx950" in lib.fgs_version()
+    assert lib.fgs_workspace_bytes(8192, 4096) >= 8
+    assert lib.fgs_last_error() is not None
+
+
+# Fake, 16-byte aligned, never-dereferenced addresses: every call below must
+# be rejected by validation, which happens before any HIP call.
+FAKE = ctypes.c_void_p(0x10000)
+NULL = ctypes.c_void_p(0)
+
+
+def _q(lib, *a):
+    return lib.fgs_quantize_blockwise(*a)
+
+
+def test_quantize_blockwise_validation(lib):
+    S = ctypes.c_void_p(0)
+    assert _q(lib, FAKE, 128, 128, 128, 7, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert b"mode" in lib.fgs_last_error()
+    assert _q(lib, FAKE, -1, 128, 128, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert _q(lib, NULL, 128, 128, 128, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert _q(lib, FAKE, 128, 128, 64, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert _q(lib, FAKE, 128, 100, 104, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert _q(lib, FAKE, 128, 192, 192, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert b"128" in lib.fgs_last_error()
+    assert _q(lib, FAKE, 100, 128, 128, 1, NULL, NULL, FAKE, FAKE, NULL, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert _q(lib, FAKE, 128, 128, 128, 1, FAKE, NULL, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert _q(lib, FAKE, 128, 128, 128, 0, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert b"workspace" in lib.fgs_last_error()
+    assert _q(lib, ctypes.c_void_p(0x10008), 128, 128, 128, 1, FAKE, FAKE, NULL, NULL, NULL, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    # empty inputs are a no-op success
+    assert _q(lib, NULL, 0, 128, 128, 1, NULL, NULL, NULL, NULL, NULL, 0, S) == _lib.FGS_OK
+
+
+def test_quantize_mx_nvfp4_validation(lib):
+    S = NULL
+    assert lib.fgs_quantize_mx(FAKE, 128, 48, 48, FAKE, FAKE, NULL, NULL, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert lib.fgs_quantize_mx(FAKE, 64, 128, 128, NULL, NULL, FAKE, FAKE, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert lib.fgs_quantize_mx(FAKE, 128, 128, 128, FAKE, NULL, NULL, NULL, S) == _lib.FGS_ERR_INVALID_ARG
+    args = [FAKE, 128, 128, 128, 4, 0, 0, 0, FAKE, FAKE, NULL, NULL, FAKE, FAKE, 256, S]
+    assert lib.fgs_quantize_nvfp4(*args) == _lib.FGS_ERR_INVALID_ARG          # rht_mask 4
+    args[4] = 1
+    args[6] = 2
+    assert lib.fgs_quantize_nvfp4(*args) == _lib.FGS_ERR_INVALID_ARG          # round 2
+    args[6] = 1
+    args[12] = NULL
+    assert lib.fgs_quantize_nvfp4(*args) == _lib.FGS_ERR_INVALID_ARG          # no tensor_scale
+    args[12] = FAKE
+    args[14] = 4
+    assert lib.fgs_quantize_nvfp4(*args) == _lib.FGS_ERR_INVALID_ARG          # workspace too small
+
+
+def _op(data=FAKE, ld=256, elem=0, mode=1, scales=FAKE, ts=NULL):
+    return _lib.FgsOperand(data.value or 0, ld, elem, mode, scales.value or 0, ts.value or 0)
+
+
+def test_gemm_validation(lib):
+    S = NULL
+    g = lib.fgs_gemm_block_scaled
+    a, b = _op(mode=1), _op(mode=2)
+    r = ctypes.byref
+    assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # K % 128
+    assert g(r(a), r(b), -1, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 64, 0, S) == _lib.FGS_ERR_INVALID_ARG       # ldc < N
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 5, S) == _lib.FGS_ERR_INVALID_ARG      # out dtype
+    assert g(r(a), r(b), 128, 128, 256, NULL, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG      # C NULL
+    a2 = _op(ld=100)
+    assert g(r(a2), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG     # ld < K
+    a3 = _op(ld=264)
+    assert g(r(a3), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED     # ld % 16
+    a4 = _op(mode=2)
+    assert g(r(a4), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED     # A block
+    a5 = _op(mode=3)
+    assert g(r(a5), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED     # mixed MX/FP32
+    an, bn = _op(elem=1, mode=4), _op(elem=1, mode=4)
+    assert g(r(an), r(bn), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG    # no tensor scale
+    a6 = _op(scales=NULL)
+    assert g(r(a6), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 0, 128, 256, NULL, 128, 0, S) == _lib.FGS_OK                     # empty
+
+
+def test_grouped_validation(lib):
+    S = NULL
+    g = lib.fgs_grouped_gemm_block_scaled
+    a, b = _op(mode=1), _op(mode=2)
+    r = ctypes.byref
+    assert g(r(a), r(b), FAKE, -1, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), NULL, 4, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    bt = _op(mode=0)
+    assert g(r(a), r(bt), FAKE, 4, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a), r(b), FAKE, 0, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_OK          # no groups

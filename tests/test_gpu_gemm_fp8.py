@@ -1,0 +1,211 @@
+"""GPU parity of the block-scaled FP8 GEMM and its grouped (MoE) variant
+against the oracle's FP64 product of the dequantized operands:
+|C - C_ref| <= 1e-5 * sum_k |a_k b_k| + 1e-6 (FP32 out), within one BF16 ulp
+of the rounded reference (BF16 out).
+
+"Can you explain the role of FP8 precision in DeepSeek-V3 training",
+sections "Mixed precision framework", "Fine-grained quantization",
+"Increasing accumulation precision".  Operands are quantized by the oracle
+and uploaded, so this isolates the GEMM from the quantization kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fine_grained_scaled_amd import synth
+
+from _helpers import gemm_within_bf16_bound, gemm_within_fp32_bound, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+MODE_CODE = {"tensor": 0, "tile": 1, "block": 2}
+
+
+@pytest.fixture(scope="module")
+def fgs():
+    import fine_grained_scaled_amd as m
+    return m
+
+
+def oracle_operand(fgs, bits, mode, colwise=False, rows_for_ref=None):
+    """Quantize with the oracle; return (GPU Operand, dequantized FP64 rows)."""
+    q, s = oracle.quant_e4m3(bits, mode, colwise=colwise)
+    if mode == "tile":
+        s_abi = np.ascontiguousarray(s.T)
+    elif mode == "block":
+        s_abi = s
+    else:
+        s_abi = s.reshape(1)
+    if rows_for_ref is None:
+        deq = oracle.dequant_e4m3(q, s, mode)
+    else:
+        qr = q[rows_for_ref]
+        if mode == "tile":
+            deq = oracle.dequant_e4m3(qr, s[rows_for_ref], mode)
+        elif mode == "tensor":
+            deq = oracle.dequant_e4m3(qr, s, mode)
+        else:
+            full = oracle.dequant_e4m3(q, s, mode)
+            deq = full[rows_for_ref]
+    op = fgs.Operand(torch.from_numpy(q).cuda(), torch.from_numpy(np.ascontiguousarray(s_abi)).cuda(),
+                     MODE_CODE[mode])
+    return op, deq
+
+
+def _run_and_check(fgs, A, B, a_hat, b_hat, out_dtype, rows=None):
+    c = fgs.gemm_block_scaled(A, B, out_dtype)
+    torch.cuda.synchronize()
+    c = c.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        c = c[rows]
+    cref, sref = oracle.gemm_ref(a_hat, b_hat)
+    if out_dtype == torch.float32:
+        ok, worst = gemm_within_fp32_bound(c, cref, sref)
+        assert ok, f"worst err/bound = {worst}"
+    else:
+        ok, nbad = gemm_within_bf16_bound(c, cref, sref)
+        assert ok, f"{nbad} BF16 outputs outside one ulp"
+
+
+def test_tiny_blockwise_fp32(fgs):
+    """128x256 A ~ N(0,1), 256x256 B ~ N(0,0.02), seed 0; A in 1x128 tiles,
+    B in 128x128 blocks; C = A B^T in FP32."""
+    a_bits = synth.activations(128, 256, seed=0)
+    b_bits = synth.weights(256, 256, seed=0)
+    A, ah = oracle_operand(fgs, a_bits, "tile")
+    B, bh = oracle_operand(fgs, b_bits, "block")
+    _run_and_check(fgs, A, B, ah, bh, torch.float32)
+
+
+MODES = [("tile", "block"), ("tile", "tile"), ("tensor", "tensor"), ("tile", "tensor"),
+         ("tensor", "block"), ("tensor", "tile")]
+
+
+@pytest.mark.parametrize("amode,bmode", MODES)
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (128, 384, 1024)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_modes_ragged(fgs, amode, bmode, M, N, K, out):
+    a_bits = synth.activations(M, K, seed=M + K)
+    b_bits = synth.weights(N, K, seed=N + K)
+    A, ah = oracle_operand(fgs, a_bits, amode)
+    B, bh = oracle_operand(fgs, b_bits, bmode)
+    _run_and_check(fgs, A, B, ah, bh, out)
+
+
+def test_gemm_row_stride_and_ldc(fgs):
+    """Operand row stride larger than K and an output with ldc > N."""
+    M, N, K = 192, 160, 256
+    a_bits = synth.activations(M, K, seed=1)
+    b_bits = synth.weights(N, K, seed=2)
+    A, ah = oracle_operand(fgs, a_bits, "tile")
+    B, bh = oracle_operand(fgs, b_bits, "block")
+    wide = torch.zeros((M, K + 128), dtype=torch.uint8, device="cuda")
+    wide[:, :K] = A.data
+    A2 = fgs.Operand(wide, A.scales, A.scale_mode)
+    assert A2.c_struct().ld == K + 128
+    out = torch.full((M, N + 40), 7.0, dtype=torch.float32, device="cuda")
+    fgs.gemm_block_scaled(A2, B, torch.float32, out=out[:, :N], K=K)
+    torch.cuda.synchronize()
+    c = out.cpu().numpy().astype(np.float64)
+    cref, sref = oracle.gemm_ref(ah, bh)
+    ok, worst = gemm_within_fp32_bound(c[:, :N], cref, sref)
+    assert ok, worst
+    assert np.all(c[:, N:] == 7.0)
+
+
+def test_gemm_adversarial_promotion(fgs):
+    """Each 128-K block of A has its own scale spanning 2^-20 .. 2^20, so an
+    accumulator without per-block FP32 promotion of the scale would fail."""
+    M, N, K = 128, 128, 1024
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=7, outliers=False)).copy()
+    for kb in range(K // 128):
+        a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
+    a_bits = synth.f32_to_bf16_bits(a)
+    b_bits = synth.weights(N, K, seed=8)
+    A, ah = oracle_operand(fgs, a_bits, "tile")
+    B, bh = oracle_operand(fgs, b_bits, "block")
+    _run_and_check(fgs, A, B, ah, bh, torch.float32)
+
+
+def test_gemm_determinism(fgs):
+    a_bits = synth.activations(512, 1024, seed=3)
+    b_bits = synth.weights(768, 1024, seed=4)
+    A, _ = oracle_operand(fgs, a_bits, "tile")
+    B, _ = oracle_operand(fgs, b_bits, "block")
+    c1 = fgs.gemm_block_scaled(A, B)
+    c2 = fgs.gemm_block_scaled(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+# ------------------------------------------------------------------ grouped --
+def _grouped_case(fgs, counts, N, K, out=torch.float32, seed=0):
+    counts = np.asarray(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(offs[-1])
+    G = len(counts)
+    a_bits = synth.activations(total, K, seed=seed)
+    A, ah = oracle_operand(fgs, a_bits, "tile")
+    qs, ss, bhs = [], [], []
+    for g in range(G):
+        wb = synth.weights(N, K, seed=seed + 100 + g)
+        q, s = oracle.quant_e4m3(wb, "block")
+        qs.append(q)
+        ss.append(s)
+        bhs.append(oracle.dequant_e4m3(q, s, "block"))
+    B = fgs.Operand(torch.from_numpy(np.concatenate(qs)).cuda(),
+                    torch.from_numpy(np.concatenate([s[None] for s in ss])).cuda(), 2)
+    off_t = torch.from_numpy(offs).cuda()
+    c = torch.full((total, N), 3.0, dtype=out, device="cuda")
+    fgs.grouped_gemm_block_scaled(A, B, off_t, N, out_dtype=out, out=c)
+    torch.cuda.synchronize()
+    c = c.float().cpu().numpy().astype(np.float64)
+    cref, sref = oracle.grouped_gemm_ref(ah, bhs, offs)
+    if out == torch.float32:
+        ok, worst = gemm_within_fp32_bound(c, cref, sref)
+        assert ok, worst
+    else:
+        ok, nbad = gemm_within_bf16_bound(c, cref, sref)
+        assert ok, nbad
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_grouped_ragged_and_empty(fgs, out):
+    _grouped_case(fgs, [0, 1, 130, 0, 257, 128, 3], N=256, K=384, out=out)
+
+
+def test_grouped_single_group_equals_dense(fgs):
+    _grouped_case(fgs, [300], N=200, K=256)
+
+
+def test_grouped_many_groups(fgs):
+    """300 groups (more than one 256-wide scan chunk), Zipf-like counts."""
+    counts = synth.expert_counts(tokens=4000, experts=300, seed=1)
+    _grouped_case(fgs, counts, N=128, K=128, seed=5)
+
+
+# ------------------------------------------------------- full-size layer --
+@pytest.mark.parametrize("orient", ["fwd", "dgrad", "wgrad"])
+def test_llama8b_qkv_layer_sampled(fgs, orient):
+    """Llama-3-8B QKV projection (K, N) = (4096, 6144), M = 8192 tokens,
+    1x128 x 128x128 blockwise; sampled rows against the oracle."""
+    M, K, N = 8192, 4096, 6144
+    if orient == "fwd":
+        a_bits = synth.activations(M, K, seed=0)
+        b_bits = synth.weights(N, K, seed=0)
+        a_mode, b_mode, a_col, b_col = "tile", "block", False, False
+    elif orient == "dgrad":
+        a_bits = synth.gradients(M, N, seed=0)          # dY [M x N], contraction over N
+        b_bits = synth.weights(N, K, seed=0)            # W^T codes [K x N]
+        a_mode, b_mode, a_col, b_col = "tile", "block", False, True
+    else:
+        a_bits = synth.gradients(M, N, seed=0)          # dY^T [N x M], contraction over M
+        b_bits = synth.activations(M, K, seed=0)        # X^T  [K x M]
+        a_mode, b_mode, a_col, b_col = "tile", "tile", True, True
+    rows_total = a_bits.shape[1] if a_col else a_bits.shape[0]
+    rs = sample_rows(rows_total)
+    A, ah = oracle_operand(fgs, a_bits, a_mode, colwise=a_col, rows_for_ref=rs)
+    B, bh = oracle_operand(fgs, b_bits, b_mode, colwise=b_col)
+    out = torch.float32 if orient == "wgrad" else torch.bfloat16
+    _run_and_check(fgs, A, B, ah, bh, out, rows=rs)
