@@ -1,26 +1,40 @@
 // gemm_fp8.hip -- block-scaled FP8 (E4M3) GEMM and its grouped (MoE)
-// variant on gfx950 MFMA.
+// variant on gfx950.
 //
 // "Can you explain the role of FP8 precision in DeepSeek-V3 training":
-// section "Mixed precision framework" (the GEMMs run in FP8), "Fine-grained
-// quantization" (1x128 activation tiles x 128x128 weight blocks) and
-// "Increasing accumulation precision" (partial sums are promoted to FP32
-// registers at fixed intervals).  Here the interval is one 128-deep K block,
-// the scale block: the MFMA unit accumulates the 128-deep partial product
-// P = sum_{k in block} qa*qb in FP32, and the kernel adds
-// sA[m, kb] * sB[n, kb] * P into a separate FP32 accumulator.  With a single
-// per-tensor scale on both operands ("Accelerating FP8 training performance
-// with the NVIDIA NeMo framework", per-tensor recipe) no per-block factor
-// exists: the MFMA accumulates all of K in FP32 and the product of the two
-// scales is applied once at the end.
+// section "Mixed precision framework" (the GEMMs run on FP8 operands),
+// "Fine-grained quantization" (1x128 activation tiles x 128x128 weight
+// blocks) and "Increasing accumulation precision" (the matrix unit's own
+// accumulation is limited, so partial sums are promoted to FP32 registers
+// at fixed intervals).  Here the interval is one 128-deep K block, the scale
+// block: the matrix unit forms P = sum_{k in block} qa*qb in FP32, and the
+// kernel adds sA[m, kb] * sB[n, kb] * P into a separate FP32 accumulator.
+// With a single per-tensor scale on both operands ("Accelerating FP8
+// training performance with the NVIDIA NeMo framework", per-tensor recipe)
+// no per-block factor exists: all of K accumulates in FP32 and the product
+// of the two scales is applied once at the end.
+//
+// Which matrix instruction: gfx950's FP8 MFMA (v_mfma_*_f8f6f4 and the older
+// *_fp8_fp8 forms) adds each group of 8 consecutive products with only about
+// 13 bits below the largest of them (measured: 256 + 2^-5 survives, 256 +
+// 2^-6 does not, and +x - x + tiny gives 0), the same limitation the DeepSeek
+// page describes for its hardware, but *inside* one instruction, where no
+// promotion interval can reach it.  Its error reaches ~1.5e-4 of
+// sum_k |a_k b_k|.  The FP16 MFMA (v_mfma_f32_32x32x16_f16) keeps a full
+// FP32-width sum (256 + 2^-15 survives).  Every E4M3 value is exactly an
+// FP16 value and every product of two is exact in FP32, so the kernel
+// decodes the E4M3 codes to FP16 with the hardware converter
+// (v_cvt_scalef32_pk_f16_fp8, unit scale: exact for all 256 codes) and runs
+// the FP16 MFMA: the result is the FP32 sum of exact products, promoted per
+// 128-K block.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]; both operands K-contiguous.
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid, 128 x 128 output tile,
-// each wave 64 x 64 = 2 x 2 MFMA 32x32x64 sub-tiles.  K advances in 128-deep
-// blocks staged in LDS (double-buffered, rows padded to 144 bytes so the
-// MFMA operand reads are bank-conflict free).  MFMA operands are swapped
-// (B fragment first) so each lane's 16 accumulators share one row m: the
-// 1x128 A scale is then one value per lane.
+// each wave 64 x 64 = 2 x 2 MFMA 32x32x16 sub-tiles.  K advances in 128-deep
+// blocks staged in LDS as FP8 bytes (double-buffered, rows padded to 144
+// bytes so the 16-byte fragment reads are bank-conflict free).  MFMA
+// operands are swapped (B fragment first) so each lane's 16 accumulators
+// share one row m: the 1x128 A scale is then one value per lane.
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -28,7 +42,8 @@ namespace fgs {
 
 namespace {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
@@ -52,20 +67,27 @@ struct GemmParams {
     int32_t tiles_m, tiles_n;
 };
 
-// E4M3 x E4M3 MFMA, 32x32 outputs, 64-deep K, FP32 accumulate (unit scales).
-__device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, const f32x16& c)
+// FP16 x FP16 MFMA, 32x32 outputs, 16-deep K, FP32 accumulate.
+__device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x8 lds_frag(const uint8_t* p)
+// 16 E4M3 codes (one 16-byte LDS read) -> two exact FP16 8-vectors: bytes
+// 0..7 feed one MFMA k-step, bytes 8..15 the next.
+__device__ __forceinline__ void decode16(const uint8_t* p, f16x8& lo, f16x8& hi)
 {
-    uint4 lo = *reinterpret_cast<const uint4*>(p);
-    uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-    i32x8 f;
-    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-    return f;
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, true);
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, false);
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, true);
+    const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.z, 1.0f, false);
+    const f16x2 f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.z, 1.0f, true);
+    const f16x2 g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.w, 1.0f, false);
+    const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.w, 1.0f, true);
+    lo = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    hi = f16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
@@ -217,34 +239,39 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
         if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_blk = sBp[(n0 / BN) * nkb + kb];
 
         f32x16 part[2][2];
+        if constexpr (PROMOTE) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+        }
         const uint8_t* la = &lds[cur][0][0];
         const uint8_t* lb = &lds[cur][1][0];
+        // lane half h reads bytes 32*ks + 16*h .. +15 of its row: the pair of
+        // k-steps (2ks, 2ks+1) then covers k = 32*ks .. 32*ks+31 once, with
+        // the same k order for A and B
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            i32x8 af[2], bf[2];
+        for (int ks = 0; ks < 4; ++ks) {
+            f16x8 af[2][2], bf[2][2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[i] = lds_frag(la + (64 * wm + 32 * i + (l & 31)) * LDS_STRIDE + 64 * kk + 32 * (l >> 5));
+                decode16(la + (64 * wm + 32 * i + (l & 31)) * LDS_STRIDE + 32 * ks + 16 * (l >> 5), af[i][0], af[i][1]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bf[j] = lds_frag(lb + (64 * wn + 32 * j + (l & 31)) * LDS_STRIDE + 64 * kk + 32 * (l >> 5));
+                decode16(lb + (64 * wn + 32 * j + (l & 31)) * LDS_STRIDE + 32 * ks + 16 * (l >> 5), bf[j][0], bf[j][1]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if constexpr (PROMOTE) {
-                        if (kk == 0) {
-                            f32x16 z;
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) z[r] = 0.0f;
-                            part[i][j] = mfma_e4m3(bf[j], af[i], z);
-                        } else {
-                            part[i][j] = mfma_e4m3(bf[j], af[i], part[i][j]);
-                        }
-                    } else {
-                        acc[i][j] = mfma_e4m3(bf[j], af[i], acc[i][j]);
+                    for (int j = 0; j < 2; ++j) {
+                        if constexpr (PROMOTE)
+                            part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+                        else
+                            acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
                     }
-                }
         }
 
         if constexpr (PROMOTE) {
