@@ -29,12 +29,19 @@
 // 128-K block.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]; both operands K-contiguous.
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, 128 x 128 output tile,
-// each wave 64 x 64 = 2 x 2 MFMA 32x32x16 sub-tiles.  K advances in 128-deep
-// blocks staged in LDS as FP8 bytes (double-buffered, rows padded to 144
-// bytes so the 16-byte fragment reads are bank-conflict free).  MFMA
-// operands are swapped (B fragment first) so each lane's 16 accumulators
-// share one row m: the 1x128 A scale is then one value per lane.
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; output tile
+// (2*WM) x 128 with WM = 128 (dense) or 64 (grouped: MoE groups are short).
+// Each wave owns WM x 64 = (WM/32) x 2 MFMA 32x32x16 sub-tiles.  K advances
+// in 128-deep blocks staged in LDS as FP8 bytes, double-buffered, by direct
+// global->LDS loads (global_load_lds_dwordx4: lane i of a wave-instruction
+// fills bytes 16i..16i+15 of a 1 KiB LDS span, i.e. 8 rows of 128 bytes), so
+// the next block streams in while the current one is multiplied without
+// passing through registers.  The 16-byte chunk c of row r sits in LDS slot
+// c ^ (r & 7): the lane that fills slot s of row r fetches chunk s ^ (r & 7),
+// and the fragment reads (8 consecutive rows, same chunk) hit 8 distinct
+// slots, i.e. all 32 banks once.  MFMA operands are swapped (B fragment
+// first) so each lane's 16 accumulators share one row m: the 1x128 A scale
+// is one value per lane and per sub-tile row.
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -46,9 +53,25 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE = BK + 16;
-constexpr int TILE_BYTES = 128 * LDS_STRIDE;
+constexpr int BN = 128, BK = 128;
+constexpr int ROW = BK;                   // LDS bytes per staged row (swizzled, unpadded)
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef const __attribute__((address_space(1))) void* gbl_ptr;
+
+// one 16-byte global->LDS load per lane; dst is the wave's 1 KiB span base
+__device__ __forceinline__ void g2lds16(const void* src, void* dst_wave_base)
+{
+    __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)dst_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* src, void* dst_wave_base)
+{
+    __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)dst_wave_base, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_lds_dma()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 struct GemmParams {
     const uint8_t* A;
@@ -56,8 +79,6 @@ struct GemmParams {
     const float* sA;
     const float* sB;
     int64_t lda, ldb, M, N, K;
-    int64_t lds_a;        // TILE scales of A: stride between K blocks (= rows of A)
-    int64_t lds_b;        // TILE scales of B: stride between K blocks (= rows of B)
     void* C;
     int64_t ldc;
     const int32_t* offsets;
@@ -75,9 +96,8 @@ __device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f
 
 // 16 E4M3 codes (one 16-byte LDS read) -> two exact FP16 8-vectors: bytes
 // 0..7 feed one MFMA k-step, bytes 8..15 the next.
-__device__ __forceinline__ void decode16(const uint8_t* p, f16x8& lo, f16x8& hi)
+__device__ __forceinline__ void decode16(const uint4 v, f16x8& lo, f16x8& hi)
 {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
     const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, false);
     const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, true);
     const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, false);
@@ -97,10 +117,25 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
+template <int WM>
+struct Lds {
+    static constexpr int BM = 2 * WM;
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int B_BYTES = BN * ROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES + BN * 4;   // + B 1x128 scales of the block
+};
+
+template <int WM, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
 {
-    __shared__ __align__(16) uint8_t lds[2][2][TILE_BYTES];   // [stage][A|B]
+    constexpr int BM = 2 * WM;
+    constexpr int TI = WM / 32;          // sub-tiles along m per wave
+    constexpr int TJ = 2;                // sub-tiles along n per wave
+    constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR);
+    constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
+    using L = Lds<WM>;
+
+    extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[256];
     __shared__ int s_sel[2];
 
@@ -114,7 +149,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     if constexpr (!GROUPED) {
         int id = blockIdx.x;
         const int T = p.tiles_m * p.tiles_n;
-        if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);   // contiguous range per XCD
+        // workgroups are dealt round-robin to the 8 XCDs: give each XCD a
+        // contiguous range of the tile order so its L2 sees neighbouring tiles
+        if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
         const int GM = 8;
         const int group = id / (GM * p.tiles_n);
         const int first_m = group * GM;
@@ -134,16 +171,14 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
         for (int chunk = 0; chunk < p.G; chunk += 256) {
             const int g = chunk + t;
             int cnt = 0;
-            int32_t o0 = 0, o1 = 0;
             if (g < p.G) {
-                o0 = p.offsets[g];
-                o1 = p.offsets[g + 1];
+                const int32_t o0 = p.offsets[g], o1 = p.offsets[g + 1];
                 if (o0 >= 0 && o1 >= o0 && o1 <= p.M) cnt = (o1 - o0 + BM - 1) / BM;
             }
             s_scan[t] = cnt;
             __syncthreads();
             for (int d = 1; d < 256; d <<= 1) {
-                int add = (t >= d) ? s_scan[t - d] : 0;
+                const int add = (t >= d) ? s_scan[t - d] : 0;
                 __syncthreads();
                 s_scan[t] += add;
                 __syncthreads();
@@ -171,102 +206,124 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     }
 
     // ------------------------------------------------------- loaders --
-    const int lrow = t >> 3, lchunk = t & 7;   // 32 rows x 8 chunks of 16 B per pass
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
+    // wave w stages rows [BM/4 * w, BM/4 * (w+1)) of A and [32w, 32w+32) of
+    // B, 8 rows per wave-instruction; lane l fills slot l & 7 of row l >> 3
+    // with chunk (l & 7) ^ (l >> 3).  Rows past the end are clamped (their
+    // products land in rows/columns that are never stored).
+    constexpr int A_INSTR = BM / 32, B_INSTR = BN / 32;
+    const int srow = l >> 3, schunk = (l & 7) ^ srow;
+    const uint8_t* a_src[A_INSTR];
+    const uint8_t* b_src[B_INSTR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t ar = m0 + 32 * i + lrow;
-        ar = ar < m_end ? ar : m_end - 1;
-        int64_t br = n0 + 32 * i + lrow;
-        br = br < p.N ? br : p.N - 1;
-        a_src[i] = p.A + ar * p.lda + 16 * lchunk;
-        b_src[i] = Bp + br * p.ldb + 16 * lchunk;
+    for (int u = 0; u < A_INSTR; ++u) {
+        int64_t r = m0 + (BM / 4) * w + 8 * u + srow;
+        r = r < m_end ? r : m_end - 1;
+        a_src[u] = p.A + r * p.lda + 16 * schunk;
     }
-    uint4 ra[4], rb[4];
-    auto load_tiles = [&](int kb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + (int64_t)kb * BK);
-            rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + (int64_t)kb * BK);
-        }
-    };
-    auto store_tiles = [&](int stage) {
+    for (int u = 0; u < B_INSTR; ++u) {
+        int64_t r = n0 + 32 * w + 8 * u + srow;
+        r = r < p.N ? r : p.N - 1;
+        b_src[u] = Bp + r * p.ldb + 16 * schunk;
+    }
+    int64_t sb_col = n0 + 64 * (w & 1) + l;        // B 1x128 scales: waves 0 and 1 stage 64 each
+    sb_col = sb_col < p.N ? sb_col : p.N - 1;
+
+    auto stage_block = [&](int64_t kb, int stage) {
+        uint8_t* st = smem + stage * L::STAGE;
+        const int64_t ko = kb * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint4*>(&lds[stage][0][(32 * i + lrow) * LDS_STRIDE + 16 * lchunk]) = ra[i];
-            *reinterpret_cast<uint4*>(&lds[stage][1][(32 * i + lrow) * LDS_STRIDE + 16 * lchunk]) = rb[i];
-        }
+        for (int u = 0; u < A_INSTR; ++u)
+            g2lds16(a_src[u] + ko, st + ((BM / 4) * w + 8 * u) * ROW);
+#pragma unroll
+        for (int u = 0; u < B_INSTR; ++u)
+            g2lds16(b_src[u] + ko, st + L::A_BYTES + (32 * w + 8 * u) * ROW);
+        if constexpr (B_TILE)
+            if (w < 2) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
     };
 
-    // ------------------------------------------------------- scales ---
-    // rows of this lane's accumulators: m = m0 + 64*wm + 32*i + (l & 31)
-    int64_t am[2];
+    // rows of this lane's accumulators: m = m0 + WM*wm + 32*i + (l & 31)
+    int64_t am[TI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int64_t m = m0 + 64 * wm + 32 * i + (l & 31);
+    for (int i = 0; i < TI; ++i) {
+        const int64_t m = m0 + WM * wm + 32 * i + (l & 31);
         am[i] = m < m_end ? m : m_end - 1;
     }
-    // columns of this lane's accumulators: n = nl + 32*j + 8*q + e
-    const int64_t nl = n0 + 64 * wn + 4 * (l >> 5);
     const int64_t nkb = p.K / BK;
 
-    f32x16 acc[2][2];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR);
-
-    load_tiles(0);
-    store_tiles(0);
+    // prologue: block 0 -> stage 0
+    stage_block(0, 0);
+    float sa_next[TI];
+    if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[am[i]];
+    }
+    float sb_next = 0.0f;
+    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb];
+    wait_lds_dma();
     __syncthreads();
+
+    // fragment read offsets: row R = base + (l & 31) has R & 7 == l & 7;
+    // chunk 2*ks + h (h = lane half) lives in slot (2*ks + h) ^ (l & 7)
+    const int swz = l & 7, half = l >> 5;
 
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int cur = (int)(kb & 1);
-        if (kb + 1 < nkb) load_tiles((int)kb + 1);
-
-        // scales of this K block
-        float sa[2] = {1.0f, 1.0f};
-        if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
+        const bool more = kb + 1 < nkb;
+        // scales of this block (prefetched one block ahead)
+        float sa[TI];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) sa[i] = p.sA[kb * p.lds_a + am[i]];
+        for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 ? sa_next[i] : 1.0f;
+        const float sb_blk = sb_next;
+        if (more) {
+            stage_block(kb + 1, cur ^ 1);
+            if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
+#pragma unroll
+                for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
+            }
+            if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb + kb + 1];
         }
-        float sb_blk = 1.0f;
-        if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_blk = sBp[(n0 / BN) * nkb + kb];
 
-        f32x16 part[2][2];
+        const uint8_t* st = smem + cur * L::STAGE;
+        const uint8_t* la = st + (WM * wm + (l & 31)) * ROW;
+        const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
+
+        f32x16 part[TI][TJ];
         if constexpr (PROMOTE) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < TJ; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
         }
-        const uint8_t* la = &lds[cur][0][0];
-        const uint8_t* lb = &lds[cur][1][0];
-        // lane half h reads bytes 32*ks + 16*h .. +15 of its row: the pair of
-        // k-steps (2ks, 2ks+1) then covers k = 32*ks .. 32*ks+31 once, with
-        // the same k order for A and B
+        // lane half h reads chunk 2*ks + h (bytes 32*ks + 16*h .. +15) of its
+        // row: the pair of k-steps (2ks, 2ks+1) then covers k = 32*ks ..
+        // 32*ks+31 once, with the same k order for A and B
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            f16x8 af[2][2], bf[2][2];
+            const int co = ((2 * ks + half) ^ swz) << 4;
+            f16x8 af[TI][2], bf[TJ][2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                decode16(la + (64 * wm + 32 * i + (l & 31)) * LDS_STRIDE + 32 * ks + 16 * (l >> 5), af[i][0], af[i][1]);
+            for (int j = 0; j < TJ; ++j)
+                decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                decode16(lb + (64 * wn + 32 * j + (l & 31)) * LDS_STRIDE + 32 * ks + 16 * (l >> 5), bf[j][0], bf[j][1]);
+            for (int i = 0; i < TI; ++i)
+                decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < TI; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
+                    for (int j = 0; j < TJ; ++j) {
                         if constexpr (PROMOTE)
                             part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
                         else
@@ -275,55 +332,60 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
         }
 
         if constexpr (PROMOTE) {
-            float sa_t = 1.0f, sb_t = 1.0f;
-            if constexpr (AMODE == FGS_SCALE_TENSOR) sa_t = p.sA[0];
-            if constexpr (BMODE == FGS_SCALE_TENSOR) sb_t = sBp[0];
+            const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
+            const float sb_t = BMODE == FGS_SCALE_TENSOR ? sBp[0] : 1.0f;
+            if constexpr (B_TILE) {
+                // columns of this lane's accumulators: n = 64*wn + 32*j + 8*q + 4*(l>>5) + e
+                const float* ssb = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float fa = (AMODE == FGS_SCALE_TENSOR) ? sa_t : sa[i];
+                for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if constexpr (BMODE == FGS_SCALE_TILE_1x128) {
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 s4 = *reinterpret_cast<const float4*>(ssb + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5));
+                        const float sbv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
+                        for (int i = 0; i < TI; ++i) {
+                            const float fa = AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                int64_t n = nl + 32 * j + 8 * q + e;
-                                n = n < p.N ? n : p.N - 1;
-                                const float f = fa * sBp[kb * p.lds_b + n];
-                                acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], f, acc[i][j][4 * q + e]);
-                            }
-                    } else {
-                        const float f = fa * ((BMODE == FGS_SCALE_TENSOR) ? sb_t : sb_blk);
+                            for (int e = 0; e < 4; ++e)
+                                acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], fa * sbv[e], acc[i][j][4 * q + e]);
+                        }
+                    }
+            } else {
+                const float fb = BMODE == FGS_SCALE_TENSOR ? sb_t : sb_blk;
+#pragma unroll
+                for (int i = 0; i < TI; ++i) {
+                    const float f = (AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i]) * fb;
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             acc[i][j][r] = __builtin_fmaf(part[i][j][r], f, acc[i][j][r]);
-                    }
                 }
             }
         }
 
-        if (kb + 1 < nkb) store_tiles(cur ^ 1);
+        wait_lds_dma();
         __syncthreads();
     }
 
     if constexpr (!PROMOTE) {
         const float f = p.sA[0] * sBp[0];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
     }
 
     // ------------------------------------------------------ epilogue --
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t m = m0 + 64 * wm + 32 * i + (l & 31);
+    for (int i = 0; i < TI; ++i) {
+        const int64_t m = m0 + WM * wm + 32 * i + (l & 31);
         if (m >= m_end) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
@@ -354,30 +416,33 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     }
 }
 
-template <int AMODE, int BMODE, bool GROUPED>
+template <int WM, int AMODE, int BMODE, bool GROUPED>
 hipError_t launch_modes(const GemmParams& p, bool bf16, dim3 grid, hipStream_t s)
 {
-    if (bf16)
-        hipLaunchKernelGGL((gemm_fp8_kernel<AMODE, BMODE, true, GROUPED>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((gemm_fp8_kernel<AMODE, BMODE, false, GROUPED>), grid, dim3(256), 0, s, p);
+    const size_t lds = 2 * (size_t)Lds<WM>::STAGE;
+    auto k = bf16 ? gemm_fp8_kernel<WM, AMODE, BMODE, true, GROUPED>
+                  : gemm_fp8_kernel<WM, AMODE, BMODE, false, GROUPED>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 
-template <bool GROUPED>
+template <int WM, bool GROUPED>
 hipError_t dispatch(const GemmParams& p, int amode, int bmode, bool bf16, dim3 grid, hipStream_t s)
 {
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUPED>(p, bf16, grid, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUPED>(p, bf16, grid, s);
         if constexpr (!GROUPED) {
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TENSOR) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
         }
     } else if constexpr (!GROUPED) {
         if (amode == FGS_SCALE_TENSOR) {
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TENSOR) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
         }
     }
     return hipErrorInvalidValue;
@@ -397,8 +462,6 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
-    p.lds_a = a.M;
-    p.lds_b = a.N;
     p.C = a.C;
     p.ldc = a.ldc;
     p.offsets = a.group_offsets;
@@ -406,16 +469,18 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.tiles_n = (int32_t)((a.N + BN - 1) / BN);
     if (a.M == 0 || a.N == 0) return hipSuccess;
     if (a.group_offsets) {
+        constexpr int WM = 64, BM = 2 * WM;
         p.b_group_stride = a.N * a.B.ld;
         p.sb_group_stride = ((a.N + BN - 1) / BN) * (a.K / BK);
         const int64_t max_tiles = (a.M + BM - 1) / BM + a.G;
         p.tiles_m = (int32_t)max_tiles;
         dim3 grid((unsigned)(max_tiles * p.tiles_n));
-        return dispatch<true>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+        return dispatch<WM, true>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
     }
+    constexpr int WM = 128, BM = 2 * WM;
     p.tiles_m = (int32_t)((a.M + BM - 1) / BM);
     dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
-    return dispatch<false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+    return dispatch<WM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
 }
 
 } // namespace fgs
