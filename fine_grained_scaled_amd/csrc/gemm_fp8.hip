@@ -29,19 +29,22 @@
 // 128-K block.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]; both operands K-contiguous.
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; output tile
-// (2*WM) x 128 with WM = 128 (dense) or 64 (grouped: MoE groups are short).
-// Each wave owns WM x 64 = (WM/32) x 2 MFMA 32x32x16 sub-tiles.  K advances
-// in 128-deep blocks staged in LDS as FP8 bytes, double-buffered, by direct
+// Workgroup: NWM x 2 waves, each owning a 64 x 64 output sub-block (2 x 2
+// MFMA 32x32x16 tiles), so the workgroup tile is (64*NWM) x 128: NWM = 4
+// (512 threads, two waves per SIMD so one wave's decode/promotion VALU work
+// overlaps the other's MFMAs) for dense GEMMs, NWM = 2 for the grouped one
+// (MoE groups are short).  The promoted accumulators and the per-block
+// partial sums of a wave (2 x 64 VGPRs) both stay in VGPRs.  K advances in
+// 128-deep blocks staged in LDS as FP8 bytes, double-buffered, by direct
 // global->LDS loads (global_load_lds_dwordx4: lane i of a wave-instruction
 // fills bytes 16i..16i+15 of a 1 KiB LDS span, i.e. 8 rows of 128 bytes), so
 // the next block streams in while the current one is multiplied without
 // passing through registers.  The 16-byte chunk c of row r sits in LDS slot
-// c ^ (r & 7): the lane that fills slot s of row r fetches chunk s ^ (r & 7),
-// and the fragment reads (8 consecutive rows, same chunk) hit 8 distinct
-// slots, i.e. all 32 banks once.  MFMA operands are swapped (B fragment
-// first) so each lane's 16 accumulators share one row m: the 1x128 A scale
-// is one value per lane and per sub-tile row.
+// c ^ ((r >> 1) & 7): the lane that fills slot s of row r fetches chunk
+// s ^ ((r >> 1) & 7), and a fragment read (16 consecutive rows, same chunk,
+// 256 bytes) touches each of the 64 LDS banks once.  MFMA operands are
+// swapped (B fragment first) so each lane's 16 accumulators share one row m:
+// the 1x128 A scale is one value per lane and per sub-tile row.
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -117,30 +120,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int WM>
+template <int NWM>
 struct Lds {
-    static constexpr int BM = 2 * WM;
+    static constexpr int BM = 64 * NWM;
     static constexpr int A_BYTES = BM * ROW;
     static constexpr int B_BYTES = BN * ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES + BN * 4;   // + B 1x128 scales of the block
 };
 
-template <int WM, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
+template <int NWM, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
+__global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 {
-    constexpr int BM = 2 * WM;
-    constexpr int TI = WM / 32;          // sub-tiles along m per wave
+    constexpr int NW = 2 * NWM;          // waves
+    constexpr int NT = 64 * NW;          // threads
+    constexpr int BM = 64 * NWM;
+    constexpr int WM = 64;
+    constexpr int TI = 2;                // sub-tiles along m per wave
     constexpr int TJ = 2;                // sub-tiles along n per wave
     constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR);
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
-    using L = Lds<WM>;
+    using L = Lds<NWM>;
 
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int s_scan[256];
+    __shared__ int s_scan[NT];
     __shared__ int s_sel[2];
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 1, wn = w & 1;      // wave grid NWM x 2
 
     // ------------------------------------------------------------ tile --
     int64_t m0, m_end, n0;
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
         const int64_t v = blockIdx.x;
         int running = 0;
         if (t == 0) s_sel[0] = -1;
-        for (int chunk = 0; chunk < p.G; chunk += 256) {
+        for (int chunk = 0; chunk < p.G; chunk += NT) {
             const int g = chunk + t;
             int cnt = 0;
             if (g < p.G) {
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
             }
             s_scan[t] = cnt;
             __syncthreads();
-            for (int d = 1; d < 256; d <<= 1) {
+            for (int d = 1; d < NT; d <<= 1) {
                 const int add = (t >= d) ? s_scan[t - d] : 0;
                 __syncthreads();
                 s_scan[t] += add;
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
                 s_sel[0] = g;
                 s_sel[1] = excl;
             }
-            running += s_scan[255];
+            running += s_scan[NT - 1];
             __syncthreads();
         }
         __syncthreads();
@@ -206,25 +212,29 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     }
 
     // ------------------------------------------------------- loaders --
-    // wave w stages rows [BM/4 * w, BM/4 * (w+1)) of A and [32w, 32w+32) of
-    // B, 8 rows per wave-instruction; lane l fills slot l & 7 of row l >> 3
-    // with chunk (l & 7) ^ (l >> 3).  Rows past the end are clamped (their
-    // products land in rows/columns that are never stored).
-    constexpr int A_INSTR = BM / 32, B_INSTR = BN / 32;
-    const int srow = l >> 3, schunk = (l & 7) ^ srow;
+    // wave w stages rows [A_ROWS*w, A_ROWS*(w+1)) of A and [B_ROWS*w, ...)
+    // of B, 8 rows per wave-instruction; lane l fills slot l & 7 of row
+    // rbase + (l >> 3) with chunk (l & 7) ^ ((row >> 1) & 7).  Rows past the
+    // end are clamped (their products land in rows/columns never stored).
+    constexpr int A_ROWS = BM / NW, B_ROWS = BN / NW;
+    constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
+    static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the wave count");
+    const int srow = l >> 3;
     const uint8_t* a_src[A_INSTR];
     const uint8_t* b_src[B_INSTR];
 #pragma unroll
     for (int u = 0; u < A_INSTR; ++u) {
-        int64_t r = m0 + (BM / 4) * w + 8 * u + srow;
+        const int lr = A_ROWS * w + 8 * u + srow;
+        int64_t r = m0 + lr;
         r = r < m_end ? r : m_end - 1;
-        a_src[u] = p.A + r * p.lda + 16 * schunk;
+        a_src[u] = p.A + r * p.lda + 16 * ((l & 7) ^ ((lr >> 1) & 7));
     }
 #pragma unroll
     for (int u = 0; u < B_INSTR; ++u) {
-        int64_t r = n0 + 32 * w + 8 * u + srow;
+        const int lr = B_ROWS * w + 8 * u + srow;
+        int64_t r = n0 + lr;
         r = r < p.N ? r : p.N - 1;
-        b_src[u] = Bp + r * p.ldb + 16 * schunk;
+        b_src[u] = Bp + r * p.ldb + 16 * ((l & 7) ^ ((lr >> 1) & 7));
     }
     int64_t sb_col = n0 + 64 * (w & 1) + l;        // B 1x128 scales: waves 0 and 1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
@@ -234,10 +244,10 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
         const int64_t ko = kb * BK;
 #pragma unroll
         for (int u = 0; u < A_INSTR; ++u)
-            g2lds16(a_src[u] + ko, st + ((BM / 4) * w + 8 * u) * ROW);
+            g2lds16(a_src[u] + ko, st + (A_ROWS * w + 8 * u) * ROW);
 #pragma unroll
         for (int u = 0; u < B_INSTR; ++u)
-            g2lds16(b_src[u] + ko, st + L::A_BYTES + (32 * w + 8 * u) * ROW);
+            g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + 8 * u) * ROW);
         if constexpr (B_TILE)
             if (w < 2) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
     };
@@ -271,9 +281,10 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     wait_lds_dma();
     __syncthreads();
 
-    // fragment read offsets: row R = base + (l & 31) has R & 7 == l & 7;
-    // chunk 2*ks + h (h = lane half) lives in slot (2*ks + h) ^ (l & 7)
-    const int swz = l & 7, half = l >> 5;
+    // fragment read offsets: row R = base + (l & 31) (base a multiple of
+    // 32) has (R >> 1) & 7 == (l >> 1) & 7; chunk 2*ks + h (h = lane half)
+    // lives in slot (2*ks + h) ^ ((l >> 1) & 7)
+    const int swz = (l >> 1) & 7, half = l >> 5;
 
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int cur = (int)(kb & 1);
@@ -416,33 +427,33 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmParams p)
     }
 }
 
-template <int WM, int AMODE, int BMODE, bool GROUPED>
+template <int NWM, int AMODE, int BMODE, bool GROUPED>
 hipError_t launch_modes(const GemmParams& p, bool bf16, dim3 grid, hipStream_t s)
 {
-    const size_t lds = 2 * (size_t)Lds<WM>::STAGE;
-    auto k = bf16 ? gemm_fp8_kernel<WM, AMODE, BMODE, true, GROUPED>
-                  : gemm_fp8_kernel<WM, AMODE, BMODE, false, GROUPED>;
+    const size_t lds = 2 * (size_t)Lds<NWM>::STAGE;
+    auto k = bf16 ? gemm_fp8_kernel<NWM, AMODE, BMODE, true, GROUPED>
+                  : gemm_fp8_kernel<NWM, AMODE, BMODE, false, GROUPED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL(k, grid, dim3(128 * NWM), lds, s, p);
     return hipGetLastError();
 }
 
-template <int WM, bool GROUPED>
+template <int NWM, bool GROUPED>
 hipError_t dispatch(const GemmParams& p, int amode, int bmode, bool bf16, dim3 grid, hipStream_t s)
 {
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUPED>(p, bf16, grid, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUPED>(p, bf16, grid, s);
         if constexpr (!GROUPED) {
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<WM, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
         }
     } else if constexpr (!GROUPED) {
         if (amode == FGS_SCALE_TENSOR) {
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<WM, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
+            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
         }
     }
     return hipErrorInvalidValue;
@@ -469,18 +480,18 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.tiles_n = (int32_t)((a.N + BN - 1) / BN);
     if (a.M == 0 || a.N == 0) return hipSuccess;
     if (a.group_offsets) {
-        constexpr int WM = 64, BM = 2 * WM;
+        constexpr int NWM = 2, BM = 64 * NWM;
         p.b_group_stride = a.N * a.B.ld;
         p.sb_group_stride = ((a.N + BN - 1) / BN) * (a.K / BK);
         const int64_t max_tiles = (a.M + BM - 1) / BM + a.G;
         p.tiles_m = (int32_t)max_tiles;
         dim3 grid((unsigned)(max_tiles * p.tiles_n));
-        return dispatch<WM, true>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+        return dispatch<NWM, true>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
     }
-    constexpr int WM = 128, BM = 2 * WM;
+    constexpr int NWM = 4, BM = 64 * NWM;
     p.tiles_m = (int32_t)((a.M + BM - 1) / BM);
     dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
-    return dispatch<WM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+    return dispatch<NWM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
 }
 
 } // namespace fgs
