@@ -54,6 +54,8 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128, BK = 128;
@@ -113,6 +115,48 @@ __device__ __forceinline__ void decode16(const uint4 v, f16x8& lo, f16x8& hi)
     hi = f16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
+// BF16 x BF16 MFMA, 32x32 outputs, 16-deep K, FP32 accumulate.
+__device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const f32x16& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// MXFP8: 16 E4M3 codes of one 32-element block -> two BF16 8-vectors of
+// code * s, with s = 2^d (d <= 0) the block's scale relative to the
+// reference exponent; exact whenever code * s is a BF16 number (every code
+// for d >= -124).
+__device__ __forceinline__ void decode16(const uint4 v, float s, bf16x8& lo, bf16x8& hi)
+{
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, true);
+    const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, s, false);
+    const bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, s, true);
+    const bf16x2 g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, s, false);
+    const bf16x2 h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, s, true);
+    lo = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    hi = bf16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
+}
+
+// E8M0 helpers: the largest of the four scale bytes of a 128-K block, the
+// FP32 value 2^(c - 127) of a scale byte (c = 0 is 2^-127, 255 gives Inf so a
+// NaN block stays NaN), and the converter scale 2^(c - ref) (c <= ref),
+// clamped at 2^-127.
+__device__ __forceinline__ uint32_t max_byte(uint32_t u)
+{
+    return max(max(u & 0xFFu, (u >> 8) & 0xFFu), max((u >> 16) & 0xFFu, u >> 24));
+}
+__device__ __forceinline__ float e8m0_value(uint32_t c)
+{
+    return c == 0 ? as_f32(0x00400000u) : as_f32(c << 23);
+}
+__device__ __forceinline__ float e8m0_rel(uint32_t c, uint32_t ref)
+{
+    const int e = 127 + (int)c - (int)ref;
+    return as_f32((uint32_t)(e > 0 ? e : 0) << 23);
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
     uint32_t u = as_u32(f);
@@ -139,11 +183,13 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
     constexpr int TJ = 2;                // sub-tiles along n per wave
     constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR);
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
+    constexpr bool MX = AMODE == FGS_SCALE_MX32_E8M0;
     using L = Lds<NWM>;
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
     __shared__ int s_sel[2];
+    __shared__ uint32_t s_ebt[2][2];       // MX: B tile reference exponent, [block parity][wn]
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int wm = w >> 1, wn = w & 1;      // wave grid NWM x 2
@@ -269,6 +315,38 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // MXFP8 scales.  A (per lane row m): E_A[m] = the largest E8M0 byte of
+    // the row's four 32-blocks in the 128-K block; each code is decoded as
+    // code * 2^(e - E_A) (exact), and the block's FP32 partial sum is
+    // promoted with 2^(E_A + E_B).  B: one reference E_B per tile and block
+    // (the largest byte over the tile's 128 rows), so the promotion factor
+    // stays one value per lane.  The four bytes of a row's block are one
+    // aligned 32-bit word.
+    const int64_t ksc = p.K / 32;
+    const uint8_t* sA8 = reinterpret_cast<const uint8_t*>(p.sA);
+    const uint8_t* sB8 = reinterpret_cast<const uint8_t*>(sBp);
+    int64_t bn[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int64_t n = n0 + 64 * wn + 32 * j + (l & 31);
+        bn[j] = n < p.N ? n : p.N - 1;
+    }
+    uint32_t a_sw_next[TI], b_sw_next[TJ];
+    // wave-wide max of the B bytes this wave holds (its 64 B rows), published
+    // by the wm == 0 waves for the other waves of the same wn
+    auto publish_ebt = [&](int parity) {
+        uint32_t m = max(max_byte(b_sw_next[0]), max_byte(b_sw_next[1]));
+        m = max_xor32(max_xor16(max_lanes16(m)));
+        if (wm == 0 && l == 0) s_ebt[parity][wn] = m;
+    };
+    if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc);
+        publish_ebt(0);
+    }
+
     // prologue: block 0 -> stage 0
     stage_block(0, 0);
     float sa_next[TI];
@@ -294,6 +372,13 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 #pragma unroll
         for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 ? sa_next[i] : 1.0f;
         const float sb_blk = sb_next;
+        uint32_t a_sw[TI], b_sw[TJ];
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) a_sw[i] = a_sw_next[i];
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) b_sw[j] = b_sw_next[j];
+        }
         if (more) {
             stage_block(kb + 1, cur ^ 1);
             if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
@@ -301,6 +386,24 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
                 for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
             }
             if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb + kb + 1];
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc + 4 * (kb + 1));
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc + 4 * (kb + 1));
+            }
+        }
+        // MX: reference exponents and the per-lane converter scales of this block
+        uint32_t ea[TI], ebt = 0;
+        float fmx[TI];
+        if constexpr (MX) {
+            ebt = max(s_ebt[kb & 1][0], s_ebt[kb & 1][1]);
+            const float fb = e8m0_value(ebt);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                ea[i] = max_byte(a_sw[i]);
+                fmx[i] = e8m0_value(ea[i]) * fb;
+            }
         }
 
         const uint8_t* st = smem + cur * L::STAGE;
@@ -322,24 +425,43 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int co = ((2 * ks + half) ^ swz) << 4;
-            f16x8 af[TI][2], bf[TJ][2];
+            if constexpr (MX) {
+                // k-steps 2ks, 2ks+1 are MX block ks of this 128-K block
+                bf16x8 af[TI][2], bf[TJ][2];
 #pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-                decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
+                for (int j = 0; j < TJ; ++j)
+                    decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co),
+                             e8m0_rel((b_sw[j] >> (8 * ks)) & 0xFFu, ebt), bf[j][0], bf[j][1]);
 #pragma unroll
                 for (int i = 0; i < TI; ++i)
+                    decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co),
+                             e8m0_rel((a_sw[i] >> (8 * ks)) & 0xFFu, ea[i]), af[i][0], af[i][1]);
 #pragma unroll
-                    for (int j = 0; j < TJ; ++j) {
-                        if constexpr (PROMOTE)
-                            part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
-                        else
-                            acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
-                    }
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < TI; ++i)
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j) part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+            } else {
+                f16x8 af[TI][2], bf[TJ][2];
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+                    decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < TI; ++i)
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j) {
+                            if constexpr (PROMOTE)
+                                part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+                            else
+                                acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
+                        }
+            }
         }
 
         if constexpr (PROMOTE) {
@@ -362,6 +484,14 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
                                 acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], fa * sbv[e], acc[i][j][4 * q + e]);
                         }
                     }
+            } else if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] = __builtin_fmaf(part[i][j][r], fmx[i], acc[i][j][r]);
             } else {
                 const float fb = BMODE == FGS_SCALE_TENSOR ? sb_t : sb_blk;
 #pragma unroll
@@ -376,6 +506,8 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
             }
         }
 
+        if constexpr (MX)
+            if (more) publish_ebt((int)((kb + 1) & 1));
         wait_lds_dma();
         __syncthreads();
     }
@@ -450,6 +582,8 @@ hipError_t dispatch(const GemmParams& p, int amode, int bmode, bool bf16, dim3 g
             if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
         }
     } else if constexpr (!GROUPED) {
+        if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0)
+            return launch_modes<NWM, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, bf16, grid, s);
         if (amode == FGS_SCALE_TENSOR) {
             if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
             if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
@@ -492,6 +626,12 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.tiles_m = (int32_t)((a.M + BM - 1) / BM);
     dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
     return dispatch<NWM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+}
+
+// MXFP8 operands take the same kernel (E8M0 scale handling selected by mode).
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t stream)
+{
+    return launch_gemm_fp8(a, stream);
 }
 
 } // namespace fgs

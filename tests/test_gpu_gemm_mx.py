@@ -1,0 +1,117 @@
+"""GPU parity of the MXFP8 GEMM (E4M3 codes with one E8M0 scale per 32
+K-elements on both operands) against the oracle's FP64 product of the
+dequantized operands: |C - C_ref| <= 1e-5 * sum_k |a_k b_k| + 1e-6 (FP32
+out), within one BF16 ulp of the rounded reference (BF16 out).
+
+"Accelerating FP8 training performance with the NVIDIA NeMo framework":
+MXFP8 with blocks of 32 values.  Operands are quantized by the oracle and
+uploaded, so this isolates the GEMM.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fine_grained_scaled_amd import synth
+
+from _helpers import gemm_within_bf16_bound, gemm_within_fp32_bound, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fgs():
+    import fine_grained_scaled_amd as m
+    return m
+
+
+def mx_operand(fgs, bits, colwise=False, rows=None):
+    q, s = oracle.quant_mx(bits, colwise=colwise)
+    deq = oracle.dequant_mx(q if rows is None else q[rows], s if rows is None else s[rows])
+    op = fgs.Operand(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), fgs.SCALE_MX32_E8M0)
+    return op, deq
+
+
+def _check(fgs, A, B, ah, bh, out, rows=None):
+    c = fgs.gemm_block_scaled(A, B, out)
+    torch.cuda.synchronize()
+    c = c.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        c = c[rows]
+    cref, sref = oracle.gemm_ref(ah, bh)
+    if out == torch.float32:
+        ok, worst = gemm_within_fp32_bound(c, cref, sref)
+        assert ok, f"worst err/bound = {worst}"
+    else:
+        ok, nbad = gemm_within_bf16_bound(c, cref, sref)
+        assert ok, f"{nbad} BF16 outputs outside one ulp"
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (256, 384, 1024)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_mx_gemm_ragged(fgs, M, N, K, out):
+    A, ah = mx_operand(fgs, synth.activations(M, K, seed=M + 3, outliers=False))
+    B, bh = mx_operand(fgs, synth.weights(N, K, seed=N + 5))
+    _check(fgs, A, B, ah, bh, out)
+
+
+def test_mx_gemm_exponent_spread(fgs):
+    """Every 32-block of both operands scaled by its own power of two in
+    2^-40 .. 2^40, so the E8M0 exponents inside one 128-K block and across
+    the rows of a tile differ widely: exercises the per-row (A) and per-tile
+    (B) reference exponents and the promotion factor."""
+    M, N, K = 256, 256, 512
+    rng = np.random.default_rng(21)
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=22, outliers=False)).copy()
+    b = oracle.bf16_bits_to_f32(synth.weights(N, K, seed=23)).copy()
+    a *= np.repeat(np.ldexp(1.0, rng.integers(-40, 41, (M, K // 32))), 32, axis=1).astype(np.float32)
+    b *= np.repeat(np.ldexp(1.0, rng.integers(-40, 41, (N, K // 32))), 32, axis=1).astype(np.float32)
+    A, ah = mx_operand(fgs, synth.f32_to_bf16_bits(a))
+    B, bh = mx_operand(fgs, synth.f32_to_bf16_bits(b))
+    _check(fgs, A, B, ah, bh, torch.float32)
+
+
+def test_mx_gemm_zero_and_tiny_blocks(fgs):
+    """All-zero 32-blocks (scale byte 127) next to blocks of tiny values."""
+    M, N, K = 128, 128, 256
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=24, outliers=False)).copy()
+    b = oracle.bf16_bits_to_f32(synth.weights(N, K, seed=25)).copy()
+    a[:, 0:32] = 0.0
+    a[::3, 32:64] *= np.float32(2.0 ** -30)
+    b[::2, 64:96] = 0.0
+    b[1::5, 96:128] *= np.float32(2.0 ** -25)
+    A, ah = mx_operand(fgs, synth.f32_to_bf16_bits(a))
+    B, bh = mx_operand(fgs, synth.f32_to_bf16_bits(b))
+    _check(fgs, A, B, ah, bh, torch.float32)
+
+
+def test_mx_gemm_determinism(fgs):
+    A, _ = mx_operand(fgs, synth.activations(512, 1024, seed=26, outliers=False))
+    B, _ = mx_operand(fgs, synth.weights(384, 1024, seed=27))
+    c1 = fgs.gemm_block_scaled(A, B)
+    c2 = fgs.gemm_block_scaled(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("orient", ["fwd", "wgrad"])
+def test_mx_llama405b_qkv_sampled(fgs, orient):
+    """Llama-3.1-405B QKV projection, one GPU's share: M = 4096 tokens,
+    (K, N) = (16384, 18432); fwd in BF16 out, wgrad (contraction over the
+    4096 tokens, both operands MX-quantized along M) in FP32; sampled rows."""
+    M, K, N = 4096, 16384, 18432
+    if orient == "fwd":
+        a_bits = synth.activations(M, K, seed=0, outliers=False)
+        b_bits = synth.weights(N, K, seed=0)
+        a_col = b_col = False
+        out = torch.bfloat16
+    else:
+        a_bits = synth.normal_gradients(M, N, seed=0)       # dY [M x N] -> dY^T [N x M]
+        b_bits = synth.activations(M, K, seed=0, outliers=False)   # X -> X^T [K x M]
+        a_col = b_col = True
+        out = torch.float32
+    rows_total = a_bits.shape[1] if a_col else a_bits.shape[0]
+    rs = sample_rows(rows_total)
+    A, ah = mx_operand(fgs, a_bits, colwise=a_col, rows=rs)
+    B, bh = mx_operand(fgs, b_bits, colwise=b_col)
+    _check(fgs, A, B, ah, bh, out, rows=rs)
