@@ -159,6 +159,35 @@ def quantize_nvfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
     return Quantized(q, s, qT, sT, SCALE_NV16_E4M3, ELEM_E2M1, ts)
 
 
+def _check_operand(op: Operand, rows: int, K: int, name: str, groups: int = 1):
+    """Shape checks of an operand's device buffers against what the kernels
+    read for `rows` x `K` (per group), so a mis-sized tensor raises here
+    instead of being read out of bounds."""
+    if op.data.dtype != torch.uint8 or op.data.dim() != 2:
+        raise TypeError(f"{name}.data must be a 2-D uint8 tensor")
+    per_byte = 2 if op.elem == ELEM_E2M1 else 1
+    if op.data.shape[0] < rows * groups or op.data.shape[1] * per_byte < K or op.data.stride(1) != 1:
+        raise ValueError(f"{name}.data has shape {tuple(op.data.shape)}; needs {rows * groups} x {K} codes, unit column stride")
+    m = op.scale_mode
+    if m == SCALE_TENSOR:
+        need, dt = 1, torch.float32
+    elif m == SCALE_TILE_1x128:
+        need, dt = (K // 128) * rows, torch.float32
+    elif m == SCALE_BLOCK_128x128:
+        need, dt = groups * ((rows + 127) // 128) * (K // 128), torch.float32
+    elif m == SCALE_MX32_E8M0:
+        need, dt = rows * (K // 32), torch.uint8
+    elif m == SCALE_NV16_E4M3:
+        need, dt = rows * (K // 16), torch.uint8
+        if op.tensor_scale is None or op.tensor_scale.numel() < 1 or op.tensor_scale.dtype != torch.float32:
+            raise ValueError(f"{name}.tensor_scale must be a float32 tensor with one element")
+    else:
+        raise ValueError(f"{name}: unknown scale mode {m}")
+    if op.scales.dtype != dt or op.scales.numel() < need or not op.scales.is_contiguous():
+        raise ValueError(f"{name}.scales must be a contiguous {dt} tensor of at least {need} elements "
+                         f"(got {op.scales.dtype}, {op.scales.numel()})")
+
+
 def _out_code(out_dtype):
     if out_dtype == torch.float32:
         return OUT_FP32
@@ -175,8 +204,12 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
     if K is None:
         K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
     code = _out_code(out_dtype)
+    _check_operand(A, M, K, "A")
+    _check_operand(B, N, K, "B")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=A.data.device)
+    if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] < M or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError("out must be a [M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
     check(_lib.load().fgs_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), M, N, K,
                                             _ptr(out), out.stride(0), code, _stream()))
@@ -196,8 +229,14 @@ def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tenso
     if K is None:
         K = A.data.shape[1]
     code = _out_code(out_dtype)
+    _check_operand(A, total_M, K, "A")
+    if B.scale_mode != SCALE_BLOCK_128x128 or B.data.shape[0] < G * N:
+        raise ValueError("B must hold G x N rows of codes with 128x128 block scales")
+    _check_operand(B, N, K, "B", groups=G)
     if out is None:
         out = torch.empty((total_M, N), dtype=out_dtype, device=A.data.device)
+    if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] < total_M or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError("out must be a [total_M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
     check(_lib.load().fgs_grouped_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
                                                     G, total_M, N, K, _ptr(out), out.stride(0), code, _stream()))

@@ -124,3 +124,31 @@ def test_grouped_validation(lib):
     bt = _op(mode=0)
     assert g(r(a), r(bt), FAKE, 4, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
     assert g(r(a), r(b), FAKE, 0, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_OK          # no groups
+
+
+def test_binding_rejects_mis_sized_operands():
+    """The Python binding checks operand buffer sizes before any C call, so a
+    mis-sized scale tensor raises instead of being read out of bounds."""
+    import torch
+    from fine_grained_scaled_amd import ops
+    M, K = 256, 512
+    codes = torch.zeros((M, K), dtype=torch.uint8)
+    ok = [
+        ops.Operand(codes, torch.zeros(1), _lib.SCALE_TENSOR),
+        ops.Operand(codes, torch.zeros((K // 128, M)), _lib.SCALE_TILE_1x128),
+        ops.Operand(codes, torch.zeros((M // 128, K // 128)), _lib.SCALE_BLOCK_128x128),
+        ops.Operand(codes, torch.zeros((M, K // 32), dtype=torch.uint8), _lib.SCALE_MX32_E8M0),
+    ]
+    for op in ok:
+        ops._check_operand(op, M, K, "A")
+    bad = [
+        ops.Operand(codes, torch.zeros((M // 128, K // 128)), _lib.SCALE_MX32_E8M0),      # FP32 block grid as MX
+        ops.Operand(codes, torch.zeros((K // 128, M - 1)), _lib.SCALE_TILE_1x128),        # one row short
+        ops.Operand(codes[:, :256], torch.zeros(1), _lib.SCALE_TENSOR),                   # K too short
+        ops.Operand(codes, torch.zeros((M, K // 32), dtype=torch.uint8), 9),              # unknown mode
+        ops.Operand(torch.zeros((M, K // 2), dtype=torch.uint8), torch.zeros((M, K // 16), dtype=torch.uint8),
+                    _lib.SCALE_NV16_E4M3, _lib.ELEM_E2M1, None),                          # NVFP4 without tensor scale
+    ]
+    for op in bad:
+        with pytest.raises((ValueError, TypeError)):
+            ops._check_operand(op, M, K, "A")
