@@ -80,6 +80,9 @@ def _load():
     lib.orc_quant_e4m3_blocks.argtypes = [P, I64, I64, I64, I64, P, P]
     lib.orc_quant_mx.argtypes = [P, I64, I64, P, P]
     lib.orc_quant_nvfp4.argtypes = [P, I64, I64, ctypes.c_int, U64, I64, I64, P, P, P]
+    lib.orc_nvfp4_tensor_scale.restype = ctypes.c_float
+    lib.orc_nvfp4_tensor_scale.argtypes = [P, I64]
+    lib.orc_quant_nvfp4_blocks.argtypes = [P, I64, I64, ctypes.c_float, ctypes.c_int, U64, I64, I64, I64, P, P]
     lib.orc_e4m3_encode_array.argtypes = [P, I64, P]
     lib.orc_e2m1_encode_array.argtypes = [P, I64, ctypes.c_int, P, P]
     lib.orc_sr_word_array.argtypes = [U64, P, I64, P]
@@ -238,6 +241,38 @@ def quant_nvfp4(x, colwise: bool = False, rht: bool = False, rht_seed: int = 0,
     _load().orc_quant_nvfp4(_ptr(np.ascontiguousarray(xf)), rows, cols, int(stochastic),
                             sr_seed & (2**64 - 1), idx_rs, idx_cs, _ptr(q), _ptr(scales), _ptr(ts))
     return q, scales, ts[0]
+
+
+def nvfp4_operand_values(x, colwise: bool = False, rht: bool = False, rht_seed: int = 0) -> np.ndarray:
+    """The FP32 values NVFP4 quantizes: the BF16 matrix (transposed when
+    colwise) widened, with the random Hadamard transform along the quantized
+    dimension when rht."""
+    xf = bf16_bits_to_f32(_as_bf16_bits(x))
+    if colwise:
+        xf = np.ascontiguousarray(xf.T)
+    if rht:
+        xf = rht_rows(xf, rht_seed)
+    return np.ascontiguousarray(xf)
+
+
+def nvfp4_tensor_scale(values_f32: np.ndarray) -> np.float32:
+    """s_t of NVFP4 quantization over all of the given FP32 values."""
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    return np.float32(_load().orc_nvfp4_tensor_scale(_ptr(v), v.size))
+
+
+def quant_nvfp4_rows(values_f32: np.ndarray, tensor_scale, stochastic: bool = False, sr_seed: int = 0,
+                     idx_base: int = 0, idx_rs: int = 0, idx_cs: int = 1):
+    """NVFP4 blocks of the given rows under a given tensor scale (the rows
+    may be a sample of a larger matrix); the SR word of element (r, c) uses
+    source index idx_base + r * idx_rs + c * idx_cs.  Returns (packed, scales)."""
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    rows, cols = v.shape
+    q = np.empty((rows, (cols + 1) // 2), dtype=np.uint8)
+    scales = np.empty((rows, (cols + 15) // 16), dtype=np.uint8)
+    _load().orc_quant_nvfp4_blocks(_ptr(v), rows, cols, float(tensor_scale), int(stochastic),
+                                   sr_seed & (2**64 - 1), idx_base, idx_rs, idx_cs, _ptr(q), _ptr(scales))
+    return q, scales
 
 
 # --------------------------------------------------------------------------

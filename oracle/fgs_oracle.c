@@ -362,37 +362,44 @@ void orc_quant_mx(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q, uin
 }
 
 /*
- * NVFP4: E2M1 elements, one E4M3 scale per 16 contiguous elements along
- * cols, and one FP32 tensor scale [NVFP4 "How it works"].
- * READING (two-level scale): s_t = fl32(amax_t / 2688) with 2688 = 448 * 6
+ * NVFP4 tensor scale [NVFP4 "How it works"].
+ * READING (two-level scale): s_t = fl32(amax_t / 2688) with 2688 = 448 * 6,
  * so the tensor amax maps to the top of the E4M3-scale x E2M1 range;
- * per block s_b = E4M3(fl32(amax_b / fl32(6 * s_t))), d = fl32(dec(s_b) * s_t),
- * y = fl32(x / d) saturated to +-6, then E2M1 by RNE or stochastic rounding.
- * amax_t == 0 -> s_t = 1; amax_t non-finite -> s_t = NaN; d == 0 or NaN ->
- * every code of the block is 0.
- * x holds FP32 values (BF16 inputs widened, possibly Hadamard-transformed).
- * The SR word of element (r, c) uses the linear index
- * i = r * idx_rs + c * idx_cs of that element in the source tensor, so it
- * does not depend on layout or tiling.
- * q: [rows x ceil(cols/2)] packed, element 2j in the low nibble;
- * scales: [rows x ceil(cols/16)] E4M3 codes; *tensor_scale: s_t.
+ * amax_t == 0 -> s_t = 1; amax_t non-finite -> s_t = NaN.
+ * x holds the n FP32 values being quantized (BF16 inputs widened, possibly
+ * Hadamard-transformed).
  */
-void orc_quant_nvfp4(const float *x, int64_t rows, int64_t cols,
-                     int stochastic, uint64_t sr_seed, int64_t idx_rs, int64_t idx_cs,
-                     uint8_t *q, uint8_t *scales, float *tensor_scale)
+float orc_nvfp4_tensor_scale(const float *x, int64_t n)
+{
+    float amax_t = 0.0f;
+    int64_t i;
+    for (i = 0; i < n; i++)
+        amax_t = amax_update(amax_t, x[i]);
+    if (!isfinite(amax_t))
+        return NAN;
+    if (amax_t == 0.0f)
+        return 1.0f;
+    return amax_t / 2688.0f;
+}
+
+/*
+ * NVFP4 blocks: E2M1 elements, one E4M3 scale per 16 contiguous elements
+ * along cols, under the tensor scale s_t [NVFP4 "How it works"].
+ * Per block s_b = E4M3(fl32(amax_b / fl32(6 * s_t))), d = fl32(dec(s_b) * s_t),
+ * y = fl32(x / d) saturated to +-6, then E2M1 by RNE or stochastic rounding;
+ * d == 0 or NaN -> every code of the block is 0.
+ * The SR word of element (r, c) uses the linear index
+ * i = idx_base + r * idx_rs + c * idx_cs of that element in the source
+ * tensor, so it does not depend on layout, tiling or sampling.
+ * q: [rows x ceil(cols/2)] packed, element 2j in the low nibble;
+ * scales: [rows x ceil(cols/16)] E4M3 codes.
+ */
+void orc_quant_nvfp4_blocks(const float *x, int64_t rows, int64_t cols, float s_t,
+                            int stochastic, uint64_t sr_seed,
+                            int64_t idx_base, int64_t idx_rs, int64_t idx_cs,
+                            uint8_t *q, uint8_t *scales)
 {
     int64_t nb = (cols + 15) / 16, qc = (cols + 1) / 2, r, b, c;
-    float amax_t = 0.0f, s_t;
-    for (r = 0; r < rows; r++)
-        for (c = 0; c < cols; c++)
-            amax_t = amax_update(amax_t, x[r * cols + c]);
-    if (!isfinite(amax_t))
-        s_t = NAN;
-    else if (amax_t == 0.0f)
-        s_t = 1.0f;
-    else
-        s_t = amax_t / 2688.0f;
-    *tensor_scale = s_t;
     memset(q, 0, (size_t)(rows * qc));
     for (r = 0; r < rows; r++) {
         for (b = 0; b < nb; b++) {
@@ -416,7 +423,8 @@ void orc_quant_nvfp4(const float *x, int64_t rows, int64_t cols,
                     if (y < -6.0f)
                         y = -6.0f;
                     if (stochastic)
-                        code = orc_e2m1_encode_sr(y, orc_sr_word(sr_seed, (uint64_t)(r * idx_rs + c * idx_cs)));
+                        code = orc_e2m1_encode_sr(y, orc_sr_word(sr_seed,
+                                   (uint64_t)(idx_base + r * idx_rs + c * idx_cs)));
                     else
                         code = orc_e2m1_encode_rne(y);
                 }
@@ -427,6 +435,17 @@ void orc_quant_nvfp4(const float *x, int64_t rows, int64_t cols,
             }
         }
     }
+}
+
+/* Whole-tensor NVFP4 quantization: the tensor scale from all of x, then the
+ * blocks.  *tensor_scale receives s_t. */
+void orc_quant_nvfp4(const float *x, int64_t rows, int64_t cols,
+                     int stochastic, uint64_t sr_seed, int64_t idx_rs, int64_t idx_cs,
+                     uint8_t *q, uint8_t *scales, float *tensor_scale)
+{
+    float s_t = orc_nvfp4_tensor_scale(x, rows * cols);
+    *tensor_scale = s_t;
+    orc_quant_nvfp4_blocks(x, rows, cols, s_t, stochastic, sr_seed, 0, idx_rs, idx_cs, q, scales);
 }
 
 /* ------------------------------------------------------------------ */

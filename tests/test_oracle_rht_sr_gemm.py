@@ -147,3 +147,23 @@ def test_quantized_gemm_close_to_bf16_gemm():
     c_true, s_true = oracle.gemm_ref(oracle.bf16_bits_to_f32(a), oracle.bf16_bits_to_f32(b))
     assert np.all(np.abs(c - c_true) <= 0.13 * s_true)
     assert np.sqrt(np.mean((c - c_true) ** 2)) < 0.05 * np.sqrt(np.mean(s_true ** 2))
+
+
+def test_nvfp4_sampled_rows_match_whole_tensor():
+    """Quantizing sampled rows under the whole tensor's scale, with the SR
+    index base of each row, reproduces those rows of the whole-tensor
+    quantization (row-wise and column-wise, RHT and SR on)."""
+    from fine_grained_scaled_amd import synth
+    bits = synth.gradients(64, 96, seed=31)
+    for colwise in (False, True):
+        q, s, ts = oracle.quant_nvfp4(bits, colwise=colwise, rht=True, rht_seed=5, stochastic=True, sr_seed=77)
+        vals = oracle.nvfp4_operand_values(bits, colwise=colwise, rht=True, rht_seed=5)
+        assert oracle.nvfp4_tensor_scale(vals) == ts
+        for r in (0, 7, vals.shape[0] - 1):
+            if colwise:      # quantized row r = source column r; elements run down the source rows
+                base, cs = r, bits.shape[1]
+            else:
+                base, cs = r * bits.shape[1], 1
+            qr, sr = oracle.quant_nvfp4_rows(vals[r:r + 1], ts, stochastic=True, sr_seed=77,
+                                             idx_base=base, idx_cs=cs)
+            assert np.array_equal(qr[0], q[r]) and np.array_equal(sr[0], s[r])
