@@ -144,7 +144,7 @@ int fgs_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ldx,
     if (!workspace || workspace_bytes < 8 || !aligned(workspace, 4)) return fail(FGS_ERR_INVALID_ARG, "NVFP4 needs a workspace of >= 8 bytes");
     if (q) {
         if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
-        if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0");
+        if (cols % 16) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 16 == 0");
         if (!aligned(q, 16)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte aligned");
     }
     if (qT) {

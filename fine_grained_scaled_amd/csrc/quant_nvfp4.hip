@@ -1,0 +1,384 @@
+// quant_nvfp4.hip -- NVFP4 quantization on gfx950: E2M1 codes (two per
+// byte), one E4M3 scale per 16 contiguous elements, one FP32 tensor scale;
+// optional random 16x16 Hadamard transform along the quantized dimension and
+// stochastic rounding.
+//
+// "NVIDIA developed a method to train neural networks at 4-bit", section
+// "How it works": the 4-bit NVFP4 format, random 16x16 Hadamard transforms
+// of the gradient inputs, stochastic rounding.  The two-level scale:
+//   s_t = fl32(amax_t / 2688)          (2688 = 448 * 6; 1 if amax_t = 0,
+//                                       NaN if amax_t is not finite)
+//   s_b = E4M3_RNE_SAT(fl32(amax_b / fl32(6 * s_t)))   per 16 elements
+//   d   = fl32(dec(s_b) * s_t)
+//   code = E2M1(sat6(fl32(x / d)))     RNE (ties to the even code) or
+//                                       stochastic; d = 0 or NaN -> code 0
+// amax_t is taken over the (transformed) tensor being quantized, so a
+// row-wise and a column-wise output have their own tensor scale.
+//
+// Random Hadamard transform of a 16-chunk: z = d (.) x with the signs d_j
+// (-1 where bit j of sign_mask is set), four butterfly stages with strides
+// 1, 2, 4, 8 ((a, b) -> (a + b, a - b) in FP32), then the exact factor 1/4.
+// Stochastic rounding of |y| between neighbours lo < hi: round up iff
+// (r >> 8) < p * 2^24 with p = (|y| - lo) / (hi - lo) (exact), where the
+// random word of source element i (row * cols + col of x) is
+// r = fmix32(lo32(i) ^ fmix32(lo32(seed) ^ fmix32(hi32(seed) ^ hi32(i)))),
+// fmix32 being MurmurHash3's 32-bit finalizer.
+//
+// Two kernels: a tensor-amax pass (both orientations from one read, one
+// atomic max per workgroup and orientation into the workspace) and the
+// quantize pass.  One workgroup (256 threads, 4 waves) owns a 128 x 128
+// tile of x; thread t (wave w, lane l) holds the 8 x 8 sub-block with
+// columns 8*(l & 15) .. +7 and rows 8*(4w + (l >> 4)) .. +7.  A row-wise
+// 16-chunk spans lanes l, l ^ 1; a column-wise one spans lanes l, l ^ 16.
+#include "fgs_device.h"
+#include "fgs_internal.h"
+
+namespace fgs {
+
+namespace {
+
+constexpr int TB = 128;
+constexpr int TPAD = 16;
+
+__device__ __forceinline__ uint32_t fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+__device__ __forceinline__ float bf16_at(const uint4& v, int j)
+{
+    const uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+__device__ __forceinline__ float xor1(float v)
+{
+    return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), DPP_XOR1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16(float v)
+{
+    return __shfl_xor(v, 16);
+}
+
+// Random Hadamard transform of the 16-chunk whose elements 8*hpos .. 8*hpos+7
+// this lane holds (the partner lane holds the other 8).
+template <bool ROWWISE>
+__device__ __forceinline__ void rht16(float z[8], int hpos, uint32_t sign_mask)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if ((sign_mask >> (8 * hpos + i)) & 1u) z[i] = -z[i];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & h)) {
+                const float a = z[i], b = z[i + h];
+                z[i] = a + b;
+                z[i + h] = a - b;
+            }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float other = ROWWISE ? xor1(z[i]) : xor16(z[i]);
+        z[i] = hpos == 0 ? z[i] + other : other - z[i];
+        z[i] *= 0.25f;
+    }
+}
+
+__device__ __forceinline__ uint32_t fabs_bits(float v) { return as_u32(v) & 0x7FFFFFFFu; }
+
+// max of |z| as FP32 bits (integer order = value order; NaN above Inf)
+__device__ __forceinline__ uint32_t amax8(const float z[8])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, fabs_bits(z[i]));
+    return m;
+}
+
+// E4M3 code of a non-negative FP32 value (RNE, saturating; NaN -> 0x7F)
+__device__ __forceinline__ uint32_t e4m3_code_f32(float a)
+{
+    if (a != a) return 0x7Fu;
+    return e4m3_code_abs(a < 448.0f ? a : 448.0f);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+    return v[0];
+}
+
+// E2M1 magnitude code of a in [0, 6]: nearest, ties to the even code
+__device__ __forceinline__ uint32_t e2m1_rne(float a)
+{
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+           (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+}
+
+// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r
+__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
+{
+    const uint32_t idx = (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) + (uint32_t)(a >= 2.0f) +
+                         (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f) + (uint32_t)(a >= 6.0f);
+    if (idx == 7) return 7;
+    const float lo = idx < 4 ? 0.5f * (float)idx : (idx == 4 ? 2.0f : (idx == 5 ? 3.0f : 4.0f));
+    const float inv_gap = idx < 4 ? 2.0f : (idx < 6 ? 1.0f : 0.5f);
+    const float p = (a - lo) * inv_gap;                    // exact
+    return ((float)(r >> 8) < p * 16777216.0f) ? idx + 1 : idx;
+}
+
+struct TensorScale {
+    float st, six_st;
+};
+
+__device__ __forceinline__ TensorScale tensor_scale_from(uint32_t amax_bits)
+{
+    TensorScale s;
+    if (amax_bits >= 0x7F800000u) s.st = __builtin_nanf("");
+    else if (amax_bits == 0) s.st = 1.0f;
+    else s.st = as_f32(amax_bits) / 2688.0f;
+    s.six_st = 6.0f * s.st;
+    return s;
+}
+
+// Codes of 8 values of one 16-block whose (two-lane) amax bits are amax_b.
+// Returns the 8 nibbles packed (element 2j in the low nibble) and the scale byte.
+template <bool SR>
+__device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b, const TensorScale& ts,
+                                              const uint32_t rw[8], uint32_t& sb_out)
+{
+    const uint32_t sb = e4m3_code_f32(as_f32(amax_b) / ts.six_st);
+    sb_out = sb;
+    const float d = e4m3_value(sb) * ts.st;
+    uint32_t packed = 0;
+    if (d == 0.0f || d != d) return 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float q = y[i] / d;
+        q = q > 6.0f ? 6.0f : (q < -6.0f ? -6.0f : q);
+        const float a = __builtin_fabsf(q);
+        uint32_t c = SR ? e2m1_sr(a, rw[i]) : e2m1_rne(a);
+        c |= (as_u32(q) >> 28) & 0x8u;
+        packed |= c << (4 * i);
+    }
+    return packed;
+}
+
+__device__ __forceinline__ uint32_t sr_word(uint32_t seed_lo, uint32_t seed_hi, uint64_t i)
+{
+    const uint32_t inner = fmix32(seed_hi ^ (uint32_t)(i >> 32));
+    return fmix32((uint32_t)i ^ fmix32(seed_lo ^ inner));
+}
+
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                          int64_t r0, int64_t col, int rg, bool col_ok, uint4 v[8])
+{
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t row = r0 + 8 * rg + u;
+        if (col_ok && row < rows)
+            v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+        else
+            v[u] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------- pass 1 --
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    int rht_mask, uint32_t sign_mask, uint32_t* __restrict__ ws)
+{
+    __shared__ uint32_t red[2][4];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = l & 15, rg = 4 * w + (l >> 4);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    const int64_t col = c0 + 8 * cg;
+    uint4 v[8];
+    load_tile(x, rows, cols, ldx, r0, col, rg, col < cols, v);
+
+    uint32_t plain = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) plain = max(plain, fabs_bits(bf16_at(v[u], j)));
+
+    uint32_t mrow = plain, mcol = plain;
+    if (rht_mask & 1) {
+        mrow = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            float z[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) z[j] = bf16_at(v[u], j);
+            rht16<true>(z, cg & 1, sign_mask);
+            mrow = max(mrow, amax8(z));
+        }
+    }
+    if (rht_mask & 2) {
+        mcol = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float z[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) z[u] = bf16_at(v[u], j);
+            rht16<false>(z, (l >> 4) & 1, sign_mask);
+            mcol = max(mcol, amax8(z));
+        }
+    }
+    mrow = max_xor32(max_xor16(max_lanes16(mrow)));
+    mcol = max_xor32(max_xor16(max_lanes16(mcol)));
+    if (l == 0) {
+        red[0][w] = mrow;
+        red[1][w] = mcol;
+    }
+    __syncthreads();
+    if (t < 2) {
+        const uint32_t m = max(max(red[t][0], red[t][1]), max(red[t][2], red[t][3]));
+        atomicMax(ws + t, m);
+    }
+}
+
+// ---------------------------------------------------------------- pass 2 --
+template <bool SR>
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    int rht_mask, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+    uint8_t* __restrict__ qT, uint8_t* __restrict__ scalesT,
+    float* __restrict__ tensor_scale, const uint32_t* __restrict__ ws)
+{
+    __shared__ __align__(16) uint8_t tbuf[TB][TB / 2 + TPAD];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = l & 15, rg = 4 * w + (l >> 4);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    const int64_t col = c0 + 8 * cg;
+    const bool col_ok = col < cols;
+    uint4 v[8];
+    load_tile(x, rows, cols, ldx, r0, col, rg, col_ok, v);
+
+    const TensorScale ts_row = tensor_scale_from(ws[0]);
+    const TensorScale ts_col = tensor_scale_from(ws[1]);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+        tensor_scale[0] = ts_row.st;
+        tensor_scale[1] = ts_col.st;
+    }
+
+    // ---------------- row-wise: 16-blocks along columns ----------------
+    if (q) {
+        const int64_t qcols = cols / 2, nsc = cols / 16;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            float z[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) z[j] = bf16_at(v[u], j);
+            if (rht_mask & 1) rht16<true>(z, cg & 1, sign_mask);
+            uint32_t mb = amax8(z);
+            const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, DPP_XOR1, 0xF, 0xF, false);
+            mb = max(mb, other);
+            const int64_t row = r0 + 8 * rg + u;
+            uint32_t rw[8];
+            if constexpr (SR) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) rw[j] = sr_word(seed_lo, seed_hi, (uint64_t)(row * cols + col + j));
+            }
+            uint32_t sb;
+            const uint32_t packed = nv_block8<SR>(z, mb, ts_row, rw, sb);
+            if (col_ok && row < rows) {
+                *reinterpret_cast<uint32_t*>(q + row * qcols + col / 2) = packed;
+                if (!(cg & 1)) scales[row * nsc + col / 16] = (uint8_t)sb;
+            }
+        }
+    }
+
+    // ---------------- column-wise: 16-blocks along rows ----------------
+    if (qT) {
+        const int64_t nscT = rows / 16;
+        const int hpos = (l >> 4) & 1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float z[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) z[u] = bf16_at(v[u], j);
+            if (rht_mask & 2) rht16<false>(z, hpos, sign_mask);
+            uint32_t mb = amax8(z);
+            mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+            uint32_t rw[8];
+            if constexpr (SR) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    rw[u] = sr_word(seed_lo, seed_hi, (uint64_t)((r0 + 8 * rg + u) * cols + col + j));
+            }
+            uint32_t sb;
+            const uint32_t packed = nv_block8<SR>(z, mb, ts_col, rw, sb);
+            *reinterpret_cast<uint32_t*>(&tbuf[8 * cg + j][4 * rg]) = packed;
+            if (hpos == 0 && col_ok) scalesT[(col + j) * nscT + (r0 + 8 * rg) / 16] = (uint8_t)sb;
+        }
+        __syncthreads();
+        // 4 lanes write one 64-byte row of qT
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int trow = 64 * i + (t >> 2), chunk = t & 3;
+            const int64_t orow = c0 + trow;
+            if (orow < cols) {
+                const uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
+                *reinterpret_cast<uint4*>(qT + orow * (rows / 2) + r0 / 2 + 16 * chunk) = d;
+            }
+        }
+    }
+}
+
+__global__ void nvfp4_clear_kernel(uint32_t* ws)
+{
+    if (threadIdx.x < 2) ws[threadIdx.x] = 0u;
+}
+
+// Sign mask of the random Hadamard transform: bit j set <=> d_j = -1, with
+// d_j from bit 0 of fmix32(j ^ key), key = fmix32(lo32(seed) ^ fmix32(hi32(seed))).
+uint32_t host_fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+uint32_t rht_sign_mask(uint64_t seed)
+{
+    const uint32_t key = host_fmix32((uint32_t)seed ^ host_fmix32((uint32_t)(seed >> 32)));
+    uint32_t m = 0;
+    for (uint32_t j = 0; j < 16; ++j) m |= (host_fmix32(j ^ key) & 1u) << j;
+    return m;
+}
+
+} // namespace
+
+hipError_t launch_quant_nvfp4(const QuantNVFP4Args& a, hipStream_t stream)
+{
+    const int64_t nbr = (a.rows + TB - 1) / TB, nbc = (a.cols + TB - 1) / TB;
+    if (nbr == 0 || nbc == 0) return hipSuccess;
+    const dim3 grid((unsigned)nbc, (unsigned)nbr), block(256);
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    uint32_t* ws = static_cast<uint32_t*>(a.workspace);
+    const uint32_t mask = rht_sign_mask(a.rht_seed);
+    hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, ws);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask, mask, ws);
+    const uint32_t slo = (uint32_t)a.sr_seed, shi = (uint32_t)(a.sr_seed >> 32);
+    if (a.stochastic)
+        hipLaunchKernelGGL(nvfp4_quant_kernel<true>, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask,
+                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws);
+    else
+        hipLaunchKernelGGL(nvfp4_quant_kernel<false>, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask,
+                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws);
+    return hipGetLastError();
+}
+
+} // namespace fgs

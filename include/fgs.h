@@ -140,7 +140,7 @@ int fgs_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  * round    FGS_ROUND_RNE or FGS_ROUND_STOCHASTIC (applies to both outputs);
  *   the SR word of an element hashes sr_seed with its linear index
  *   row * cols + col in x.
- * Row-wise (needs cols % 128 == 0): q [rows x cols/2], scales u8 [rows][cols/16].
+ * Row-wise (needs cols % 16 == 0): q [rows x cols/2], scales u8 [rows][cols/16].
  * Column-wise (needs rows % 128 == 0): qT [cols x rows/2], scalesT u8
  *   [cols][rows/16].
  * tensor_scale  device FP32 [2]: [0] row-wise s_t, [1] column-wise s_t.
