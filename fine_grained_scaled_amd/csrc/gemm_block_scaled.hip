@@ -1,5 +1,6 @@
-// gemm_fp8.hip -- block-scaled FP8 (E4M3) GEMM and its grouped (MoE)
-// variant on gfx950.
+// gemm_block_scaled.hip -- the block-scaled low-precision GEMM on gfx950:
+// FP32-scaled E4M3 (1x128 / 128x128 / per-tensor), MXFP8 and NVFP4 operands,
+// and the grouped (MoE) variant of the E4M3 blockwise case.
 //
 // "Can you explain the role of FP8 precision in DeepSeek-V3 training":
 // section "Mixed precision framework" (the GEMMs run on FP8 operands),
@@ -12,7 +13,11 @@
 // With a single per-tensor scale on both operands ("Accelerating FP8
 // training performance with the NVIDIA NeMo framework", per-tensor recipe)
 // no per-block factor exists: all of K accumulates in FP32 and the product
-// of the two scales is applied once at the end.
+// of the two scales is applied once at the end.  MXFP8 (same page: one
+// power-of-two scale per 32 values) and NVFP4 ("NVIDIA developed a method to
+// train neural networks at 4-bit": E2M1 with an E4M3 scale per 16 values and
+// an FP32 tensor scale) are decoded exactly into the MFMA operand format, as
+// described at their decoders below.
 //
 // Which matrix instruction: gfx950's FP8 MFMA (v_mfma_*_f8f6f4 and the older
 // *_fp8_fp8 forms) adds each group of 8 consecutive products with only about
@@ -20,13 +25,12 @@
 // 2^-6 does not, and +x - x + tiny gives 0), the same limitation the DeepSeek
 // page describes for its hardware, but *inside* one instruction, where no
 // promotion interval can reach it.  Its error reaches ~1.5e-4 of
-// sum_k |a_k b_k|.  The FP16 MFMA (v_mfma_f32_32x32x16_f16) keeps a full
-// FP32-width sum (256 + 2^-15 survives).  Every E4M3 value is exactly an
-// FP16 value and every product of two is exact in FP32, so the kernel
-// decodes the E4M3 codes to FP16 with the hardware converter
+// sum_k |a_k b_k|.  The FP16 and BF16 MFMAs (v_mfma_f32_32x32x16_{f16,bf16})
+// keep a full FP32-width sum (256 + 2^-15 survives).  Every E4M3 value is
+// exactly an FP16 value and every product of two is exact in FP32, so the
+// kernel decodes the E4M3 codes to FP16 with the hardware converter
 // (v_cvt_scalef32_pk_f16_fp8, unit scale: exact for all 256 codes) and runs
-// the FP16 MFMA: the result is the FP32 sum of exact products, promoted per
-// 128-K block.
+// the FP16 MFMA: the result is the FP32 sum of exact products.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]; both operands K-contiguous.
 // Workgroup: NWM x 2 waves, each owning a 64 x 64 output sub-block (2 x 2
@@ -35,16 +39,17 @@
 // overlaps the other's MFMAs) for dense GEMMs, NWM = 2 for the grouped one
 // (MoE groups are short).  The promoted accumulators and the per-block
 // partial sums of a wave (2 x 64 VGPRs) both stay in VGPRs.  K advances in
-// 128-deep blocks staged in LDS as FP8 bytes, double-buffered, by direct
-// global->LDS loads (global_load_lds_dwordx4: lane i of a wave-instruction
-// fills bytes 16i..16i+15 of a 1 KiB LDS span, i.e. 8 rows of 128 bytes), so
-// the next block streams in while the current one is multiplied without
-// passing through registers.  The 16-byte chunk c of row r sits in LDS slot
-// c ^ ((r >> 1) & 7): the lane that fills slot s of row r fetches chunk
-// s ^ ((r >> 1) & 7), and a fragment read (16 consecutive rows, same chunk,
-// 256 bytes) touches each of the 64 LDS banks once.  MFMA operands are
-// swapped (B fragment first) so each lane's 16 accumulators share one row m:
-// the 1x128 A scale is one value per lane and per sub-tile row.
+// 128-deep blocks staged in LDS as code bytes (128 bytes per row for E4M3,
+// 64 for E2M1), double-buffered, by direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of a wave-instruction fills bytes
+// 16i..16i+15 of a 1 KiB LDS span), so the next block streams in while the
+// current one is multiplied without passing through registers.  The 16-byte
+// chunk c of staged row r sits in LDS slot c ^ ((r >> 1) & 7) (128-byte
+// rows) or c ^ ((r >> 2) & 3) (64-byte rows): the lane that fills a slot
+// fetches the matching chunk, and a fragment read (16 consecutive rows, same
+// chunk, 256 bytes) touches each of the 64 LDS banks once.  MFMA operands
+// are swapped (B fragment first) so each lane's 16 accumulators share one
+// row m: the 1x128 A scale is one value per lane and per sub-tile row.
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -59,7 +64,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128, BK = 128;
-constexpr int ROW = BK;                   // LDS bytes per staged row (swizzled, unpadded)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* gbl_ptr;
@@ -83,7 +87,9 @@ struct GemmParams {
     const uint8_t* B;
     const float* sA;
     const float* sB;
-    int64_t lda, ldb, M, N, K;
+    const float* tsA;             // NVFP4 tensor scales (device FP32 [1])
+    const float* tsB;
+    int64_t lda, ldb, M, N, K;    // lda, ldb in bytes
     void* C;
     int64_t ldc;
     const int32_t* offsets;
@@ -164,7 +170,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int NWM>
+// NVFP4: 32 E2M1 codes (one 16-byte LDS read of a lane) -> four FP16
+// 8-vectors, word g holding the codes of MFMA k-step g; each code is
+// multiplied by its 16-block's E4M3 scale (s01: the scales of words 0-1 and
+// 2-3).  E2M1 * E4M3 lies in {0} u [2^-10, 2688] with at most 6 significant
+// bits, so every product is an exact FP16 value.
+__device__ __forceinline__ f16x8 decode_nv_word(uint32_t w, _Float16 s)
+{
+    const f16x2 ss = {s, s};
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int NWM, int ROW>
 struct Lds {
     static constexpr int BM = 64 * NWM;
     static constexpr int A_BYTES = BM * ROW;
@@ -181,10 +202,17 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
     constexpr int WM = 64;
     constexpr int TI = 2;                // sub-tiles along m per wave
     constexpr int TJ = 2;                // sub-tiles along n per wave
-    constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR);
+    constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR) &&
+                             AMODE != FGS_SCALE_NV16_E4M3;
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
     constexpr bool MX = AMODE == FGS_SCALE_MX32_E8M0;
-    using L = Lds<NWM>;
+    constexpr bool NV = AMODE == FGS_SCALE_NV16_E4M3;
+    // staged row: 128 K-elements = 128 bytes (E4M3) or 64 bytes (E2M1)
+    constexpr int ROW = NV ? 64 : 128;
+    constexpr int CPR = ROW / 16;            // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
+    constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
+    using L = Lds<NWM, ROW>;
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
@@ -259,41 +287,42 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 
     // ------------------------------------------------------- loaders --
     // wave w stages rows [A_ROWS*w, A_ROWS*(w+1)) of A and [B_ROWS*w, ...)
-    // of B, 8 rows per wave-instruction; lane l fills slot l & 7 of row
-    // rbase + (l >> 3) with chunk (l & 7) ^ ((row >> 1) & 7).  Rows past the
-    // end are clamped (their products land in rows/columns never stored).
+    // of B, RPI rows per wave-instruction; lane l fills slot l % CPR of row
+    // rbase + l / CPR with chunk (l % CPR) ^ ((row >> SH) & (CPR - 1)).  Rows
+    // past the end are clamped (their products land in rows/columns never
+    // stored).
     constexpr int A_ROWS = BM / NW, B_ROWS = BN / NW;
-    constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
+    constexpr int A_INSTR = A_ROWS / RPI, B_INSTR = B_ROWS / RPI;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the wave count");
-    const int srow = l >> 3;
+    const int srow = l / CPR, sslot = l % CPR;
     const uint8_t* a_src[A_INSTR];
     const uint8_t* b_src[B_INSTR];
 #pragma unroll
     for (int u = 0; u < A_INSTR; ++u) {
-        const int lr = A_ROWS * w + 8 * u + srow;
+        const int lr = A_ROWS * w + RPI * u + srow;
         int64_t r = m0 + lr;
         r = r < m_end ? r : m_end - 1;
-        a_src[u] = p.A + r * p.lda + 16 * ((l & 7) ^ ((lr >> 1) & 7));
+        a_src[u] = p.A + r * p.lda + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
 #pragma unroll
     for (int u = 0; u < B_INSTR; ++u) {
-        const int lr = B_ROWS * w + 8 * u + srow;
+        const int lr = B_ROWS * w + RPI * u + srow;
         int64_t r = n0 + lr;
         r = r < p.N ? r : p.N - 1;
-        b_src[u] = Bp + r * p.ldb + 16 * ((l & 7) ^ ((lr >> 1) & 7));
+        b_src[u] = Bp + r * p.ldb + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
     int64_t sb_col = n0 + 64 * (w & 1) + l;        // B 1x128 scales: waves 0 and 1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
 
     auto stage_block = [&](int64_t kb, int stage) {
         uint8_t* st = smem + stage * L::STAGE;
-        const int64_t ko = kb * BK;
+        const int64_t ko = kb * ROW;
 #pragma unroll
         for (int u = 0; u < A_INSTR; ++u)
-            g2lds16(a_src[u] + ko, st + (A_ROWS * w + 8 * u) * ROW);
+            g2lds16(a_src[u] + ko, st + (A_ROWS * w + RPI * u) * ROW);
 #pragma unroll
         for (int u = 0; u < B_INSTR; ++u)
-            g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + 8 * u) * ROW);
+            g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
         if constexpr (B_TILE)
             if (w < 2) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
     };
@@ -346,6 +375,20 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
         for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc);
         publish_ebt(0);
     }
+    // NVFP4 scales: the eight E4M3 bytes of a fragment row's 128-K block are
+    // two aligned 32-bit words (16-blocks 0-3 and 4-7)
+    const int64_t ksn = p.K / 16;
+    uint32_t a_nw_next[TI][2], b_nw_next[TJ][2];
+    if constexpr (NV) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) a_nw_next[i][h] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksn + 4 * h);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) b_nw_next[j][h] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksn + 4 * h);
+    }
 
     // prologue: block 0 -> stage 0
     stage_block(0, 0);
@@ -360,9 +403,9 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
     __syncthreads();
 
     // fragment read offsets: row R = base + (l & 31) (base a multiple of
-    // 32) has (R >> 1) & 7 == (l >> 1) & 7; chunk 2*ks + h (h = lane half)
-    // lives in slot (2*ks + h) ^ ((l >> 1) & 7)
-    const int swz = (l >> 1) & 7, half = l >> 5;
+    // 32) has (R >> SH) & (CPR - 1) == (l >> SH) & (CPR - 1); chunk c of the
+    // row lives in slot c ^ swz
+    const int swz = (l >> SH) & (CPR - 1), half = l >> 5;
 
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int cur = (int)(kb & 1);
@@ -372,7 +415,13 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 #pragma unroll
         for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 ? sa_next[i] : 1.0f;
         const float sb_blk = sb_next;
-        uint32_t a_sw[TI], b_sw[TJ];
+        uint32_t a_sw[TI], b_sw[TJ], a_nw[TI][2], b_nw[TJ][2];
+        if constexpr (NV) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) { a_nw[i][0] = a_nw_next[i][0]; a_nw[i][1] = a_nw_next[i][1]; }
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) { b_nw[j][0] = b_nw_next[j][0]; b_nw[j][1] = b_nw_next[j][1]; }
+        }
         if constexpr (MX) {
 #pragma unroll
             for (int i = 0; i < TI; ++i) a_sw[i] = a_sw_next[i];
@@ -386,6 +435,18 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
                 for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
             }
             if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb + kb + 1];
+            if constexpr (NV) {
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        a_nw_next[i][h] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksn + 8 * (kb + 1) + 4 * h);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        b_nw_next[j][h] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksn + 8 * (kb + 1) + 4 * h);
+            }
             if constexpr (MX) {
 #pragma unroll
                 for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc + 4 * (kb + 1));
@@ -422,6 +483,45 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
         // lane half h reads chunk 2*ks + h (bytes 32*ks + 16*h .. +15) of its
         // row: the pair of k-steps (2ks, 2ks+1) then covers k = 32*ks ..
         // 32*ks+31 once, with the same k order for A and B
+        if constexpr (NV) {
+            // lane half h reads chunk 2*ks2 + h (32 codes, k = 64*ks2 + 32*h ..
+            // +31); word g of it feeds MFMA k-step (ks2, g), whose 16-block is
+            // 4*ks2 + 2*h + g/2
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                const int co = ((2 * ks2 + half) ^ swz) << 4;
+                f16x2 sa2[TI], sb2[TJ];
+                uint4 ra[TI], rb[TJ];
+#pragma unroll
+                for (int i = 0; i < TI; ++i) {
+                    sa2[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_nw[i][ks2] >> (16 * half), 1.0f, false);
+                    ra[i] = *reinterpret_cast<const uint4*>(la + 32 * i * ROW + co);
+                }
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    sb2[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_nw[j][ks2] >> (16 * half), 1.0f, false);
+                    rb[j] = *reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co);
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f16x8 af[TI], bf[TJ];
+#pragma unroll
+                    for (int i = 0; i < TI; ++i) {
+                        const uint32_t wd = g == 0 ? ra[i].x : g == 1 ? ra[i].y : g == 2 ? ra[i].z : ra[i].w;
+                        af[i] = decode_nv_word(wd, sa2[i][g >> 1]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j) {
+                        const uint32_t wd = g == 0 ? rb[j].x : g == 1 ? rb[j].y : g == 2 ? rb[j].z : rb[j].w;
+                        bf[j] = decode_nv_word(wd, sb2[j][g >> 1]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < TI; ++i)
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
+                }
+            }
+        } else
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int co = ((2 * ks + half) ^ swz) << 4;
@@ -513,7 +613,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
     }
 
     if constexpr (!PROMOTE) {
-        const float f = p.sA[0] * sBp[0];
+        const float f = NV ? p.tsA[0] * p.tsB[0] : p.sA[0] * sBp[0];
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -562,7 +662,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
 template <int NWM, int AMODE, int BMODE, bool GROUPED>
 hipError_t launch_modes(const GemmParams& p, bool bf16, dim3 grid, hipStream_t s)
 {
-    const size_t lds = 2 * (size_t)Lds<NWM>::STAGE;
+    const size_t lds = 2 * (size_t)Lds<NWM, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128>::STAGE;
     auto k = bf16 ? gemm_fp8_kernel<NWM, AMODE, BMODE, true, GROUPED>
                   : gemm_fp8_kernel<NWM, AMODE, BMODE, false, GROUPED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -584,6 +684,8 @@ hipError_t dispatch(const GemmParams& p, int amode, int bmode, bool bf16, dim3 g
     } else if constexpr (!GROUPED) {
         if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0)
             return launch_modes<NWM, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, bf16, grid, s);
+        if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3)
+            return launch_modes<NWM, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, bf16, grid, s);
         if (amode == FGS_SCALE_TENSOR) {
             if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
             if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
@@ -602,8 +704,11 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.B = static_cast<const uint8_t*>(a.B.data);
     p.sA = static_cast<const float*>(a.A.scales);
     p.sB = static_cast<const float*>(a.B.scales);
-    p.lda = a.A.ld;
-    p.ldb = a.B.ld;
+    const bool nv = a.A.elem == FGS_ELEM_E2M1;
+    p.lda = nv ? a.A.ld / 2 : a.A.ld;
+    p.ldb = nv ? a.B.ld / 2 : a.B.ld;
+    p.tsA = a.A.tensor_scale;
+    p.tsB = a.B.tensor_scale;
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
@@ -628,8 +733,14 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     return dispatch<NWM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
 }
 
-// MXFP8 operands take the same kernel (E8M0 scale handling selected by mode).
+// MXFP8 and NVFP4 operands take the same kernel (decode and scale handling
+// selected by the scale mode).
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t stream)
+{
+    return launch_gemm_fp8(a, stream);
+}
+
+hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t stream)
 {
     return launch_gemm_fp8(a, stream);
 }
