@@ -1,30 +1,37 @@
 #!/usr/bin/env python3
-"""Throughput of the fine-grained scaled FP8 training path on one MI355X.
+"""Throughput of the fine-grained scaled low-precision training path on one
+MI355X.
 
-One step is one pass of the whole path over the Llama-3-8B linear layers
-(M = 8192 tokens; (K, N) = (4096, 6144) QKV, (4096, 4096) O, (4096, 28672)
-gate+up, (14336, 4096) down) in both scaling recipes the pages compare
-("Accelerating FP8 training performance with the NVIDIA NeMo framework":
-per-tensor current scaling vs block-wise scaling; "Can you explain the role of
-FP8 precision in DeepSeek-V3 training", "Fine-grained quantization": 1x128
-activation/gradient tiles, 128x128 weight blocks).  For every layer and
-recipe the step runs:
+The headline workload (`value`): one step is one pass of the path over the
+Llama-3-8B linear layers (M = 8192 tokens; (K, N) = (4096, 6144) QKV,
+(4096, 4096) O, (4096, 28672) gate+up, (14336, 4096) down) in both scaling
+recipes the pages compare ("Accelerating FP8 training performance with the
+NVIDIA NeMo framework": per-tensor current scaling vs block-wise scaling;
+"Can you explain the role of FP8 precision in DeepSeek-V3 training",
+"Fine-grained quantization": 1x128 activation/gradient tiles, 128x128
+weight blocks).  For every layer and recipe the step runs
   quantize X  (row-wise for fwd, column-wise along M for wgrad; one read)
   quantize W  (row-wise for fwd, transposed for dgrad; one read)
   quantize dY (row-wise along N for dgrad, column-wise along M for wgrad)
   fwd   Y  = X  W^T   (BF16 out)
   dgrad dX = dY W     (BF16 out)
   wgrad dW = dY^T X   (FP32 out)
-Inputs are seeded synthetic BF16 tensors with the pages' shapes and
-statistics, resident in HBM before timing starts.  `value` is the step's
-GEMM FLOPs over its wall time (quantization included) in TFLOP/s.
+`value` is the step's GEMM FLOPs over its wall time (quantization
+included) in TFLOP/s.  Inputs are seeded synthetic BF16 tensors resident in
+HBM before timing starts.
 
-Prints ONE JSON line on stdout; a per-kernel breakdown goes to stderr.
+The other workloads of the path are measured in the same run and reported
+under "workloads" (per-kernel throughput against the roofline): the tiny
+blockwise GEMM, the DeepSeek-V3 MoE grouped GEMM, MXFP8 at Llama-3.1-405B
+shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes.
+
+Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -34,93 +41,367 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "block-scaled FP8 GEMM TFLOP/s + quant GB/s (% of MI355X peak), 8B/405B shapes"
-M_TOKENS = 8192
-LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
+PEAK_FP16_MFMA = 2500.0     # TFLOP/s, MI355X dense FP16/BF16 matrix peak
+PEAK_FP8_MFMA = 5000.0      # TFLOP/s, MI355X dense FP8 matrix peak (context)
+PEAK_HBM = 8000.0           # GB/s, MI355X HBM3E
+
+LLAMA8B_M = 8192
+LLAMA8B_LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
 RECIPES = [("blockwise", "tile", "block"), ("per_tensor", "tensor", "tensor")]
-PEAK_FP16_MFMA_TFLOPS = 2500.0     # MI355X dense FP16 matrix peak
-PEAK_FP8_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (context)
-PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+
+MOE_TOKENS, MOE_EXPERTS, MOE_HIDDEN, MOE_INTER = 32768, 256, 7168, 2048
+MX_M = 4096
+MX_LAYERS = [("qkv", 16384, 18432), ("o", 16384, 16384), ("gate_up", 16384, 106496), ("down", 53248, 16384)]
+NV_M = 8192
+NV_LAYERS = [("up", 5120, 20480), ("down", 20480, 5120)]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def quant_bytes(rows, cols, mode):
-    """Algorithmic HBM bytes of one dual-output (row-wise + column-wise)
-    E4M3 quantization: read BF16 once, write both code tensors and their
-    scales; per-tensor scaling reads the input a second time for the amax."""
+# --------------------------------------------------------------------------
+# algorithmic byte counts (what the method itself must move)
+# --------------------------------------------------------------------------
+def e4m3_bytes(rows, cols, mode, outputs=2):
+    """Read BF16 once, write `outputs` code tensors and their FP32 scales;
+    per-tensor scaling reads the input a second time for the amax."""
     n = rows * cols
-    b = 2 * n + 2 * n
+    b = 2 * n + outputs * n
     if mode == "tile":
-        b += 4 * (n // 128) * 2
+        b += outputs * 4 * (n // 128)
     elif mode == "block":
-        b += 4 * (rows // 128) * (cols // 128) * 2
+        b += outputs * 4 * math.ceil(rows / 128) * math.ceil(cols / 128)
     else:
-        b += 2 * n + 8
+        b += 2 * n + 4 * outputs
     return b
 
 
-class Inputs:
-    def __init__(self, dev):
-        import torch
-        from fine_grained_scaled_amd import synth
+def mx_bytes(rows, cols, outputs):
+    n = rows * cols
+    return 2 * n + outputs * (n + n // 32)
+
+
+def nvfp4_bytes(rows, cols, outputs):
+    """Tensor-amax pass (read) + quantize pass (read, codes at 4 bits, one
+    E4M3 scale byte per 16)."""
+    n = rows * cols
+    return 2 * n + 2 * n + outputs * (n // 2 + n // 16)
+
+
+# --------------------------------------------------------------------------
+# timing of individual launches with HIP events on torch's current stream
+# (the stream the library launches on)
+# --------------------------------------------------------------------------
+class Timer:
+    def __init__(self, torch, enabled=True):
+        self.torch = torch
+        self.enabled = enabled
+        self.rec = []
+
+    def run(self, kind, label, units, fn):
+        if not self.enabled:
+            return fn()
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn()
+        e1.record()
+        self.rec.append((kind, label, units, e0, e1))
+        return r
+
+    def summary(self):
+        kinds, labels = {}, {}
+        for kind, label, units, e0, e1 in self.rec:
+            t = e0.elapsed_time(e1) * 1e-3
+            u, s, n = kinds.get(kind, (0.0, 0.0, 0))
+            kinds[kind] = (u + units, s + t, n + 1)
+            u, s, n = labels.get((kind, label), (0.0, 0.0, 0))
+            labels[(kind, label)] = (u + units, s + t, n + 1)
+        return kinds, labels
+
+
+def gpu_normal(torch, shape, seed, sigma=1.0, outlier_cols=None):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    v = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    if sigma != 1.0:
+        v *= sigma
+    if outlier_cols is not None and len(outlier_cols):
+        v[:, torch.as_tensor(outlier_cols, device="cuda")] *= 50.0
+    return v.to(torch.bfloat16)
+
+
+def gpu_t3(torch, shape, seed):
+    """Student-t(3) scaled to std 1e-3: Z / sqrt(chi2_3 / 3) * 1e-3 / sqrt(3)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    z = torch.randn((4,) + tuple(shape), generator=g, device="cuda", dtype=torch.float32)
+    v = (z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0
+    return (z[0] / v.sqrt() * (1e-3 / math.sqrt(3.0))).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------
+# headline: Llama-3-8B linear layers, both recipes
+# --------------------------------------------------------------------------
+class Llama8B:
+    name = "llama3_8b_linears"
+
+    def __init__(self, torch, fgs, synth):
+        self.torch, self.fgs = torch, fgs
         t0 = time.time()
-        self.x = {}
-        self.w = {}
-        self.dy = {}
-        for name, K, N in LAYERS:
+        self.x, self.w, self.dy, self.out = {}, {}, {}, {}
+        for i, (name, K, N) in enumerate(LLAMA8B_LAYERS):
             if K not in self.x:
-                self.x[K] = synth.to_torch_bf16(synth.activations(M_TOKENS, K, seed=0)).to(dev)
-            self.w[name] = synth.to_torch_bf16(synth.weights(N, K, seed=0, tag=synth.TAG_W + 16 * (1 + LAYERS.index((name, K, N))))).to(dev)
+                self.x[K] = synth.to_torch_bf16(synth.activations(LLAMA8B_M, K, seed=0)).cuda()
+            self.w[name] = synth.to_torch_bf16(synth.weights(N, K, seed=0, tag=synth.TAG_W + 16 * (1 + i))).cuda()
             if N not in self.dy:
-                self.dy[N] = synth.to_torch_bf16(synth.gradients(M_TOKENS, N, seed=0)).to(dev)
+                self.dy[N] = synth.to_torch_bf16(synth.gradients(LLAMA8B_M, N, seed=0)).cuda()
+            for rname, _, _ in RECIPES:
+                self.out[(rname, name, "y")] = torch.empty((LLAMA8B_M, N), dtype=torch.bfloat16, device="cuda")
+                self.out[(rname, name, "dx")] = torch.empty((LLAMA8B_M, K), dtype=torch.bfloat16, device="cuda")
+                self.out[(rname, name, "dw")] = torch.empty((N, K), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        log(f"[bench] synthetic inputs generated and uploaded in {time.time() - t0:.1f} s")
+        log(f"[bench] {self.name}: inputs generated and uploaded in {time.time() - t0:.1f} s")
+
+    def flops(self):
+        return len(RECIPES) * sum(3 * 2.0 * LLAMA8B_M * N * K for _, K, N in LLAMA8B_LAYERS)
+
+    def step(self, tm):
+        torch, fgs = self.torch, self.fgs
+        for rname, amode, wmode in RECIPES:
+            for name, K, N in LLAMA8B_LAYERS:
+                X, W, dY = self.x[K], self.w[name], self.dy[N]
+                lab = f"{rname}/{name}"
+                qx = tm.run("quant", lab + "/X", e4m3_bytes(LLAMA8B_M, K, amode),
+                            lambda: fgs.quantize_blockwise(X, amode, rowwise=True, colwise=True))
+                qw = tm.run("quant", lab + "/W", e4m3_bytes(N, K, wmode),
+                            lambda: fgs.quantize_blockwise(W, wmode, rowwise=True, colwise=True))
+                qdy = tm.run("quant", lab + "/dY", e4m3_bytes(LLAMA8B_M, N, amode),
+                             lambda: fgs.quantize_blockwise(dY, amode, rowwise=True, colwise=True))
+                f = 2.0 * LLAMA8B_M * N * K
+                o = self.out
+                tm.run("gemm", lab + "/fwd", f, lambda: fgs.gemm_block_scaled(
+                    qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(rname, name, "y")]))
+                tm.run("gemm", lab + "/dgrad", f, lambda: fgs.gemm_block_scaled(
+                    qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(rname, name, "dx")]))
+                tm.run("gemm", lab + "/wgrad", f, lambda: fgs.gemm_block_scaled(
+                    qdy.colwise(), qx.colwise(), torch.float32, out=o[(rname, name, "dw")]))
 
 
-def run_step(fgs, torch, inp, outs, rec):
-    """One pass of the path; `rec` collects (kind, algorithmic units, start, end) events."""
-    for rname, amode, wmode in RECIPES:
-        for name, K, N in LAYERS:
-            X, W, dY = inp.x[K], inp.w[name], inp.dy[N]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
-            e[0].record()
-            qx = fgs.quantize_blockwise(X, amode, rowwise=True, colwise=True)
-            e[1].record()
-            qw = fgs.quantize_blockwise(W, wmode, rowwise=True, colwise=True)
-            e[2].record()
-            qdy = fgs.quantize_blockwise(dY, amode, rowwise=True, colwise=True)
-            e[3].record()
-            e[4].record()
-            fgs.gemm_block_scaled(qx.rowwise(), qw.rowwise(), torch.bfloat16, out=outs[(rname, name, "y")])
-            e[5].record()
-            e[6].record()
-            fgs.gemm_block_scaled(qdy.rowwise(), qw.colwise(), torch.bfloat16, out=outs[(rname, name, "dx")])
-            e[7].record()
-            e[8].record()
-            fgs.gemm_block_scaled(qdy.colwise(), qx.colwise(), torch.float32, out=outs[(rname, name, "dw")])
-            e[9].record()
-            if rec is not None:
-                rec.append(("quant", quant_bytes(M_TOKENS, K, amode), e[0], e[1], f"{rname}/{name}/X"))
-                rec.append(("quant", quant_bytes(N, K, wmode), e[1], e[2], f"{rname}/{name}/W"))
-                rec.append(("quant", quant_bytes(M_TOKENS, N, amode), e[2], e[3], f"{rname}/{name}/dY"))
-                f = 2.0 * M_TOKENS * N * K
-                rec.append(("gemm", f, e[4], e[5], f"{rname}/{name}/fwd"))
-                rec.append(("gemm", f, e[6], e[7], f"{rname}/{name}/dgrad"))
-                rec.append(("gemm", f, e[8], e[9], f"{rname}/{name}/wgrad"))
+# --------------------------------------------------------------------------
+# tiny blockwise GEMM (launch-bound; time only)
+# --------------------------------------------------------------------------
+class Tiny:
+    name = "tiny_blockwise_128x256x256"
+
+    def __init__(self, torch, fgs, synth):
+        self.torch, self.fgs = torch, fgs
+        self.a = synth.to_torch_bf16(synth.activations(128, 256, seed=0)).cuda()
+        self.b = synth.to_torch_bf16(synth.weights(256, 256, seed=0)).cuda()
+        self.c = torch.empty((128, 256), dtype=torch.float32, device="cuda")
+
+    def flops(self):
+        return 2.0 * 128 * 256 * 256
+
+    def step(self, tm):
+        fgs = self.fgs
+        qa = tm.run("quant", "A", e4m3_bytes(128, 256, "tile", 1), lambda: fgs.quantize_blockwise(self.a, "tile"))
+        qb = tm.run("quant", "B", e4m3_bytes(256, 256, "block", 1), lambda: fgs.quantize_blockwise(self.b, "block"))
+        tm.run("gemm", "fwd", self.flops(), lambda: fgs.gemm_block_scaled(
+            qa.rowwise(), qb.rowwise(), self.torch.float32, out=self.c))
 
 
-def step_flops():
-    return len(RECIPES) * sum(3 * 2.0 * M_TOKENS * N * K for _, K, N in LAYERS)
+# --------------------------------------------------------------------------
+# DeepSeek-V3 MoE: grouped GEMMs over 256 experts, Zipf(1.1) token counts
+# --------------------------------------------------------------------------
+class MoE:
+    name = "deepseek_v3_moe_grouped"
+
+    def __init__(self, torch, fgs, synth):
+        import numpy as np
+        self.torch, self.fgs = torch, fgs
+        t0 = time.time()
+        counts = synth.expert_counts(MOE_TOKENS, MOE_EXPERTS, 1.1, seed=0)
+        self.counts = counts
+        self.offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+        T, H, I, G = MOE_TOKENS, MOE_HIDDEN, MOE_INTER, MOE_EXPERTS
+        self.a1 = gpu_normal(torch, (T, H), 101, outlier_cols=synth.outlier_channels(H, 0))
+        self.a2 = gpu_normal(torch, (T, I), 102, outlier_cols=synth.outlier_channels(I, 0))
+        # expert weights, quantized once (128x128 blocks never straddle experts)
+        self.w1 = self._expert_weights(G, 2 * I, H, 103)     # gate+up: 7168 -> 4096
+        self.w2 = self._expert_weights(G, H, I, 104)         # down:    2048 -> 7168
+        self.y1 = torch.empty((T, 2 * I), dtype=torch.bfloat16, device="cuda")
+        self.y2 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {self.name}: expert weights generated and quantized in {time.time() - t0:.1f} s "
+            f"(token counts max {counts.max()}, min {counts.min()}, {int((counts < 128).sum())} experts < 128)")
+
+    def _expert_weights(self, G, N, K, seed):
+        torch, fgs = self.torch, self.fgs
+        codes = torch.empty((G * N, K), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((G * (N // 128), K // 128), dtype=torch.float32, device="cuda")
+        chunk = 8
+        for g0 in range(0, G, chunk):
+            w = gpu_normal(torch, (chunk * N, K), seed * 1000 + g0, sigma=0.02)
+            q = fgs.quantize_blockwise(w, "block")
+            codes[g0 * N:(g0 + chunk) * N] = q.q
+            scales[g0 * (N // 128):(g0 + chunk) * (N // 128)] = q.scales
+            del w, q
+        return fgs.Operand(codes, scales, fgs.SCALE_BLOCK_128x128)
+
+    def flops(self):
+        return 2.0 * MOE_TOKENS * (2 * MOE_INTER * MOE_HIDDEN + MOE_HIDDEN * MOE_INTER)
+
+    def gemm_bytes(self, N, K):
+        """Algorithmic HBM bytes of one grouped GEMM: A codes and scales,
+        the weights of every expert that has tokens, BF16 output."""
+        active = int((self.counts > 0).sum())
+        return MOE_TOKENS * K * (1 + 4 / 128) + active * N * K * (1 + 4 / 16384) + 2 * MOE_TOKENS * N
+
+    def roofline_seconds(self, N, K):
+        """Sum over experts of max(MFMA time at the FP16 peak, HBM time)."""
+        t = 0.0
+        for c in self.counts:
+            if c == 0:
+                continue
+            fl = 2.0 * c * N * K
+            by = c * K * (1 + 4 / 128) + N * K * (1 + 4 / 16384) + 2 * c * N
+            t += max(fl / (PEAK_FP16_MFMA * 1e12), by / (PEAK_HBM * 1e9))
+        return t
+
+    def step(self, tm):
+        torch, fgs = self.torch, self.fgs
+        T, H, I = MOE_TOKENS, MOE_HIDDEN, MOE_INTER
+        qa1 = tm.run("quant", "A1", e4m3_bytes(T, H, "tile", 1), lambda: fgs.quantize_blockwise(self.a1, "tile"))
+        tm.run("gemm", "gate_up", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
+            qa1.rowwise(), self.w1, self.offsets, 2 * I, torch.bfloat16, out=self.y1))
+        qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 1), lambda: fgs.quantize_blockwise(self.a2, "tile"))
+        tm.run("gemm", "down", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
+            qa2.rowwise(), self.w2, self.offsets, H, torch.bfloat16, out=self.y2))
+
+
+# --------------------------------------------------------------------------
+# MXFP8 at Llama-3.1-405B shapes (one GPU's share, one layer): fwd + wgrad
+# --------------------------------------------------------------------------
+class MX405B:
+    name = "llama31_405b_mxfp8"
+
+    def __init__(self, torch, fgs, synth):
+        self.torch, self.fgs = torch, fgs
+        t0 = time.time()
+        self.x, self.w, self.dy, self.out = {}, {}, {}, {}
+        for i, (name, K, N) in enumerate(MX_LAYERS):
+            if K not in self.x:
+                self.x[K] = gpu_normal(torch, (MX_M, K), 200 + i)
+            self.w[name] = gpu_normal(torch, (N, K), 210 + i, sigma=0.02)
+            self.dy[name] = gpu_normal(torch, (MX_M, N), 220 + i)
+            self.out[(name, "y")] = torch.empty((MX_M, N), dtype=torch.bfloat16, device="cuda")
+            self.out[(name, "dw")] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {self.name}: inputs generated in {time.time() - t0:.1f} s")
+
+    def flops(self):
+        return sum(2 * 2.0 * MX_M * N * K for _, K, N in MX_LAYERS)
+
+    def step(self, tm):
+        torch, fgs = self.torch, self.fgs
+        for name, K, N in MX_LAYERS:
+            X, W, dY = self.x[K], self.w[name], self.dy[name]
+            qx = tm.run("quant", name + "/X", mx_bytes(MX_M, K, 2), lambda: fgs.quantize_mx(X, rowwise=True, colwise=True))
+            qw = tm.run("quant", name + "/W", mx_bytes(N, K, 1), lambda: fgs.quantize_mx(W))
+            qdy = tm.run("quant", name + "/dY", mx_bytes(MX_M, N, 1),
+                         lambda: fgs.quantize_mx(dY, rowwise=False, colwise=True))
+            f = 2.0 * MX_M * N * K
+            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
+                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")]))
+            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
+                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")]))
+
+
+# --------------------------------------------------------------------------
+# NVFP4 at 12B-hybrid-like shapes: fwd, dgrad, wgrad (RHT + SR on wgrad)
+# --------------------------------------------------------------------------
+class NV12B:
+    name = "hybrid12b_nvfp4"
+
+    def __init__(self, torch, fgs, synth):
+        self.torch, self.fgs = torch, fgs
+        self.rht_seed = synth.derived_seed(0, synth.TAG_RHT)
+        self.sr_seed = synth.derived_seed(0, synth.TAG_SR)
+        t0 = time.time()
+        self.x, self.w, self.dy, self.out = {}, {}, {}, {}
+        for i, (name, K, N) in enumerate(NV_LAYERS):
+            self.x[name] = gpu_normal(torch, (NV_M, K), 300 + i)
+            self.w[name] = gpu_normal(torch, (N, K), 310 + i, sigma=0.02)
+            self.dy[name] = gpu_t3(torch, (NV_M, N), 320 + i)
+            self.out[(name, "y")] = torch.empty((NV_M, N), dtype=torch.bfloat16, device="cuda")
+            self.out[(name, "dx")] = torch.empty((NV_M, K), dtype=torch.bfloat16, device="cuda")
+            self.out[(name, "dw")] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {self.name}: inputs generated in {time.time() - t0:.1f} s")
+
+    def flops(self):
+        return sum(3 * 2.0 * NV_M * N * K for _, K, N in NV_LAYERS)
+
+    def step(self, tm):
+        torch, fgs = self.torch, self.fgs
+        for name, K, N in NV_LAYERS:
+            X, W, dY = self.x[name], self.w[name], self.dy[name]
+            qx = tm.run("quant", name + "/X", nvfp4_bytes(NV_M, K, 2), lambda: fgs.quantize_nvfp4(
+                X, rowwise=True, colwise=True, rht_mask=2, rht_seed=self.rht_seed))
+            qw = tm.run("quant", name + "/W", nvfp4_bytes(N, K, 2), lambda: fgs.quantize_nvfp4(
+                W, rowwise=True, colwise=True))
+            qdy = tm.run("quant", name + "/dY", nvfp4_bytes(NV_M, N, 2), lambda: fgs.quantize_nvfp4(
+                dY, rowwise=True, colwise=True, rht_mask=2, rht_seed=self.rht_seed,
+                stochastic=True, sr_seed=self.sr_seed))
+            f = 2.0 * NV_M * N * K
+            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
+                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")]))
+            tm.run("gemm", name + "/dgrad", f, lambda: fgs.gemm_block_scaled(
+                qdy.rowwise(), qw.colwise(), torch.bfloat16, out=self.out[(name, "dx")]))
+            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
+                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")]))
+
+
+WORKLOADS = {"llama3_8b": Llama8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B, "nv12b": NV12B}
+
+
+def measure(torch, wl, steps, warmup):
+    for _ in range(warmup):
+        wl.step(Timer(torch, enabled=False))
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kinds, labels = tm.summary()
+    for (kind, label), (u, t, n) in labels.items():
+        rate = f"{u / t / 1e12:8.1f} TFLOP/s" if kind == "gemm" else f"{u / t / 1e9:8.1f} GB/s"
+        log(f"  {wl.name:28s} {label:24s} {t / n * 1e6:9.1f} us  {rate}")
+    return wall, kinds
+
+
+def kind_report(kinds, steps):
+    out = {}
+    if "gemm" in kinds:
+        f, t, n = kinds["gemm"]
+        out["gemm"] = {"TFLOP/s": round(f / t / 1e12, 2), "frac_fp16_mfma_peak": round(f / t / 1e12 / PEAK_FP16_MFMA, 4),
+                       "ms_per_step": round(t / steps * 1e3, 4)}
+    if "quant" in kinds:
+        b, t, n = kinds["quant"]
+        out["quant"] = {"GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM, 4),
+                        "ms_per_step": round(t / steps * 1e3, 4)}
+    return out
 
 
 def cpu_baseline():
-    """The oracle, untuned, on a bounded sample of the same workload: the QKV
-    layer (K = 4096, N = 6144) with M cut to 256 tokens, both recipes:
+    """The oracle, untuned, on a bounded sample of the headline workload: the
+    QKV layer (K = 4096, N = 6144) with M cut to 256 tokens, both recipes:
     oracle quantization of X, W, dY (row-wise and column-wise) and the three
     FP64 GEMMs.  Reported in the metric's unit (GEMM TFLOP/s of the sample)."""
-    import numpy as np
     import oracle
     from fine_grained_scaled_amd import synth
     try:
@@ -129,9 +410,9 @@ def cpu_baseline():
     except Exception:
         blas = 1
     K, N, Ms = 4096, 6144, 256
-    x = synth.activations(M_TOKENS, K, seed=0, row_range=(0, Ms))
+    x = synth.activations(LLAMA8B_M, K, seed=0, row_range=(0, Ms))
     w = synth.weights(N, K, seed=0, tag=synth.TAG_W + 16)
-    dy = synth.gradients(M_TOKENS, N, seed=0, row_range=(0, Ms))
+    dy = synth.gradients(LLAMA8B_M, N, seed=0, row_range=(0, Ms))
     t0 = time.perf_counter()
     for _, amode, wmode in RECIPES:
         qx, sx = oracle.quant_e4m3(x, amode)
@@ -148,8 +429,7 @@ def cpu_baseline():
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
             "sample": (f"QKV layer (K=4096, N=6144) with M=256 of 8192 tokens, both recipes: oracle quantization "
                        f"(single-threaded C) of X, W, dY row- and column-wise + 3 FP64 numpy GEMMs "
-                       f"({blas} BLAS threads); {dt:.1f} s wall"),
-            "seconds": round(dt, 2)}
+                       f"({blas} BLAS threads); {dt:.1f} s wall")}
 
 
 def main():
@@ -157,6 +437,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="llama3_8b,tiny,moe,mx405b,nv12b",
+                    help="comma list of " + ",".join(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -166,57 +448,48 @@ def main():
 
     import torch
     import fine_grained_scaled_amd as fgs
-    from fine_grained_scaled_amd import _lib
+    from fine_grained_scaled_amd import _lib, synth
     _lib.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] device {torch.cuda.get_device_name(dev)}; steps {args.steps} warmup {args.warmup}")
-    inp = Inputs(dev)
-    outs = {}
-    for rname, _, _ in RECIPES:
-        for name, K, N in LAYERS:
-            outs[(rname, name, "y")] = torch.empty((M_TOKENS, N), dtype=torch.bfloat16, device=dev)
-            outs[(rname, name, "dx")] = torch.empty((M_TOKENS, K), dtype=torch.bfloat16, device=dev)
-            outs[(rname, name, "dw")] = torch.empty((N, K), dtype=torch.float32, device=dev)
+    torch.cuda.set_device(0)
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; steps {args.steps} warmup {args.warmup}")
+    names = [n for n in args.workloads.split(",") if n]
 
-    for _ in range(args.warmup):
-        run_step(fgs, torch, inp, outs, None)
-    torch.cuda.synchronize()
-    rec = []
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(fgs, torch, inp, outs, rec)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    head = Llama8B(torch, fgs, synth)
+    wall, kinds = measure(torch, head, args.steps, args.warmup)
     ms = wall * 1e3 / args.steps
-    value = step_flops() / (wall / args.steps) / 1e12
+    value = head.flops() / (wall / args.steps) / 1e12
+    rep = kind_report(kinds, args.steps)
+    log(f"[bench] {head.name}: step {ms:.2f} ms, {value:.1f} TFLOP/s; {rep}")
 
-    agg = {}
-    per = {}
-    for kind, units, a, b, label in rec:
-        t = a.elapsed_time(b) * 1e-3
-        s_units, s_t, n = agg.get(kind, (0.0, 0.0, 0))
-        agg[kind] = (s_units + units, s_t + t, n + 1)
-        pu, pt, pn = per.get(label, (0.0, 0.0, 0))
-        per[label] = (pu + units, pt + t, pn + 1)
-    for label, (u, t, n) in per.items():
-        if "/fwd" in label or "/dgrad" in label or "/wgrad" in label:
-            log(f"  {label:28s} {t / n * 1e6:9.1f} us  {u / t / 1e12:8.1f} TFLOP/s")
-        else:
-            log(f"  {label:28s} {t / n * 1e6:9.1f} us  {u / t / 1e9:8.1f} GB/s")
-    gf, gt, gn = agg["gemm"]
-    qb, qt, qn = agg["quant"]
-    gemm_tflops = gf / gt / 1e12
-    quant_gbps = qb / qt / 1e9
-    log(f"[bench] step {ms:.2f} ms; GEMM kernels {gt / args.steps * 1e3:.2f} ms/step at {gemm_tflops:.1f} TFLOP/s; "
-        f"quant {qt / args.steps * 1e3:.2f} ms/step at {quant_gbps:.0f} GB/s")
+    extra = {}
+    for n in names:
+        if n == "llama3_8b":
+            continue
+        wl = WORKLOADS[n](torch, fgs, synth)
+        w_wall, w_kinds = measure(torch, wl, args.steps, args.warmup)
+        r = kind_report(w_kinds, args.steps)
+        r["ms_per_step"] = round(w_wall * 1e3 / args.steps, 4)
+        r["step_TFLOP/s"] = round(wl.flops() / (w_wall / args.steps) / 1e12, 2)
+        if isinstance(wl, MoE):
+            f, t, _ = w_kinds["gemm"]
+            roof = wl.roofline_seconds(2 * MOE_INTER, MOE_HIDDEN) + wl.roofline_seconds(MOE_HIDDEN, MOE_INTER)
+            by = wl.gemm_bytes(2 * MOE_INTER, MOE_HIDDEN) + wl.gemm_bytes(MOE_HIDDEN, MOE_INTER)
+            gemm_s = t / args.steps
+            r["gemm"]["roofline_ms"] = round(roof * 1e3, 4)
+            r["gemm"]["frac_roofline"] = round(roof / gemm_s, 4)
+            r["gemm"]["GB/s"] = round(by / gemm_s / 1e9, 1)
+        log(f"[bench] {wl.name}: {r}")
+        extra[wl.name] = r
+        del wl
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample (CPU) ...")
         cpu = cpu_baseline()
-        log(f"[bench] oracle sample: {cpu['value']} TFLOP/s in {cpu['seconds']} s")
+        log(f"[bench] oracle sample: {cpu['value']} TFLOP/s; {cpu['sample']}")
 
+    g = rep["gemm"]
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -229,16 +502,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3 codes, fp16 mfma, fp32 accumulate",
-        "data": "synthetic (seeded BF16: activations N(0,1) with x50 outlier channels, weights N(0,0.02), gradients t3 std 1e-3)",
+        "data": "synthetic (seeded BF16: activations N(0,1) with x50 outlier channels, weights N(0,0.02), "
+                "gradients Student-t(3) std 1e-3)",
         "config": {"workload": "llama3-8b linear layers fwd+dgrad+wgrad, blockwise 1x128/128x128 and per-tensor E4M3",
-                   "tokens": M_TOKENS, "layers": {n: [K, N] for n, K, N in LAYERS},
-                   "recipes": [r[0] for r in RECIPES], "step_gemm_tflop": round(step_flops() / 1e12, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP16_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP16_MFMA_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_fp8_kernel (all launches of the step)",
-                     "frac_of_fp8_peak": round(gemm_tflops / PEAK_FP8_MFMA_TFLOPS, 4)},
-        "quant": {"achieved": round(quant_gbps, 1), "unit": "GB/s", "peak": PEAK_HBM_GBPS,
-                  "frac": round(quant_gbps / PEAK_HBM_GBPS, 4)},
+                   "tokens": LLAMA8B_M, "layers": {n: [K, N] for n, K, N in LLAMA8B_LAYERS},
+                   "recipes": [r[0] for r in RECIPES], "step_gemm_tflop": round(head.flops() / 1e12, 4)},
+        "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP16_MFMA, "unit": "TFLOP/s",
+                     "frac": g["frac_fp16_mfma_peak"], "traffic": None,
+                     "kernel": "gemm_block_scaled (all GEMM launches of the step)",
+                     "frac_of_fp8_peak": round(g["TFLOP/s"] / PEAK_FP8_MFMA, 4)},
+        "quant": rep.get("quant"),
+        "workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
