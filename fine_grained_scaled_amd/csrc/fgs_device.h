@@ -134,6 +134,33 @@ __device__ __forceinline__ E4M3Block e4m3_block_from_amax_bits(uint32_t amax_bit
     return b;
 }
 
+// E4M3 codes of four FP32 values, packed little-endian into one word, by
+// the hardware converter v_cvt_pk_fp8_f32 (round to nearest even, OCP
+// E4M3).  On [-449, 449] it equals the saturating encoder above with the sign
+// of the input (checked exhaustively over every FP32 bit pattern in that
+// range on gfx950), and every quotient x / s of a finite block lies there:
+// |x| <= amax and s = fl32(amax / 448) give |x / s| <= 448 (1 + 2^-23).
+// NaN never reaches it (a block holding a NaN or Inf takes the all-0x7F
+// path).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// fl32(x / s) of a block element given as FP32 bits: the correctly rounded
+// quotient of |x| (abs is a free source modifier) with the sign bit of x put
+// back (so -0 stays -0).  Blocks with amax < 2^-64 (b.k != 1) take the
+// pre-scaled form, a branch that real data does not enter.
+__device__ __forceinline__ float e4m3_quotient_bits(uint32_t xb, const E4M3Block& b)
+{
+    float a = __builtin_fabsf(as_f32(xb));
+    if (__builtin_expect(b.k != 1.0f, 0)) a *= b.k;
+    const float q = div_by_scale(a, b.sp, b.r);
+    return as_f32(as_u32(q) | (xb & 0x80000000u));
+}
+
 // code of one BF16 element (raw 16-bit pattern in the low half of h)
 __device__ __forceinline__ uint32_t e4m3_quant_bf16(uint32_t h, const E4M3Block& b)
 {

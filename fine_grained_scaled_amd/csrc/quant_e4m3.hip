@@ -49,15 +49,29 @@ __device__ __forceinline__ uint32_t raw_elem(const uint4& v, int j)
     return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// FP32 value of element j (0..7) of an 8-element BF16 vector (exact)
+__device__ __forceinline__ uint32_t val_bits(const uint4& v, int j)
+{
+    const uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
+    return (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+}
+
+// Codes of 8 values (FP32 bit patterns of BF16 numbers) of one block.
+__device__ __forceinline__ uint2 quant8_vals(const uint32_t xb[8], const E4M3Block& b)
+{
+    if (b.nan) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient_bits(xb[j], b);
+    return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
+}
+
 __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
 {
-    uint32_t c[8];
+    uint32_t xb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = e4m3_quant_bf16(raw_elem(v, j), b);
-    uint2 o;
-    o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    return o;
+    for (int j = 0; j < 8; ++j) xb[j] = val_bits(v, j);
+    return quant8_vals(xb, b);
 }
 
 template <int MODE>   // FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
@@ -171,13 +185,10 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
         // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint32_t c[8];
+            uint32_t xb[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = e4m3_quant_bf16(raw_elem(v[u], j), bcol[j]);
-            uint2 o;
-            o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = o;
+            for (int u = 0; u < 8; ++u) xb[u] = val_bits(v[u], j);
+            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = quant8_vals(xb, bcol[j]);
         }
         __syncthreads();
         // 8 lanes write one 128-byte row of qT
