@@ -167,6 +167,29 @@ class Llama8B:
     def flops(self):
         return len(RECIPES) * sum(3 * 2.0 * LLAMA8B_M * N * K for _, K, N in LLAMA8B_LAYERS)
 
+    def gemm_only(self, steps):
+        """Quantize once, then run only the step's GEMM launches `steps` times."""
+        torch, fgs = self.torch, self.fgs
+        ops = []
+        for rname, amode, wmode in RECIPES:
+            for name, K, N in LLAMA8B_LAYERS:
+                qx = fgs.quantize_blockwise(self.x[K], amode, rowwise=True, colwise=True)
+                qw = fgs.quantize_blockwise(self.w[name], wmode, rowwise=True, colwise=True)
+                qdy = fgs.quantize_blockwise(self.dy[N], amode, rowwise=True, colwise=True)
+                o = self.out
+                ops.append((qx.rowwise(), qw.rowwise(), torch.bfloat16, o[(rname, name, "y")]))
+                ops.append((qdy.rowwise(), qw.colwise(), torch.bfloat16, o[(rname, name, "dx")]))
+                ops.append((qdy.colwise(), qx.colwise(), torch.float32, o[(rname, name, "dw")]))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for a, b, dt, out in ops:
+                fgs.gemm_block_scaled(a, b, dt, out=out)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        log(f"[bench] GEMM launches only: {dt / steps * 1e3:.2f} ms per step, "
+            f"{self.flops() / (dt / steps) / 1e12:.1f} TFLOP/s")
+
     def step(self, tm):
         torch, fgs = self.torch, self.fgs
         for rname, amode, wmode in RECIPES:
@@ -440,6 +463,12 @@ def main():
     ap.add_argument("--workloads", default="llama3_8b,tiny,moe,mx405b,nv12b",
                     help="comma list of " + ",".join(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="headline workload: quantize once, then time only the GEMM launches "
+                         "(for counter collection on the GEMM kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -451,6 +480,18 @@ def main():
     from fine_grained_scaled_amd import _lib, synth
     _lib.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB 5 times (counter calibration)")
+        return
+    if args.gemm_only:
+        head = Llama8B(torch, fgs, synth)
+        head.gemm_only(args.steps)
+        return
     log(f"[bench] device {torch.cuda.get_device_name(0)}; steps {args.steps} warmup {args.warmup}")
     names = [n for n in args.workloads.split(",") if n]
 

@@ -122,16 +122,24 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a)
            (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
-// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r
+// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r.
+// The magnitudes split into three segments of equal spacing: [0, 2) with
+// step 1/2 (codes 0-3), [2, 4) with step 1 (codes 4-5), [4, 6] with step 2
+// (codes 6-7).  u = (a - base) / step is exact (a power-of-two multiple of a
+// difference that Sterbenz's lemma makes exact); its integer part k gives
+// the lower neighbour, code0 + k, and p = u - k = (a - lo) / (hi - lo) is
+// exact.  Round up iff (r >> 8) < p * 2^24.
 __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
 {
-    const uint32_t idx = (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) + (uint32_t)(a >= 2.0f) +
-                         (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f) + (uint32_t)(a >= 6.0f);
-    if (idx == 7) return 7;
-    const float lo = idx < 4 ? 0.5f * (float)idx : (idx == 4 ? 2.0f : (idx == 5 ? 3.0f : 4.0f));
-    const float inv_gap = idx < 4 ? 2.0f : (idx < 6 ? 1.0f : 0.5f);
-    const float p = (a - lo) * inv_gap;                    // exact
-    return ((float)(r >> 8) < p * 16777216.0f) ? idx + 1 : idx;
+    const bool s0 = a < 2.0f, s1 = a < 4.0f;
+    const float base = s0 ? 0.0f : (s1 ? 2.0f : 4.0f);
+    const float inv_step = s0 ? 2.0f : (s1 ? 1.0f : 0.5f);
+    const uint32_t code0 = s0 ? 0u : (s1 ? 4u : 6u);
+    const float u = (a - base) * inv_step;
+    const float k = __builtin_floorf(u);
+    const float p = u - k;
+    const uint32_t up = (float)(r >> 8) < p * 16777216.0f ? 1u : 0u;
+    return code0 + (uint32_t)k + up;
 }
 
 struct TensorScale {
@@ -148,8 +156,31 @@ __device__ __forceinline__ TensorScale tensor_scale_from(uint32_t amax_bits)
     return s;
 }
 
+// fl32(a / d) for a >= 0 from r = RN(1/d): Markstein's correction
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", IBM J. Res. Dev., 1990): q0 = RN(a r), the
+// residual a - q0 d is exact with an FMA, and RN(q0 + residual * r) is the
+// correctly rounded quotient while the residual stays a normal number.
+// Checked against IEEE division on gfx950 for every BF16 a >= 2^-90 with
+// every divisor mantissa of three binades and for 1.7e10 random FP32 pairs.
+__device__ __forceinline__ float div_rn(float a, float d, float r)
+{
+    const float q0 = a * r;
+    const float res = __builtin_fmaf(-q0, d, a);
+    return __builtin_fmaf(res, r, q0);
+}
+
 // Codes of 8 values of one 16-block whose (two-lane) amax bits are amax_b.
-// Returns the 8 nibbles packed (element 2j in the low nibble) and the scale byte.
+// Returns the 8 nibbles packed (element 2j in the low nibble) and the scale
+// byte.  The quotient y / d is taken on |y| with the sign put back bitwise
+// (so -0 gives the negative-zero code 0x8) and saturated at 6.  A block with
+// amax_b < 2^-30 divides y * 2^64 by d * 2^64 (both exact), which keeps every
+// residual normal; in other blocks an element below 2^-90 has a quotient
+// below 2^-57, where RNE gives 0 and stochastic rounding makes the same
+// choice for every positive value, so its rounding cannot change a code.
+// RNE codes come from the hardware converter v_cvt_scalef32_pk_fp4_f32
+// (unit scale), which equals the RNE encoder above with the sign of the
+// input for every FP32 value in [-6, 6] (checked exhaustively on gfx950).
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b, const TensorScale& ts,
                                               const uint32_t rw[8], uint32_t& sb_out)
@@ -157,24 +188,52 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
     const uint32_t sb = e4m3_code_f32(as_f32(amax_b) / ts.six_st);
     sb_out = sb;
     const float d = e4m3_value(sb) * ts.st;
-    uint32_t packed = 0;
     if (d == 0.0f || d != d) return 0;
+    float k = 1.0f;
+    if (__builtin_expect(as_f32(amax_b) < 0x1p-30f, 0)) k = 0x1p64f;
+    const float dk = d * k;
+    const float r = 1.0f / dk;
+    float q[8];
+    uint32_t sg[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float q = y[i] / d;
-        q = q > 6.0f ? 6.0f : (q < -6.0f ? -6.0f : q);
-        const float a = __builtin_fabsf(q);
-        uint32_t c = SR ? e2m1_sr(a, rw[i]) : e2m1_rne(a);
-        c |= (as_u32(q) >> 28) & 0x8u;
-        packed |= c << (4 * i);
+        float a = __builtin_fabsf(y[i]);
+        if (__builtin_expect(k != 1.0f, 0)) a *= k;
+        q[i] = __builtin_fminf(div_rn(a, dk, r), 6.0f);
+        sg[i] = as_u32(y[i]) & 0x80000000u;
     }
-    return packed;
+    if constexpr (SR) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) packed |= (e2m1_sr(q[i], rw[i]) | (sg[i] >> 28)) << (4 * i);
+        return packed;
+    } else {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = as_f32(as_u32(q[i]) | sg[i]);
+        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+        return w;
+    }
 }
 
-__device__ __forceinline__ uint32_t sr_word(uint32_t seed_lo, uint32_t seed_hi, uint64_t i)
+// The counter hash's last round: r = fmix32(lo32(i) ^ mid) with
+// mid = fmix32(lo32(seed) ^ fmix32(hi32(seed) ^ hi32(i))), which is the same
+// for every element whose index has the same upper 32 bits.
+__device__ __forceinline__ uint32_t sr_mid(uint32_t seed_lo, uint32_t seed_hi, uint64_t i)
 {
-    const uint32_t inner = fmix32(seed_hi ^ (uint32_t)(i >> 32));
-    return fmix32((uint32_t)i ^ fmix32(seed_lo ^ inner));
+    return fmix32(seed_lo ^ fmix32(seed_hi ^ (uint32_t)(i >> 32)));
+}
+
+// Random word of element i0 + j (0 <= j < 8) from lo32(i0) and the seed
+// rounds of i0.  Every run of 8 starts at a multiple of 8 (cols and the
+// column offset are multiples of 8), so lo32(i0) + j never carries into
+// hi32 and the seed rounds of i0 hold for the whole run.
+__device__ __forceinline__ uint32_t sr_word_at(uint32_t lo0, uint32_t mid0, int j)
+{
+    return fmix32((lo0 + (uint32_t)j) ^ mid0);
 }
 
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -265,6 +324,16 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
 
     const TensorScale ts_row = tensor_scale_from(ws[0]);
     const TensorScale ts_col = tensor_scale_from(ws[1]);
+    // SR: the hash's seed rounds per row of this thread (shared by both outputs)
+    uint32_t midr[8], ilo[8];
+    if constexpr (SR) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint64_t i0 = (uint64_t)((r0 + 8 * rg + u) * cols + col);
+            midr[u] = sr_mid(seed_lo, seed_hi, i0);
+            ilo[u] = (uint32_t)i0;
+        }
+    }
     if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
         tensor_scale[0] = ts_row.st;
         tensor_scale[1] = ts_col.st;
@@ -286,7 +355,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             uint32_t rw[8];
             if constexpr (SR) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) rw[j] = sr_word(seed_lo, seed_hi, (uint64_t)(row * cols + col + j));
+                for (int j = 0; j < 8; ++j) rw[j] = sr_word_at(ilo[u], midr[u], j);
             }
             uint32_t sb;
             const uint32_t packed = nv_block8<SR>(z, mb, ts_row, rw, sb);
@@ -312,8 +381,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             uint32_t rw[8];
             if constexpr (SR) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    rw[u] = sr_word(seed_lo, seed_hi, (uint64_t)((r0 + 8 * rg + u) * cols + col + j));
+                for (int u = 0; u < 8; ++u) rw[u] = sr_word_at(ilo[u], midr[u], j);
             }
             uint32_t sb;
             const uint32_t packed = nv_block8<SR>(z, mb, ts_col, rw, sb);
