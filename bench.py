@@ -30,6 +30,8 @@ Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -44,6 +46,14 @@ METRIC = "block-scaled FP8 GEMM TFLOP/s + quant GB/s (% of MI355X peak), 8B/405B
 PEAK_FP16_MFMA = 2500.0     # TFLOP/s, MI355X dense FP16/BF16 matrix peak
 PEAK_FP8_MFMA = 5000.0      # TFLOP/s, MI355X dense FP8 matrix peak (context)
 PEAK_HBM = 8000.0           # GB/s, MI355X HBM3E
+
+# HBM traffic of the GEMM kernel comes from two committed rocprofv3 counter
+# runs (FETCH_SIZE, WRITE_SIZE) summarised here; it is reported only while
+# the kernel's sources still hash to the digest recorded with the counters.
+COUNTER_PROFILE = os.path.join("profiles", "counters_llama3_8b_linears.md")
+GEMM_SOURCES = [os.path.join("fine_grained_scaled_amd", "csrc", f)
+                for f in ("gemm_block_scaled.hip", "fgs_device.h", "fgs_internal.h")]
+CALIBRATION_BYTES = 1 << 30
 
 LLAMA8B_M = 8192
 LLAMA8B_LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
@@ -166,6 +176,20 @@ class Llama8B:
 
     def flops(self):
         return len(RECIPES) * sum(3 * 2.0 * LLAMA8B_M * N * K for _, K, N in LLAMA8B_LAYERS)
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of the step's GEMMs: every operand code, scale
+        and output element once."""
+        tot = 0.0
+        for _, amode, wmode in RECIPES:
+            for _, K, N in LLAMA8B_LAYERS:
+                M = LLAMA8B_M
+                sc = lambda r, c, mode: 4.0 * (r * c / 128 if mode == "tile" else
+                                               r * c / 16384 if mode == "block" else 1)
+                tot += M * K + N * K + sc(M, K, amode) + sc(N, K, wmode) + 2.0 * M * N      # fwd
+                tot += M * N + N * K + sc(M, N, amode) + sc(N, K, wmode) + 2.0 * M * K      # dgrad
+                tot += M * N + M * K + sc(M, N, amode) + sc(M, K, amode) + 4.0 * N * K      # wgrad
+        return tot
 
     def gemm_only(self, steps):
         """Quantize once, then run only the step's GEMM launches `steps` times."""
@@ -420,6 +444,120 @@ def kind_report(kinds, steps):
     return out
 
 
+# --------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# --------------------------------------------------------------------------
+def gemm_source_digest():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_short(name):
+    name = name.replace("fgs::(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def _counter_rows(d, counter):
+    """{short kernel name: [per-dispatch values in KiB]} from a rocprofv3 --pmc
+    csv directory."""
+    out = {}
+    files = [os.path.join(r, f) for r, _, fs in os.walk(d) for f in fs if f.endswith("counter_collection.csv")]
+    if len(files) != 1:
+        raise SystemExit(f"expected one *counter_collection.csv under {d}, found {len(files)}")
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(_kernel_short(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+    return out
+
+
+def write_counter_profile(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command):
+    """Summarise FETCH_SIZE / WRITE_SIZE runs of one headline step (and of the
+    1 GiB copy that calibrates both counters) into COUNTER_PROFILE."""
+    fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    cf, cw = _counter_rows(cal_fetch_dir, "FETCH_SIZE"), _counter_rows(cal_write_dir, "WRITE_SIZE")
+    copy = [k for k in cf if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy kernel in the calibration runs")
+    kib = CALIBRATION_BYTES / 1024.0
+    f_fetch = kib / (sum(cf[copy[0]]) / len(cf[copy[0]]))
+    f_write = kib / (sum(cw[copy[0]]) / len(cw[copy[0]]))
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (calibrated) |",
+             "|---|---:|---:|---:|---:|"]
+    g_n, g_bytes, g_fetch, g_write = 0, 0.0, 0.0, 0.0
+    for k in sorted(fetch):
+        fv, wv = fetch[k], write.get(k, [])
+        if len(fv) != len(wv):
+            raise SystemExit(f"dispatch counts differ for {k}: {len(fv)} vs {len(wv)}")
+        af, aw = sum(fv) / len(fv), sum(wv) / len(wv)
+        by = 1024.0 * (af * f_fetch + aw * f_write)
+        lines.append(f"| `{k}` | {len(fv)} | {af:.1f} | {aw:.1f} | {by / 1e6:.2f} MB |")
+        if k.startswith("gemm_block_scaled_kernel"):
+            g_n += len(fv)
+            g_fetch += 1024.0 * f_fetch * sum(fv)
+            g_write += 1024.0 * f_write * sum(wv)
+    if g_n == 0:
+        raise SystemExit("no gemm_block_scaled_kernel dispatches in the counter runs")
+    launches_per_step = 3 * len(LLAMA8B_LAYERS) * len(RECIPES)
+    alg = Llama8B.gemm_bytes(None) / launches_per_step
+    summary = {"source_digest": gemm_source_digest(), "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+               "gemm_launches": g_n, "gemm_fetch_bytes_per_launch": round(g_fetch / g_n),
+               "gemm_write_bytes_per_launch": round(g_write / g_n),
+               "gemm_traffic_bytes_per_launch": round((g_fetch + g_write) / g_n),
+               "gemm_algorithmic_bytes_per_launch": round(alg)}
+    text = [
+        "# HBM traffic of the headline step's kernels (rocprofv3 counters)",
+        "",
+        "Commands (repository root, one MI355X; each counter in a run of its own):",
+        "",
+        "```",
+        *command,
+        "```",
+        "",
+        f"Calibration: the 1 GiB device copy reads {kib / f_fetch:.1f} KiB of FETCH_SIZE and writes "
+        f"{kib / f_write:.1f} KiB of WRITE_SIZE per dispatch, so FETCH_SIZE is scaled by {f_fetch:.4f} and "
+        f"WRITE_SIZE by {f_write:.4f} to give bytes.",
+        "",
+        *lines,
+        "",
+        f"GEMM kernel, average over its {g_n} dispatches (one step: {launches_per_step} launches): "
+        f"{summary['gemm_traffic_bytes_per_launch'] / 1e6:.1f} MB of HBM traffic per launch against "
+        f"{alg / 1e6:.1f} MB algorithmic (operand codes, scales and output once), ratio "
+        f"{summary['gemm_traffic_bytes_per_launch'] / alg:.2f}.",
+        "",
+        "Machine-readable summary (read by bench.py; `source_digest` is the SHA-256 prefix of the GEMM kernel's "
+        "sources when the counters were taken):",
+        "",
+        "```json",
+        json.dumps(summary),
+        "```",
+        "",
+    ]
+    with open(os.path.join(ROOT, COUNTER_PROFILE), "w") as f:
+        f.write("\n".join(text))
+    log(f"[bench] wrote {COUNTER_PROFILE}: {summary}")
+
+
+def read_gemm_traffic():
+    """HBM bytes per GEMM launch from COUNTER_PROFILE, or None when the file
+    is missing or the kernel's sources changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, COUNTER_PROFILE)) as f:
+            text = f.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        summary = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if summary.get("source_digest") != gemm_source_digest():
+        return None
+    return summary
+
+
 def cpu_baseline():
     """The oracle, untuned, on a bounded sample of the headline workload: the
     QKV layer (K = 4096, N = 6144) with M cut to 256 tokens, both recipes:
@@ -466,6 +604,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--write-counter-profile", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="summarise four rocprofv3 --pmc csv directories (FETCH_SIZE and WRITE_SIZE of one headline "
+                         "step, then of --copy-calibration) into " + COUNTER_PROFILE + " and exit (no GPU needed)")
+    ap.add_argument("--counter-command", action="append", default=[],
+                    help="command line recorded in the counter profile (repeatable)")
     ap.add_argument("--gemm-only", action="store_true",
                     help="headline workload: quantize once, then time only the GEMM launches "
                          "(for counter collection on the GEMM kernel)")
@@ -474,6 +617,9 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path has no cross-GPU exchange; run --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.write_counter_profile:
+        write_counter_profile(*args.write_counter_profile, args.counter_command)
+        return
 
     import torch
     import fine_grained_scaled_amd as fgs
@@ -531,6 +677,14 @@ def main():
         log(f"[bench] oracle sample: {cpu['value']} TFLOP/s; {cpu['sample']}")
 
     g = rep["gemm"]
+    counters = read_gemm_traffic()
+    traffic = None
+    if counters is not None:
+        traffic = counters["gemm_traffic_bytes_per_launch"]
+        log(f"[bench] GEMM HBM traffic {traffic / 1e6:.1f} MB per launch ({COUNTER_PROFILE}); algorithmic "
+            f"{counters['gemm_algorithmic_bytes_per_launch'] / 1e6:.1f} MB")
+    else:
+        log(f"[bench] no GEMM traffic: {COUNTER_PROFILE} missing or taken on other kernel sources")
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -549,7 +703,7 @@ def main():
                    "tokens": LLAMA8B_M, "layers": {n: [K, N] for n, K, N in LLAMA8B_LAYERS},
                    "recipes": [r[0] for r in RECIPES], "step_gemm_tflop": round(head.flops() / 1e12, 4)},
         "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP16_MFMA, "unit": "TFLOP/s",
-                     "frac": g["frac_fp16_mfma_peak"], "traffic": None,
+                     "frac": g["frac_fp16_mfma_peak"], "traffic": traffic,
                      "kernel": "gemm_block_scaled (all GEMM launches of the step)",
                      "frac_of_fp8_peak": round(g["TFLOP/s"] / PEAK_FP8_MFMA, 4)},
         "quant": rep.get("quant"),

@@ -194,7 +194,7 @@ struct Lds {
 };
 
 template <int NWM, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(128 * NWM) void gemm_fp8_kernel(GemmParams p)
+__global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams p)
 {
     constexpr int NW = 2 * NWM;          // waves
     constexpr int NT = 64 * NW;          // threads
@@ -663,8 +663,8 @@ template <int NWM, int AMODE, int BMODE, bool GROUPED>
 hipError_t launch_modes(const GemmParams& p, bool bf16, dim3 grid, hipStream_t s)
 {
     const size_t lds = 2 * (size_t)Lds<NWM, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128>::STAGE;
-    auto k = bf16 ? gemm_fp8_kernel<NWM, AMODE, BMODE, true, GROUPED>
-                  : gemm_fp8_kernel<NWM, AMODE, BMODE, false, GROUPED>;
+    auto k = bf16 ? gemm_block_scaled_kernel<NWM, AMODE, BMODE, true, GROUPED>
+                  : gemm_block_scaled_kernel<NWM, AMODE, BMODE, false, GROUPED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
