@@ -68,14 +68,26 @@ constexpr int BN = 128, BK = 128;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* gbl_ptr;
 
-// one 16-byte global->LDS load per lane; dst is the wave's 1 KiB span base
+// Direct global->LDS loads.  dst is the wave's LDS span base (wave-uniform,
+// passed in M0); lane i writes bytes [size*i, size*(i+1)) of it.  They are
+// issued from inline assembly on purpose: seen as LDS writes, the compiler
+// would make every later LDS read wait for the loads to land (it cannot tell
+// that they fill the other stage of the ring), which serialises the next
+// block's fetch with this block's MFMAs.  Completion is tracked by hand with
+// wait_lds_dma() before the barrier that publishes a stage.
+__device__ __forceinline__ uint32_t lds_offset(const void* p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)p));
+}
 __device__ __forceinline__ void g2lds16(const void* src, void* dst_wave_base)
 {
-    __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)dst_wave_base, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_offset(dst_wave_base)) : "memory", "m0");
 }
 __device__ __forceinline__ void g2lds4(const void* src, void* dst_wave_base)
 {
-    __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)dst_wave_base, 4, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(lds_offset(dst_wave_base)) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_lds_dma()
 {
