@@ -12,6 +12,7 @@ ELEM_E4M3, ELEM_E2M1 = 0, 1
 SCALE_TENSOR, SCALE_TILE_1x128, SCALE_BLOCK_128x128, SCALE_MX32_E8M0, SCALE_NV16_E4M3 = 0, 1, 2, 3, 4
 ROUND_RNE, ROUND_STOCHASTIC = 0, 1
 OUT_FP32, OUT_BF16 = 0, 1
+TILE_AUTO, TILE_NARROW, TILE_WIDE = 0, 1, 2
 
 EXPORTS = (
     "fgs_quantize_blockwise",
@@ -19,6 +20,7 @@ EXPORTS = (
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
     "fgs_grouped_gemm_block_scaled",
+    "fgs_gemm_tile_policy",
     "fgs_workspace_bytes",
     "fgs_last_error",
     "fgs_version",
@@ -61,6 +63,8 @@ def load() -> ctypes.CDLL:
     OP = ctypes.POINTER(FgsOperand)
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_gemm_tile_policy.argtypes = [ctypes.c_int]
+    lib.fgs_gemm_tile_policy.restype = ctypes.c_int
     lib.fgs_workspace_bytes.argtypes = [I64, I64]
     lib.fgs_workspace_bytes.restype = SZ
     lib.fgs_last_error.restype = ctypes.c_char_p

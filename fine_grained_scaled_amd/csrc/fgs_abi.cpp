@@ -76,6 +76,11 @@ const char* fgs_last_error(void) { return g_last_error.c_str(); }
 
 const char* fgs_version(void) { return "fgs 0.1.0 (gfx950)"; }
 
+int fgs_gemm_tile_policy(int policy)
+{
+    return fgs::set_gemm_tile_policy(policy);
+}
+
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols)
 {
     (void)rows;

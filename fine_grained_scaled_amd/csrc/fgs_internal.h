@@ -58,6 +58,10 @@ struct GemmArgs {
     const int32_t* group_offsets;   // nullptr for the dense GEMM
     int32_t G;
 };
+// GEMM tile policy (FGS_TILE_*), read at launch.
+int gemm_tile_policy();
+int set_gemm_tile_policy(int policy);
+
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t stream);

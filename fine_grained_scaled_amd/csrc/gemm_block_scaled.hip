@@ -33,12 +33,16 @@
 // the FP16 MFMA: the result is the FP32 sum of exact products.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]; both operands K-contiguous.
-// Workgroup: NWM x 2 waves, each owning a 64 x 64 output sub-block (2 x 2
-// MFMA 32x32x16 tiles), so the workgroup tile is (64*NWM) x 128: NWM = 4
-// (512 threads, two waves per SIMD so one wave's decode/promotion VALU work
-// overlaps the other's MFMAs) for dense GEMMs, NWM = 2 for the grouped one
-// (MoE groups are short).  The promoted accumulators and the per-block
-// partial sums of a wave (2 x 64 VGPRs) both stay in VGPRs.  K advances in
+// Workgroup: NWM x NWN waves, each owning a (32*TI) x 64 output sub-block
+// (TI x 2 MFMA 32x32x16 tiles).  Promoted modes: 4 x 2 waves of 64 x 64
+// (tile 256 x 128; 512 threads, two waves per SIMD so one wave's decode and
+// promotion VALU work overlaps the other's MFMAs); the promoted accumulators
+// and the per-block partial sums (2 x 64 VGPRs) both stay in VGPRs, which
+// caps the wave tile there.  Modes with a single scale per operand (per-tensor
+// E4M3, NVFP4) need no partial sums, so their waves own 128 x 64 (2 x 4
+// waves, tile 256 x 256): each decoded fragment feeds more MFMAs and each
+// staged byte more FLOPs.  The grouped (MoE) kernel uses 2 x 2 waves of
+// 64 x 64 (tile 128 x 128; groups are short).  K advances in
 // 128-deep blocks staged in LDS as code bytes (128 bytes per row for E4M3,
 // 64 for E2M1), double-buffered, by direct global->LDS loads
 // (global_load_lds_dwordx4: lane i of a wave-instruction fills bytes
@@ -50,6 +54,8 @@
 // chunk, 256 bytes) touches each of the 64 LDS banks once.  MFMA operands
 // are swapped (B fragment first) so each lane's 16 accumulators share one
 // row m: the 1x128 A scale is one value per lane and per sub-tile row.
+#include <atomic>
+
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -63,7 +69,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 128, BK = 128;
+constexpr int BK = 128;      // K block: the scale block and the promotion interval
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* gbl_ptr;
@@ -197,23 +203,33 @@ __device__ __forceinline__ f16x8 decode_nv_word(uint32_t w, _Float16 s)
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int NWM, int ROW>
+// Workgroup shapes: NWM x NWN waves, each owning (32*TI) x 64 outputs.
+template <int NWM_, int NWN_, int TI_>
+struct Shape {
+    static constexpr int NWM = NWM_, NWN = NWN_, TI = TI_, TJ = 2;
+    static constexpr int BM = 32 * TI * NWM, BN = 64 * NWN;
+};
+using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
+using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
+using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
+
+template <class S, int ROW>
 struct Lds {
-    static constexpr int BM = 64 * NWM;
-    static constexpr int A_BYTES = BM * ROW;
-    static constexpr int B_BYTES = BN * ROW;
-    static constexpr int STAGE = A_BYTES + B_BYTES + BN * 4;   // + B 1x128 scales of the block
+    static constexpr int A_BYTES = S::BM * ROW;
+    static constexpr int B_BYTES = S::BN * ROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S::BN * 4;   // + B 1x128 scales of the block
 };
 
-template <int NWM, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams p)
+template <class S, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
+__global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel(GemmParams p)
 {
-    constexpr int NW = 2 * NWM;          // waves
+    constexpr int NWM = S::NWM, NWN = S::NWN;
+    constexpr int NW = NWM * NWN;        // waves
     constexpr int NT = 64 * NW;          // threads
-    constexpr int BM = 64 * NWM;
-    constexpr int WM = 64;
-    constexpr int TI = 2;                // sub-tiles along m per wave
-    constexpr int TJ = 2;                // sub-tiles along n per wave
+    constexpr int BM = S::BM, BN = S::BN;
+    constexpr int TI = S::TI;            // sub-tiles along m per wave
+    constexpr int TJ = S::TJ;            // sub-tiles along n per wave
+    constexpr int WM = 32 * TI;
     constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR) &&
                              AMODE != FGS_SCALE_NV16_E4M3;
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
@@ -224,15 +240,17 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
     constexpr int CPR = ROW / 16;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
     constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
-    using L = Lds<NWM, ROW>;
+    using L = Lds<S, ROW>;
+    static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN != 128), "128x128 B blocks need 128-wide tiles");
+    static_assert(BN / 64 <= NW, "B 1x128 scale staging needs BN / 64 waves");
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
     __shared__ int s_sel[2];
-    __shared__ uint32_t s_ebt[2][2];       // MX: B tile reference exponent, [block parity][wn]
+    __shared__ uint32_t s_ebt[2][NWN];     // MX: B tile reference exponent, [block parity][wn]
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
-    const int wm = w >> 1, wn = w & 1;      // wave grid NWM x 2
+    const int wm = w / NWN, wn = w % NWN;   // wave grid NWM x NWN
 
     // ------------------------------------------------------------ tile --
     int64_t m0, m_end, n0;
@@ -323,7 +341,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
         r = r < p.N ? r : p.N - 1;
         b_src[u] = Bp + r * p.ldb + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
-    int64_t sb_col = n0 + 64 * (w & 1) + l;        // B 1x128 scales: waves 0 and 1 stage 64 each
+    int64_t sb_col = n0 + 64 * (w % (BN / 64)) + l;   // B 1x128 scales: waves 0 .. BN/64-1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
 
     auto stage_block = [&](int64_t kb, int stage) {
@@ -336,7 +354,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
         for (int u = 0; u < B_INSTR; ++u)
             g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
         if constexpr (B_TILE)
-            if (w < 2) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
+            if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
     };
 
     // rows of this lane's accumulators: m = m0 + WM*wm + 32*i + (l & 31)
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
         for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[am[i]];
     }
     float sb_next = 0.0f;
-    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb];
+    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / 128) * nkb];
     wait_lds_dma();
     __syncthreads();
 
@@ -446,7 +464,7 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
 #pragma unroll
                 for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
             }
-            if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / BN) * nkb + kb + 1];
+            if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / 128) * nkb + kb + 1];
             if constexpr (NV) {
 #pragma unroll
                 for (int i = 0; i < TI; ++i)
@@ -470,7 +488,9 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
         uint32_t ea[TI], ebt = 0;
         float fmx[TI];
         if constexpr (MX) {
-            ebt = max(s_ebt[kb & 1][0], s_ebt[kb & 1][1]);
+            ebt = s_ebt[kb & 1][0];
+#pragma unroll
+            for (int q = 1; q < NWN; ++q) ebt = max(ebt, s_ebt[kb & 1][q]);
             const float fb = e8m0_value(ebt);
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
@@ -671,43 +691,94 @@ __global__ __launch_bounds__(128 * NWM) void gemm_block_scaled_kernel(GemmParams
     }
 }
 
-template <int NWM, int AMODE, int BMODE, bool GROUPED>
-hipError_t launch_modes(const GemmParams& p, bool bf16, dim3 grid, hipStream_t s)
+template <class S, int AMODE, int BMODE, bool GROUPED>
+hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
-    const size_t lds = 2 * (size_t)Lds<NWM, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128>::STAGE;
-    auto k = bf16 ? gemm_block_scaled_kernel<NWM, AMODE, BMODE, true, GROUPED>
-                  : gemm_block_scaled_kernel<NWM, AMODE, BMODE, false, GROUPED>;
+    p.tiles_n = (int32_t)((a.N + S::BN - 1) / S::BN);
+    // grouped: every group can add one partial m-tile
+    p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUPED ? a.G : 0));
+    const dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
+    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128>::STAGE;
+    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUPED>
+                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUPED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(128 * NWM), lds, s, p);
+    hipLaunchKernelGGL(k, grid, dim3(64 * S::NWM * S::NWN), lds, s, p);
     return hipGetLastError();
 }
 
-template <int NWM, bool GROUPED>
-hipError_t dispatch(const GemmParams& p, int amode, int bmode, bool bf16, dim3 grid, hipStream_t s)
+// Compute units of the current device (one workgroup of either dense shape
+// fills a CU's LDS, so a launch runs in rounds of this many tiles).
+int device_cus()
 {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// The wide tile does twice the work of the 256 x 128 one in about 1.85x its
+// time (measured on the Llama-3-8B shapes), but halves the tile count, so a
+// problem whose wide tiles fill the last round poorly runs faster on the
+// narrow tile: compare rounds x time per round.
+std::atomic<int> g_tile_policy{FGS_TILE_AUTO};
+
+bool prefer_wide(const GemmArgs& a)
+{
+    const int policy = g_tile_policy.load(std::memory_order_relaxed);
+    if (policy != FGS_TILE_AUTO) return policy == FGS_TILE_WIDE;
+    const int64_t cus = device_cus();
+    const int64_t tm = (a.M + ShapeWide::BM - 1) / ShapeWide::BM;
+    const int64_t wide = tm * ((a.N + ShapeWide::BN - 1) / ShapeWide::BN);
+    const int64_t narrow = ((a.M + ShapeDense::BM - 1) / ShapeDense::BM) * ((a.N + ShapeDense::BN - 1) / ShapeDense::BN);
+    const double t_wide = 1.85 * (double)((wide + cus - 1) / cus);
+    const double t_narrow = (double)((narrow + cus - 1) / cus);
+    return t_wide <= t_narrow;
+}
+
+// Modes without promotion (one scale per operand for all of K: per-tensor
+// E4M3, NVFP4) keep 128 accumulators per lane and can take the wide tile; the
+// promoted modes hold partial sums too and take the 256 x 128 tile.
+hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hipStream_t s)
+{
+    using D = ShapeDense;
+    const bool wide = prefer_wide(a);
+    const int amode = a.A.scale_mode, bmode = a.B.scale_mode;
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUPED>(p, bf16, grid, s);
-        if constexpr (!GROUPED) {
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, false>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
+    } else if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0) {
+        return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, a, bf16, s);
+    } else if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3) {
+        if (wide) return launch_modes<ShapeWide, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, a, bf16, s);
+        return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, a, bf16, s);
+    } else if (amode == FGS_SCALE_TENSOR) {
+        if (bmode == FGS_SCALE_TENSOR) {
+            if (wide) return launch_modes<ShapeWide, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
+            return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
         }
-    } else if constexpr (!GROUPED) {
-        if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0)
-            return launch_modes<NWM, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, bf16, grid, s);
-        if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3)
-            return launch_modes<NWM, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, bf16, grid, s);
-        if (amode == FGS_SCALE_TENSOR) {
-            if (bmode == FGS_SCALE_TENSOR) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, bf16, grid, s);
-            if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<NWM, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, bf16, grid, s);
-        }
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, a, bf16, s);
     }
     return hipErrorInvalidValue;
 }
 
 } // namespace
+
+int gemm_tile_policy() { return g_tile_policy.load(); }
+
+int set_gemm_tile_policy(int policy)
+{
+    if (policy != FGS_TILE_AUTO && policy != FGS_TILE_NARROW && policy != FGS_TILE_WIDE) return -1;
+    return g_tile_policy.exchange(policy);
+}
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
 {
@@ -728,21 +799,16 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.ldc = a.ldc;
     p.offsets = a.group_offsets;
     p.G = a.G;
-    p.tiles_n = (int32_t)((a.N + BN - 1) / BN);
     if (a.M == 0 || a.N == 0) return hipSuccess;
+    const bool bf16 = a.out_bf16 != 0;
     if (a.group_offsets) {
-        constexpr int NWM = 2, BM = 64 * NWM;
         p.b_group_stride = a.N * a.B.ld;
-        p.sb_group_stride = ((a.N + BN - 1) / BN) * (a.K / BK);
-        const int64_t max_tiles = (a.M + BM - 1) / BM + a.G;
-        p.tiles_m = (int32_t)max_tiles;
-        dim3 grid((unsigned)(max_tiles * p.tiles_n));
-        return dispatch<NWM, true>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+        p.sb_group_stride = ((a.N + 127) / 128) * (a.K / BK);
+        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128)
+            return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, true>(p, a, bf16, stream);
+        return hipErrorInvalidValue;
     }
-    constexpr int NWM = 4, BM = 64 * NWM;
-    p.tiles_m = (int32_t)((a.M + BM - 1) / BM);
-    dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
-    return dispatch<NWM, false>(p, a.A.scale_mode, a.B.scale_mode, a.out_bf16 != 0, grid, stream);
+    return dispatch_dense(p, a, bf16, stream);
 }
 
 // MXFP8 and NVFP4 operands take the same kernel (decode and scale handling

@@ -188,6 +188,17 @@ def _check_operand(op: Operand, rows: int, K: int, name: str, groups: int = 1):
                          f"(got {op.scales.dtype}, {op.scales.numel()})")
 
 
+def gemm_tile_policy(policy: str) -> str:
+    """Set the workgroup tile of the single-scale GEMM modes ("auto",
+    "narrow" = 256 x 128, "wide" = 256 x 256); returns the previous one.
+    Results are bit-identical across policies."""
+    codes = {"auto": _lib.TILE_AUTO, "narrow": _lib.TILE_NARROW, "wide": _lib.TILE_WIDE}
+    if policy not in codes:
+        raise ValueError(f"tile policy must be one of {sorted(codes)}")
+    prev = _lib.load().fgs_gemm_tile_policy(codes[policy])
+    return {v: k for k, v in codes.items()}[prev]
+
+
 def _out_code(out_dtype):
     if out_dtype == torch.float32:
         return OUT_FP32

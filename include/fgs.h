@@ -199,6 +199,17 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
                                   int64_t total_M, int64_t N, int64_t K,
                                   void *C, int64_t ldc, int out_dtype, void *stream);
 
+/* Workgroup tile of the GEMMs whose operands carry one scale for all of K
+ * (per-tensor x per-tensor E4M3, NVFP4): FGS_TILE_AUTO (default) picks per
+ * problem from the tile counts and the device's compute units,
+ * FGS_TILE_NARROW forces 256 x 128 outputs per workgroup, FGS_TILE_WIDE
+ * 256 x 256.  Every output is accumulated in the same order either way, so
+ * the results are bit-identical; only the speed differs.  Other modes ignore
+ * the policy.  Process-wide; returns the previous policy, or -1 (nothing
+ * changed) for an unknown value. */
+enum { FGS_TILE_AUTO = 0, FGS_TILE_NARROW = 1, FGS_TILE_WIDE = 2 };
+int fgs_gemm_tile_policy(int policy);
+
 /* Device workspace needed by TENSOR-mode and NVFP4 quantization (bytes). */
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols);
 

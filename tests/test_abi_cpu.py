@@ -38,6 +38,18 @@ def test_version_and_workspace(lib):
     assert lib.fgs_last_error() is not None
 
 
+def test_gemm_tile_policy_setter(lib):
+    """Host-side state only: set, read back through the return value, reject
+    unknown values without changing the policy."""
+    prev = lib.fgs_gemm_tile_policy(_lib.TILE_WIDE)
+    try:
+        assert lib.fgs_gemm_tile_policy(_lib.TILE_NARROW) == _lib.TILE_WIDE
+        assert lib.fgs_gemm_tile_policy(7) == -1
+        assert lib.fgs_gemm_tile_policy(_lib.TILE_AUTO) == _lib.TILE_NARROW
+    finally:
+        lib.fgs_gemm_tile_policy(prev)
+
+
 # Fake, 16-byte aligned, never-dereferenced addresses: every call below must
 # be rejected by validation, which happens before any HIP call.
 FAKE = ctypes.c_void_p(0x10000)

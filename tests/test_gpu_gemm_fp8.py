@@ -83,7 +83,7 @@ MODES = [("tile", "block"), ("tile", "tile"), ("tensor", "tensor"), ("tile", "te
 
 
 @pytest.mark.parametrize("amode,bmode", MODES)
-@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (128, 384, 1024)])
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (128, 384, 1024), (520, 777, 384)])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_gemm_modes_ragged(fgs, amode, bmode, M, N, K, out):
     a_bits = synth.activations(M, K, seed=M + K)
@@ -91,6 +91,25 @@ def test_gemm_modes_ragged(fgs, amode, bmode, M, N, K, out):
     A, ah = oracle_operand(fgs, a_bits, amode)
     B, bh = oracle_operand(fgs, b_bits, bmode)
     _run_and_check(fgs, A, B, ah, bh, out)
+
+
+@pytest.mark.parametrize("M,N,K", [(257, 129, 256), (520, 777, 384), (1000, 600, 512)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_tile_policies_bit_identical(fgs, M, N, K, out):
+    """Per-tensor x per-tensor runs on either workgroup tile (256 x 128 or
+    256 x 256); both meet the bound and give the same bits."""
+    A, ah = oracle_operand(fgs, synth.activations(M, K, seed=M), "tensor")
+    B, bh = oracle_operand(fgs, synth.weights(N, K, seed=N), "tensor")
+    res = {}
+    prev = fgs.gemm_tile_policy("narrow")
+    try:
+        for pol in ("narrow", "wide"):
+            fgs.gemm_tile_policy(pol)
+            _run_and_check(fgs, A, B, ah, bh, out)
+            res[pol] = fgs.gemm_block_scaled(A, B, out).cpu()
+    finally:
+        fgs.gemm_tile_policy(prev)
+    assert torch.equal(res["narrow"].view(torch.uint8), res["wide"].view(torch.uint8))
 
 
 def test_gemm_row_stride_and_ldc(fgs):

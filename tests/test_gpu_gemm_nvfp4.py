@@ -54,12 +54,29 @@ def _check(fgs, A, B, ah, bh, out, rows=None):
         assert ok, f"{nbad} BF16 outputs outside one ulp"
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (256, 384, 1024)])
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (256, 384, 1024), (520, 777, 384)])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_nvfp4_gemm_ragged(fgs, M, N, K, out):
     A, ah = nv_operand(fgs, synth.activations(M, K, seed=M + 7))
     B, bh = nv_operand(fgs, synth.weights(N, K, seed=N + 9))
     _check(fgs, A, B, ah, bh, out)
+
+
+@pytest.mark.parametrize("M,N,K", [(257, 129, 256), (520, 777, 384)])
+def test_nvfp4_gemm_tile_policies_bit_identical(fgs, M, N, K):
+    """The NVFP4 GEMM runs on either workgroup tile with the same bits."""
+    A, ah = nv_operand(fgs, synth.activations(M, K, seed=M + 3))
+    B, bh = nv_operand(fgs, synth.weights(N, K, seed=N + 5))
+    res = {}
+    prev = fgs.gemm_tile_policy("narrow")
+    try:
+        for pol in ("narrow", "wide"):
+            fgs.gemm_tile_policy(pol)
+            _check(fgs, A, B, ah, bh, torch.float32)
+            res[pol] = fgs.gemm_block_scaled(A, B, torch.float32).cpu()
+    finally:
+        fgs.gemm_tile_policy(prev)
+    assert torch.equal(res["narrow"].view(torch.uint8), res["wide"].view(torch.uint8))
 
 
 def test_nvfp4_gemm_wgrad_rht_sr(fgs):
