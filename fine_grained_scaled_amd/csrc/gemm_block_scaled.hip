@@ -273,18 +273,38 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         m_end = p.M;
         n0 = (int64_t)tn * BN;
     } else {
-        // Device-side schedule: exclusive prefix of per-group m-tile counts;
-        // virtual tile v -> (group, n-tile, m-tile), m-tile fastest.
-        const int64_t v = blockIdx.x;
-        int running = 0;
-        if (t == 0) s_sel[0] = -1;
-        for (int chunk = 0; chunk < p.G; chunk += NT) {
-            const int g = chunk + t;
+        // Device-side schedule over the tiles of all groups in canonical
+        // order u (group, then n-tile, then m-tile fastest).  Workgroup v
+        // takes u from the front for even runs of 8 and from the back for odd
+        // runs, so short (HBM-bound) and long (MFMA-bound) groups run side by
+        // side whatever order the groups come in.  v -> u is a bijection on
+        // [0, T): the front takes [0, F) and the back [T - B, T) with F + B = T.
+        auto m_tiles = [&](int g) {
             int cnt = 0;
             if (g < p.G) {
                 const int32_t o0 = p.offsets[g], o1 = p.offsets[g + 1];
                 if (o0 >= 0 && o1 >= o0 && o1 <= p.M) cnt = (o1 - o0 + BM - 1) / BM;
             }
+            return cnt;
+        };
+        int my_tiles = 0;
+        for (int g = t; g < p.G; g += NT) my_tiles += m_tiles(g);
+        s_scan[t] = my_tiles;
+        __syncthreads();
+        for (int d = NT / 2; d > 0; d >>= 1) {
+            if (t < d) s_scan[t] += s_scan[t + d];
+            __syncthreads();
+        }
+        const int64_t total = (int64_t)s_scan[0] * p.tiles_n;
+        __syncthreads();
+        if ((int64_t)blockIdx.x >= total) return;                  // beyond the last tile
+        const int64_t vb = (int64_t)blockIdx.x >> 3, vbase = ((vb >> 1) << 3) + (blockIdx.x & 7);
+        const int64_t v = (vb & 1) ? total - 1 - vbase : vbase;
+        int running = 0;
+        if (t == 0) s_sel[0] = -1;
+        for (int chunk = 0; chunk < p.G; chunk += NT) {
+            const int g = chunk + t;
+            const int cnt = m_tiles(g);
             s_scan[t] = cnt;
             __syncthreads();
             for (int d = 1; d < NT; d <<= 1) {
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         }
         __syncthreads();
         const int g = s_sel[0];
-        if (g < 0) return;                                    // beyond the last tile
+        if (g < 0) return;                                    // unreachable for v < total
         const int32_t o0 = p.offsets[g], o1 = p.offsets[g + 1];
         const int mt_g = (o1 - o0 + BM - 1) / BM;
         const int64_t local = v - (int64_t)s_sel[1] * p.tiles_n;
@@ -344,15 +364,22 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     int64_t sb_col = n0 + 64 * (w % (BN / 64)) + l;   // B 1x128 scales: waves 0 .. BN/64-1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
 
+    // Rows of the tile that exist; a wave-instruction whose rows all lie past
+    // them is not issued (its LDS rows only feed outputs that are never
+    // stored), and waves whose accumulator rows all lie past them skip the
+    // MFMAs: short MoE groups then move and multiply only what they own.
+    const int a_live = (int)(m_end - m0 < BM ? m_end - m0 : BM);
+    const int b_live = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const bool wave_live = WM * wm < a_live;
     auto stage_block = [&](int64_t kb, int stage) {
         uint8_t* st = smem + stage * L::STAGE;
         const int64_t ko = kb * ROW;
 #pragma unroll
         for (int u = 0; u < A_INSTR; ++u)
-            g2lds16(a_src[u] + ko, st + (A_ROWS * w + RPI * u) * ROW);
+            if (A_ROWS * w + RPI * u < a_live) g2lds16(a_src[u] + ko, st + (A_ROWS * w + RPI * u) * ROW);
 #pragma unroll
         for (int u = 0; u < B_INSTR; ++u)
-            g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
+            if (B_ROWS * w + RPI * u < b_live) g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
         if constexpr (B_TILE)
             if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
     };
@@ -499,141 +526,143 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             }
         }
 
-        const uint8_t* st = smem + cur * L::STAGE;
-        const uint8_t* la = st + (WM * wm + (l & 31)) * ROW;
-        const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
+        if (wave_live) {
+            const uint8_t* st = smem + cur * L::STAGE;
+            const uint8_t* la = st + (WM * wm + (l & 31)) * ROW;
+            const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
 
-        f32x16 part[TI][TJ];
-        if constexpr (PROMOTE) {
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-        }
-        // lane half h reads chunk 2*ks + h (bytes 32*ks + 16*h .. +15) of its
-        // row: the pair of k-steps (2ks, 2ks+1) then covers k = 32*ks ..
-        // 32*ks+31 once, with the same k order for A and B
-        if constexpr (NV) {
-            // lane half h reads chunk 2*ks2 + h (32 codes, k = 64*ks2 + 32*h ..
-            // +31); word g of it feeds MFMA k-step (ks2, g), whose 16-block is
-            // 4*ks2 + 2*h + g/2
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
-                const int co = ((2 * ks2 + half) ^ swz) << 4;
-                f16x2 sa2[TI], sb2[TJ];
-                uint4 ra[TI], rb[TJ];
-#pragma unroll
-                for (int i = 0; i < TI; ++i) {
-                    sa2[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_nw[i][ks2] >> (16 * half), 1.0f, false);
-                    ra[i] = *reinterpret_cast<const uint4*>(la + 32 * i * ROW + co);
-                }
-#pragma unroll
-                for (int j = 0; j < TJ; ++j) {
-                    sb2[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_nw[j][ks2] >> (16 * half), 1.0f, false);
-                    rb[j] = *reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co);
-                }
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f16x8 af[TI], bf[TJ];
-#pragma unroll
+            f32x16 part[TI][TJ];
+            if constexpr (PROMOTE) {
+    #pragma unroll
+                for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+            }
+            // lane half h reads chunk 2*ks + h (bytes 32*ks + 16*h .. +15) of its
+            // row: the pair of k-steps (2ks, 2ks+1) then covers k = 32*ks ..
+            // 32*ks+31 once, with the same k order for A and B
+            if constexpr (NV) {
+                // lane half h reads chunk 2*ks2 + h (32 codes, k = 64*ks2 + 32*h ..
+                // +31); word g of it feeds MFMA k-step (ks2, g), whose 16-block is
+                // 4*ks2 + 2*h + g/2
+    #pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const int co = ((2 * ks2 + half) ^ swz) << 4;
+                    f16x2 sa2[TI], sb2[TJ];
+                    uint4 ra[TI], rb[TJ];
+    #pragma unroll
                     for (int i = 0; i < TI; ++i) {
-                        const uint32_t wd = g == 0 ? ra[i].x : g == 1 ? ra[i].y : g == 2 ? ra[i].z : ra[i].w;
-                        af[i] = decode_nv_word(wd, sa2[i][g >> 1]);
+                        sa2[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_nw[i][ks2] >> (16 * half), 1.0f, false);
+                        ra[i] = *reinterpret_cast<const uint4*>(la + 32 * i * ROW + co);
                     }
-#pragma unroll
+    #pragma unroll
                     for (int j = 0; j < TJ; ++j) {
-                        const uint32_t wd = g == 0 ? rb[j].x : g == 1 ? rb[j].y : g == 2 ? rb[j].z : rb[j].w;
-                        bf[j] = decode_nv_word(wd, sb2[j][g >> 1]);
+                        sb2[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_nw[j][ks2] >> (16 * half), 1.0f, false);
+                        rb[j] = *reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co);
                     }
-#pragma unroll
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        f16x8 af[TI], bf[TJ];
+    #pragma unroll
+                        for (int i = 0; i < TI; ++i) {
+                            const uint32_t wd = g == 0 ? ra[i].x : g == 1 ? ra[i].y : g == 2 ? ra[i].z : ra[i].w;
+                            af[i] = decode_nv_word(wd, sa2[i][g >> 1]);
+                        }
+    #pragma unroll
+                        for (int j = 0; j < TJ; ++j) {
+                            const uint32_t wd = g == 0 ? rb[j].x : g == 1 ? rb[j].y : g == 2 ? rb[j].z : rb[j].w;
+                            bf[j] = decode_nv_word(wd, sb2[j][g >> 1]);
+                        }
+    #pragma unroll
+                        for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
+                    }
+                }
+            } else
+    #pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int co = ((2 * ks + half) ^ swz) << 4;
+                if constexpr (MX) {
+                    // k-steps 2ks, 2ks+1 are MX block ks of this 128-K block
+                    bf16x8 af[TI][2], bf[TJ][2];
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co),
+                                 e8m0_rel((b_sw[j] >> (8 * ks)) & 0xFFu, ebt), bf[j][0], bf[j][1]);
+    #pragma unroll
                     for (int i = 0; i < TI; ++i)
-#pragma unroll
-                        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
+                        decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co),
+                                 e8m0_rel((a_sw[i] >> (8 * ks)) & 0xFFu, ea[i]), af[i][0], af[i][1]);
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                        for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                            for (int j = 0; j < TJ; ++j) part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+                } else {
+                    f16x8 af[TI][2], bf[TJ][2];
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
+    #pragma unroll
+                    for (int i = 0; i < TI; ++i)
+                        decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                        for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                            for (int j = 0; j < TJ; ++j) {
+                                if constexpr (PROMOTE)
+                                    part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+                                else
+                                    acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
+                            }
                 }
             }
-        } else
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int co = ((2 * ks + half) ^ swz) << 4;
-            if constexpr (MX) {
-                // k-steps 2ks, 2ks+1 are MX block ks of this 128-K block
-                bf16x8 af[TI][2], bf[TJ][2];
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co),
-                             e8m0_rel((b_sw[j] >> (8 * ks)) & 0xFFu, ebt), bf[j][0], bf[j][1]);
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-                    decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co),
-                             e8m0_rel((a_sw[i] >> (8 * ks)) & 0xFFu, ea[i]), af[i][0], af[i][1]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < TI; ++i)
-#pragma unroll
-                        for (int j = 0; j < TJ; ++j) part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
-            } else {
-                f16x8 af[TI][2], bf[TJ][2];
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-                    decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < TI; ++i)
-#pragma unroll
-                        for (int j = 0; j < TJ; ++j) {
-                            if constexpr (PROMOTE)
-                                part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
-                            else
-                                acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
-                        }
-            }
-        }
 
-        if constexpr (PROMOTE) {
-            const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
-            const float sb_t = BMODE == FGS_SCALE_TENSOR ? sBp[0] : 1.0f;
-            if constexpr (B_TILE) {
-                // columns of this lane's accumulators: n = 64*wn + 32*j + 8*q + 4*(l>>5) + e
-                const float* ssb = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES);
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 s4 = *reinterpret_cast<const float4*>(ssb + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5));
-                        const float sbv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                        for (int i = 0; i < TI; ++i) {
-                            const float fa = AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], fa * sbv[e], acc[i][j][4 * q + e]);
+            if constexpr (PROMOTE) {
+                const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
+                const float sb_t = BMODE == FGS_SCALE_TENSOR ? sBp[0] : 1.0f;
+                if constexpr (B_TILE) {
+                    // columns of this lane's accumulators: n = 64*wn + 32*j + 8*q + 4*(l>>5) + e
+                    const float* ssb = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES);
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 s4 = *reinterpret_cast<const float4*>(ssb + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5));
+                            const float sbv[4] = {s4.x, s4.y, s4.z, s4.w};
+    #pragma unroll
+                            for (int i = 0; i < TI; ++i) {
+                                const float fa = AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i];
+    #pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], fa * sbv[e], acc[i][j][4 * q + e]);
+                            }
                         }
+                } else if constexpr (MX) {
+    #pragma unroll
+                    for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                        for (int j = 0; j < TJ; ++j)
+    #pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                acc[i][j][r] = __builtin_fmaf(part[i][j][r], fmx[i], acc[i][j][r]);
+                } else {
+                    const float fb = BMODE == FGS_SCALE_TENSOR ? sb_t : sb_blk;
+    #pragma unroll
+                    for (int i = 0; i < TI; ++i) {
+                        const float f = (AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i]) * fb;
+    #pragma unroll
+                        for (int j = 0; j < TJ; ++j)
+    #pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                acc[i][j][r] = __builtin_fmaf(part[i][j][r], f, acc[i][j][r]);
                     }
-            } else if constexpr (MX) {
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            acc[i][j][r] = __builtin_fmaf(part[i][j][r], fmx[i], acc[i][j][r]);
-            } else {
-                const float fb = BMODE == FGS_SCALE_TENSOR ? sb_t : sb_blk;
-#pragma unroll
-                for (int i = 0; i < TI; ++i) {
-                    const float f = (AMODE == FGS_SCALE_TENSOR ? sa_t : sa[i]) * fb;
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            acc[i][j][r] = __builtin_fmaf(part[i][j][r], f, acc[i][j][r]);
                 }
             }
         }
