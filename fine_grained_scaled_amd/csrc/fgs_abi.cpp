@@ -1,6 +1,7 @@
 // fgs_abi.cpp -- the extern "C" entry points of libfgs: argument validation
 // (before any HIP call), error reporting, and dispatch to the launchers.
 // The operations themselves are documented in include/fgs.h.
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -69,6 +70,23 @@ int check_operand(const fgs_operand* op, const char* name, int64_t rows, int64_t
 }
 
 } // namespace
+
+namespace fgs {
+
+int device_cus()
+{
+    static std::atomic<int> cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+} // namespace fgs
 
 extern "C" {
 

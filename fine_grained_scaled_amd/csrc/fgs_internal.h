@@ -58,6 +58,10 @@ struct GemmArgs {
     const int32_t* group_offsets;   // nullptr for the dense GEMM
     int32_t G;
 };
+// Compute units of the current device (cached per device; 256 if the
+// query fails).
+int device_cus();
+
 // GEMM tile policy (FGS_TILE_*), read at launch.
 int gemm_tile_policy();
 int set_gemm_tile_policy(int policy);

@@ -737,21 +737,6 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     return hipGetLastError();
 }
 
-// Compute units of the current device (one workgroup of either dense shape
-// fills a CU's LDS, so a launch runs in rounds of this many tiles).
-int device_cus()
-{
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 // The wide tile does twice the work of the 256 x 128 one in about 1.85x its
 // time (measured on the Llama-3-8B shapes), but halves the tile count, so a
 // problem whose wide tiles fill the last round poorly runs faster on the
@@ -762,7 +747,7 @@ bool prefer_wide(const GemmArgs& a)
 {
     const int policy = g_tile_policy.load(std::memory_order_relaxed);
     if (policy != FGS_TILE_AUTO) return policy == FGS_TILE_WIDE;
-    const int64_t cus = device_cus();
+    const int64_t cus = device_cus();   // one workgroup of either dense shape fills a CU's LDS
     const int64_t tm = (a.M + ShapeWide::BM - 1) / ShapeWide::BM;
     const int64_t wide = tm * ((a.N + ShapeWide::BN - 1) / ShapeWide::BN);
     const int64_t narrow = ((a.M + ShapeDense::BM - 1) / ShapeDense::BM) * ((a.N + ShapeDense::BN - 1) / ShapeDense::BN);

@@ -228,3 +228,67 @@ def test_llama8b_qkv_layer_sampled(fgs, orient):
     B, bh = oracle_operand(fgs, b_bits, b_mode, colwise=b_col)
     out = torch.float32 if orient == "wgrad" else torch.bfloat16
     _run_and_check(fgs, A, B, ah, bh, out, rows=rs)
+
+
+# ------------------------------------------------- full-size MoE (sampled) --
+@pytest.mark.parametrize("N,K", [(4096, 7168), (7168, 2048)], ids=["gate_up", "down"])
+def test_grouped_deepseek_moe_sampled(fgs, N, K):
+    """DeepSeek-V3 MoE grouped GEMM at full size: 256 experts, 32768 routed
+    rows (4096 tokens x top-8) with seeded Zipf(1.1) counts, one expert made
+    empty; gate/up (K, N) = (7168, 4096) and down (2048, 7168).  Only the
+    sampled experts (the largest, one just over 128 rows, one under 16) carry
+    oracle-quantized weights and only the sampled rows oracle-quantized
+    activations; every other code is zero (scale 1), so a row that reads the
+    wrong expert or the wrong rows gives a wrong (zero) result."""
+    G = 256
+    counts = synth.expert_counts(32768, G, 1.1, seed=0).copy()
+    empty = G - 1
+    counts[0] += counts[empty]
+    counts[empty] = 0
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(offs[-1])
+    mid = int(np.flatnonzero((counts > 128) & (counts < 256))[0])
+    small = int(np.flatnonzero((counts > 0) & (counts < 16))[0])
+    experts = [0, mid, small]
+    rows = []
+    for g in experts:
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for d in (0, 1, 127, 128, 255, 256, (r1 - r0) // 2, r1 - r0 - 2, r1 - r0 - 1):
+            if 0 <= d < r1 - r0:
+                rows.append(r0 + d)
+    rows = np.unique(np.array(rows))
+
+    # activations: oracle-quantized sampled rows, zero codes elsewhere
+    a_bits = synth.activations(len(rows), K, seed=21)
+    qa, sa = oracle.quant_e4m3(a_bits, "tile")
+    ah = oracle.dequant_e4m3(qa, sa, "tile")
+    qa_full = torch.zeros((total, K), dtype=torch.uint8)
+    qa_full[torch.from_numpy(rows)] = torch.from_numpy(qa)
+    sa_full = torch.ones((K // 128, total), dtype=torch.float32)
+    sa_full[:, torch.from_numpy(rows)] = torch.from_numpy(np.ascontiguousarray(sa.T))
+    A = fgs.Operand(qa_full.cuda(), sa_full.cuda(), 1)
+
+    # weights: oracle-quantized for the sampled experts, zero codes elsewhere
+    qb = torch.zeros((G * N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.ones((G * (N // 128), K // 128), dtype=torch.float32, device="cuda")
+    bh = {}
+    for g in experts:
+        q, s = oracle.quant_e4m3(synth.weights(N, K, seed=300 + g), "block")
+        qb[g * N:(g + 1) * N] = torch.from_numpy(q).cuda()
+        sb[g * (N // 128):(g + 1) * (N // 128)] = torch.from_numpy(s).cuda()
+        bh[g] = oracle.dequant_e4m3(q, s, "block")
+    B = fgs.Operand(qb, sb, 2)
+
+    c = torch.full((total, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    fgs.grouped_gemm_block_scaled(A, B, torch.from_numpy(offs).cuda(), N, out_dtype=torch.bfloat16, out=c)
+    torch.cuda.synchronize()
+    got = c[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    group_of = np.searchsorted(offs, rows, side="right") - 1
+    for g in experts:
+        sel = group_of == g
+        cref, sref = oracle.gemm_ref(ah[sel], bh[g])
+        ok, nbad = gemm_within_bf16_bound(got[sel], cref, sref)
+        assert ok, f"expert {g}: {nbad} BF16 outputs outside one ulp"
+    # an unsampled row of a zero-weight expert is exactly zero
+    other = int(offs[1])
+    assert float(c[other].float().abs().max()) == 0.0
