@@ -58,7 +58,8 @@ __device__ __forceinline__ float bf16_at(const uint4& v, int j)
 
 __device__ __forceinline__ float xor1(float v)
 {
-    return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), DPP_XOR1, 0xF, 0xF, false));
+    // every lane is written (full row and bank masks), so no old value is needed
+    return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), DPP_XOR1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float xor16(float v)
 {
@@ -66,13 +67,15 @@ __device__ __forceinline__ float xor16(float v)
 }
 
 // Random Hadamard transform of the 16-chunk whose elements 8*hpos .. 8*hpos+7
-// this lane holds (the partner lane holds the other 8).
+// this lane holds (the partner lane holds the other 8), without the final
+// factor 1/4: z holds d (.) x on entry (the signs are applied to the packed
+// BF16 pairs, see rht_pair_signs) and 4 * (H d x) on return.  The caller
+// folds the exact 1/4 into the block amax and the divisor.  sgn is +1 for
+// hpos 0 and -1 for hpos 1: the stride-8 stage is other + sgn * z, one FMA
+// whose product by +-1 is exact.
 template <bool ROWWISE>
-__device__ __forceinline__ void rht16(float z[8], int hpos, uint32_t sign_mask)
+__device__ __forceinline__ void rht16x4(float z[8], float sgn)
 {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if ((sign_mask >> (8 * hpos + i)) & 1u) z[i] = -z[i];
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
@@ -85,9 +88,35 @@ __device__ __forceinline__ void rht16(float z[8], int hpos, uint32_t sign_mask)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float other = ROWWISE ? xor1(z[i]) : xor16(z[i]);
-        z[i] = hpos == 0 ? z[i] + other : other - z[i];
-        z[i] *= 0.25f;
+        z[i] = __builtin_fmaf(sgn, z[i], other);
     }
+}
+
+// XOR masks that apply the RHT signs to packed BF16 pairs.  Row-wise chunks
+// run along the 8 columns of a lane (positions 8*hpos + j, pair k = columns
+// 2k, 2k+1); column-wise chunks run along its 8 rows (position 8*hpos + u,
+// the same sign for every column of row u).
+__device__ __forceinline__ void rht_pair_signs(uint32_t sign_mask, int hpos_row, int hpos_col,
+                                               uint32_t row_m[4], uint32_t col_m[8])
+{
+    const uint32_t sr = sign_mask >> (8 * hpos_row), sc = sign_mask >> (8 * hpos_col);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        row_m[k] = (((sr >> (2 * k)) & 1u) << 15) | (((sr >> (2 * k + 1)) & 1u) << 31);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) col_m[u] = ((sc >> u) & 1u) * 0x80008000u;
+}
+
+__device__ __forceinline__ uint4 xor4(const uint4& v, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return make_uint4(v.x ^ a, v.y ^ b, v.z ^ c, v.w ^ d);
+}
+
+// FP32 bits of a quarter of the FP32 value with bits m (exact for every
+// value a transformed chunk can hold; NaN stays NaN, Inf stays Inf)
+__device__ __forceinline__ uint32_t quarter_bits(uint32_t m)
+{
+    return as_u32(as_f32(m) * 0.25f);
 }
 
 __device__ __forceinline__ uint32_t fabs_bits(float v) { return as_u32(v) & 0x7FFFFFFFu; }
@@ -181,9 +210,14 @@ __device__ __forceinline__ float div_rn(float a, float d, float r)
 // RNE codes come from the hardware converter v_cvt_scalef32_pk_fp4_f32
 // (unit scale), which equals the RNE encoder above with the sign of the
 // input for every FP32 value in [-6, 6] (checked exhaustively on gfx950).
+//
+// y = z / zscale: z is either the value itself (zscale 1) or four times the
+// transformed value (zscale 4, see rht16x4); amax_b is the amax of y.  The
+// quotient fl32(y / d) is the correctly rounded z / (zscale d), and zscale d
+// is exact (d <= 448 * 2^128 / 2688 leaves room for the factor 4).
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b, const TensorScale& ts,
-                                              const uint32_t rw[8], uint32_t& sb_out)
+                                              const uint32_t rw[8], uint32_t& sb_out, float zscale)
 {
     const uint32_t sb = e4m3_code_f32(as_f32(amax_b) / ts.six_st);
     sb_out = sb;
@@ -191,7 +225,7 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
     if (d == 0.0f || d != d) return 0;
     float k = 1.0f;
     if (__builtin_expect(as_f32(amax_b) < 0x1p-30f, 0)) k = 0x1p64f;
-    const float dk = d * k;
+    const float dk = d * zscale * k;
     const float r = 1.0f / dk;
     float q[8];
     uint32_t sg[8];
@@ -269,27 +303,37 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
         for (int j = 0; j < 8; ++j) plain = max(plain, fabs_bits(bf16_at(v[u], j)));
 
     uint32_t mrow = plain, mcol = plain;
+    uint32_t row_m[4], col_m[8];
+    rht_pair_signs(sign_mask, cg & 1, (l >> 4) & 1, row_m, col_m);
     if (rht_mask & 1) {
         mrow = 0;
+        const float sgn = (cg & 1) ? -1.0f : 1.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+            const uint4 vs = xor4(v[u], row_m[0], row_m[1], row_m[2], row_m[3]);
             float z[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) z[j] = bf16_at(v[u], j);
-            rht16<true>(z, cg & 1, sign_mask);
+            for (int j = 0; j < 8; ++j) z[j] = bf16_at(vs, j);
+            rht16x4<true>(z, sgn);
             mrow = max(mrow, amax8(z));
         }
+        mrow = quarter_bits(mrow);
     }
     if (rht_mask & 2) {
         mcol = 0;
+        const float sgn = ((l >> 4) & 1) ? -1.0f : 1.0f;
+        uint4 vs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vs[u] = xor4(v[u], col_m[u], col_m[u], col_m[u], col_m[u]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float z[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) z[u] = bf16_at(v[u], j);
-            rht16<false>(z, (l >> 4) & 1, sign_mask);
+            for (int u = 0; u < 8; ++u) z[u] = bf16_at(vs[u], j);
+            rht16x4<false>(z, sgn);
             mcol = max(mcol, amax8(z));
         }
+        mcol = quarter_bits(mcol);
     }
     mrow = max_xor32(max_xor16(max_lanes16(mrow)));
     mcol = max_xor32(max_xor16(max_lanes16(mcol)));
@@ -339,18 +383,25 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
         tensor_scale[1] = ts_col.st;
     }
 
+    uint32_t row_m[4], col_m[8];
+    rht_pair_signs(sign_mask, cg & 1, (l >> 4) & 1, row_m, col_m);
+
     // ---------------- row-wise: 16-blocks along columns ----------------
     if (q) {
         const int64_t qcols = cols / 2, nsc = cols / 16;
+        const bool rht = rht_mask & 1;
+        const float sgn = (cg & 1) ? -1.0f : 1.0f, zscale = rht ? 4.0f : 1.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             float z[8];
+            const uint4 vs = rht ? xor4(v[u], row_m[0], row_m[1], row_m[2], row_m[3]) : v[u];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) z[j] = bf16_at(v[u], j);
-            if (rht_mask & 1) rht16<true>(z, cg & 1, sign_mask);
+            for (int j = 0; j < 8; ++j) z[j] = bf16_at(vs, j);
+            if (rht) rht16x4<true>(z, sgn);
             uint32_t mb = amax8(z);
             const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, DPP_XOR1, 0xF, 0xF, false);
             mb = max(mb, other);
+            if (rht) mb = quarter_bits(mb);
             const int64_t row = r0 + 8 * rg + u;
             uint32_t rw[8];
             if constexpr (SR) {
@@ -358,7 +409,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
                 for (int j = 0; j < 8; ++j) rw[j] = sr_word_at(ilo[u], midr[u], j);
             }
             uint32_t sb;
-            const uint32_t packed = nv_block8<SR>(z, mb, ts_row, rw, sb);
+            const uint32_t packed = nv_block8<SR>(z, mb, ts_row, rw, sb, zscale);
             if (col_ok && row < rows) {
                 *reinterpret_cast<uint32_t*>(q + row * qcols + col / 2) = packed;
                 if (!(cg & 1)) scales[row * nsc + col / 16] = (uint8_t)sb;
@@ -370,21 +421,28 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     if (qT) {
         const int64_t nscT = rows / 16;
         const int hpos = (l >> 4) & 1;
+        const bool rht = rht_mask & 2;
+        const float sgn = hpos ? -1.0f : 1.0f, zscale = rht ? 4.0f : 1.0f;
+        if (rht) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = xor4(v[u], col_m[u], col_m[u], col_m[u], col_m[u]);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float z[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) z[u] = bf16_at(v[u], j);
-            if (rht_mask & 2) rht16<false>(z, hpos, sign_mask);
+            if (rht) rht16x4<false>(z, sgn);
             uint32_t mb = amax8(z);
             mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+            if (rht) mb = quarter_bits(mb);
             uint32_t rw[8];
             if constexpr (SR) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) rw[u] = sr_word_at(ilo[u], midr[u], j);
             }
             uint32_t sb;
-            const uint32_t packed = nv_block8<SR>(z, mb, ts_col, rw, sb);
+            const uint32_t packed = nv_block8<SR>(z, mb, ts_col, rw, sb, zscale);
             *reinterpret_cast<uint32_t*>(&tbuf[8 * cg + j][4 * rg]) = packed;
             if (hpos == 0 && col_ok) scalesT[(col + j) * nscT + (r0 + 8 * rg) / 16] = (uint8_t)sb;
         }
