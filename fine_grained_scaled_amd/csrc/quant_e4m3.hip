@@ -204,7 +204,9 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     }
 }
 
-// Tensor amax (|BF16| bits) of a 128 x 128-block grid, one atomic per workgroup.
+// Tensor amax (|BF16| bits) of a 128 x 128-block grid: persistent over the
+// blocks with stride gridDim.x, the next block's rows loaded before the
+// current ones are reduced; one atomic per workgroup.
 __global__ __launch_bounds__(256) void amax_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     int64_t nbr, int64_t nbc, uint32_t* __restrict__ out)
@@ -212,16 +214,29 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(
     __shared__ uint32_t red[4];
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int cg = l & 15, rg = 4 * w + (l >> 4);
-    uint32_t m = 0;
-    for (int64_t blk = blockIdx.x; blk < nbr * nbc; blk += gridDim.x) {
-        const int64_t r0 = (blk / nbc) * TB, c0 = (blk % nbc) * TB;
-        const int64_t col = c0 + 8 * cg;
-        if (col >= cols) continue;
+    const int64_t nblk = nbr * nbc;
+    auto load = [&](int64_t blk, uint4 v[8]) {
+        const int64_t r0 = (blk / nbc) * TB, col = (blk % nbc) * TB + 8 * cg;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t row = r0 + 8 * rg + u;
-            if (row < rows) m = max(m, abs_max8(*reinterpret_cast<const uint4*>(x + row * ldx + col)));
+            v[u] = (col < cols && row < rows) ? *reinterpret_cast<const uint4*>(x + row * ldx + col)
+                                              : make_uint4(0, 0, 0, 0);
         }
+    };
+    uint32_t m = 0;
+    int64_t blk = blockIdx.x;
+    uint4 v[8];
+    if (blk < nblk) load(blk, v);
+    while (blk < nblk) {
+        const int64_t next = blk + gridDim.x;
+        uint4 vn[8];
+        if (next < nblk) load(next, vn);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = max(m, abs_max8(v[u]));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = vn[u];
+        blk = next;
     }
     m = max_xor32(max_xor16(max_lanes16(m)));
     if (l == 0) red[w] = m;
@@ -257,8 +272,8 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
     case FGS_SCALE_TENSOR: {
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
         hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, amax, 1, 0u);
-        const int64_t nblk = nbr * nbc;
-        const unsigned g = (unsigned)(nblk < 1024 ? nblk : 1024);
+        const int64_t nblk = nbr * nbc, cap = (int64_t)device_cus() * 8;
+        const unsigned g = (unsigned)(nblk < cap ? nblk : cap);
         hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
                            x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
         hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_TENSOR>, grid, block, 0, stream,

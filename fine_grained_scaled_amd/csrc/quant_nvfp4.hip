@@ -172,7 +172,7 @@ __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
 }
 
 struct TensorScale {
-    float st, six_st;
+    float st, six_st, r6;    // s_t, fl32(6 s_t), RN(1 / fl32(6 s_t))
 };
 
 __device__ __forceinline__ TensorScale tensor_scale_from(uint32_t amax_bits)
@@ -182,6 +182,7 @@ __device__ __forceinline__ TensorScale tensor_scale_from(uint32_t amax_bits)
     else if (amax_bits == 0) s.st = 1.0f;
     else s.st = as_f32(amax_bits) / 2688.0f;
     s.six_st = 6.0f * s.st;
+    s.r6 = 1.0f / s.six_st;
     return s;
 }
 
@@ -219,7 +220,18 @@ template <bool SR>
 __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b, const TensorScale& ts,
                                               const uint32_t rw[8], uint32_t& sb_out, float zscale)
 {
-    const uint32_t sb = e4m3_code_f32(as_f32(amax_b) / ts.six_st);
+    // fl32(amax_b / (6 s_t)) by the same correction as the elements (the
+    // residual is normal for amax_b >= 2^-90; smaller block maxima take IEEE
+    // division), then the hardware E4M3 cast: the quotient is at most
+    // 448 (1 + 2^-23) because amax_b <= amax_t, and the med3 clamp to 448
+    // makes the cast saturate exactly as the encoder does.
+    const float amb = as_f32(amax_b);
+    float qs;
+    if (__builtin_expect(amb >= 0x1p-90f, 1)) qs = div_rn(amb, ts.six_st, ts.r6);
+    else qs = amb / ts.six_st;
+    uint32_t sb;
+    if (qs != qs) sb = 0x7Fu;
+    else sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(qs, 448.0f), 0.0f, 0, false) & 0xFFu;
     sb_out = sb;
     const float d = e4m3_value(sb) * ts.st;
     if (d == 0.0f || d != d) return 0;
@@ -284,6 +296,21 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
 }
 
 // ---------------------------------------------------------------- pass 1 --
+// max |x| of 8 BF16 values as FP32 bits (BF16 magnitude order is FP32 order;
+// NaN above Inf)
+__device__ __forceinline__ uint32_t bf16_amax8_bits(const uint4& v)
+{
+    const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
+    const uint32_t m = max(max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)),
+                           max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16)));
+    return m << 16;
+}
+
+// Tensor amax of both orientations (of the transformed values where the
+// transform applies).  Persistent over 128 x 128 tiles with stride
+// gridDim.x, the next tile's rows loaded before the current one is reduced;
+// one atomic max per workgroup and orientation, a few per CU in all (one
+// per tile made the atomics on the two words the bottleneck).
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     int rht_mask, uint32_t sign_mask, uint32_t* __restrict__ ws)
@@ -291,50 +318,60 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
     __shared__ uint32_t red[2][4];
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int cg = l & 15, rg = 4 * w + (l >> 4);
-    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
-    const int64_t col = c0 + 8 * cg;
-    uint4 v[8];
-    load_tile(x, rows, cols, ldx, r0, col, rg, col < cols, v);
-
-    uint32_t plain = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) plain = max(plain, fabs_bits(bf16_at(v[u], j)));
-
-    uint32_t mrow = plain, mcol = plain;
+    const int64_t nbc = (cols + TB - 1) / TB, nblk = ((rows + TB - 1) / TB) * nbc;
     uint32_t row_m[4], col_m[8];
     rht_pair_signs(sign_mask, cg & 1, (l >> 4) & 1, row_m, col_m);
-    if (rht_mask & 1) {
-        mrow = 0;
-        const float sgn = (cg & 1) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint4 vs = xor4(v[u], row_m[0], row_m[1], row_m[2], row_m[3]);
-            float z[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) z[j] = bf16_at(vs, j);
-            rht16x4<true>(z, sgn);
-            mrow = max(mrow, amax8(z));
-        }
-        mrow = quarter_bits(mrow);
+    const float sgn_row = (cg & 1) ? -1.0f : 1.0f, sgn_col = ((l >> 4) & 1) ? -1.0f : 1.0f;
+    const bool rht_row = rht_mask & 1, rht_col = rht_mask & 2;
+
+    uint32_t plain = 0, mrow4 = 0, mcol4 = 0;     // mrow4 / mcol4: amax of 4 x the transform
+    int64_t blk = blockIdx.x;
+    uint4 v[8];
+    if (blk < nblk) {
+        const int64_t col = (blk % nbc) * TB + 8 * cg;
+        load_tile(x, rows, cols, ldx, (blk / nbc) * TB, col, rg, col < cols, v);
     }
-    if (rht_mask & 2) {
-        mcol = 0;
-        const float sgn = ((l >> 4) & 1) ? -1.0f : 1.0f;
-        uint4 vs[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) vs[u] = xor4(v[u], col_m[u], col_m[u], col_m[u], col_m[u]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float z[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) z[u] = bf16_at(vs[u], j);
-            rht16x4<false>(z, sgn);
-            mcol = max(mcol, amax8(z));
+    while (blk < nblk) {
+        const int64_t next = blk + gridDim.x;
+        uint4 vn[8];
+        if (next < nblk) {
+            const int64_t col = (next % nbc) * TB + 8 * cg;
+            load_tile(x, rows, cols, ldx, (next / nbc) * TB, col, rg, col < cols, vn);
         }
-        mcol = quarter_bits(mcol);
+        if (!(rht_row && rht_col)) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) plain = max(plain, bf16_amax8_bits(v[u]));
+        }
+        if (rht_row) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint4 vs = xor4(v[u], row_m[0], row_m[1], row_m[2], row_m[3]);
+                float z[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) z[jj] = bf16_at(vs, jj);
+                rht16x4<true>(z, sgn_row);
+                mrow4 = max(mrow4, amax8(z));
+            }
+        }
+        if (rht_col) {
+            uint4 vs[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) vs[u] = xor4(v[u], col_m[u], col_m[u], col_m[u], col_m[u]);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                float z[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) z[u] = bf16_at(vs[u], jj);
+                rht16x4<false>(z, sgn_col);
+                mcol4 = max(mcol4, amax8(z));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = vn[u];
+        blk = next;
     }
+    uint32_t mrow = rht_row ? quarter_bits(mrow4) : plain;
+    uint32_t mcol = rht_col ? quarter_bits(mcol4) : plain;
     mrow = max_xor32(max_xor16(max_lanes16(mrow)));
     mcol = max_xor32(max_xor16(max_lanes16(mcol)));
     if (l == 0) {
@@ -496,7 +533,9 @@ hipError_t launch_quant_nvfp4(const QuantNVFP4Args& a, hipStream_t stream)
     uint32_t* ws = static_cast<uint32_t*>(a.workspace);
     const uint32_t mask = rht_sign_mask(a.rht_seed);
     hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, ws);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask, mask, ws);
+    const int64_t nblk = nbr * nbc, cap = (int64_t)device_cus() * 8;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)(nblk < cap ? nblk : cap)), block, 0, stream,
+                       x, a.rows, a.cols, a.ldx, a.rht_mask, mask, ws);
     const uint32_t slo = (uint32_t)a.sr_seed, shi = (uint32_t)(a.sr_seed >> 32);
     if (a.stochastic)
         hipLaunchKernelGGL(nvfp4_quant_kernel<true>, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask,
