@@ -73,11 +73,18 @@ __device__ __forceinline__ MXBlock mx_block(uint32_t amax16)
     return b;
 }
 
-__device__ __forceinline__ uint32_t mx_code(uint32_t h, const MXBlock& b)
+// Codes of eight BF16 values (raw 16-bit patterns) of one block.  x * 2^-e
+// is exact and lies in [-448, 448] (e is the smallest exponent with
+// amax <= 448 * 2^e; a clamp at e = -127 only shrinks |x * 2^-e|), where
+// the hardware converter equals the saturating RNE encoder with the sign of
+// the input (see e4m3_pack4).  A non-finite block takes 0x7F codes.
+__device__ __forceinline__ uint2 mx_code8(const uint32_t h[8], const MXBlock& b)
 {
-    if (b.nan) return 0x7Fu;
-    const float a = as_f32((h & 0x7FFFu) << 16) * b.inv;
-    return e4m3_code_abs(a) | ((h >> 8) & 0x80u);
+    if (b.nan) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = as_f32(h[j] << 16) * b.inv;
+    return make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
 }
 
 __global__ __launch_bounds__(256) void quant_mx_kernel(
@@ -109,14 +116,13 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const MXBlock b = mx_block(max_lanes4(abs_max8(v[u])));
-            uint32_t c[8];
+            uint32_t h[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = mx_code(raw_elem(v[u], j), b);
+            for (int j = 0; j < 8; ++j) h[j] = raw_elem(v[u], j);
+            const uint2 codes = mx_code8(h, b);
             const int64_t row = r0 + 8 * rg + u;
             if (col_ok && row < rows) {
-                *reinterpret_cast<uint2*>(q + row * cols + col) =
-                    make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+                *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
                 if ((cg & 3) == 0) scales[row * nsc + col / 32] = (uint8_t)b.code;
             }
         }
@@ -132,12 +138,10 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
             for (int u = 0; u < 8; ++u) m = max(m, raw_elem(v[u], j) & 0x7FFFu);
             m = max_xor32(max_xor16(m));
             const MXBlock b = mx_block(m);
-            uint32_t c[8];
+            uint32_t h[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = mx_code(raw_elem(v[u], j), b);
-            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) =
-                make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                           c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+            for (int u = 0; u < 8; ++u) h[u] = raw_elem(v[u], j);
+            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = mx_code8(h, b);
             if ((l >> 4) == 0 && col_ok) scalesT[(col + j) * nscT + r0 / 32 + w] = (uint8_t)b.code;
         }
         __syncthreads();
