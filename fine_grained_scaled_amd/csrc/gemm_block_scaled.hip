@@ -213,11 +213,11 @@ using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
 
-template <class S, int ROW>
+template <class S, int ROW, bool B_TILE>
 struct Lds {
     static constexpr int A_BYTES = S::BM * ROW;
     static constexpr int B_BYTES = S::BN * ROW;
-    static constexpr int STAGE = A_BYTES + B_BYTES + S::BN * 4;   // + B 1x128 scales of the block
+    static constexpr int STAGE = A_BYTES + B_BYTES + (B_TILE ? S::BN * 4 : 0);   // + B 1x128 scales of the block
 };
 
 template <class S, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int CPR = ROW / 16;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
     constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
-    using L = Lds<S, ROW>;
-    static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN != 128), "128x128 B blocks need 128-wide tiles");
+    using L = Lds<S, ROW, B_TILE>;
+    static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN % 128 != 0), "128x128 B blocks need 128-aligned tiles");
     static_assert(BN / 64 <= NW, "B 1x128 scale staging needs BN / 64 waves");
 
     extern __shared__ __align__(16) uint8_t smem[];
@@ -455,7 +455,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[am[i]];
     }
     float sb_next = 0.0f;
-    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / 128) * nkb];
+    // 128x128 B blocks: a wave's 64 columns lie in one block (clamped for
+    // waves past N, whose columns are never stored)
+    int64_t sb_row = (n0 + 64 * wn) / 128;
+    if (sb_row > (p.N - 1) / 128) sb_row = (p.N - 1) / 128;
+    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[sb_row * nkb];
     wait_lds_dma();
     __syncthreads();
 
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
 #pragma unroll
                 for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
             }
-            if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[(n0 / 128) * nkb + kb + 1];
+            if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[sb_row * nkb + kb + 1];
             if constexpr (NV) {
 #pragma unroll
                 for (int i = 0; i < TI; ++i)
@@ -727,7 +731,7 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     // grouped: every group can add one partial m-tile
     p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUPED ? a.G : 0));
     const dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
-    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128>::STAGE;
+    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128>::STAGE;
     auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUPED>
                   : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUPED>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
