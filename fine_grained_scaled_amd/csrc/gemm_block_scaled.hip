@@ -80,7 +80,10 @@ typedef const __attribute__((address_space(1))) void* gbl_ptr;
 // would make every later LDS read wait for the loads to land (it cannot tell
 // that they fill the other stage of the ring), which serialises the next
 // block's fetch with this block's MFMAs.  Completion is tracked by hand with
-// wait_lds_dma() before the barrier that publishes a stage.
+// wait_lds_dma() before the barrier that publishes a stage.  No other
+// instruction of these kernels reads M0, so the statements may clobber it;
+// the s_nop is the one wait state the hardware needs between an SALU write
+// of M0 and an LDS-DMA load that uses it.
 __device__ __forceinline__ uint32_t lds_offset(const void* p)
 {
     return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)p));
