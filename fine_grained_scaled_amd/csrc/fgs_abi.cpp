@@ -210,6 +210,8 @@ int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M,
     if (st != FGS_OK) return st;
     if (M == 0 || N == 0) return ok();
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
+    // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
+    if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (A->elem == FGS_ELEM_E4M3 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {

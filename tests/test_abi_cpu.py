@@ -124,6 +124,10 @@ def test_gemm_validation(lib):
     a6 = _op(scales=NULL)
     assert g(r(a6), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
     assert g(r(a), r(b), 0, 128, 256, NULL, 128, 0, S) == _lib.FGS_OK                     # empty
+    big = 1 << 30
+    assert g(r(a), r(b), big + 1, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED  # M too large
+    assert g(r(a), r(b), big, big, 256, FAKE, big, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # 2^45 tiles
+    assert b"tiles" in lib.fgs_last_error()
 
 
 def test_grouped_validation(lib):
