@@ -38,10 +38,12 @@
 // (tile 256 x 128; 512 threads, two waves per SIMD so one wave's decode and
 // promotion VALU work overlaps the other's MFMAs); the promoted accumulators
 // and the per-block partial sums (2 x 64 VGPRs) both stay in VGPRs, which
-// caps the wave tile there.  Modes with a single scale per operand (per-tensor
-// E4M3, NVFP4) need no partial sums, so their waves own 128 x 64 (2 x 4
-// waves, tile 256 x 256): each decoded fragment feeds more MFMAs and each
-// staged byte more FLOPs.  The grouped (MoE) kernel uses 2 x 2 waves of
+// caps the wave tile there.  Modes without promotion (per-tensor E4M3, and
+// NVFP4, whose block scales are folded into the exact decode) need no
+// partial sums, so their waves can own 128 x 64 (2 x 4 waves, tile
+// 256 x 256): each decoded fragment feeds more MFMAs and each staged byte
+// more FLOPs; a launch takes this tile unless its last round of workgroups
+// would be poorly filled (see prefer_wide).  The grouped (MoE) kernel uses 2 x 2 waves of
 // 64 x 64 (tile 128 x 128; groups are short).  K advances in
 // 128-deep blocks staged in LDS as code bytes (128 bytes per row for E4M3,
 // 64 for E2M1), double-buffered, by direct global->LDS loads
