@@ -168,18 +168,9 @@ __device__ __forceinline__ void decode16(const uint4 v, float s, bf16x8& lo, bf1
     hi = bf16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
-// E8M0 helpers: the largest of the four scale bytes of a 128-K block, the
-// FP32 value 2^(c - 127) of a scale byte (c = 0 is 2^-127, 255 gives Inf so a
-// NaN block stays NaN), and the converter scale 2^(c - ref) (c <= ref),
-// clamped at 2^-127.
-__device__ __forceinline__ uint32_t max_byte(uint32_t u)
-{
-    return max(max(u & 0xFFu, (u >> 8) & 0xFFu), max((u >> 16) & 0xFFu, u >> 24));
-}
-__device__ __forceinline__ float e8m0_value(uint32_t c)
-{
-    return c == 0 ? as_f32(0x00400000u) : as_f32(c << 23);
-}
+// E8M0 helper: the converter scale 2^(c - ref) (c <= ref) as an FP32 power
+// of two, clamped at 2^-127 (exponent field 0, which the converters read as
+// 2^-127).
 __device__ __forceinline__ float e8m0_rel(uint32_t c, uint32_t ref)
 {
     const int e = 127 + (int)c - (int)ref;
@@ -236,7 +227,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int TJ = S::TJ;            // sub-tiles along n per wave
     constexpr int WM = 32 * TI;
     constexpr bool PROMOTE = !(AMODE == FGS_SCALE_TENSOR && BMODE == FGS_SCALE_TENSOR) &&
-                             AMODE != FGS_SCALE_NV16_E4M3;
+                             AMODE != FGS_SCALE_NV16_E4M3 && AMODE != FGS_SCALE_MX32_E8M0;
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
     constexpr bool MX = AMODE == FGS_SCALE_MX32_E8M0;
     constexpr bool NV = AMODE == FGS_SCALE_NV16_E4M3;
@@ -252,7 +243,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
     __shared__ int s_sel[2];
-    __shared__ uint32_t s_ebt[2][NWN];     // MX: B tile reference exponent, [block parity][wn]
+    // MX: reference E8M0 byte of every A row and B row of the tile (largest
+    // non-NaN scale byte over all of K), NaN-scale flags, the B tile's reference
+    __shared__ uint8_t s_mx_ref[AMODE == FGS_SCALE_MX32_E8M0 ? BM + BN : 1];
+    __shared__ uint8_t s_mx_nan[AMODE == FGS_SCALE_MX32_E8M0 ? BM + BN : 1];
+    __shared__ uint32_t s_mx_eb;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int wm = w / NWN, wn = w % NWN;   // wave grid NWM x NWN
@@ -407,11 +402,14 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // MXFP8 scales.  A (per lane row m): E_A[m] = the largest E8M0 byte of
-    // the row's four 32-blocks in the 128-K block; each code is decoded as
-    // code * 2^(e - E_A) (exact), and the block's FP32 partial sum is
-    // promoted with 2^(E_A + E_B).  B: one reference E_B per tile and block
-    // (the largest byte over the tile's 128 rows), so the promotion factor
-    // stays one value per lane.  The four bytes of a row's block are one
+    // the row over all of K; B: one E_B for the tile (the largest byte of its
+    // rows over all of K).  Every code is decoded as code * 2^(e - E) into
+    // BF16, exact whenever e - E >= -124, the FP16/BF16 matrix unit sums the
+    // exact products over all of K in FP32, and the epilogue multiplies by
+    // 2^(E_A + E_B - 254) (exact scaling), so no per-block promotion is
+    // needed.  NaN scale bytes (0xFF) are left out of the references and
+    // flagged: their rows (A) and columns (B) of C are NaN, as in the
+    // dequantized product.  The four bytes of a row's 128-K block are one
     // aligned 32-bit word.
     const int64_t ksc = p.K / 32;
     const uint8_t* sA8 = reinterpret_cast<const uint8_t*>(p.sA);
@@ -423,19 +421,40 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         bn[j] = n < p.N ? n : p.N - 1;
     }
     uint32_t a_sw_next[TI], b_sw_next[TJ];
-    // wave-wide max of the B bytes this wave holds (its 64 B rows), published
-    // by the wm == 0 waves for the other waves of the same wn
-    auto publish_ebt = [&](int parity) {
-        uint32_t m = max(max_byte(b_sw_next[0]), max_byte(b_sw_next[1]));
-        m = max_xor32(max_xor16(max_lanes16(m)));
-        if (wm == 0 && l == 0) s_ebt[parity][wn] = m;
-    };
+    uint32_t ea[TI], eb = 0;
     if constexpr (MX) {
+        // one tile row per thread: A rows 0 .. BM-1, then B rows (rows past
+        // the end clamped; they only feed outputs that are never stored)
+        if (t == 0) s_mx_eb = 0;
+        __syncthreads();
+        for (int rr = t; rr < BM + BN; rr += NT) {
+            const bool is_a = rr < BM;
+            int64_t row = is_a ? m0 + rr : n0 + (rr - BM);
+            const int64_t lim = is_a ? m_end : p.N;
+            row = row < lim ? row : lim - 1;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>((is_a ? sA8 : sB8) + row * ksc);
+            uint32_t mref = 0, nan = 0;
+            for (int64_t c = 0; c < ksc / 4; ++c) {
+                const uint32_t w4 = src[c];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t v = (w4 >> (8 * b)) & 0xFFu;
+                    nan |= v == 0xFFu;
+                    mref = max(mref, v == 0xFFu ? 0u : v);
+                }
+            }
+            s_mx_ref[rr] = (uint8_t)mref;
+            s_mx_nan[rr] = (uint8_t)nan;
+            if (!is_a) atomicMax(&s_mx_eb, mref);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TI; ++i) ea[i] = s_mx_ref[WM * wm + 32 * i + (l & 31)];
+        eb = s_mx_eb;
 #pragma unroll
         for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc);
-        publish_ebt(0);
     }
     // NVFP4 scales: the eight E4M3 bytes of a fragment row's 128-K block are
     // two aligned 32-bit words (16-blocks 0-3 and 4-7)
@@ -520,20 +539,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc + 4 * (kb + 1));
             }
         }
-        // MX: reference exponents and the per-lane converter scales of this block
-        uint32_t ea[TI], ebt = 0;
-        float fmx[TI];
-        if constexpr (MX) {
-            ebt = s_ebt[kb & 1][0];
-#pragma unroll
-            for (int q = 1; q < NWN; ++q) ebt = max(ebt, s_ebt[kb & 1][q]);
-            const float fb = e8m0_value(ebt);
-#pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                ea[i] = max_byte(a_sw[i]);
-                fmx[i] = e8m0_value(ea[i]) * fb;
-            }
-        }
 
         if (wave_live) {
             const uint8_t* st = smem + cur * L::STAGE;
@@ -600,7 +605,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     #pragma unroll
                     for (int j = 0; j < TJ; ++j)
                         decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co),
-                                 e8m0_rel((b_sw[j] >> (8 * ks)) & 0xFFu, ebt), bf[j][0], bf[j][1]);
+                                 e8m0_rel((b_sw[j] >> (8 * ks)) & 0xFFu, eb), bf[j][0], bf[j][1]);
     #pragma unroll
                     for (int i = 0; i < TI; ++i)
                         decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co),
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     #pragma unroll
                         for (int i = 0; i < TI; ++i)
     #pragma unroll
-                            for (int j = 0; j < TJ; ++j) part[i][j] = mfma16(bf[j][h], af[i][h], part[i][j]);
+                            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
                 } else {
                     f16x8 af[TI][2], bf[TJ][2];
     #pragma unroll
@@ -653,14 +658,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                                     acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], fa * sbv[e], acc[i][j][4 * q + e]);
                             }
                         }
-                } else if constexpr (MX) {
-    #pragma unroll
-                    for (int i = 0; i < TI; ++i)
-    #pragma unroll
-                        for (int j = 0; j < TJ; ++j)
-    #pragma unroll
-                            for (int r = 0; r < 16; ++r)
-                                acc[i][j][r] = __builtin_fmaf(part[i][j][r], fmx[i], acc[i][j][r]);
                 } else {
                     const float fb = BMODE == FGS_SCALE_TENSOR ? sb_t : sb_blk;
     #pragma unroll
@@ -676,13 +673,27 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             }
         }
 
-        if constexpr (MX)
-            if (more) publish_ebt((int)((kb + 1) & 1));
         wait_lds_dma();
         __syncthreads();
     }
 
-    if constexpr (!PROMOTE) {
+    if constexpr (MX) {
+        // 2^(E_A + E_B - 254) by exponent arithmetic (exact up to FP32
+        // overflow or underflow); NaN rows and columns
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const int sh = (int)ea[i] + (int)eb - 254;
+            const bool rnan = s_mx_nan[WM * wm + 32 * i + (l & 31)] != 0;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int cn = 64 * wn + 32 * j + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+                    const float v = __builtin_ldexpf(acc[i][j][r], sh);
+                    acc[i][j][r] = (rnan || s_mx_nan[BM + cn]) ? __builtin_nanf("") : v;
+                }
+        }
+    } else if constexpr (!PROMOTE) {
         const float f = NV ? p.tsA[0] * p.tsB[0] : p.sA[0] * sBp[0];
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -778,6 +789,7 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
         if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, a, bf16, s);
         if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0) {
+        if (wide) return launch_modes<ShapeWide, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, a, bf16, s);
         return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3) {
         if (wide) return launch_modes<ShapeWide, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, a, bf16, s);

@@ -85,6 +85,47 @@ def test_mx_gemm_zero_and_tiny_blocks(fgs):
     _check(fgs, A, B, ah, bh, torch.float32)
 
 
+@pytest.mark.parametrize("policy", ["narrow", "wide"])
+def test_mx_gemm_nan_blocks(fgs, policy):
+    """A NaN in one 32-block of an A row and of a B row gives that block the
+    NaN scale byte 0xFF: exactly that row and that column of C are NaN (as in
+    the dequantized product), every other output meets the bound."""
+    M, N, K = 300, 260, 512
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=28, outliers=False)).copy()
+    b = oracle.bf16_bits_to_f32(synth.weights(N, K, seed=29)).copy()
+    a[7, 70] = np.nan
+    b[131, 300] = np.nan
+    A, ah = mx_operand(fgs, synth.f32_to_bf16_bits(a))
+    B, bh = mx_operand(fgs, synth.f32_to_bf16_bits(b))
+    prev = fgs.gemm_tile_policy(policy)
+    try:
+        c = fgs.gemm_block_scaled(A, B, torch.float32)
+        torch.cuda.synchronize()
+    finally:
+        fgs.gemm_tile_policy(prev)
+    c = c.cpu().numpy().astype(np.float64)
+    cref, sref = oracle.gemm_ref(ah, bh)
+    assert np.array_equal(np.isnan(c), np.isnan(cref))
+    assert np.isnan(c[7]).all() and np.isnan(c[:, 131]).all()
+    ok = ~np.isnan(cref)
+    good, worst = gemm_within_fp32_bound(c[ok], cref[ok], sref[ok])
+    assert good, worst
+
+
+@pytest.mark.parametrize("policy", ["narrow", "wide"])
+def test_mx_gemm_tile_policies(fgs, policy):
+    """The MX GEMM on either workgroup tile, ragged shapes, both outputs."""
+    M, N, K = 520, 777, 384
+    A, ah = mx_operand(fgs, synth.activations(M, K, seed=30, outliers=False))
+    B, bh = mx_operand(fgs, synth.weights(N, K, seed=31))
+    prev = fgs.gemm_tile_policy(policy)
+    try:
+        _check(fgs, A, B, ah, bh, torch.float32)
+        _check(fgs, A, B, ah, bh, torch.bfloat16)
+    finally:
+        fgs.gemm_tile_policy(prev)
+
+
 def test_mx_gemm_determinism(fgs):
     A, _ = mx_operand(fgs, synth.activations(512, 1024, seed=26, outliers=False))
     B, _ = mx_operand(fgs, synth.weights(384, 1024, seed=27))
