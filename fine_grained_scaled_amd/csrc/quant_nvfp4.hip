@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
 
     const TensorScale ts_row = tensor_scale_from(ws[0]);
     const TensorScale ts_col = tensor_scale_from(ws[1]);
-    // SR: the hash's seed rounds per row of this thread (shared by both outputs)
+    // SR: the hash's seed rounds per row of this thread
     uint32_t midr[8], ilo[8];
     if constexpr (SR) {
 #pragma unroll
@@ -414,6 +414,15 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             midr[u] = sr_mid(seed_lo, seed_hi, i0);
             ilo[u] = (uint32_t)i0;
         }
+    }
+    // the random word of an element does not depend on the orientation: hash
+    // each of the thread's 64 elements once for both outputs
+    uint32_t W[8][8];
+    if constexpr (SR) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) W[u][j] = sr_word_at(ilo[u], midr[u], j);
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
         tensor_scale[0] = ts_row.st;
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             uint32_t rw[8];
             if constexpr (SR) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) rw[j] = sr_word_at(ilo[u], midr[u], j);
+                for (int j = 0; j < 8; ++j) rw[j] = W[u][j];
             }
             uint32_t sb;
             const uint32_t packed = nv_block8<SR>(z, mb, ts_row, rw, sb, zscale);
@@ -476,7 +485,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             uint32_t rw[8];
             if constexpr (SR) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) rw[u] = sr_word_at(ilo[u], midr[u], j);
+                for (int u = 0; u < 8; ++u) rw[u] = W[u][j];
             }
             uint32_t sb;
             const uint32_t packed = nv_block8<SR>(z, mb, ts_col, rw, sb, zscale);
