@@ -161,9 +161,11 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *     TENSOR}: MFMA partial sums over one 128-deep K block are scaled by
  *     sA * sB and added into FP32 accumulators once per block (promotion);
  *   E4M3 with MX32_E8M0 on both: each code decoded exactly to BF16 as
- *     code * 2^(e - E) (E the row's (A) or the 128-row tile's (B) largest
- *     scale exponent in the 128-K block), BF16 MFMA, FP32 promotion per
- *     128-K block with 2^(E_A + E_B);
+ *     code * 2^(e - E) (E the largest non-NaN scale exponent of the row (A)
+ *     or of the workgroup tile's rows (B) over all of K; exact while
+ *     e - E >= -124), BF16 MFMA with FP32 accumulation over all of K, then
+ *     2^(E_A + E_B) applied by exponent arithmetic; a NaN scale byte makes
+ *     its A row or B column of C NaN;
  *   E2M1 with NV16_E4M3 on both: each code times its E4M3 block scale,
  *     exact in FP16, FP16 MFMA with FP32 accumulation over all of K, the
  *     two tensor scales applied at the end.
