@@ -260,7 +260,8 @@ class Tiny:
 
 
 # --------------------------------------------------------------------------
-# DeepSeek-V3 MoE: grouped GEMMs over 256 experts, Zipf(1.1) token counts
+# DeepSeek-V3 MoE: grouped GEMMs over 256 experts, Zipf(1.1) token counts:
+# gate/up and down forward, then their dgrad on the transposed expert weights
 # --------------------------------------------------------------------------
 class MoE:
     name = "deepseek_v3_moe_grouped"
@@ -275,30 +276,41 @@ class MoE:
         T, H, I, G = MOE_TOKENS, MOE_HIDDEN, MOE_INTER, MOE_EXPERTS
         self.a1 = gpu_normal(torch, (T, H), 101, outlier_cols=synth.outlier_channels(H, 0))
         self.a2 = gpu_normal(torch, (T, I), 102, outlier_cols=synth.outlier_channels(I, 0))
-        # expert weights, quantized once (128x128 blocks never straddle experts)
-        self.w1 = self._expert_weights(G, 2 * I, H, 103)     # gate+up: 7168 -> 4096
-        self.w2 = self._expert_weights(G, H, I, 104)         # down:    2048 -> 7168
+        self.g1 = gpu_t3(torch, (T, 2 * I), 105)             # dY of gate+up
+        self.g2 = gpu_t3(torch, (T, H), 106)                 # dY of down
+        # expert weights, quantized once (128x128 blocks never straddle experts):
+        # row-wise for the forward GEMMs, transposed for dgrad
+        self.w1, self.w1t = self._expert_weights(G, 2 * I, H, 103)     # gate+up: 7168 -> 4096
+        self.w2, self.w2t = self._expert_weights(G, H, I, 104)         # down:    2048 -> 7168
         self.y1 = torch.empty((T, 2 * I), dtype=torch.bfloat16, device="cuda")
         self.y2 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        self.dx1 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        self.dx2 = torch.empty((T, I), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
         log(f"[bench] {self.name}: expert weights generated and quantized in {time.time() - t0:.1f} s "
             f"(token counts max {counts.max()}, min {counts.min()}, {int((counts < 128).sum())} experts < 128)")
 
     def _expert_weights(self, G, N, K, seed):
+        """Per-expert [N x K] weights: row-wise codes [G*N x K] for the forward
+        GEMM and transposed codes [G*K x N] for dgrad, 128x128 blocks."""
         torch, fgs = self.torch, self.fgs
         codes = torch.empty((G * N, K), dtype=torch.uint8, device="cuda")
         scales = torch.empty((G * (N // 128), K // 128), dtype=torch.float32, device="cuda")
-        chunk = 8
-        for g0 in range(0, G, chunk):
-            w = gpu_normal(torch, (chunk * N, K), seed * 1000 + g0, sigma=0.02)
-            q = fgs.quantize_blockwise(w, "block")
-            codes[g0 * N:(g0 + chunk) * N] = q.q
-            scales[g0 * (N // 128):(g0 + chunk) * (N // 128)] = q.scales
+        codes_t = torch.empty((G * K, N), dtype=torch.uint8, device="cuda")
+        scales_t = torch.empty((G * (K // 128), N // 128), dtype=torch.float32, device="cuda")
+        for g in range(G):
+            w = gpu_normal(torch, (N, K), seed * 1000 + g, sigma=0.02)
+            q = fgs.quantize_blockwise(w, "block", rowwise=True, colwise=True)
+            codes[g * N:(g + 1) * N] = q.q
+            scales[g * (N // 128):(g + 1) * (N // 128)] = q.scales
+            codes_t[g * K:(g + 1) * K] = q.qT
+            scales_t[g * (K // 128):(g + 1) * (K // 128)] = q.scalesT
             del w, q
-        return fgs.Operand(codes, scales, fgs.SCALE_BLOCK_128x128)
+        return (fgs.Operand(codes, scales, fgs.SCALE_BLOCK_128x128),
+                fgs.Operand(codes_t, scales_t, fgs.SCALE_BLOCK_128x128))
 
     def flops(self):
-        return 2.0 * MOE_TOKENS * (2 * MOE_INTER * MOE_HIDDEN + MOE_HIDDEN * MOE_INTER)
+        return 2 * 2.0 * MOE_TOKENS * (2 * MOE_INTER * MOE_HIDDEN + MOE_HIDDEN * MOE_INTER)
 
     def gemm_bytes(self, N, K):
         """Algorithmic HBM bytes of one grouped GEMM: A codes and scales,
@@ -326,6 +338,13 @@ class MoE:
         qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 1), lambda: fgs.quantize_blockwise(self.a2, "tile"))
         tm.run("gemm", "down", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
             qa2.rowwise(), self.w2, self.offsets, H, torch.bfloat16, out=self.y2))
+        # dgrad: dZ = dY2 W2 (2048 outputs, contraction over 7168), dH = dY1 W1
+        qg2 = tm.run("quant", "dY2", e4m3_bytes(T, H, "tile", 1), lambda: fgs.quantize_blockwise(self.g2, "tile"))
+        tm.run("gemm", "down_dgrad", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
+            qg2.rowwise(), self.w2t, self.offsets, I, torch.bfloat16, out=self.dx2))
+        qg1 = tm.run("quant", "dY1", e4m3_bytes(T, 2 * I, "tile", 1), lambda: fgs.quantize_blockwise(self.g1, "tile"))
+        tm.run("gemm", "gate_up_dgrad", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
+            qg1.rowwise(), self.w1t, self.offsets, H, torch.bfloat16, out=self.dx1))
 
 
 # --------------------------------------------------------------------------
@@ -659,8 +678,12 @@ def main():
         r["step_TFLOP/s"] = round(wl.flops() / (w_wall / args.steps) / 1e12, 2)
         if isinstance(wl, MoE):
             f, t, _ = w_kinds["gemm"]
-            roof = wl.roofline_seconds(2 * MOE_INTER, MOE_HIDDEN) + wl.roofline_seconds(MOE_HIDDEN, MOE_INTER)
-            by = wl.gemm_bytes(2 * MOE_INTER, MOE_HIDDEN) + wl.gemm_bytes(MOE_HIDDEN, MOE_INTER)
+            # forward (gate/up N=4096 K=7168, down N=7168 K=2048) and dgrad
+            # (down N=2048 K=7168, gate/up N=7168 K=4096)
+            shapes = [(2 * MOE_INTER, MOE_HIDDEN), (MOE_HIDDEN, MOE_INTER), (MOE_INTER, MOE_HIDDEN),
+                      (MOE_HIDDEN, 2 * MOE_INTER)]
+            roof = sum(wl.roofline_seconds(n, k) for n, k in shapes)
+            by = sum(wl.gemm_bytes(n, k) for n, k in shapes)
             gemm_s = t / args.steps
             r["gemm"]["roofline_ms"] = round(roof * 1e3, 4)
             r["gemm"]["frac_roofline"] = round(roof / gemm_s, 4)

@@ -159,17 +159,25 @@ def test_gemm_determinism(fgs):
 
 
 # ------------------------------------------------------------------ grouped --
-def _grouped_case(fgs, counts, N, K, out=torch.float32, seed=0):
+def _grouped_case(fgs, counts, N, K, out=torch.float32, seed=0, dgrad=False):
+    """Grouped GEMM of row-wise 1x128 A against per-group 128x128 B.  With
+    dgrad=True, A is a gradient and each group's B is the transpose of a
+    forward weight W_g [K x N] (a layer N -> K), quantized column-wise: the
+    GEMM contracts over the forward layer's output dimension K."""
     counts = np.asarray(counts)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     total = int(offs[-1])
     G = len(counts)
-    a_bits = synth.activations(total, K, seed=seed)
+    a_bits = synth.gradients(total, K, seed=seed) if dgrad else synth.activations(total, K, seed=seed)
     A, ah = oracle_operand(fgs, a_bits, "tile")
     qs, ss, bhs = [], [], []
     for g in range(G):
-        wb = synth.weights(N, K, seed=seed + 100 + g)
-        q, s = oracle.quant_e4m3(wb, "block")
+        if dgrad:
+            wb = synth.weights(K, N, seed=seed + 100 + g)          # forward weight [K out x N in]
+            q, s = oracle.quant_e4m3(wb, "block", colwise=True)    # W_g^T codes [N x K]
+        else:
+            wb = synth.weights(N, K, seed=seed + 100 + g)
+            q, s = oracle.quant_e4m3(wb, "block")
         qs.append(q)
         ss.append(s)
         bhs.append(oracle.dequant_e4m3(q, s, "block"))
@@ -192,6 +200,13 @@ def _grouped_case(fgs, counts, N, K, out=torch.float32, seed=0):
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_grouped_ragged_and_empty(fgs, out):
     _grouped_case(fgs, [0, 1, 130, 0, 257, 128, 3], N=256, K=384, out=out)
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_grouped_dgrad_orientation(fgs, out):
+    """MoE expert dgrad: dX_g = dY_g W_g with W_g^T taken from the column-wise
+    (transposed) 128x128 quantization of each expert's forward weight."""
+    _grouped_case(fgs, [0, 1, 130, 0, 257, 128, 3], N=384, K=256, out=out, seed=3, dgrad=True)
 
 
 def test_grouped_single_group_equals_dense(fgs):
