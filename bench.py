@@ -22,7 +22,7 @@ HBM before timing starts.
 
 The other workloads of the path are measured in the same run and reported
 under "workloads" (per-kernel throughput against the roofline): the tiny
-blockwise GEMM, the DeepSeek-V3 MoE grouped GEMM, MXFP8 at Llama-3.1-405B
+blockwise GEMM, the DeepSeek-V3 MoE grouped GEMMs (forward and dgrad), MXFP8 at Llama-3.1-405B
 shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes.
 
 Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
