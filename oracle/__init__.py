@@ -275,6 +275,32 @@ def quant_nvfp4_rows(values_f32: np.ndarray, tensor_scale, stochastic: bool = Fa
     return q, scales
 
 
+def quant_e4m3_grouped_colwise(x, offsets):
+    """Per-group transposed 1x128 quantization of the MoE weight-gradient
+    operands ([DSV3] "Fine-grained quantization", "Online quantization",
+    "Mixed precision framework": the expert GEMMs, wgrad included, take
+    1x128 tiles along their contraction, which for wgrad is the tokens).
+
+    Group g holds rows offsets[g] .. offsets[g+1]-1 of x [T x C] (the tokens
+    routed to expert g).  Its wgrad operand is the transpose [C x M_g],
+    quantized in 1x128 tiles along the tokens; tiles never mix tokens of two
+    experts, so the last tile of a group is partial whenever M_g % 128 != 0
+    and takes its scale from the tokens present (zero padding would leave
+    the amax unchanged).  Returns one (codes uint8 [C x M_g], scales float32
+    [C x ceil(M_g/128)]) per group; an empty group gives empty arrays.
+    """
+    xb = _as_bf16_bits(x)
+    cols = xb.shape[1]
+    out = []
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 <= r0:
+            out.append((np.zeros((cols, 0), np.uint8), np.zeros((cols, 0), np.float32)))
+        else:
+            out.append(quant_e4m3(xb[r0:r1], "tile", colwise=True))
+    return out
+
+
 # --------------------------------------------------------------------------
 # dequantization (exact in FP64)
 # --------------------------------------------------------------------------
@@ -324,6 +350,22 @@ def gemm_ref(a_hat: np.ndarray, b_hat: np.ndarray):
     b = np.asarray(b_hat, dtype=np.float64)
     c = a @ b.T
     s = np.abs(a) @ np.abs(b).T
+    return c, s
+
+
+def grouped_wgrad_ref(a_hat_groups, b_hat_groups):
+    """MoE weight gradients: per group g, C_g = A_g B_g^T with the
+    contraction over the group's tokens (A_g = dequantized dY_g^T [M x M_g],
+    B_g = dequantized X_g^T [N x M_g]); a group with no tokens gives C_g = 0.
+    Returns (C [G x M x N], S [G x M x N]) in FP64."""
+    G = len(a_hat_groups)
+    m = a_hat_groups[0].shape[0] if G else 0
+    n = b_hat_groups[0].shape[0] if G else 0
+    c = np.zeros((G, m, n))
+    s = np.zeros((G, m, n))
+    for g in range(G):
+        if a_hat_groups[g].shape[1] > 0:
+            c[g], s[g] = gemm_ref(a_hat_groups[g], b_hat_groups[g])
     return c, s
 
 
