@@ -247,4 +247,63 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, co
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_gemm_block_scaled launch");
 }
 
+int64_t fgs_grouped_colwise_blocks(int64_t rows, int32_t G)
+{
+    if (rows < 0 || G < 0) return 0;
+    return rows / 128 + G;
+}
+
+int fgs_quantize_grouped_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 const int32_t* group_offsets, int32_t G,
+                                 uint8_t* q, float* scales,
+                                 uint8_t* qT, int64_t ldqT, float* scalesT, void* stream)
+{
+    if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
+    int st = check_bf16_source(x, rows, cols, ldx);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || G == 0) return ok();
+    if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
+    if (!qT || !scalesT) return fail(FGS_ERR_INVALID_ARG, "qT and scalesT are required");
+    const int64_t blocks = fgs_grouped_colwise_blocks(rows, G);
+    if (blocks > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many token blocks");
+    if ((cols + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "cols too large (%lld)", (long long)cols);
+    if (ldqT < 128 * blocks)
+        return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,
+                    (long long)(128 * blocks));
+    if (ldqT % 16) return fail(FGS_ERR_UNSUPPORTED, "ldqT must be a multiple of 16");
+    if (!aligned(qT, 16) || !aligned(scalesT, 4)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
+    if (q) {
+        if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
+        if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0 (cols = %lld)", (long long)cols);
+        if (!aligned(q, 16) || !aligned(scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte and scales 4-byte aligned");
+    }
+    fgs::QuantGroupedArgs a{x, rows, cols, ldx, group_offsets, G, q, scales, qT, ldqT, scalesT};
+    return hip_status(fgs::launch_quant_grouped_colwise(a, static_cast<hipStream_t>(stream)),
+                      "quantize_grouped_colwise launch");
+}
+
+int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                   int32_t G, int64_t total_T, int64_t M, int64_t N,
+                                   void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
+    if (total_T < 0) return fail(FGS_ERR_INVALID_ARG, "total_T must be >= 0");
+    if (G == 0) {
+        if (M < 0 || N < 0) return fail(FGS_ERR_INVALID_ARG, "M, N, K must be >= 0");
+        return ok();
+    }
+    const int64_t Kcap = 128 * fgs_grouped_colwise_blocks(total_T, G);
+    int st = check_gemm_common(A, B, M, N, Kcap, C, ldc, out_dtype);
+    if (st != FGS_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
+    if (A->elem != FGS_ELEM_E4M3 || A->scale_mode != FGS_SCALE_TILE_1x128 || B->scale_mode != FGS_SCALE_TILE_1x128)
+        return fail(FGS_ERR_UNSUPPORTED, "grouped wgrad supports E4M3 TILE_1x128 x TILE_1x128");
+    if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
+    const int64_t tiles = (int64_t)G * ((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
+    fgs::GemmArgs a{*A, *B, M, N, Kcap, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 1, total_T};
+    return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_wgrad_block_scaled launch");
+}
+
 } // extern "C"

@@ -22,6 +22,21 @@ struct QuantE4M3Args {
 };
 hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream);
 
+// Per-group column-wise 1x128 quantization (plus the optional row-wise
+// output of the grouped rows), TILE mode only.
+struct QuantGroupedArgs {
+    const void* x;
+    int64_t rows, cols, ldx;
+    const int32_t* group_offsets;   // device int32 [G + 1]
+    int32_t G;
+    uint8_t* q;
+    float* scales;
+    uint8_t* qT;
+    int64_t ldqT;
+    float* scalesT;
+};
+hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t stream);
+
 struct QuantMXArgs {
     const void* x;
     int64_t rows, cols, ldx;
@@ -54,9 +69,11 @@ struct GemmArgs {
     void* C;
     int64_t ldc;
     int out_bf16;
-    // grouped variant
+    // grouped variants
     const int32_t* group_offsets;   // nullptr for the dense GEMM
     int32_t G;
+    int group_k;                    // groups split the contraction (MoE wgrad)
+    int64_t T;                      // group_k: tokens the offsets index
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).

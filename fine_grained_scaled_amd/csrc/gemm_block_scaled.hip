@@ -117,6 +117,7 @@ struct GemmParams {
     int64_t ldc;
     const int32_t* offsets;
     int32_t G;
+    int64_t T;                    // contraction groups: tokens (rows of the quantized source)
     int64_t b_group_stride;       // elements between groups of B codes
     int64_t sb_group_stride;      // floats between groups of B block scales
     int32_t tiles_m, tiles_n;
@@ -219,7 +220,11 @@ struct Lds {
     static constexpr int STAGE = A_BYTES + B_BYTES + (B_TILE ? S::BN * 4 : 0);   // + B 1x128 scales of the block
 };
 
-template <class S, int AMODE, int BMODE, bool OUT_BF16, bool GROUPED>
+// Tile schedules: one dense problem; MoE groups of rows (each with its own
+// B); MoE groups of the contraction (weight gradients, one C per group).
+enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
+
+template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP>
 __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel(GemmParams p)
 {
     constexpr int NWM = S::NWM, NWN = S::NWN;
@@ -257,9 +262,13 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
 
     // ------------------------------------------------------------ tile --
     int64_t m0, m_end, n0;
+    const uint8_t* Ap = p.A;
+    const float* sAp = p.sA;
     const uint8_t* Bp = p.B;
     const float* sBp = p.sB;
-    if constexpr (!GROUPED) {
+    int64_t nkb = p.K / BK;
+    int64_t c_off = 0;                    // elements from C to this tile's C matrix
+    if constexpr (GROUP == GROUP_NONE) {
         int id = blockIdx.x;
         const int T = p.tiles_m * p.tiles_n;
         // workgroups are dealt round-robin to the 8 XCDs: give each XCD a
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         m0 = (int64_t)tm * BM;
         m_end = p.M;
         n0 = (int64_t)tn * BN;
-    } else {
+    } else if constexpr (GROUP == GROUP_M) {
         // Device-side schedule over the tiles of all groups in canonical
         // order u (group, then n-tile, then m-tile fastest).  Workgroup v
         // takes u from the front for even runs of 8 and from the back for odd
@@ -336,6 +345,36 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         n0 = (int64_t)tn * BN;
         Bp = p.B + (int64_t)g * p.b_group_stride;
         sBp = p.sB + (int64_t)g * p.sb_group_stride;
+    } else {
+        // Contraction groups: group g owns the 128-token blocks
+        // floor(o_g / 128) + g .. + ceil(M_g / 128) - 1 of both operands (the
+        // layout of the per-group column-wise quantizer) and the C matrix at
+        // g * M * ldc.  Workgroups run group by group; within a group of
+        // per % 8 == 0 tiles, the eight XCDs (dealt workgroups round-robin)
+        // each take a contiguous eighth of the tile order.  A group without
+        // tokens, or with offsets out of order or range, runs no K block and
+        // writes zeros.
+        const int64_t per = (int64_t)p.tiles_m * p.tiles_n;
+        const int g = (int)(blockIdx.x / per);
+        int id = (int)(blockIdx.x % per);
+        if ((per & 7) == 0) id = (id & 7) * (int)(per >> 3) + (id >> 3);
+        const int GM = 8;
+        const int group = id / (GM * p.tiles_n);
+        const int first_m = group * GM;
+        const int gsz = min(p.tiles_m - first_m, GM);
+        const int in_group = id % (GM * p.tiles_n);
+        m0 = (int64_t)(first_m + in_group % gsz) * BM;
+        m_end = p.M;
+        n0 = (int64_t)(in_group / gsz) * BN;
+        const int32_t o0 = p.offsets[g], o1 = p.offsets[g + 1];
+        const bool ok = o0 >= 0 && o1 >= o0 && (int64_t)o1 <= p.T;
+        const int64_t kb0 = ok ? (int64_t)(o0 >> 7) + g : 0;
+        nkb = ok ? (o1 - o0 + BK - 1) / BK : 0;
+        Ap = p.A + kb0 * BK;
+        Bp = p.B + kb0 * BK;
+        sAp = p.sA + kb0 * p.M;
+        sBp = p.sB + kb0 * p.N;
+        c_off = (int64_t)g * p.M * p.ldc;
     }
 
     // ------------------------------------------------------- loaders --
@@ -355,7 +394,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         const int lr = A_ROWS * w + RPI * u + srow;
         int64_t r = m0 + lr;
         r = r < m_end ? r : m_end - 1;
-        a_src[u] = p.A + r * p.lda + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
+        a_src[u] = Ap + r * p.lda + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
 #pragma unroll
     for (int u = 0; u < B_INSTR; ++u) {
@@ -394,7 +433,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         const int64_t m = m0 + WM * wm + 32 * i + (l & 31);
         am[i] = m < m_end ? m : m_end - 1;
     }
-    const int64_t nkb = p.K / BK;
 
     f32x16 acc[TI][TJ];
 #pragma unroll
@@ -475,18 +513,18 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
 
     // prologue: block 0 -> stage 0
-    stage_block(0, 0);
+    if (nkb > 0) stage_block(0, 0);
     float sa_next[TI];
     if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[am[i]];
+        for (int i = 0; i < TI; ++i) sa_next[i] = nkb > 0 ? sAp[am[i]] : 0.0f;
     }
     float sb_next = 0.0f;
     // 128x128 B blocks: a wave's 64 columns lie in one block (clamped for
     // waves past N, whose columns are never stored)
     int64_t sb_row = (n0 + 64 * wn) / 128;
     if (sb_row > (p.N - 1) / 128) sb_row = (p.N - 1) / 128;
-    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[sb_row * nkb];
+    if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) if (nkb > 0) sb_next = sBp[sb_row * nkb];
     wait_lds_dma();
     __syncthreads();
 
@@ -520,7 +558,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             stage_block(kb + 1, cur ^ 1);
             if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
 #pragma unroll
-                for (int i = 0; i < TI; ++i) sa_next[i] = p.sA[(kb + 1) * p.M + am[i]];
+                for (int i = 0; i < TI; ++i) sa_next[i] = sAp[(kb + 1) * p.M + am[i]];
             }
             if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[sb_row * nkb + kb + 1];
             if constexpr (NV) {
@@ -717,7 +755,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             for (int q = 0; q < 4; ++q) {
                 const int64_t n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
                 if constexpr (OUT_BF16) {
-                    uint16_t* C = static_cast<uint16_t*>(p.C) + m * p.ldc + n;
+                    uint16_t* C = static_cast<uint16_t*>(p.C) + c_off + m * p.ldc + n;
                     const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
                     const uint32_t h23 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                     if (n + 3 < p.N && ((reinterpret_cast<uintptr_t>(C) & 7) == 0)) {
@@ -729,7 +767,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                             if (n + e < p.N) C[e] = (uint16_t)h[e];
                     }
                 } else {
-                    float* C = static_cast<float*>(p.C) + m * p.ldc + n;
+                    float* C = static_cast<float*>(p.C) + c_off + m * p.ldc + n;
                     if (n + 3 < p.N && ((reinterpret_cast<uintptr_t>(C) & 15) == 0)) {
                         *reinterpret_cast<float4*>(C) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
                                                                     acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
@@ -743,16 +781,17 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
 }
 
-template <class S, int AMODE, int BMODE, bool GROUPED>
+template <class S, int AMODE, int BMODE, int GROUP>
 hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
     p.tiles_n = (int32_t)((a.N + S::BN - 1) / S::BN);
-    // grouped: every group can add one partial m-tile
-    p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUPED ? a.G : 0));
-    const dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n));
+    // row groups: every group can add one partial m-tile
+    p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUP == GROUP_M ? a.G : 0));
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
+    const dim3 grid((unsigned)tiles);
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128>::STAGE;
-    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUPED>
-                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUPED>;
+    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP>
+                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -788,22 +827,22 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
     const bool wide = prefer_wide(a);
     const int amode = a.A.scale_mode, bmode = a.B.scale_mode;
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, false>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, false>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_NONE>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_NONE>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0) {
-        if (wide) return launch_modes<ShapeWide, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, a, bf16, s);
-        return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, false>(p, a, bf16, s);
+        if (wide) return launch_modes<ShapeWide, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, GROUP_NONE>(p, a, bf16, s);
+        return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, GROUP_NONE>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3) {
-        if (wide) return launch_modes<ShapeWide, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, a, bf16, s);
-        return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, false>(p, a, bf16, s);
+        if (wide) return launch_modes<ShapeWide, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, GROUP_NONE>(p, a, bf16, s);
+        return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, GROUP_NONE>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_TENSOR) {
         if (bmode == FGS_SCALE_TENSOR) {
-            if (wide) return launch_modes<ShapeWide, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
-            return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, false>(p, a, bf16, s);
+            if (wide) return launch_modes<ShapeWide, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
+            return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
         }
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, false>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, false>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, GROUP_NONE>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, GROUP_NONE>(p, a, bf16, s);
     }
     return hipErrorInvalidValue;
 }
@@ -837,13 +876,20 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.ldc = a.ldc;
     p.offsets = a.group_offsets;
     p.G = a.G;
+    p.T = a.T;
     if (a.M == 0 || a.N == 0) return hipSuccess;
     const bool bf16 = a.out_bf16 != 0;
+    if (a.group_k) {
+        if (a.G == 0) return hipSuccess;
+        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_TILE_1x128)
+            return launch_modes<ShapeDense, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_K>(p, a, bf16, stream);
+        return hipErrorInvalidValue;
+    }
     if (a.group_offsets) {
         p.b_group_stride = a.N * a.B.ld;
         p.sb_group_stride = ((a.N + 127) / 128) * (a.K / BK);
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128)
-            return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, true>(p, a, bf16, stream);
+            return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(p, a, bf16, stream);
         return hipErrorInvalidValue;
     }
     return dispatch_dense(p, a, bf16, stream);

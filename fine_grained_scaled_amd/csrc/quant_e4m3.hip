@@ -74,19 +74,62 @@ __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
     return quant8_vals(xb, b);
 }
 
-template <int MODE>   // FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
+// GROUPED (TILE mode only): the rows are split into groups (MoE experts,
+// rows offsets[g] .. offsets[g+1]-1), and the column-wise tiles run along the
+// rows of one group only.  Group g's transposed codes take the 128-column
+// blocks kb_g = floor(offsets[g] / 128) + g .. kb_g + ceil(M_g / 128) - 1 of
+// qT (row stride ldqT) and the same rows of scalesT; those blocks never
+// overlap for non-decreasing offsets, so no scan over the groups is needed.
+// Workgroup (blockIdx.x = block j, blockIdx.y = column block) finds the group
+// that owns block j; rows past the group's end read as zero (zero codes in
+// qT, no effect on the amax).
+template <int MODE, bool GROUPED>   // MODE: FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, float* __restrict__ scales,
     uint8_t* __restrict__ qT, float* __restrict__ scalesT,
-    const uint32_t* __restrict__ tensor_amax)
+    const uint32_t* __restrict__ tensor_amax,
+    const int32_t* __restrict__ offsets, int32_t G, int64_t ldqT)
 {
+    static_assert(!GROUPED || MODE == FGS_SCALE_TILE_1x128, "groups take 1x128 tiles");
     __shared__ uint32_t red[4][TB];
     __shared__ __align__(16) uint8_t tbuf[TB][TB + TPAD];
+    __shared__ int s_group;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int cg = l & 15, rg = 4 * w + (l >> 4);
-    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    // r0: first source row; live: rows of this block that exist (from r0);
+    // tc: first column of qT; tb: row of scalesT; ldt: row stride of qT
+    int64_t r0, c0, live, tc, tb, ldt;
+    if constexpr (!GROUPED) {
+        r0 = (int64_t)blockIdx.y * TB;
+        c0 = (int64_t)blockIdx.x * TB;
+        live = rows - r0;
+        tc = r0;
+        tb = blockIdx.y;
+        ldt = rows;
+    } else {
+        const int64_t j = blockIdx.x;
+        if (t == 0) s_group = -1;
+        __syncthreads();
+        for (int g = t; g < G; g += 256) {
+            const int32_t o0 = offsets[g], o1 = offsets[g + 1];
+            if (o0 >= 0 && o1 >= o0 && (int64_t)o1 <= rows) {
+                const int64_t kb = (int64_t)(o0 >> 7) + g;
+                if (j >= kb && j < kb + (o1 - o0 + TB - 1) / TB) s_group = g;
+            }
+        }
+        __syncthreads();
+        const int g = s_group;
+        if (g < 0) return;                       // a block no group owns
+        const int32_t o0 = offsets[g], o1 = offsets[g + 1];
+        r0 = (int64_t)o0 + (j - ((int64_t)(o0 >> 7) + g)) * TB;
+        c0 = (int64_t)blockIdx.y * TB;
+        live = (int64_t)o1 - r0;
+        tc = j * TB;
+        tb = j;
+        ldt = ldqT;
+    }
     const int64_t col = c0 + 8 * cg;
     const bool col_ok = col < cols;
 
@@ -94,7 +137,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int64_t row = r0 + 8 * rg + u;
-        if (col_ok && row < rows)
+        if (col_ok && 8 * rg + u < live)
             v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
         else
             v[u] = make_uint4(0, 0, 0, 0);
@@ -137,15 +180,15 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
             }
             const int64_t row = r0 + 8 * rg + u;
             uint2 codes = quant8(v[u], b);
-            if (col_ok && row < rows)
+            if (col_ok && 8 * rg + u < live)
                 *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
         }
         if constexpr (MODE == FGS_SCALE_TILE_1x128) {
             if (cg == 0) {
-                float* dst = scales + blockIdx.x * rows + r0 + 8 * rg;
+                float* dst = scales + (c0 / TB) * rows + r0 + 8 * rg;
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (r0 + 8 * rg + u < rows) dst[u] = srow[u];
+                    if (8 * rg + u < live) dst[u] = srow[u];
             }
         }
     }
@@ -174,7 +217,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
                 bcol[j] = e4m3_block_from_amax_bits(m);
             }
             if (w == 0 && (l >> 4) == 0 && col_ok) {
-                float* dst = scalesT + blockIdx.y * cols + col;
+                float* dst = scalesT + tb * cols + col;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) dst[j] = bcol[j].s;
             }
@@ -198,7 +241,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
             const int64_t orow = c0 + trow;
             if (orow < cols) {
                 uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
-                *reinterpret_cast<uint4*>(qT + orow * rows + r0 + 16 * chunk) = d;
+                *reinterpret_cast<uint4*>(qT + orow * ldt + tc + 16 * chunk) = d;
             }
         }
     }
@@ -262,12 +305,12 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     switch (a.mode) {
     case FGS_SCALE_TILE_1x128:
-        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_TILE_1x128>, grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr);
+        hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, false>), grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0);
         break;
     case FGS_SCALE_BLOCK_128x128:
-        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128>, grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr);
+        hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128, false>), grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0);
         break;
     case FGS_SCALE_TENSOR: {
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
@@ -276,13 +319,24 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
         const unsigned g = (unsigned)(nblk < cap ? nblk : cap);
         hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
                            x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
-        hipLaunchKernelGGL(quant_e4m3_kernel<FGS_SCALE_TENSOR>, grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax);
+        hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TENSOR, false>), grid, block, 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0);
         break;
     }
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t stream)
+{
+    // every group owns at most floor(rows / 128) + G blocks in total
+    const int64_t nblk = a.rows / TB + a.G, nbc = (a.cols + TB - 1) / TB;
+    if (a.G == 0 || a.rows == 0 || nbc == 0) return hipSuccess;
+    hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true>), dim3((unsigned)nblk, (unsigned)nbc),
+                       dim3(256), 0, stream, static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ldx,
+                       a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets, a.G, a.ldqT);
     return hipGetLastError();
 }
 

@@ -252,3 +252,68 @@ def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tenso
     check(_lib.load().fgs_grouped_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
                                                     G, total_M, N, K, _ptr(out), out.stride(0), code, _stream()))
     return out
+
+
+def grouped_colwise_blocks(rows: int, G: int) -> int:
+    """128-token blocks of the per-group column-wise layout: rows // 128 + G."""
+    return int(_lib.load().fgs_grouped_colwise_blocks(rows, G))
+
+
+def quantize_grouped_colwise(x: torch.Tensor, group_offsets: torch.Tensor,
+                             rowwise: bool = False) -> Quantized:
+    """MoE weight-gradient operand: per-group transposed 1x128 E4M3
+    quantization of x [T x C] (rows offsets[g]..offsets[g+1]-1 are group g).
+    qT is [C x 128 * blocks]: group g takes the 128-column blocks from
+    offsets[g] // 128 + g on, zero-padded to whole blocks; scalesT is
+    [blocks x C].  rowwise=True adds the ordinary 1x128 row-wise output of
+    the grouped rows from the same read."""
+    rows, cols, ldx = _bf16_matrix(x)
+    _need_gpu(group_offsets)
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or not group_offsets.is_contiguous():
+        raise TypeError("group_offsets must be a contiguous 1-D int32 tensor")
+    G = group_offsets.numel() - 1
+    if G < 0:
+        raise ValueError("group_offsets needs G + 1 >= 1 entries")
+    nb = grouped_colwise_blocks(rows, G)
+    dev = x.device
+    qT = torch.empty((cols, 128 * nb), dtype=torch.uint8, device=dev)
+    sT = torch.empty((nb, cols), dtype=torch.float32, device=dev)
+    q = s = None
+    if rowwise:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s = torch.empty(((cols + 127) // 128, rows), dtype=torch.float32, device=dev)
+    check(_lib.load().fgs_quantize_grouped_colwise(
+        _ptr(x), rows, cols, ldx, _ptr(group_offsets), G, _ptr(q), _ptr(s),
+        _ptr(qT), 128 * nb, _ptr(sT), _stream()))
+    return Quantized(q, s, qT, sT, SCALE_TILE_1x128)
+
+
+def grouped_wgrad_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, total_T: int,
+                               out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MoE weight gradients: C_g [M x N] = sum over group g's tokens of
+    A^[m, t] B^[n, t], for operands from quantize_grouped_colwise (A of dY,
+    B of X) over total_T tokens.  Returns [G x M x N]; empty groups get 0."""
+    _need_gpu(A.data, B.data, group_offsets)
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1:
+        raise TypeError("group_offsets must be a 1-D int32 tensor")
+    G = group_offsets.numel() - 1
+    M, N = A.data.shape[0], B.data.shape[0]
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((max(G, 0), M, N), dtype=out_dtype, device=A.data.device)
+    if G <= 0:
+        return out
+    Kcap = 128 * grouped_colwise_blocks(total_T, G)
+    if A.scale_mode != SCALE_TILE_1x128 or B.scale_mode != SCALE_TILE_1x128:
+        raise ValueError("grouped wgrad takes 1x128-tile operands")
+    _check_operand(A, M, Kcap, "A")
+    _check_operand(B, N, Kcap, "B")
+    if (out.dtype != out_dtype or out.dim() != 3 or out.shape[0] < G or out.shape[1] < M or out.shape[2] < N
+            or out.stride(2) != 1 or out.stride(0) != M * out.stride(1)):
+        raise ValueError("out must be a [G x M x N] tensor of out_dtype, rows contiguous, "
+                         "matrices M * ldc elements apart")
+    a, b = A.c_struct(), B.c_struct()
+    check(_lib.load().fgs_grouped_wgrad_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
+                                                     G, total_T, M, N, _ptr(out), out.stride(1), code,
+                                                     _stream()))
+    return out

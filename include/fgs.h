@@ -201,6 +201,68 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
                                   int64_t total_M, int64_t N, int64_t K,
                                   void *C, int64_t ldc, int out_dtype, void *stream);
 
+/*
+ * fgs_quantize_grouped_colwise -- the MoE weight-gradient operands: per-group
+ *   transposed 1x128 E4M3 quantization.   [DSV3] "Fine-grained
+ *   quantization", "Online quantization", "Mixed precision framework" (the
+ *   expert GEMMs, wgrad included, in FP8 with 1x128 tiles along the
+ *   contraction, which for wgrad runs over each expert's tokens).
+ * x        BF16 [rows x cols], row stride ldx (elements, multiple of 8); row
+ *          t is a token, grouped by expert.
+ * group_offsets  DEVICE int32 [G+1]: group g is rows offsets[g] ..
+ *          offsets[g+1]-1 (M_g tokens).  Read on the device.  A group with
+ *          offsets[g] < 0, offsets[g+1] < offsets[g] or offsets[g+1] > rows
+ *          is treated as empty; offsets that decrease from one group to the
+ *          next give unspecified codes, but every write stays inside the
+ *          buffers below.
+ * Column-wise output (required): group g's transpose [cols x M_g] in 1x128
+ *   tiles along its tokens (a tile never holds two groups' tokens; the last
+ *   one is partial when M_g % 128 != 0, scaled from the tokens present and
+ *   padded with code 0x00, or 0x7F like the rest of a tile whose scale is
+ *   NaN).  Group g occupies the 128-column blocks
+ *   kb_g .. kb_g + ceil(M_g/128) - 1 with kb_g = floor(offsets[g]/128) + g,
+ *   so the layout needs no scan and no host synchronisation; blocks no group
+ *   owns are not written.  There are at most
+ *   fgs_grouped_colwise_blocks(rows, G) = floor(rows/128) + G blocks.
+ *   qT       E4M3 [cols x ldqT], ldqT >= 128 * fgs_grouped_colwise_blocks,
+ *            ldqT % 16 == 0.
+ *   scalesT  FP32 [fgs_grouped_colwise_blocks][cols] (the TILE_1x128 layout
+ *            of an operand of cols rows and K = 128 * blocks).
+ * Row-wise output (optional, NULL q skips it; needs cols % 128 == 0): the
+ *   ordinary 1x128 quantization of every row that a valid group covers, from
+ *   the same read: q [rows x cols], scales [cols/128][rows]; rows of no
+ *   group are not written.
+ */
+int fgs_quantize_grouped_colwise(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                                 const int32_t *group_offsets, int32_t G,
+                                 uint8_t *q, float *scales,
+                                 uint8_t *qT, int64_t ldqT, float *scalesT, void *stream);
+
+/* Number of 128-token blocks of the per-group column-wise layout for rows
+ * tokens in G groups: floor(rows/128) + G (0 for negative arguments). */
+int64_t fgs_grouped_colwise_blocks(int64_t rows, int32_t G);
+
+/*
+ * fgs_grouped_wgrad_block_scaled -- MoE expert weight gradients: for every
+ *   group g, C_g[m][n] = sum over the tokens t of group g of A^[m,t] B^[n,t].
+ *   [DSV3] "Mixed precision framework", "Fine-grained quantization",
+ *   "Increasing accumulation precision" (partial sums over each 128-token
+ *   tile scaled by both tiles' scales and added into FP32 accumulators).
+ * A: M x (128 * blocks) E4M3 TILE_1x128 operand from
+ *   fgs_quantize_grouped_colwise of dY [total_T x M] (ld = its ldqT).
+ * B: N x (128 * blocks) E4M3 TILE_1x128 operand, the same for X [total_T x N].
+ *   blocks = fgs_grouped_colwise_blocks(total_T, G).
+ * group_offsets: the DEVICE int32 [G+1] both operands were quantized with.
+ * C: G matrices [M x N] of FP32 or BF16 (RNE), C_g at C + g * M * ldc,
+ *   row stride ldc >= N.  A group without tokens (or one the quantizer
+ *   treats as empty) gets C_g = 0.
+ * Accuracy as fgs_gemm_block_scaled.
+ */
+int fgs_grouped_wgrad_block_scaled(const fgs_operand *A, const fgs_operand *B,
+                                   const int32_t *group_offsets, int32_t G, int64_t total_T,
+                                   int64_t M, int64_t N, void *C, int64_t ldc, int out_dtype,
+                                   void *stream);
+
 /* Workgroup tile of the GEMMs whose operands carry one scale for all of K
  * (per-tensor x per-tensor E4M3, NVFP4): FGS_TILE_AUTO (default) picks per
  * problem from the tile counts and the device's compute units,

@@ -142,6 +142,45 @@ def test_grouped_validation(lib):
     assert g(r(a), r(b), FAKE, 0, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_OK          # no groups
 
 
+def test_grouped_colwise_validation(lib):
+    S = NULL
+    q = lib.fgs_quantize_grouped_colwise
+    assert lib.fgs_grouped_colwise_blocks(300, 4) == 2 + 4
+    assert lib.fgs_grouped_colwise_blocks(-1, 4) == 0
+    ld = 128 * 6
+    assert q(FAKE, 300, 256, 256, FAKE, -1, NULL, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG   # G < 0
+    assert q(FAKE, 300, 256, 256, NULL, 4, NULL, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # offsets
+    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, NULL, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # qT
+    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, FAKE, ld - 16, FAKE, S) == _lib.FGS_ERR_INVALID_ARG
+    assert b"ldqT" in lib.fgs_last_error()
+    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, FAKE, ld + 8, FAKE, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert q(FAKE, 300, 200, 200, FAKE, 4, FAKE, FAKE, FAKE, ld, FAKE, S) == _lib.FGS_ERR_UNSUPPORTED    # row-wise cols % 128
+    assert q(FAKE, 300, 256, 256, FAKE, 4, FAKE, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # scales
+    assert q(FAKE, 300, 256, 256, FAKE, 0, NULL, NULL, NULL, 0, NULL, S) == _lib.FGS_OK                  # no groups
+    assert q(FAKE, 0, 256, 256, FAKE, 4, NULL, NULL, NULL, 0, NULL, S) == _lib.FGS_OK                    # no rows
+
+
+def test_grouped_wgrad_validation(lib):
+    S = NULL
+    g = lib.fgs_grouped_wgrad_block_scaled
+    r = ctypes.byref
+    ld = 128 * (2 + 4)
+    a, b = _op(mode=1, ld=ld), _op(mode=1, ld=ld)
+    assert g(r(a), r(b), FAKE, -1, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), FAKE, 4, -5, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), NULL, 4, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    short = _op(mode=1, ld=ld - 128)
+    assert g(r(short), r(b), FAKE, 4, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG       # ld < 128 * blocks
+    blk = _op(mode=2, ld=ld)
+    assert g(r(a), r(blk), FAKE, 4, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a), r(b), FAKE, 4, 300, 128, 128, FAKE, 64, 0, S) == _lib.FGS_ERR_INVALID_ARG          # ldc < N
+    assert g(r(a), r(b), FAKE, 0, 300, 128, 128, NULL, 128, 0, S) == _lib.FGS_OK                      # no groups
+    assert g(r(a), r(b), FAKE, 4, 300, 0, 128, NULL, 128, 0, S) == _lib.FGS_OK                        # M = 0
+    big = 1 << 30
+    wide = _op(mode=1, ld=128 * (2 + 100000))
+    assert g(r(wide), r(wide), FAKE, 100000, 300, big, big, FAKE, big, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+
+
 def test_binding_rejects_mis_sized_operands():
     """The Python binding checks operand buffer sizes before any C call, so a
     mis-sized scale tensor raises instead of being read out of bounds."""
