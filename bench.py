@@ -22,7 +22,7 @@ HBM before timing starts.
 
 The other workloads of the path are measured in the same run and reported
 under "workloads" (per-kernel throughput against the roofline): the tiny
-blockwise GEMM, the DeepSeek-V3 MoE grouped GEMMs (forward and dgrad), MXFP8 at Llama-3.1-405B
+blockwise GEMM, the DeepSeek-V3 MoE grouped GEMMs (forward, dgrad and wgrad), MXFP8 at Llama-3.1-405B
 shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes.
 
 Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
@@ -261,7 +261,8 @@ class Tiny:
 
 # --------------------------------------------------------------------------
 # DeepSeek-V3 MoE: grouped GEMMs over 256 experts, Zipf(1.1) token counts:
-# gate/up and down forward, then their dgrad on the transposed expert weights
+# gate/up and down forward, their dgrad on the transposed expert weights,
+# and their wgrad (one dW per expert, contraction over its tokens)
 # --------------------------------------------------------------------------
 class MoE:
     name = "deepseek_v3_moe_grouped"
@@ -286,6 +287,9 @@ class MoE:
         self.y2 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         self.dx1 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         self.dx2 = torch.empty((T, I), dtype=torch.bfloat16, device="cuda")
+        # FP32 expert weight gradients: 256 x [4096 x 7168] and 256 x [7168 x 2048]
+        self.dw1 = torch.empty((G, 2 * I, H), dtype=torch.float32, device="cuda")
+        self.dw2 = torch.empty((G, H, I), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
         log(f"[bench] {self.name}: expert weights generated and quantized in {time.time() - t0:.1f} s "
             f"(token counts max {counts.max()}, min {counts.min()}, {int((counts < 128).sum())} experts < 128)")
@@ -310,7 +314,7 @@ class MoE:
                 fgs.Operand(codes_t, scales_t, fgs.SCALE_BLOCK_128x128))
 
     def flops(self):
-        return 2 * 2.0 * MOE_TOKENS * (2 * MOE_INTER * MOE_HIDDEN + MOE_HIDDEN * MOE_INTER)
+        return 3 * 2.0 * MOE_TOKENS * (2 * MOE_INTER * MOE_HIDDEN + MOE_HIDDEN * MOE_INTER)
 
     def gemm_bytes(self, N, K):
         """Algorithmic HBM bytes of one grouped GEMM: A codes and scales,
@@ -329,22 +333,46 @@ class MoE:
             t += max(fl / (PEAK_FP16_MFMA * 1e12), by / (PEAK_HBM * 1e9))
         return t
 
+    def wgrad_bytes(self, M, N):
+        """Algorithmic HBM bytes of one grouped wgrad: both operands' codes
+        and 1x128 scales over the routed tokens, and every expert's FP32
+        dW [M x N] (zeros for experts without tokens)."""
+        return (M + N) * MOE_TOKENS * (1 + 4 / 128) + MOE_EXPERTS * 4.0 * M * N
+
+    def wgrad_roofline_seconds(self, M, N):
+        """Sum over experts of max(MFMA time at the FP16 peak, HBM time)."""
+        t = 0.0
+        for c in self.counts:
+            fl = 2.0 * c * M * N
+            by = (M + N) * c * (1 + 4 / 128) + 4.0 * M * N
+            t += max(fl / (PEAK_FP16_MFMA * 1e12), by / (PEAK_HBM * 1e9))
+        return t
+
     def step(self, tm):
         torch, fgs = self.torch, self.fgs
         T, H, I = MOE_TOKENS, MOE_HIDDEN, MOE_INTER
-        qa1 = tm.run("quant", "A1", e4m3_bytes(T, H, "tile", 1), lambda: fgs.quantize_blockwise(self.a1, "tile"))
+        off = self.offsets
+        # each input is read once for its row-wise codes (fwd / dgrad) and its
+        # per-expert transposed codes (wgrad)
+        grouped = lambda x: fgs.quantize_grouped_colwise(x, off, rowwise=True)
+        qa1 = tm.run("quant", "A1", e4m3_bytes(T, H, "tile", 2), lambda: grouped(self.a1))
         tm.run("gemm", "gate_up", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
-            qa1.rowwise(), self.w1, self.offsets, 2 * I, torch.bfloat16, out=self.y1))
-        qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 1), lambda: fgs.quantize_blockwise(self.a2, "tile"))
+            qa1.rowwise(), self.w1, off, 2 * I, torch.bfloat16, out=self.y1))
+        qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 2), lambda: grouped(self.a2))
         tm.run("gemm", "down", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
-            qa2.rowwise(), self.w2, self.offsets, H, torch.bfloat16, out=self.y2))
+            qa2.rowwise(), self.w2, off, H, torch.bfloat16, out=self.y2))
         # dgrad: dZ = dY2 W2 (2048 outputs, contraction over 7168), dH = dY1 W1
-        qg2 = tm.run("quant", "dY2", e4m3_bytes(T, H, "tile", 1), lambda: fgs.quantize_blockwise(self.g2, "tile"))
+        qg2 = tm.run("quant", "dY2", e4m3_bytes(T, H, "tile", 2), lambda: grouped(self.g2))
         tm.run("gemm", "down_dgrad", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
-            qg2.rowwise(), self.w2t, self.offsets, I, torch.bfloat16, out=self.dx2))
-        qg1 = tm.run("quant", "dY1", e4m3_bytes(T, 2 * I, "tile", 1), lambda: fgs.quantize_blockwise(self.g1, "tile"))
+            qg2.rowwise(), self.w2t, off, I, torch.bfloat16, out=self.dx2))
+        qg1 = tm.run("quant", "dY1", e4m3_bytes(T, 2 * I, "tile", 2), lambda: grouped(self.g1))
         tm.run("gemm", "gate_up_dgrad", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
-            qg1.rowwise(), self.w1t, self.offsets, H, torch.bfloat16, out=self.dx1))
+            qg1.rowwise(), self.w1t, off, H, torch.bfloat16, out=self.dx1))
+        # wgrad: dW2_g = dY2_g^T Z_g [7168 x 2048], dW1_g = dY1_g^T X_g [4096 x 7168]
+        tm.run("gemm", "down_wgrad", 2.0 * T * H * I, lambda: fgs.grouped_wgrad_block_scaled(
+            qg2.colwise(), qa2.colwise(), off, T, torch.float32, out=self.dw2))
+        tm.run("gemm", "gate_up_wgrad", 2.0 * T * 2 * I * H, lambda: fgs.grouped_wgrad_block_scaled(
+            qg1.colwise(), qa1.colwise(), off, T, torch.float32, out=self.dw1))
 
 
 # --------------------------------------------------------------------------
@@ -447,7 +475,7 @@ def measure(torch, wl, steps, warmup):
     for (kind, label), (u, t, n) in labels.items():
         rate = f"{u / t / 1e12:8.1f} TFLOP/s" if kind == "gemm" else f"{u / t / 1e9:8.1f} GB/s"
         log(f"  {wl.name:28s} {label:24s} {t / n * 1e6:9.1f} us  {rate}")
-    return wall, kinds
+    return wall, kinds, labels
 
 
 def kind_report(kinds, steps):
@@ -661,7 +689,7 @@ def main():
     names = [n for n in args.workloads.split(",") if n]
 
     head = Llama8B(torch, fgs, synth)
-    wall, kinds = measure(torch, head, args.steps, args.warmup)
+    wall, kinds, _ = measure(torch, head, args.steps, args.warmup)
     ms = wall * 1e3 / args.steps
     value = head.flops() / (wall / args.steps) / 1e12
     rep = kind_report(kinds, args.steps)
@@ -672,22 +700,33 @@ def main():
         if n == "llama3_8b":
             continue
         wl = WORKLOADS[n](torch, fgs, synth)
-        w_wall, w_kinds = measure(torch, wl, args.steps, args.warmup)
+        w_wall, w_kinds, w_labels = measure(torch, wl, args.steps, args.warmup)
         r = kind_report(w_kinds, args.steps)
         r["ms_per_step"] = round(w_wall * 1e3 / args.steps, 4)
         r["step_TFLOP/s"] = round(wl.flops() / (w_wall / args.steps) / 1e12, 2)
         if isinstance(wl, MoE):
             f, t, _ = w_kinds["gemm"]
             # forward (gate/up N=4096 K=7168, down N=7168 K=2048) and dgrad
-            # (down N=2048 K=7168, gate/up N=7168 K=4096)
+            # (down N=2048 K=7168, gate/up N=7168 K=4096) on the row groups;
+            # wgrad (dW [7168 x 2048] down, [4096 x 7168] gate/up) on the
+            # token groups
             shapes = [(2 * MOE_INTER, MOE_HIDDEN), (MOE_HIDDEN, MOE_INTER), (MOE_INTER, MOE_HIDDEN),
                       (MOE_HIDDEN, 2 * MOE_INTER)]
-            roof = sum(wl.roofline_seconds(n, k) for n, k in shapes)
-            by = sum(wl.gemm_bytes(n, k) for n, k in shapes)
+            wshapes = [(MOE_HIDDEN, MOE_INTER), (2 * MOE_INTER, MOE_HIDDEN)]
+            roof_rows = sum(wl.roofline_seconds(n, k) for n, k in shapes)
+            roof_w = sum(wl.wgrad_roofline_seconds(m, n) for m, n in wshapes)
+            by = sum(wl.gemm_bytes(n, k) for n, k in shapes) + sum(wl.wgrad_bytes(m, n) for m, n in wshapes)
             gemm_s = t / args.steps
-            r["gemm"]["roofline_ms"] = round(roof * 1e3, 4)
-            r["gemm"]["frac_roofline"] = round(roof / gemm_s, 4)
+            r["gemm"]["roofline_ms"] = round((roof_rows + roof_w) * 1e3, 4)
+            r["gemm"]["frac_roofline"] = round((roof_rows + roof_w) / gemm_s, 4)
             r["gemm"]["GB/s"] = round(by / gemm_s / 1e9, 1)
+            tw = sum(tt for (kind, lab), (_, tt, _) in w_labels.items() if kind == "gemm" and "wgrad" in lab)
+            tw /= args.steps
+            wby = sum(wl.wgrad_bytes(m, n) for m, n in wshapes)
+            r["gemm"]["roofline_ms"] = float(r["gemm"]["roofline_ms"])
+            r["gemm"]["frac_roofline"] = float(r["gemm"]["frac_roofline"])
+            r["wgrad"] = {"ms_per_step": round(tw * 1e3, 4), "roofline_ms": round(float(roof_w) * 1e3, 4),
+                          "frac_roofline": round(float(roof_w) / tw, 4), "GB/s": round(wby / tw / 1e9, 1)}
         log(f"[bench] {wl.name}: {r}")
         extra[wl.name] = r
         del wl

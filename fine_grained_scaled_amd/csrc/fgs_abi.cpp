@@ -300,7 +300,7 @@ int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, c
     if (A->elem != FGS_ELEM_E4M3 || A->scale_mode != FGS_SCALE_TILE_1x128 || B->scale_mode != FGS_SCALE_TILE_1x128)
         return fail(FGS_ERR_UNSUPPORTED, "grouped wgrad supports E4M3 TILE_1x128 x TILE_1x128");
     if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
-    const int64_t tiles = (int64_t)G * ((M + 255) / 256) * ((N + 127) / 128);
+    const int64_t tiles = (int64_t)G * ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, M, N, Kcap, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 1, total_T};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_wgrad_block_scaled launch");

@@ -882,7 +882,11 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     if (a.group_k) {
         if (a.G == 0) return hipSuccess;
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_TILE_1x128)
-            return launch_modes<ShapeDense, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_K>(p, a, bf16, stream);
+            // 128 x 128 tiles, two workgroups per CU: most experts hold one or
+            // two 128-token blocks, so each tile is mostly its 64 KiB of FP32
+            // output, and two resident workgroups overlap one's stores with the
+            // other's loads and MFMAs (1.4x the 256 x 128 tile on DeepSeek-V3)
+            return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_K>(p, a, bf16, stream);
         return hipErrorInvalidValue;
     }
     if (a.group_offsets) {

@@ -166,9 +166,9 @@ def _wgrad_case(fgs, counts, M, N, out, seed=0):
 
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_grouped_wgrad_ragged_and_empty(fgs, out):
-    """Ragged experts (1, 3, 130, 200, 257 tokens; two empty), M = 384 (a
-    partial 256-row tile), N = 200 (a partial 128-column tile)."""
-    _wgrad_case(fgs, COUNTS, M=384, N=200, out=out)
+    """Ragged experts (1, 3, 130, 200, 257 tokens; two empty), M = 328 (a
+    partial 128-row tile), N = 200 (a partial 128-column tile)."""
+    _wgrad_case(fgs, COUNTS, M=328, N=200, out=out)
 
 
 def test_grouped_wgrad_many_groups(fgs):
