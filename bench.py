@@ -60,6 +60,7 @@ LLAMA8B_LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 2867
 RECIPES = [("blockwise", "tile", "block"), ("per_tensor", "tensor", "tensor")]
 
 MOE_TOKENS, MOE_EXPERTS, MOE_HIDDEN, MOE_INTER = 32768, 256, 7168, 2048
+MOE_SOURCE_TOKENS = 4096          # 32768 routed rows = 4096 tokens x top-8
 MX_M = 4096
 MX_LAYERS = [("qkv", 16384, 18432), ("o", 16384, 16384), ("gate_up", 16384, 106496), ("down", 53248, 16384)]
 NV_M = 8192
@@ -275,7 +276,13 @@ class MoE:
         self.counts = counts
         self.offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
         T, H, I, G = MOE_TOKENS, MOE_HIDDEN, MOE_INTER, MOE_EXPERTS
-        self.a1 = gpu_normal(torch, (T, H), 101, outlier_cols=synth.outlier_channels(H, 0))
+        # the tokens before dispatch and the routed row -> token map (seeded
+        # random; the per-expert row counts are the Zipf draw above): the
+        # dispatch gather is fused into the quantizer's read
+        self.x_tok = gpu_normal(torch, (MOE_SOURCE_TOKENS, H), 101, outlier_cols=synth.outlier_channels(H, 0))
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(107)
+        self.route = torch.randint(0, MOE_SOURCE_TOKENS, (T,), generator=gen, device="cuda", dtype=torch.int32)
         self.a2 = gpu_normal(torch, (T, I), 102, outlier_cols=synth.outlier_channels(I, 0))
         self.g1 = gpu_t3(torch, (T, 2 * I), 105)             # dY of gate+up
         self.g2 = gpu_t3(torch, (T, H), 106)                 # dY of down
@@ -355,7 +362,11 @@ class MoE:
         # each input is read once for its row-wise codes (fwd / dgrad) and its
         # per-expert transposed codes (wgrad)
         grouped = lambda x: fgs.quantize_grouped_colwise(x, off, rowwise=True)
-        qa1 = tm.run("quant", "A1", e4m3_bytes(T, H, "tile", 2), lambda: grouped(self.a1))
+        # dispatch: the routed rows gathered from the tokens inside the read
+        # (algorithmic bytes: the tokens once, the index, both outputs)
+        a1_bytes = e4m3_bytes(T, H, "tile", 2) - 2.0 * T * H + 2.0 * MOE_SOURCE_TOKENS * H + 4.0 * T
+        qa1 = tm.run("quant", "A1", a1_bytes, lambda: fgs.quantize_grouped_colwise(
+            self.x_tok, off, rowwise=True, row_index=self.route))
         tm.run("gemm", "gate_up", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
             qa1.rowwise(), self.w1, off, 2 * I, torch.bfloat16, out=self.y1))
         qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 2), lambda: grouped(self.a2))

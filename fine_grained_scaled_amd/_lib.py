@@ -66,7 +66,7 @@ def load() -> ctypes.CDLL:
     OP = ctypes.POINTER(FgsOperand)
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
-    lib.fgs_quantize_grouped_colwise.argtypes = [P, I64, I64, I64, P, ctypes.c_int32, P, P, P, I64, P, P]
+    lib.fgs_quantize_grouped_colwise.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_int32, P, P, P, I64, P, P]
     lib.fgs_grouped_colwise_blocks.argtypes = [I64, ctypes.c_int32]
     lib.fgs_grouped_colwise_blocks.restype = I64
     lib.fgs_grouped_wgrad_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]

@@ -254,30 +254,43 @@ int64_t fgs_grouped_colwise_blocks(int64_t rows, int32_t G)
 }
 
 int fgs_quantize_grouped_colwise(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 const int32_t* row_index, int64_t src_rows,
                                  const int32_t* group_offsets, int32_t G,
                                  uint8_t* q, float* scales,
                                  uint8_t* qT, int64_t ldqT, float* scalesT, void* stream)
 {
     if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
-    int st = check_bf16_source(x, rows, cols, ldx);
+    if (rows < 0) return fail(FGS_ERR_INVALID_ARG, "rows must be >= 0");
+    int st;
+    if (row_index) {
+        if (src_rows < 0) return fail(FGS_ERR_INVALID_ARG, "src_rows must be >= 0");
+        st = check_bf16_source(x, src_rows, cols, ldx);
+        if (st == FGS_OK && (rows + 127) / 128 > kMaxRowBlocks)
+            st = fail(FGS_ERR_UNSUPPORTED, "rows too large (%lld)", (long long)rows);
+    } else {
+        st = check_bf16_source(x, rows, cols, ldx);
+    }
     if (st != FGS_OK) return st;
-    if (rows == 0 || cols == 0 || G == 0) return ok();
+    if (rows == 0 || cols == 0 || G == 0 || (!q && !qT)) return ok();
     if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
-    if (!qT || !scalesT) return fail(FGS_ERR_INVALID_ARG, "qT and scalesT are required");
+    if (row_index && src_rows > 0 && !x) return fail(FGS_ERR_INVALID_ARG, "x is NULL");
+    if (qT && !scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
     const int64_t blocks = fgs_grouped_colwise_blocks(rows, G);
     if (blocks > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many token blocks");
     if ((cols + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "cols too large (%lld)", (long long)cols);
-    if (ldqT < 128 * blocks)
-        return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,
-                    (long long)(128 * blocks));
-    if (ldqT % 16) return fail(FGS_ERR_UNSUPPORTED, "ldqT must be a multiple of 16");
-    if (!aligned(qT, 16) || !aligned(scalesT, 4)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
+    if (qT) {
+        if (ldqT < 128 * blocks)
+            return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,
+                        (long long)(128 * blocks));
+        if (ldqT % 16) return fail(FGS_ERR_UNSUPPORTED, "ldqT must be a multiple of 16");
+        if (!aligned(qT, 16) || !aligned(scalesT, 4)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
+    }
     if (q) {
         if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
         if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0 (cols = %lld)", (long long)cols);
         if (!aligned(q, 16) || !aligned(scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte and scales 4-byte aligned");
     }
-    fgs::QuantGroupedArgs a{x, rows, cols, ldx, group_offsets, G, q, scales, qT, ldqT, scalesT};
+    fgs::QuantGroupedArgs a{x, rows, cols, ldx, row_index, src_rows, group_offsets, G, q, scales, qT, ldqT, scalesT};
     return hip_status(fgs::launch_quant_grouped_colwise(a, static_cast<hipStream_t>(stream)),
                       "quantize_grouped_colwise launch");
 }

@@ -26,7 +26,9 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream);
 // output of the grouped rows), TILE mode only.
 struct QuantGroupedArgs {
     const void* x;
-    int64_t rows, cols, ldx;
+    int64_t rows, cols, ldx;        // rows: of the (gathered) matrix the groups index
+    const int32_t* row_index;       // device int32 [rows] into x, or nullptr (identity)
+    int64_t src_rows;               // rows of x when row_index is given
     const int32_t* group_offsets;   // device int32 [G + 1]
     int32_t G;
     uint8_t* q;

@@ -82,14 +82,17 @@ __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
 // overlap for non-decreasing offsets, so no scan over the groups is needed.
 // Workgroup (blockIdx.x = block j, blockIdx.y = column block) finds the group
 // that owns block j; rows past the group's end read as zero (zero codes in
-// qT, no effect on the amax).
+// qT, no effect on the amax).  With row_index, logical row t is source row
+// row_index[t] of x (the MoE dispatch gather, fused so the permuted BF16
+// copy is never written); an index outside [0, src_rows) reads as zeros.
 template <int MODE, bool GROUPED>   // MODE: FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, float* __restrict__ scales,
     uint8_t* __restrict__ qT, float* __restrict__ scalesT,
     const uint32_t* __restrict__ tensor_amax,
-    const int32_t* __restrict__ offsets, int32_t G, int64_t ldqT)
+    const int32_t* __restrict__ offsets, int32_t G, int64_t ldqT,
+    const int32_t* __restrict__ row_index, int64_t src_rows)
 {
     static_assert(!GROUPED || MODE == FGS_SCALE_TILE_1x128, "groups take 1x128 tiles");
     __shared__ uint32_t red[4][TB];
@@ -137,8 +140,16 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int64_t row = r0 + 8 * rg + u;
-        if (col_ok && 8 * rg + u < live)
-            v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+        bool ok = col_ok && 8 * rg + u < live;
+        int64_t src = row;
+        if constexpr (GROUPED) {
+            if (row_index && ok) {
+                src = row_index[row];
+                ok = src >= 0 && src < src_rows;
+            }
+        }
+        if (ok)
+            v[u] = *reinterpret_cast<const uint4*>(x + src * ldx + col);
         else
             v[u] = make_uint4(0, 0, 0, 0);
     }
@@ -306,11 +317,11 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
     switch (a.mode) {
     case FGS_SCALE_TILE_1x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0);
         break;
     case FGS_SCALE_BLOCK_128x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0);
         break;
     case FGS_SCALE_TENSOR: {
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
@@ -320,7 +331,7 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
         hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
                            x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TENSOR, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0, nullptr, 0);
         break;
     }
     default:
@@ -336,7 +347,8 @@ hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t s
     if (a.G == 0 || a.rows == 0 || nbc == 0) return hipSuccess;
     hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true>), dim3((unsigned)nblk, (unsigned)nbc),
                        dim3(256), 0, stream, static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ldx,
-                       a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets, a.G, a.ldqT);
+                       a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets, a.G, a.ldqT,
+                       a.row_index, a.src_rows);
     return hipGetLastError();
 }
 

@@ -260,15 +260,23 @@ def grouped_colwise_blocks(rows: int, G: int) -> int:
 
 
 def quantize_grouped_colwise(x: torch.Tensor, group_offsets: torch.Tensor,
-                             rowwise: bool = False) -> Quantized:
+                             rowwise: bool = False, row_index: Optional[torch.Tensor] = None,
+                             colwise: bool = True) -> Quantized:
     """MoE weight-gradient operand: per-group transposed 1x128 E4M3
     quantization of x [T x C] (rows offsets[g]..offsets[g+1]-1 are group g).
     qT is [C x 128 * blocks]: group g takes the 128-column blocks from
     offsets[g] // 128 + g on, zero-padded to whole blocks; scalesT is
     [blocks x C].  rowwise=True adds the ordinary 1x128 row-wise output of
-    the grouped rows from the same read."""
-    rows, cols, ldx = _bf16_matrix(x)
-    _need_gpu(group_offsets)
+    the grouped rows from the same read.  row_index (int32 [T] on the GPU)
+    gathers: row t is x[row_index[t]] (the MoE dispatch permutation), an
+    index outside x's rows reading as zeros."""
+    src_rows, cols, ldx = _bf16_matrix(x)
+    _need_gpu(group_offsets, row_index)
+    rows = src_rows
+    if row_index is not None:
+        if row_index.dtype != torch.int32 or row_index.dim() != 1 or not row_index.is_contiguous():
+            raise TypeError("row_index must be a contiguous 1-D int32 tensor")
+        rows = row_index.numel()
     if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or not group_offsets.is_contiguous():
         raise TypeError("group_offsets must be a contiguous 1-D int32 tensor")
     G = group_offsets.numel() - 1
@@ -276,14 +284,15 @@ def quantize_grouped_colwise(x: torch.Tensor, group_offsets: torch.Tensor,
         raise ValueError("group_offsets needs G + 1 >= 1 entries")
     nb = grouped_colwise_blocks(rows, G)
     dev = x.device
-    qT = torch.empty((cols, 128 * nb), dtype=torch.uint8, device=dev)
-    sT = torch.empty((nb, cols), dtype=torch.float32, device=dev)
-    q = s = None
+    qT = sT = q = s = None
+    if colwise:
+        qT = torch.empty((cols, 128 * nb), dtype=torch.uint8, device=dev)
+        sT = torch.empty((nb, cols), dtype=torch.float32, device=dev)
     if rowwise:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         s = torch.empty(((cols + 127) // 128, rows), dtype=torch.float32, device=dev)
     check(_lib.load().fgs_quantize_grouped_colwise(
-        _ptr(x), rows, cols, ldx, _ptr(group_offsets), G, _ptr(q), _ptr(s),
+        _ptr(x), rows, cols, ldx, _ptr(row_index), src_rows, _ptr(group_offsets), G, _ptr(q), _ptr(s),
         _ptr(qT), 128 * nb, _ptr(sT), _stream()))
     return Quantized(q, s, qT, sT, SCALE_TILE_1x128)
 

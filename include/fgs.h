@@ -207,15 +207,22 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
  *   quantization", "Online quantization", "Mixed precision framework" (the
  *   expert GEMMs, wgrad included, in FP8 with 1x128 tiles along the
  *   contraction, which for wgrad runs over each expert's tokens).
- * x        BF16 [rows x cols], row stride ldx (elements, multiple of 8); row
- *          t is a token, grouped by expert.
+ * x        BF16 [rows x cols] (or [src_rows x cols] with row_index), row
+ *          stride ldx (elements, multiple of 8); row t is a token, grouped by
+ *          expert.
+ * row_index  NULL, or DEVICE int32 [rows]: the MoE dispatch gather fused
+ *          into the read.  Row t of the matrix the groups index is then row
+ *          row_index[t] of x (x has src_rows rows; an index outside
+ *          [0, src_rows) reads as a row of zeros), so the permuted BF16 copy is
+ *          never written.  Everything below refers to the gathered rows.
+ *          [DSV3] "Mixed precision framework" (expert GEMMs in FP8).
  * group_offsets  DEVICE int32 [G+1]: group g is rows offsets[g] ..
  *          offsets[g+1]-1 (M_g tokens).  Read on the device.  A group with
  *          offsets[g] < 0, offsets[g+1] < offsets[g] or offsets[g+1] > rows
  *          is treated as empty; offsets that decrease from one group to the
  *          next give unspecified codes, but every write stays inside the
  *          buffers below.
- * Column-wise output (required): group g's transpose [cols x M_g] in 1x128
+ * Column-wise output (NULL qT skips it): group g's transpose [cols x M_g] in 1x128
  *   tiles along its tokens (a tile never holds two groups' tokens; the last
  *   one is partial when M_g % 128 != 0, scaled from the tokens present and
  *   padded with code 0x00, or 0x7F like the rest of a tile whose scale is
@@ -228,12 +235,13 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
  *            ldqT % 16 == 0.
  *   scalesT  FP32 [fgs_grouped_colwise_blocks][cols] (the TILE_1x128 layout
  *            of an operand of cols rows and K = 128 * blocks).
- * Row-wise output (optional, NULL q skips it; needs cols % 128 == 0): the
- *   ordinary 1x128 quantization of every row that a valid group covers, from
- *   the same read: q [rows x cols], scales [cols/128][rows]; rows of no
- *   group are not written.
+ * Row-wise output (NULL q skips it; needs cols % 128 == 0): the ordinary
+ *   1x128 quantization of every row that a valid group covers, from the same
+ *   read: q [rows x cols], scales [cols/128][rows]; rows of no group are not
+ *   written.  With neither output nothing is enqueued.
  */
 int fgs_quantize_grouped_colwise(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                                 const int32_t *row_index, int64_t src_rows,
                                  const int32_t *group_offsets, int32_t G,
                                  uint8_t *q, float *scales,
                                  uint8_t *qT, int64_t ldqT, float *scalesT, void *stream);

@@ -275,7 +275,18 @@ def quant_nvfp4_rows(values_f32: np.ndarray, tensor_scale, stochastic: bool = Fa
     return q, scales
 
 
-def quant_e4m3_grouped_colwise(x, offsets):
+def gather_rows(x, row_index):
+    """BF16 bits of the gathered matrix: row t = x[row_index[t]], zeros for
+    an index outside [0, rows of x)."""
+    xb = _as_bf16_bits(x)
+    idx = np.asarray(row_index, dtype=np.int64)
+    out = np.zeros((len(idx), xb.shape[1]), dtype=np.uint16)
+    ok = (idx >= 0) & (idx < xb.shape[0])
+    out[ok] = xb[idx[ok]]
+    return out
+
+
+def quant_e4m3_grouped_colwise(x, offsets, row_index=None):
     """Per-group transposed 1x128 quantization of the MoE weight-gradient
     operands ([DSV3] "Fine-grained quantization", "Online quantization",
     "Mixed precision framework": the expert GEMMs, wgrad included, take
@@ -288,8 +299,12 @@ def quant_e4m3_grouped_colwise(x, offsets):
     and takes its scale from the tokens present (zero padding would leave
     the amax unchanged).  Returns one (codes uint8 [C x M_g], scales float32
     [C x ceil(M_g/128)]) per group; an empty group gives empty arrays.
+
+    row_index: the MoE dispatch permutation.  When given, the groups index
+    the gathered matrix whose row t is x[row_index[t]] (a row of zeros for
+    an index outside x).
     """
-    xb = _as_bf16_bits(x)
+    xb = gather_rows(x, row_index) if row_index is not None else _as_bf16_bits(x)
     cols = xb.shape[1]
     out = []
     for g in range(len(offsets) - 1):

@@ -148,16 +148,26 @@ def test_grouped_colwise_validation(lib):
     assert lib.fgs_grouped_colwise_blocks(300, 4) == 2 + 4
     assert lib.fgs_grouped_colwise_blocks(-1, 4) == 0
     ld = 128 * 6
-    assert q(FAKE, 300, 256, 256, FAKE, -1, NULL, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG   # G < 0
-    assert q(FAKE, 300, 256, 256, NULL, 4, NULL, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # offsets
-    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, NULL, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # qT
-    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, FAKE, ld - 16, FAKE, S) == _lib.FGS_ERR_INVALID_ARG
+    N0 = NULL
+
+    def call(x=FAKE, rows=300, cols=256, ldx=256, idx=N0, src=0, offs=FAKE, G=4, qq=N0, s=N0, qT=FAKE,
+             ldq=ld, sT=FAKE):
+        return q(x, rows, cols, ldx, idx, src, offs, G, qq, s, qT, ldq, sT, S)
+    assert call(G=-1) == _lib.FGS_ERR_INVALID_ARG
+    assert call(offs=NULL) == _lib.FGS_ERR_INVALID_ARG
+    assert call(sT=NULL) == _lib.FGS_ERR_INVALID_ARG                      # qT without scalesT
+    assert call(ldq=ld - 16) == _lib.FGS_ERR_INVALID_ARG
     assert b"ldqT" in lib.fgs_last_error()
-    assert q(FAKE, 300, 256, 256, FAKE, 4, NULL, NULL, FAKE, ld + 8, FAKE, S) == _lib.FGS_ERR_UNSUPPORTED
-    assert q(FAKE, 300, 200, 200, FAKE, 4, FAKE, FAKE, FAKE, ld, FAKE, S) == _lib.FGS_ERR_UNSUPPORTED    # row-wise cols % 128
-    assert q(FAKE, 300, 256, 256, FAKE, 4, FAKE, NULL, FAKE, ld, FAKE, S) == _lib.FGS_ERR_INVALID_ARG    # scales
-    assert q(FAKE, 300, 256, 256, FAKE, 0, NULL, NULL, NULL, 0, NULL, S) == _lib.FGS_OK                  # no groups
-    assert q(FAKE, 0, 256, 256, FAKE, 4, NULL, NULL, NULL, 0, NULL, S) == _lib.FGS_OK                    # no rows
+    assert call(ldq=ld + 8) == _lib.FGS_ERR_UNSUPPORTED
+    assert call(cols=200, ldx=200, qq=FAKE, s=FAKE) == _lib.FGS_ERR_UNSUPPORTED   # row-wise cols % 128
+    assert call(qq=FAKE, s=NULL) == _lib.FGS_ERR_INVALID_ARG                     # scales
+    assert call(G=0, qT=NULL, ldq=0, sT=NULL) == _lib.FGS_OK                      # no groups
+    assert call(rows=0) == _lib.FGS_OK                                            # no rows
+    assert call(qT=NULL, sT=NULL) == _lib.FGS_OK                                  # no output
+    # gather: x holds src_rows rows, the groups index rows of the gathered matrix
+    assert call(idx=FAKE, src=-1) == _lib.FGS_ERR_INVALID_ARG
+    assert call(idx=FAKE, src=100, ldx=100) == _lib.FGS_ERR_INVALID_ARG           # ldx < cols
+    assert call(x=NULL, idx=FAKE, src=100) == _lib.FGS_ERR_INVALID_ARG
 
 
 def test_grouped_wgrad_validation(lib):

@@ -51,10 +51,11 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
 
 
-def _quant_abi(x_bits, offs, rowwise):
+def _quant_abi(x_bits, offs, rowwise, row_index=None):
     """fgs_quantize_grouped_colwise on sentinel-filled outputs."""
     lib = _lib.load()
-    T, C = x_bits.shape
+    src_rows, C = x_bits.shape
+    T = src_rows if row_index is None else len(row_index)
     G = len(offs) - 1
     nb = lib.fgs_grouped_colwise_blocks(T, G)
     assert nb == T // 128 + G
@@ -66,7 +67,8 @@ def _quant_abi(x_bits, offs, rowwise):
     if rowwise:
         q = torch.full((T, C), SENT_CODE, dtype=torch.uint8, device="cuda")
         s = torch.full((C // 128, T), SENT_SCALE, dtype=torch.float32, device="cuda")
-    st = lib.fgs_quantize_grouped_colwise(_ptr(x), T, C, C, _ptr(off_t), G, _ptr(q), _ptr(s),
+    idx = None if row_index is None else torch.from_numpy(np.asarray(row_index, np.int32)).cuda()
+    st = lib.fgs_quantize_grouped_colwise(_ptr(x), T, C, C, _ptr(idx), src_rows, _ptr(off_t), G, _ptr(q), _ptr(s),
                                           _ptr(qT), 128 * nb, _ptr(sT),
                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _lib.check(st)
@@ -75,9 +77,9 @@ def _quant_abi(x_bits, offs, rowwise):
     return cpu(q), cpu(s), cpu(qT), cpu(sT)
 
 
-def _check_grouped_quant(x_bits, offs, rowwise):
-    q, s, qT, sT = _quant_abi(x_bits, offs, rowwise)
-    ref = oracle.quant_e4m3_grouped_colwise(x_bits, offs)
+def _check_grouped_quant(x_bits, offs, rowwise, row_index=None):
+    q, s, qT, sT = _quant_abi(x_bits, offs, rowwise, row_index)
+    ref = oracle.quant_e4m3_grouped_colwise(x_bits, offs, row_index=row_index)
     nb = sT.shape[0]
     owned = np.zeros(nb, dtype=bool)
     for g, kb, n in _blocks_of(offs):
@@ -94,8 +96,9 @@ def _check_grouped_quant(x_bits, offs, rowwise):
         assert np.all(qT[:, 128 * b:128 * (b + 1)] == SENT_CODE), f"block {b} written"
         assert np.all(sT[b] == SENT_SCALE), f"scales of block {b} written"
     if rowwise:
-        qr, sr = oracle.quant_e4m3(x_bits, "tile")
-        covered = np.zeros(x_bits.shape[0], dtype=bool)
+        rows_bits = x_bits if row_index is None else oracle.gather_rows(x_bits, row_index)
+        qr, sr = oracle.quant_e4m3(rows_bits, "tile")
+        covered = np.zeros(rows_bits.shape[0], dtype=bool)
         for g in range(len(offs) - 1):
             covered[offs[g]:offs[g + 1]] = True
         assert np.array_equal(q[covered], qr[covered])
@@ -126,6 +129,21 @@ def test_grouped_colwise_quant_special_and_uncovered():
     xf[offs[5]:offs[6]] = 0.0
     xf[offs[5]:offs[6]:2, ::3] = -0.0
     _check_grouped_quant(synth.f32_to_bf16_bits(xf), offs.astype(np.int32), rowwise=True)
+
+
+def test_grouped_colwise_quant_gathered_dispatch():
+    """The MoE dispatch gather fused into the read: 300 tokens routed top-3
+    to 8 experts (rows sorted by expert), two routed rows with an index
+    outside the tokens (zero rows)."""
+    tokens, topk, G = 300, 3, 8
+    rng = np.random.default_rng(8)
+    expert = rng.integers(0, G, (tokens, topk)).ravel()
+    expert[expert == 5] = 4                                 # one expert without tokens
+    order = np.argsort(expert, kind="stable")
+    row_index = (order // topk).astype(np.int32)
+    row_index[[7, 500]] = [-1, tokens]
+    offs = _offsets(np.bincount(expert, minlength=G))
+    _check_grouped_quant(synth.activations(tokens, 384, seed=13), offs, rowwise=True, row_index=row_index)
 
 
 def test_grouped_colwise_quant_many_groups():

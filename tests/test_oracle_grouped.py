@@ -116,3 +116,26 @@ def test_grouped_wgrad_ref_exact_integers():
     assert not c[1].any() and not s[1].any()
     dense, _ = oracle.gemm_ref(np.concatenate(a_groups, axis=1), np.concatenate(b_groups, axis=1))
     assert np.array_equal(c.sum(axis=0), dense)
+
+
+def test_gather_rowwise_equivariance_and_invalid_rows():
+    """1x128 row tiles are per row, so quantizing gathered rows equals
+    gathering the quantized rows; an index outside x gives a zero row
+    (scale 1, zero codes), and the grouped column-wise codes of a gather
+    equal those of the explicitly permuted matrix."""
+    x = synth.activations(50, 256, seed=25)
+    g = np.random.default_rng(6)
+    idx = g.integers(0, 50, 90)
+    idx[[3, 40]] = [-1, 50]
+    gx = oracle.gather_rows(x, idx)
+    qg, sg = oracle.quant_e4m3(gx, "tile")
+    qx, sx = oracle.quant_e4m3(x, "tile")
+    ok = (idx >= 0) & (idx < 50)
+    assert np.array_equal(qg[ok], qx[idx[ok]]) and np.array_equal(sg[ok], sx[idx[ok]])
+    assert not qg[~ok].any() and np.all(sg[~ok] == 1.0)
+    offs = [0, 30, 30, 90]
+    res = oracle.quant_e4m3_grouped_colwise(x, offs, row_index=idx)
+    perm = np.where(ok[:, None], x[np.clip(idx, 0, 49)], 0).astype(np.uint16)
+    ref = oracle.quant_e4m3_grouped_colwise(perm, offs)
+    for (q0, s0), (q1, s1) in zip(res, ref):
+        assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
