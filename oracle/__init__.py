@@ -66,6 +66,12 @@ def _load():
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_encode.restype = ctypes.c_uint8
     lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e5m2_decode.restype = ctypes.c_double
+    lib.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e5m2_encode.restype = ctypes.c_uint8
+    lib.orc_e5m2_encode.argtypes = [ctypes.c_float]
+    lib.orc_e5m2_encode_array.argtypes = [P, I64, P]
+    lib.orc_quant_delayed.argtypes = [P, I64, ctypes.c_int, P, I64, P, P, P]
     lib.orc_e2m1_decode.restype = ctypes.c_double
     lib.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e8m0_decode.restype = ctypes.c_double
@@ -138,6 +144,18 @@ def e4m3_encode(y) -> np.ndarray:
     return out
 
 
+def e5m2_decode_table() -> np.ndarray:
+    lib = _load()
+    return np.array([lib.orc_e5m2_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e5m2_encode(y) -> np.ndarray:
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
+    out = np.empty(y.shape, dtype=np.uint8)
+    _load().orc_e5m2_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
 def e2m1_encode(y, r=None) -> np.ndarray:
     """E2M1 codes (4-bit, one per uint8); RNE when r is None, else SR with words r."""
     y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
@@ -204,6 +222,32 @@ def quant_e4m3(x, mode: str, colwise: bool = False):
     scales = np.empty(((rows + br - 1) // br, (cols + bc - 1) // bc), dtype=np.float32)
     _load().orc_quant_e4m3_blocks(_ptr(xb), rows, cols, br, bc, _ptr(q), _ptr(scales))
     return q, scales
+
+
+def quant_delayed(x, elem: str, history, colwise: bool = False):
+    """Per-tensor delayed scaling (the recipe that online scaling replaces,
+    [DSV3] "Online quantization"; E5M2 for the hybrid recipe, [DSV3]
+    "Unified E4M3 format"): the scale comes from the NaN-propagating max of
+    the amax history, every element saturates to the format's range.
+    elem: "e4m3" or "e5m2".  Returns (codes uint8 [R x C] of x, or of its
+    transpose when colwise, scale float32, amax float32 of x: the entry to
+    record for later steps)."""
+    xb = _as_bf16_bits(x)
+    if colwise:
+        xb = np.ascontiguousarray(xb.T)
+    h = np.ascontiguousarray(np.asarray(history, dtype=np.float32).reshape(-1))
+    q = np.empty(xb.shape, dtype=np.uint8)
+    sc = np.empty(1, dtype=np.float32)
+    am = np.empty(1, dtype=np.float32)
+    _load().orc_quant_delayed(_ptr(xb), xb.size, int(elem == "e5m2"), _ptr(h), h.size,
+                              _ptr(q), _ptr(sc), _ptr(am))
+    return q, sc[0], am[0]
+
+
+def dequant_tensor(q: np.ndarray, scale, elem: str) -> np.ndarray:
+    """codes with one FP32 scale -> FP64 (E4M3 or E5M2 elements)."""
+    tab = e5m2_decode_table() if elem == "e5m2" else e4m3_decode_table()
+    return tab[q] * np.float64(scale)
 
 
 def quant_mx(x, colwise: bool = False):

@@ -104,6 +104,65 @@ uint8_t orc_e4m3_encode(float y)
 }
 
 /* ------------------------------------------------------------------ */
+/* E5M2 (OCP FP8): s.eeeee.mm, bias 15, subnormals, 0x7C = Inf,          */
+/* 0x7D..0x7F NaN, largest finite 0x7B = 57344.  The pages contrast       */
+/* DeepSeek-V3's single E4M3 format with earlier hybrid recipes (E4M3     */
+/* forward, E5M2 backward) [DSV3 "Unified E4M3 format"].                  */
+/* ------------------------------------------------------------------ */
+double orc_e5m2_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 0x1F, m = c & 0x3;
+    double v;
+    if (e == 0x1F)
+        return m ? NAN : (s ? -INFINITY : INFINITY);
+    if (e == 0)
+        v = ldexp((double)m, -16);           /* subnormal: m * 2^-16      */
+    else
+        v = ldexp(4.0 + m, e - 17);          /* (1 + m/4) * 2^(e-15)      */
+    return s ? -v : v;
+}
+
+/*
+ * Round an FP32 value to E5M2: nearest representable value, ties to the
+ * even code, saturating at +-57344.
+ * READING: as for E4M3, the cast saturates (overflow and +-Inf give
+ * +-57344, never Inf); NaN maps to 0x7F; the sign is kept (-0 -> 0x80).
+ */
+uint8_t orc_e5m2_encode(float y)
+{
+    uint8_t sign;
+    double a, lo, hi, mid;
+    int c, lo_i, hi_i;
+
+    if (isnan(y))
+        return 0x7F;
+    sign = signbit(y) ? 0x80 : 0x00;
+    a = fabs((double)y);
+    if (a >= 57344.0)
+        return sign | 0x7B;
+    lo_i = 0;
+    hi_i = 0x7B;
+    while (lo_i < hi_i) {                    /* largest code with value <= a */
+        c = (lo_i + hi_i + 1) / 2;
+        if (orc_e5m2_decode((uint8_t)c) <= a)
+            lo_i = c;
+        else
+            hi_i = c - 1;
+    }
+    c = lo_i;
+    lo = orc_e5m2_decode((uint8_t)c);
+    if (a == lo)
+        return sign | (uint8_t)c;
+    hi = orc_e5m2_decode((uint8_t)(c + 1));
+    mid = 0.5 * (lo + hi);
+    if (a < mid)
+        return sign | (uint8_t)c;
+    if (a > mid)
+        return sign | (uint8_t)(c + 1);
+    return sign | (uint8_t)((c & 1) ? c + 1 : c);
+}
+
+/* ------------------------------------------------------------------ */
 /* E2M1 (OCP FP4): s.ee.m, magnitudes {0,.5,1,1.5,2,3,4,6}, no NaN/Inf  */
 /* [NVFP4 "How it works"] names the 4-bit format.                      */
 /* ------------------------------------------------------------------ */
@@ -446,6 +505,55 @@ void orc_quant_nvfp4(const float *x, int64_t rows, int64_t cols,
     float s_t = orc_nvfp4_tensor_scale(x, rows * cols);
     *tensor_scale = s_t;
     orc_quant_nvfp4_blocks(x, rows, cols, s_t, stochastic, sr_seed, 0, idx_rs, idx_cs, q, scales);
+}
+
+/*
+ * Per-tensor delayed scaling: the scale comes from the amaxes of earlier
+ * steps, not from the tensor being cast.  The pages name it as what online
+ * scaling replaces ("delayed quantization methods that depend on
+ * historical maximum values") [DSV3 "Online quantization"]; they give no
+ * formula.  READING (the plainest one):
+ *   hmax = NaN-propagating max of the history (H entries);
+ *   hmax non-finite -> scale NaN, every code NaN (0x7F);
+ *   hmax == 0 (an empty history) -> scale 1;
+ *   otherwise s = fl32(hmax / fmax), fmax = 448 (E4M3) or 57344 (E5M2);
+ *   code = ENC_RNE_SAT(fl32(x / s)): values beyond the range of this step's
+ *   scale saturate, NaN -> 0x7F;
+ *   *amax_out = the NaN-propagating max |x| of this tensor, the entry the
+ *   caller records for later steps.
+ * x: n BF16 values; q: n codes in the same order.
+ */
+void orc_quant_delayed(const uint16_t *x, int64_t n, int e5m2, const float *hist, int64_t H,
+                       uint8_t *q, float *scale, float *amax_out)
+{
+    const float fmax = e5m2 ? 57344.0f : 448.0f;
+    float hmax = 0.0f, amax = 0.0f, s;
+    int64_t i;
+    for (i = 0; i < H; i++)
+        hmax = amax_update(hmax, hist[i]);
+    if (!isfinite(hmax))
+        s = NAN;
+    else if (hmax == 0.0f)
+        s = 1.0f;
+    else
+        s = hmax / fmax;
+    *scale = s;
+    for (i = 0; i < n; i++) {
+        float v = orc_bf16_to_f32(x[i]);
+        amax = amax_update(amax, v);
+        if (isnan(s))
+            q[i] = 0x7F;
+        else
+            q[i] = e5m2 ? orc_e5m2_encode(v / s) : orc_e4m3_encode(v / s);
+    }
+    *amax_out = amax;
+}
+
+void orc_e5m2_encode_array(const float *y, int64_t n, uint8_t *out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = orc_e5m2_encode(y[i]);
 }
 
 /* ------------------------------------------------------------------ */
