@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfgs.so")
 
 FGS_OK, FGS_ERR_INVALID_ARG, FGS_ERR_UNSUPPORTED, FGS_ERR_HIP = 0, -1, -2, -3
-ELEM_E4M3, ELEM_E2M1 = 0, 1
+ELEM_E4M3, ELEM_E2M1, ELEM_E5M2 = 0, 1, 2
 SCALE_TENSOR, SCALE_TILE_1x128, SCALE_BLOCK_128x128, SCALE_MX32_E8M0, SCALE_NV16_E4M3 = 0, 1, 2, 3, 4
 ROUND_RNE, ROUND_STOCHASTIC = 0, 1
 OUT_FP32, OUT_BF16 = 0, 1
@@ -16,6 +16,7 @@ TILE_AUTO, TILE_NARROW, TILE_WIDE = 0, 1, 2
 
 EXPORTS = (
     "fgs_quantize_blockwise",
+    "fgs_quantize_delayed",
     "fgs_quantize_mx",
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
@@ -61,6 +62,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
     lib.fgs_quantize_blockwise.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, SZ, P]
+    lib.fgs_quantize_delayed.argtypes = [P, I64, I64, I64, I32, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
     lib.fgs_quantize_mx.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     lib.fgs_quantize_nvfp4.argtypes = [P, I64, I64, I64, I32, U64, I32, U64, P, P, P, P, P, P, SZ, P]
     OP = ctypes.POINTER(FgsOperand)
@@ -76,7 +78,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_workspace_bytes.restype = SZ
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
-    for name in ("fgs_quantize_blockwise", "fgs_quantize_mx", "fgs_quantize_nvfp4",
+    for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
                  "fgs_gemm_block_scaled", "fgs_grouped_gemm_block_scaled",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled"):
         getattr(lib, name).restype = ctypes.c_int

@@ -133,6 +133,27 @@ int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ld
     return hip_status(fgs::launch_quant_e4m3(a, static_cast<hipStream_t>(stream)), "quantize_blockwise launch");
 }
 
+int fgs_quantize_delayed(const void* x, int64_t rows, int64_t cols, int64_t ldx, int elem,
+                         float* amax_history, int32_t history_len, int32_t slot,
+                         uint8_t* q, uint8_t* qT, float* scale, void* stream)
+{
+    if (elem != FGS_ELEM_E4M3 && elem != FGS_ELEM_E5M2)
+        return fail(FGS_ERR_INVALID_ARG, "elem %d is not E4M3 or E5M2", elem);
+    int st = check_bf16_source(x, rows, cols, ldx);
+    if (st != FGS_OK) return st;
+    if (!amax_history || !aligned(amax_history, 4)) return fail(FGS_ERR_INVALID_ARG, "amax_history must be a 4-byte aligned device pointer");
+    if (history_len < 1 || history_len > 65536) return fail(FGS_ERR_INVALID_ARG, "history_len (%d) must be in 1..65536", history_len);
+    if (slot < 0 || slot >= history_len) return fail(FGS_ERR_INVALID_ARG, "slot (%d) must be in [0, history_len)", slot);
+    if (!scale || !aligned(scale, 4)) return fail(FGS_ERR_INVALID_ARG, "scale must be a 4-byte aligned device pointer");
+    if (q && !aligned(q, 16)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+    if (qT) {
+        if (rows % 128) return fail(FGS_ERR_UNSUPPORTED, "column-wise output needs rows %% 128 == 0 (rows = %lld)", (long long)rows);
+        if (!aligned(qT, 16)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte aligned");
+    }
+    fgs::QuantDelayedArgs a{x, rows, cols, ldx, elem, amax_history, history_len, slot, q, qT, scale};
+    return hip_status(fgs::launch_quant_delayed(a, static_cast<hipStream_t>(stream)), "quantize_delayed launch");
+}
+
 int fgs_quantize_mx(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                     uint8_t* q, uint8_t* scales, uint8_t* qT, uint8_t* scalesT, void* stream)
 {
@@ -191,8 +212,15 @@ static int check_gemm_common(const fgs_operand* A, const fgs_operand* B, int64_t
     if (!C) return fail(FGS_ERR_INVALID_ARG, "C is NULL");
     if (ldc < N) return fail(FGS_ERR_INVALID_ARG, "ldc (%lld) < N (%lld)", (long long)ldc, (long long)N);
     if (!aligned(C, out_dtype == FGS_OUT_FP32 ? 4 : 2)) return fail(FGS_ERR_UNSUPPORTED, "C misaligned");
-    if (A->elem != B->elem) return fail(FGS_ERR_UNSUPPORTED, "A and B element formats differ");
-    if (A->elem != FGS_ELEM_E4M3 && A->elem != FGS_ELEM_E2M1) return fail(FGS_ERR_INVALID_ARG, "unknown element format %d", A->elem);
+    for (const fgs_operand* op : {A, B})
+        if (op->elem != FGS_ELEM_E4M3 && op->elem != FGS_ELEM_E2M1 && op->elem != FGS_ELEM_E5M2)
+            return fail(FGS_ERR_INVALID_ARG, "unknown element format %d", op->elem);
+    const bool fp8 = [](int e) { return e == FGS_ELEM_E4M3 || e == FGS_ELEM_E5M2; }(A->elem) &&
+                     (B->elem == FGS_ELEM_E4M3 || B->elem == FGS_ELEM_E5M2);
+    if (A->elem != B->elem && !fp8) return fail(FGS_ERR_UNSUPPORTED, "A and B element formats differ");
+    if ((A->elem == FGS_ELEM_E5M2 || B->elem == FGS_ELEM_E5M2) &&
+        (A->scale_mode != FGS_SCALE_TENSOR || B->scale_mode != FGS_SCALE_TENSOR))
+        return fail(FGS_ERR_UNSUPPORTED, "E5M2 operands take per-tensor (TENSOR) scales on both sides");
     int st = check_operand(A, "A", M, K);
     if (st != FGS_OK) return st;
     return check_operand(B, "B", N, K);
@@ -214,7 +242,7 @@ int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M,
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (A->elem == FGS_ELEM_E4M3 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
+    if (A->elem != FGS_ELEM_E2M1 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
         if (A->scale_mode == FGS_SCALE_BLOCK_128x128)
             return fail(FGS_ERR_UNSUPPORTED, "A with 128x128 block scales is not supported (use TILE_1x128 or TENSOR)");
         return hip_status(fgs::launch_gemm_fp8(a, s), "gemm_block_scaled launch");

@@ -39,6 +39,19 @@ struct QuantGroupedArgs {
 };
 hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t stream);
 
+// Per-tensor delayed scaling (E4M3 or E5M2) from an amax history.
+struct QuantDelayedArgs {
+    const void* x;
+    int64_t rows, cols, ldx;
+    int elem;                       // FGS_ELEM_E4M3 | FGS_ELEM_E5M2
+    float* history;                 // device FP32 [history_len]
+    int32_t history_len, slot;
+    uint8_t* q;
+    uint8_t* qT;
+    float* scale;                   // device FP32 [1]
+};
+hipError_t launch_quant_delayed(const QuantDelayedArgs& a, hipStream_t stream);
+
 struct QuantMXArgs {
     const void* x;
     int64_t rows, cols, ldx;

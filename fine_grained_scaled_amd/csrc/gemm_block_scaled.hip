@@ -57,6 +57,7 @@
 // are swapped (B fragment first) so each lane's 16 accumulators share one
 // row m: the 1x128 A scale is one value per lane and per sub-tile row.
 #include <atomic>
+#include <type_traits>
 
 #include "fgs_device.h"
 #include "fgs_internal.h"
@@ -151,6 +152,33 @@ __device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 E5M2 codes -> two FP16 8-vectors (same element order as decode16).
+// E5M2 is FP16 with the low 8 mantissa bits cut off, so the FP16 bits of a
+// code are the code followed by a zero byte: exact for every code,
+// subnormals, Inf and NaN included.
+__device__ __forceinline__ void decode16_e5m2(const uint4 v, f16x8& lo, f16x8& hi)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[2 * i] = ((w[i] << 8) & 0xFF00u) | ((w[i] << 16) & 0xFF000000u);      // bytes 0, 1
+        h[2 * i + 1] = ((w[i] >> 8) & 0xFF00u) | (w[i] & 0xFF000000u);          // bytes 2, 3
+    }
+    lo = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    hi = __builtin_bit_cast(f16x8, make_uint4(h[4], h[5], h[6], h[7]));
+}
+
+// One operand's 16 byte codes (E4M3, or E5M2 when E5) -> FP16.
+template <bool E5>
+__device__ __forceinline__ void decode16_fp8(const uint4 v, f16x8& lo, f16x8& hi)
+{
+    if constexpr (E5)
+        decode16_e5m2(v, lo, hi);
+    else
+        decode16(v, lo, hi);
+}
+
 // MXFP8: 16 E4M3 codes of one 32-element block -> two BF16 8-vectors of
 // code * s, with s = 2^d (d <= 0) the block's scale relative to the
 // reference exponent; exact whenever code * s is a BF16 number (every code
@@ -224,7 +252,8 @@ struct Lds {
 // B); MoE groups of the contraction (weight gradients, one C per group).
 enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
 
-template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP>
+// ELEMS (FP8 per-tensor operands only): bit 0 = A is E5M2, bit 1 = B is E5M2.
+template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP, int ELEMS = 0>
 __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel(GemmParams p)
 {
     constexpr int NWM = S::NWM, NWN = S::NWN;
@@ -661,10 +690,10 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                     f16x8 af[TI][2], bf[TJ][2];
     #pragma unroll
                     for (int j = 0; j < TJ; ++j)
-                        decode16(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
+                        decode16_fp8<(ELEMS & 2) != 0>(*reinterpret_cast<const uint4*>(lb + 32 * j * ROW + co), bf[j][0], bf[j][1]);
     #pragma unroll
                     for (int i = 0; i < TI; ++i)
-                        decode16(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
+                        decode16_fp8<(ELEMS & 1) != 0>(*reinterpret_cast<const uint4*>(la + 32 * i * ROW + co), af[i][0], af[i][1]);
     #pragma unroll
                     for (int h = 0; h < 2; ++h)
     #pragma unroll
@@ -781,7 +810,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
 }
 
-template <class S, int AMODE, int BMODE, int GROUP>
+template <class S, int AMODE, int BMODE, int GROUP, int ELEMS = 0>
 hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
     p.tiles_n = (int32_t)((a.N + S::BN - 1) / S::BN);
@@ -790,8 +819,8 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128>::STAGE;
-    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP>
-                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP>;
+    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS>
+                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -838,8 +867,22 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
         return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, GROUP_NONE>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_TENSOR) {
         if (bmode == FGS_SCALE_TENSOR) {
-            if (wide) return launch_modes<ShapeWide, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
-            return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
+            const int elems = (a.A.elem == FGS_ELEM_E5M2 ? 1 : 0) | (a.B.elem == FGS_ELEM_E5M2 ? 2 : 0);
+            using T = std::integral_constant<int, FGS_SCALE_TENSOR>;
+            switch (elems) {
+            case 1:
+                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 1>(p, a, bf16, s);
+                return launch_modes<D, T::value, T::value, GROUP_NONE, 1>(p, a, bf16, s);
+            case 2:
+                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 2>(p, a, bf16, s);
+                return launch_modes<D, T::value, T::value, GROUP_NONE, 2>(p, a, bf16, s);
+            case 3:
+                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 3>(p, a, bf16, s);
+                return launch_modes<D, T::value, T::value, GROUP_NONE, 3>(p, a, bf16, s);
+            default:
+                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE>(p, a, bf16, s);
+                return launch_modes<D, T::value, T::value, GROUP_NONE>(p, a, bf16, s);
+            }
         }
         if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, GROUP_NONE>(p, a, bf16, s);
         if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, GROUP_NONE>(p, a, bf16, s);

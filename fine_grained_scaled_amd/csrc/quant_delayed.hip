@@ -1,0 +1,207 @@
+// quant_delayed.hip -- per-tensor delayed scaling to E4M3 or E5M2 on gfx950.
+//
+// "Can you explain the role of FP8 precision in DeepSeek-V3 training",
+// section "Online quantization": online scales replace delayed ones, which
+// come from the maxima of earlier steps; section "Unified E4M3 format":
+// earlier frameworks used E4M3 forward and E5M2 backward.  The pages give
+// neither formula; the rule built here: the scale is s = fl32(hmax / fmax)
+// with hmax the NaN-propagating max of the caller's amax history (s = 1 for
+// an all-zero history, NaN for a non-finite one) and fmax = 448 (E4M3) or
+// 57344 (E5M2); every element is code = ENC_RNE_SAT(fl32(x / s)) (values
+// past this step's range saturate, NaN gives 0x7F); this tensor's amax is
+// recorded into the history slot the caller names.
+//
+// Because the scale is known before the data is read, one pass over x
+// suffices (current per-tensor scaling needs an amax pass first): the amax
+// for later steps is reduced in the same pass, one atomic per workgroup.
+//
+// Two kernels on the stream: delayed_scale_kernel (one workgroup) reads the
+// history, writes the scale and clears the slot; quant_delayed_kernel casts
+// 128 x 128 blocks (the thread layout of the E4M3 quantizer: 8 x 8 values
+// per thread, 16 lanes over one 256-byte row segment) and atomically maxes
+// the block amax into the slot.
+#include "fgs_device.h"
+#include "fgs_internal.h"
+
+namespace fgs {
+
+namespace {
+
+constexpr int TB = 128;
+constexpr int TPAD = 16;
+
+__device__ __forceinline__ uint32_t abs_max8_bf16(const uint4& v)
+{
+    const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0xFFFFu, w[i] >> 16));
+    return m;
+}
+
+// FP32 bit pattern of element j (0..7) of an 8-element BF16 vector (exact)
+__device__ __forceinline__ uint32_t bf16_elem_bits(const uint4& v, int j)
+{
+    const uint32_t w = (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w;
+    return (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+}
+
+// E5M2 magnitude code of a non-negative FP32 value a <= 57344, round to
+// nearest even.  Below 2^-14 the grid is uniform with step 2^-16 (round
+// a * 2^16, an exact scaling, to the nearest even integer 0..4; 4 is the
+// code of 2^-14).  Above, drop 21 of the 23 mantissa bits with RNE and
+// rebias the exponent from 127 to 15 (a carry out of the mantissa bumps the
+// exponent).
+__device__ __forceinline__ uint32_t e5m2_code_abs(float a)
+{
+    const uint32_t sub = (uint32_t)__builtin_rintf(a * 65536.0f);
+    const uint32_t b = as_u32(a);
+    const uint32_t nrm = ((b + 0xFFFFFu + ((b >> 21) & 1u)) >> 21) - (112u << 2);
+    const uint32_t c = (a < 0x1p-14f) ? sub : nrm;
+    return c < 0x7Bu ? c : 0x7Bu;
+}
+
+// Code of one element (FP32 bits of a BF16 value) under scale s.  The
+// quotient is the IEEE FP32 division: unlike the online scales, s need not
+// come from this tensor's amax, so the quotient may lie anywhere.
+template <bool E5M2>
+__device__ __forceinline__ uint32_t delayed_code(uint32_t xb, float s)
+{
+    const float y = as_f32(xb) / s;
+    if (y != y) return 0x7Fu;                          // NaN x, or a NaN / zero scale
+    const uint32_t sign = (as_u32(y) >> 24) & 0x80u;
+    const float a = __builtin_fminf(__builtin_fabsf(y), E5M2 ? 57344.0f : 448.0f);
+    return sign | (E5M2 ? e5m2_code_abs(a) : e4m3_code_abs(a));
+}
+
+template <bool E5M2>
+__device__ __forceinline__ uint2 delayed_code8(const uint32_t xb[8], float s)
+{
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = delayed_code<E5M2>(xb[j], s);
+    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// One workgroup: s from the history, then the slot is cleared for this
+// step's amax (after every thread has read the history).
+__global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ hist, int32_t H, int32_t slot,
+                                                            float fmax, float* __restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x;
+    uint32_t m = 0;
+    for (int i = t; i < H; i += 256) m = max(m, as_u32(hist[i]) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    if (t == 0) {
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        float s;
+        if (m >= 0x7F800000u)
+            s = __builtin_nanf("");
+        else if (m == 0)
+            s = 1.0f;
+        else
+            s = as_f32(m) / fmax;
+        scale[0] = s;
+        hist[slot] = 0.0f;
+    }
+}
+
+template <bool E5M2>
+__global__ __launch_bounds__(256) void quant_delayed_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    const float* __restrict__ scale, uint32_t* __restrict__ amax_slot,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ qT)
+{
+    __shared__ uint32_t red[4];
+    __shared__ __align__(16) uint8_t tbuf[TB][TB + TPAD];
+
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = l & 15, rg = 4 * w + (l >> 4);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    const int64_t col = c0 + 8 * cg;
+    const bool col_ok = col < cols;
+
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t row = r0 + 8 * rg + u;
+        v[u] = (col_ok && row < rows) ? *reinterpret_cast<const uint4*>(x + row * ldx + col)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+    const float s = scale[0];
+
+    // amax of the block (|BF16| bits order like the values, NaN on top)
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max(m, abs_max8_bf16(v[u]));
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+    if (l == 0) red[w] = m;
+
+    if (q) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t row = r0 + 8 * rg + u;
+            uint32_t xb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+            const uint2 codes = delayed_code8<E5M2>(xb, s);
+            if (col_ok && row < rows) *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+        }
+    }
+    if (qT) {
+        // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t xb[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) xb[u] = bf16_elem_bits(v[u], j);
+            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = delayed_code8<E5M2>(xb, s);
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(amax_slot, m << 16);               // FP32 bits of the BF16 amax
+    }
+    if (qT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int trow = 32 * i + (t >> 3), chunk = t & 7;
+            const int64_t orow = c0 + trow;
+            if (orow < cols) {
+                const uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
+                *reinterpret_cast<uint4*>(qT + orow * rows + r0 + 16 * chunk) = d;
+            }
+        }
+    }
+}
+
+} // namespace
+
+hipError_t launch_quant_delayed(const QuantDelayedArgs& a, hipStream_t stream)
+{
+    const bool e5 = a.elem == FGS_ELEM_E5M2;
+    hipLaunchKernelGGL(delayed_scale_kernel, dim3(1), dim3(256), 0, stream,
+                       a.history, a.history_len, a.slot, e5 ? 57344.0f : 448.0f, a.scale);
+    const int64_t nbr = (a.rows + TB - 1) / TB, nbc = (a.cols + TB - 1) / TB;
+    if (nbr > 0 && nbc > 0) {
+        const dim3 grid((unsigned)nbc, (unsigned)nbr);
+        const uint16_t* x = static_cast<const uint16_t*>(a.x);
+        uint32_t* slot = reinterpret_cast<uint32_t*>(a.history + a.slot);
+        if (e5)
+            hipLaunchKernelGGL(quant_delayed_kernel<true>, grid, dim3(256), 0, stream,
+                               x, a.rows, a.cols, a.ldx, a.scale, slot, a.q, a.qT);
+        else
+            hipLaunchKernelGGL(quant_delayed_kernel<false>, grid, dim3(256), 0, stream,
+                               x, a.rows, a.cols, a.ldx, a.scale, slot, a.q, a.qT);
+    }
+    return hipGetLastError();
+}
+
+} // namespace fgs

@@ -14,7 +14,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (ELEM_E2M1, ELEM_E4M3, OUT_BF16, OUT_FP32, ROUND_RNE, ROUND_STOCHASTIC,
+from ._lib import (ELEM_E2M1, ELEM_E4M3, ELEM_E5M2, OUT_BF16, OUT_FP32, ROUND_RNE, ROUND_STOCHASTIC,
                    SCALE_BLOCK_128x128, SCALE_MX32_E8M0, SCALE_NV16_E4M3, SCALE_TENSOR,
                    SCALE_TILE_1x128, FgsOperand, check)
 
@@ -119,6 +119,28 @@ def quantize_blockwise(x: torch.Tensor, mode: str = "tile", rowwise: bool = True
         _ptr(x), rows, cols, ldx, m, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
     return Quantized(q, s, qT, sT, m)
+
+
+def quantize_delayed(x: torch.Tensor, amax_history: torch.Tensor, slot: int, elem: str = "e4m3",
+                     rowwise: bool = True, colwise: bool = False) -> Quantized:
+    """Per-tensor delayed scaling: the scale comes from the max of
+    amax_history (float32 [H] on the GPU, zeros before the first step),
+    this tensor's amax is then stored in amax_history[slot]; codes saturate.
+    elem "e4m3" (448) or "e5m2" (57344, the hybrid recipe's gradients)."""
+    rows, cols, ldx = _bf16_matrix(x)
+    _need_gpu(amax_history)
+    if amax_history.dtype != torch.float32 or amax_history.dim() != 1 or not amax_history.is_contiguous():
+        raise TypeError("amax_history must be a contiguous 1-D float32 tensor")
+    codes = {"e4m3": ELEM_E4M3, "e5m2": ELEM_E5M2}
+    if elem not in codes:
+        raise ValueError("elem must be 'e4m3' or 'e5m2'")
+    dev = x.device
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if rowwise else None
+    qT = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if colwise else None
+    s = torch.empty(1, dtype=torch.float32, device=dev)
+    check(_lib.load().fgs_quantize_delayed(_ptr(x), rows, cols, ldx, codes[elem], _ptr(amax_history),
+                                           amax_history.numel(), slot, _ptr(q), _ptr(qT), _ptr(s), _stream()))
+    return Quantized(q, s, qT, None, SCALE_TENSOR, codes[elem])
 
 
 def quantize_mx(x: torch.Tensor, rowwise: bool = True, colwise: bool = False) -> Quantized:

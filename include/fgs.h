@@ -25,7 +25,8 @@
  *  - Matrices are row-major.  BF16 inputs are raw 16-bit patterns.  Every
  *    GEMM operand is K-contiguous ("NT"): C[m][n] = sum_k A[m][k] * B[n][k].
  *  - Element codes: E4M3 = OCP E4M3FN byte (0x7E = 448, 0x7F/0xFF NaN);
- *    E2M1 = OCP FP4 nibble, two per byte, element 2j in the low nibble.
+ *    E5M2 = OCP E5M2 byte (0x7B = 57344); E2M1 = OCP FP4 nibble, two per
+ *    byte, element 2j in the low nibble.
  *  - Quantization is online: every scale comes from the amax of the data
  *    being quantized in this call.  FP32-scaled blocks use
  *    scale = fl32(amax / 448) and code = E4M3_RNE_SAT(fl32(x / scale));
@@ -58,7 +59,9 @@ typedef enum {
 /* Element formats of a quantized operand. */
 typedef enum {
     FGS_ELEM_E4M3 = 0, /* one byte per element */
-    FGS_ELEM_E2M1 = 1  /* two elements per byte */
+    FGS_ELEM_E2M1 = 1, /* two elements per byte */
+    FGS_ELEM_E5M2 = 2  /* one byte per element: OCP E5M2 (bias 15, 0x7B =
+                          57344, 0x7C Inf, 0x7D-0x7F NaN); TENSOR scale only */
 } fgs_elem;
 
 /*
@@ -118,6 +121,33 @@ int fgs_quantize_blockwise(const void *x, int64_t rows, int64_t cols, int64_t ld
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fgs_quantize_delayed -- per-tensor DELAYED scaling to E4M3 or E5M2: the
+ *   scale comes from the amaxes of earlier steps, the recipe that online
+ *   scaling replaces, and E5M2 gives the hybrid recipe (E4M3 forward, E5M2
+ *   gradients) that the single E4M3 format replaces.   [DSV3] "Online
+ *   quantization", "Unified E4M3 format".
+ * elem     FGS_ELEM_E4M3 (fmax 448) or FGS_ELEM_E5M2 (fmax 57344).
+ * amax_history  DEVICE FP32 [history_len] (1 <= history_len <= 65536),
+ *   owned by the caller, all zeros before the first step.  The call reads
+ *   every entry: hmax = NaN-propagating max of |entries|; scale s = 1 if
+ *   hmax == 0, NaN if hmax is not finite, else fl32(hmax / fmax).  Then it
+ *   stores this tensor's amax (NaN-propagating max |x|) into
+ *   amax_history[slot] (0 <= slot < history_len; a rolling window passes
+ *   slot = step % history_len).  rows or cols 0 record 0.
+ * code = ENC_RNE_SAT(fl32(x / s)): RNE to the nearest code, ties to even,
+ *   |x / s| beyond fmax (and +-Inf) saturating to +-fmax, the sign kept
+ *   (-0 -> 0x80), NaN (or a NaN scale) -> 0x7F.
+ * One read of x (the scale is known before the data).
+ * Row-wise (NULL q skips it): q [rows x cols].  Column-wise (NULL qT skips
+ *   it; needs rows % 128 == 0): qT [cols x rows], the byte transpose (one
+ *   scale is transpose-invariant).  scale: DEVICE FP32 [1], the s used (both
+ *   outputs' FGS_SCALE_TENSOR scale).
+ */
+int fgs_quantize_delayed(const void *x, int64_t rows, int64_t cols, int64_t ldx, int elem,
+                         float *amax_history, int32_t history_len, int32_t slot,
+                         uint8_t *q, uint8_t *qT, float *scale, void *stream);
+
+/*
  * fgs_quantize_mx -- MXFP8: E4M3 codes with one E8M0 scale 2^e per 32
  *   contiguous elements, e the smallest integer with amax <= 448 * 2^e
  *   (clamped to [-127, 127]); code = E4M3_RNE_SAT(x * 2^-e).   [NEMO] MXFP8.
@@ -166,6 +196,10 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *     e - E >= -124), BF16 MFMA with FP32 accumulation over all of K, then
  *     2^(E_A + E_B) applied by exponent arithmetic; a NaN scale byte makes
  *     its A row or B column of C NaN;
+ *   E4M3 or E5M2 on each side with TENSOR on both (the delayed-scaling
+ *     recipes; E5M2 gradients against E4M3 weights or activations): every
+ *     E5M2 code is exactly the FP16 number with the code as its upper byte,
+ *     FP16 MFMA with FP32 accumulation over all of K, sA * sB at the end;
  *   E2M1 with NV16_E4M3 on both: each code times its E4M3 block scale,
  *     exact in FP16, FP16 MFMA with FP32 accumulation over all of K, the
  *     two tensor scales applied at the end.

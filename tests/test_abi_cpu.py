@@ -142,6 +142,34 @@ def test_grouped_validation(lib):
     assert g(r(a), r(b), FAKE, 0, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_OK          # no groups
 
 
+def test_quantize_delayed_validation(lib):
+    S = NULL
+    f = lib.fgs_quantize_delayed
+
+    def call(elem=0, rows=256, cols=256, hist=FAKE, H=4, slot=1, q=FAKE, qT=FAKE, sc=FAKE):
+        return f(FAKE, rows, cols, cols, elem, hist, H, slot, q, qT, sc, S)
+    assert call(elem=1) == _lib.FGS_ERR_INVALID_ARG                 # E2M1 is not an FP8 format
+    assert call(hist=NULL) == _lib.FGS_ERR_INVALID_ARG
+    assert call(H=0, slot=0) == _lib.FGS_ERR_INVALID_ARG
+    assert call(slot=4) == _lib.FGS_ERR_INVALID_ARG
+    assert call(slot=-1) == _lib.FGS_ERR_INVALID_ARG
+    assert call(sc=NULL) == _lib.FGS_ERR_INVALID_ARG
+    assert call(rows=200) == _lib.FGS_ERR_UNSUPPORTED                # column-wise needs rows % 128
+    assert call(rows=-1) == _lib.FGS_ERR_INVALID_ARG
+
+
+def test_gemm_e5m2_operands_need_tensor_scales(lib):
+    S = NULL
+    g = lib.fgs_gemm_block_scaled
+    r = ctypes.byref
+    a5, b4 = _op(elem=2, mode=0), _op(elem=0, mode=0)
+    assert g(r(a5), r(_op(elem=2, mode=1)), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert b"TENSOR" in lib.fgs_last_error()
+    assert g(r(_op(elem=2, mode=2)), r(b4), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a5), r(_op(elem=1, mode=4)), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(_op(elem=7, mode=0)), r(b4), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+
+
 def test_grouped_colwise_validation(lib):
     S = NULL
     q = lib.fgs_quantize_grouped_colwise
