@@ -22,7 +22,9 @@ HBM before timing starts.
 
 The other workloads of the path are measured in the same run and reported
 under "workloads" (per-kernel throughput against the roofline): the tiny
-blockwise GEMM, the DeepSeek-V3 MoE grouped GEMMs (forward, dgrad and wgrad), MXFP8 at Llama-3.1-405B
+blockwise GEMM, the Llama-3-8B layers in the hybrid delayed-scaling recipe
+(per-tensor scales from an amax history, E5M2 gradients), the DeepSeek-V3
+MoE grouped GEMMs (forward, dgrad and wgrad), MXFP8 at Llama-3.1-405B
 shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes.
 
 Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
@@ -235,6 +237,56 @@ class Llama8B:
                     qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(rname, name, "dx")]))
                 tm.run("gemm", lab + "/wgrad", f, lambda: fgs.gemm_block_scaled(
                     qdy.colwise(), qx.colwise(), torch.float32, out=o[(rname, name, "dw")]))
+
+
+# --------------------------------------------------------------------------
+# Llama-3-8B linear layers in the hybrid delayed-scaling recipe: per-tensor
+# scales from a 16-step amax history, X and W in E4M3, dY in E5M2; one pass
+# over each tensor (no amax pass first)
+# --------------------------------------------------------------------------
+class Hybrid8B:
+    name = "llama3_8b_hybrid_delayed"
+    HISTORY = 16
+
+    def __init__(self, torch, fgs, synth):
+        self.torch, self.fgs = torch, fgs
+        self.x, self.w, self.dy, self.out, self.hist = {}, {}, {}, {}, {}
+        for i, (name, K, N) in enumerate(LLAMA8B_LAYERS):
+            if K not in self.x:
+                self.x[K] = gpu_normal(torch, (LLAMA8B_M, K), 300 + i, outlier_cols=synth.outlier_channels(K, 0))
+            self.w[name] = gpu_normal(torch, (N, K), 310 + i, sigma=0.02)
+            if N not in self.dy:
+                self.dy[N] = gpu_t3(torch, (LLAMA8B_M, N), 320 + i)
+            for role in ("x", "w", "dy"):
+                self.hist[(name, role)] = torch.zeros(self.HISTORY, dtype=torch.float32, device="cuda")
+            self.out[(name, "y")] = torch.empty((LLAMA8B_M, N), dtype=torch.bfloat16, device="cuda")
+            self.out[(name, "dx")] = torch.empty((LLAMA8B_M, K), dtype=torch.bfloat16, device="cuda")
+            self.out[(name, "dw")] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        self.step_no = 0
+        torch.cuda.synchronize()
+
+    def flops(self):
+        return sum(3 * 2.0 * LLAMA8B_M * N * K for _, K, N in LLAMA8B_LAYERS)
+
+    def step(self, tm):
+        torch, fgs = self.torch, self.fgs
+        slot = self.step_no % self.HISTORY
+        self.step_no += 1
+        for name, K, N in LLAMA8B_LAYERS:
+            X, W, dY, h, o = self.x[K], self.w[name], self.dy[N], self.hist, self.out
+            qx = tm.run("quant", name + "/X", 4.0 * LLAMA8B_M * K, lambda: fgs.quantize_delayed(
+                X, h[(name, "x")], slot, "e4m3", rowwise=True, colwise=True))
+            qw = tm.run("quant", name + "/W", 4.0 * N * K, lambda: fgs.quantize_delayed(
+                W, h[(name, "w")], slot, "e4m3", rowwise=True, colwise=True))
+            qdy = tm.run("quant", name + "/dY", 4.0 * LLAMA8B_M * N, lambda: fgs.quantize_delayed(
+                dY, h[(name, "dy")], slot, "e5m2", rowwise=True, colwise=True))
+            f = 2.0 * LLAMA8B_M * N * K
+            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
+                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(name, "y")]))
+            tm.run("gemm", name + "/dgrad", f, lambda: fgs.gemm_block_scaled(
+                qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(name, "dx")]))
+            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
+                qdy.colwise(), qx.colwise(), torch.float32, out=o[(name, "dw")]))
 
 
 # --------------------------------------------------------------------------
@@ -469,7 +521,8 @@ class NV12B:
                 qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")]))
 
 
-WORKLOADS = {"llama3_8b": Llama8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B, "nv12b": NV12B}
+WORKLOADS = {"llama3_8b": Llama8B, "hybrid8b": Hybrid8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B,
+             "nv12b": NV12B}
 
 
 def measure(torch, wl, steps, warmup):
@@ -656,7 +709,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="llama3_8b,tiny,moe,mx405b,nv12b",
+    ap.add_argument("--workloads", default="llama3_8b,hybrid8b,tiny,moe,mx405b,nv12b",
                     help="comma list of " + ",".join(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -143,25 +143,32 @@ __global__ __launch_bounds__(256) void quant_delayed_kernel(
     for (int d = 32; d > 0; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
     if (l == 0) red[w] = m;
 
+    // the codes of the thread's 8 x 8 values, computed once: row u is c[u]
+    // (byte j = column j); the column-wise output is their byte transpose
+    uint2 c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        uint32_t xb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+        c[u] = delayed_code8<E5M2>(xb, s);
+    }
     if (q) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t row = r0 + 8 * rg + u;
-            uint32_t xb[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
-            const uint2 codes = delayed_code8<E5M2>(xb, s);
-            if (col_ok && row < rows) *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+            if (col_ok && row < rows) *reinterpret_cast<uint2*>(q + row * cols + col) = c[u];
         }
     }
     if (qT) {
-        // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+        // column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint32_t xb[8];
+            uint32_t b[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) xb[u] = bf16_elem_bits(v[u], j);
-            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = delayed_code8<E5M2>(xb, s);
+            for (int u = 0; u < 8; ++u) b[u] = (((j < 4) ? c[u].x : c[u].y) >> (8 * (j & 3))) & 0xFFu;
+            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) =
+                make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
         }
     }
     __syncthreads();
