@@ -1,0 +1,132 @@
+"""The autograd Linear layer over the library's kernels: its forward,
+dgrad and wgrad products match the oracle on the oracle's quantization of
+the same BF16 operands (per recipe), and a toy teacher-student regression
+trains under every recipe to a loss close to the FP32 one.
+
+"Accelerating FP8 training performance with the NVIDIA NeMo framework"
+compares per-tensor and block-wise scaling in training; "Can you explain
+the role of FP8 precision in DeepSeek-V3 training" ("Fine-grained
+quantization", "Online quantization", "Unified E4M3 format") gives the
+block-wise recipe and names the delayed / hybrid one it replaces.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fine_grained_scaled_amd import synth
+
+from _helpers import gemm_within_bf16_bound, gemm_within_fp32_bound
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def fgs():
+    import fine_grained_scaled_amd as m
+    return m
+
+
+def _bits(t):
+    return t.detach().to(torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _deq(bits, recipe, role, colwise, hist):
+    if recipe == "delayed":
+        q, s, _ = oracle.quant_delayed(bits, "e5m2" if role == "dy" else "e4m3", hist, colwise=colwise)
+        return oracle.dequant_tensor(q, s, "e5m2" if role == "dy" else "e4m3")
+    mode = "tensor" if recipe == "per_tensor" else ("block" if role == "w" else "tile")
+    q, s = oracle.quant_e4m3(bits, mode, colwise=colwise)
+    return oracle.dequant_e4m3(q, s, mode)
+
+
+def _amax(bits):
+    return F32(np.abs(oracle.bf16_bits_to_f32(bits)).max())
+
+
+@pytest.mark.parametrize("recipe", ["blockwise", "per_tensor", "delayed"])
+def test_linear_products_match_oracle(fgs, recipe):
+    """Two steps (the second reads the delayed histories the first wrote):
+    Y (BF16), dX (BF16) and dW (FP32) of the second step against the oracle."""
+    T, K, N = 256, 384, 256
+    layer = fgs.Linear(K, N, recipe=recipe, device="cuda")
+    hist = {"x": np.zeros(16, F32), "w": np.zeros(16, F32), "dy": np.zeros(16, F32)}
+    for step in range(2):
+        x = synth.to_torch_bf16(synth.activations(T, K, seed=10 + step)).cuda().requires_grad_(True)
+        dy = synth.to_torch_bf16(synth.gradients(T, N, seed=20 + step)).cuda()
+        y = layer(x)
+        y.backward(dy)
+        torch.cuda.synchronize()
+        xb, wb, dyb = _bits(x), _bits(layer.weight), _bits(dy)
+        if step == 1:
+            yr, ys = oracle.gemm_ref(_deq(xb, recipe, "x", False, hist["x"]), _deq(wb, recipe, "w", False, hist["w"]))
+            ok, nbad = gemm_within_bf16_bound(y.detach().float().cpu().numpy(), yr, ys)
+            assert ok, f"Y: {nbad} outside one BF16 ulp"
+            dxr, dxs = oracle.gemm_ref(_deq(dyb, recipe, "dy", False, hist["dy"]),
+                                       _deq(wb, recipe, "w", True, hist["w"]))
+            ok, nbad = gemm_within_bf16_bound(x.grad.float().cpu().numpy(), dxr, dxs)
+            assert ok, f"dX: {nbad} outside one BF16 ulp"
+            dwr, dws = oracle.gemm_ref(_deq(dyb, recipe, "dy", True, hist["dy"]),
+                                       _deq(xb, recipe, "x", True, hist["x"]))
+            ok, worst = gemm_within_fp32_bound(layer.weight.grad.cpu().numpy().astype(np.float64), dwr, dws)
+            assert ok, f"dW: worst err/bound {worst}"
+            assert layer.weight.grad.dtype == torch.float32
+        for k, b in (("x", xb), ("w", wb), ("dy", dyb)):
+            hist[k][step] = _amax(b)
+        layer.weight.grad = None
+
+
+def test_linear_rejects_unaligned_shapes(fgs):
+    layer = fgs.Linear(256, 256, device="cuda")
+    with pytest.raises(ValueError):
+        layer(torch.zeros((100, 256), dtype=torch.bfloat16, device="cuda"))
+
+
+def _train(fgs, recipe, steps=120, T=1024, D=256, H=512, seed=0):
+    """Student MLP D -> H -> D (GELU) regressing a fixed random teacher on
+    Gaussian inputs; Adam, MSE.  recipe None: FP32 torch layers."""
+    torch.manual_seed(seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    t1 = torch.randn(H, D, device="cuda", generator=g) * D ** -0.5
+    t2 = torch.randn(D, H, device="cuda", generator=g) * H ** -0.5
+    if recipe is None:
+        l1 = torch.nn.Linear(D, H, bias=False, device="cuda")
+        l2 = torch.nn.Linear(H, D, bias=False, device="cuda")
+        torch.nn.init.normal_(l1.weight, std=D ** -0.5)
+        torch.nn.init.normal_(l2.weight, std=H ** -0.5)
+    else:
+        l1 = fgs.Linear(D, H, recipe=recipe, device="cuda")
+        l2 = fgs.Linear(H, D, recipe=recipe, device="cuda")
+    opt = torch.optim.Adam(list(l1.parameters()) + list(l2.parameters()), lr=2e-3)
+    losses = []
+    for s in range(steps):
+        x = torch.randn(T, D, device="cuda", generator=g)
+        with torch.no_grad():
+            target = torch.nn.functional.gelu(x @ t1.t().contiguous()) @ t2.t().contiguous()
+        h = torch.nn.functional.gelu(l1(x).float())
+        out = l2(h).float()
+        loss = torch.mean((out - target) ** 2)
+        opt.zero_grad()
+        loss.backward()
+        opt.step()
+        losses.append(float(loss.detach()))
+    return np.array(losses)
+
+
+def test_toy_training_tracks_fp32(fgs):
+    """Every recipe learns (the loss falls by 4x in 120 steps; FP32: ~7x)
+    and ends within 25% of the FP32 run's final loss (mean of the last 10
+    steps)."""
+    ref = _train(fgs, None)
+    tail = lambda a: float(a[-10:].mean())
+    print(f"fp32: first {ref[0]:.4f} last-10 {tail(ref):.4f}")
+    assert tail(ref) < ref[0] / 4
+    for recipe in ("blockwise", "per_tensor", "delayed"):
+        got = _train(fgs, recipe)
+        print(f"{recipe}: first {got[0]:.4f} last-10 {tail(got):.4f}")
+        assert np.all(np.isfinite(got)), recipe
+        assert tail(got) < got[0] / 4, (recipe, got[0], tail(got))
+        assert tail(got) < 1.25 * tail(ref), (recipe, tail(got), tail(ref))
