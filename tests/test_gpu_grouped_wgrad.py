@@ -259,3 +259,49 @@ def test_grouped_wgrad_deepseek_moe_sampled(fgs, M, N, out):
         else:
             ok, nbad = gemm_within_bf16_bound(got, cref, sref)
             assert ok, f"expert {g}: {nbad} BF16 outputs outside one ulp"
+
+
+# ------------------------------------------- offsets out of order or range --
+def test_invalid_offsets_stay_in_bounds(fgs):
+    """Offsets that decrease or leave [0, T]: groups with such bounds are
+    empty (no codes; dW = 0), overlapping valid groups give unspecified
+    values, and no write lands outside the buffers (guard bytes around each
+    output stay as filled)."""
+    lib = _lib.load()
+    T, C, M = 719, 256, 256
+    offs = np.array([0, 500, 100, 719, 600, 719, 800], dtype=np.int32)   # groups 1, 3 decrease; 5 leaves [0, T]
+    G = len(offs) - 1
+    nb = T // 128 + G
+    x = synth.to_torch_bf16(synth.activations(T, C, seed=81)).cuda()
+    off_t = torch.from_numpy(offs).cuda()
+    guard = 4096
+    qbuf = torch.full((C * 128 * nb + 2 * guard,), SENT_CODE, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((nb * C + 2 * guard,), SENT_SCALE, dtype=torch.float32, device="cuda")
+    qT = qbuf[guard:guard + C * 128 * nb]
+    sT = sbuf[guard:guard + nb * C]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    _lib.check(lib.fgs_quantize_grouped_colwise(_ptr(x), T, C, C, None, 0, _ptr(off_t), G, None, None,
+                                                _ptr(qT), 128 * nb, _ptr(sT), stream))
+    torch.cuda.synchronize()
+    q = qbuf.cpu().numpy()
+    s = sbuf.cpu().numpy()
+    assert np.all(q[:guard] == SENT_CODE) and np.all(q[-guard:] == SENT_CODE)
+    assert np.all(s[:guard] == SENT_SCALE) and np.all(s[-guard:] == SENT_SCALE)
+    # group 4 ([600, 719)) alone owns block 600 // 128 + 4 = 8: exact codes there
+    qo, so = oracle.quant_e4m3_grouped_colwise(synth.activations(T, C, seed=81), [600, 719])[0]
+    qmat = q[guard:guard + C * 128 * nb].reshape(C, 128 * nb)
+    assert np.array_equal(qmat[:, 128 * 8:128 * 8 + 119], qo)
+
+    # the wgrad GEMM over the same offsets: empty groups exactly zero, no stray writes
+    qa = fgs.quantize_grouped_colwise(synth.to_torch_bf16(synth.gradients(T, M, seed=82)).cuda(), off_t)
+    qb = fgs.Operand(qT.view(C, 128 * nb), sT.view(nb, C), fgs.SCALE_TILE_1x128)
+    cbuf = torch.full((G * M * C + 2 * guard,), 3.0, dtype=torch.float32, device="cuda")
+    c = cbuf[guard:guard + G * M * C].view(G, M, C)
+    fgs.grouped_wgrad_block_scaled(qa.colwise(), qb, off_t, T, torch.float32, out=c)
+    torch.cuda.synchronize()
+    cb = cbuf.cpu().numpy()
+    assert np.all(cb[:guard] == 3.0) and np.all(cb[-guard:] == 3.0)
+    cc = cb[guard:guard + G * M * C].reshape(G, M, C)
+    for g in (1, 3, 5):
+        assert not cc[g].any(), g
+    assert np.all(np.isfinite(cc))
