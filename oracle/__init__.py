@@ -72,6 +72,9 @@ def _load():
     lib.orc_e5m2_encode.argtypes = [ctypes.c_float]
     lib.orc_e5m2_encode_array.argtypes = [P, I64, P]
     lib.orc_quant_delayed.argtypes = [P, I64, ctypes.c_int, P, I64, P, P, P]
+    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.orc_f64_to_bf16_array.argtypes = [P, I64, P]
     lib.orc_e2m1_decode.restype = ctypes.c_double
     lib.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e8m0_decode.restype = ctypes.c_double
@@ -317,6 +320,29 @@ def quant_nvfp4_rows(values_f32: np.ndarray, tensor_scale, stochastic: bool = Fa
     _load().orc_quant_nvfp4_blocks(_ptr(v), rows, cols, float(tensor_scale), int(stochastic),
                                    sr_seed & (2**64 - 1), idx_base, idx_rs, idx_cs, _ptr(q), _ptr(scales))
     return q, scales
+
+
+def f64_to_bf16(v) -> np.ndarray:
+    """BF16 bits of FP64 values, rounded once to nearest even."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().orc_f64_to_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def swiglu_f64(gate_up, inter: int) -> np.ndarray:
+    """The SwiGLU activation between the two expert GEMMs, exact up to FP64:
+    h = silu(g) * u = g / (1 + exp(-g)) * u, with [g | u] the two halves of
+    the gate/up GEMM's BF16 output [T x 2*inter]."""
+    v = bf16_bits_to_f32(_as_bf16_bits(gate_up)).astype(np.float64)
+    g, u = v[:, :inter], v[:, inter:2 * inter]
+    with np.errstate(over="ignore", invalid="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def swiglu_bf16(gate_up, inter: int) -> np.ndarray:
+    """BF16 bits of the SwiGLU activation (one rounding of swiglu_f64)."""
+    return f64_to_bf16(swiglu_f64(gate_up, inter))
 
 
 def gather_rows(x, row_index):

@@ -556,6 +556,49 @@ void orc_e5m2_encode_array(const float *y, int64_t n, uint8_t *out)
         out[i] = orc_e5m2_encode(y[i]);
 }
 
+/*
+ * FP64 -> BF16 with one rounding (RNE): BF16 keeps 8 significant bits and
+ * FP32's exponent range (subnormal step 2^-133); overflow past the largest
+ * finite value by half an ulp or more gives Inf.  Used for the SwiGLU
+ * activation, whose exact value is rounded to the BF16 the next GEMM's
+ * quantizer reads.
+ */
+uint16_t orc_f64_to_bf16(double v)
+{
+    uint16_t sign;
+    double a, q, r;
+    int e;
+    float f;
+    uint32_t b;
+
+    if (isnan(v))
+        return 0x7FC0;
+    sign = signbit(v) ? 0x8000 : 0x0000;
+    a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    frexp(a, &e);                  /* a in [2^(e-1), 2^e) */
+    e -= 1;
+    if (e < -126)
+        e = -126;                  /* subnormal grid */
+    q = ldexp(1.0, e - 7);         /* spacing of BF16 numbers at a */
+    r = rint(a / q) * q;           /* a / q is exact; rint rounds half to even */
+    if (r >= 0x1p128)
+        return sign | 0x7F80;
+    f = (float)r;                  /* exact: r has <= 8 significant bits */
+    memcpy(&b, &f, sizeof b);
+    return sign | (uint16_t)(b >> 16);
+}
+
+void orc_f64_to_bf16_array(const double *v, int64_t n, uint16_t *out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = orc_f64_to_bf16(v[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Array helpers for the tests (element-wise loops over the codecs).    */
 /* ------------------------------------------------------------------ */
