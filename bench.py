@@ -314,8 +314,9 @@ class Tiny:
 
 # --------------------------------------------------------------------------
 # DeepSeek-V3 MoE: grouped GEMMs over 256 experts, Zipf(1.1) token counts:
-# gate/up and down forward, their dgrad on the transposed expert weights,
-# and their wgrad (one dW per expert, contraction over its tokens)
+# gate/up and down forward (the SwiGLU between them fused into the down
+# projection's quantizer), their dgrad on the transposed expert weights, and
+# their wgrad (one dW per expert, contraction over its tokens)
 # --------------------------------------------------------------------------
 class MoE:
     name = "deepseek_v3_moe_grouped"
@@ -335,7 +336,6 @@ class MoE:
         gen = torch.Generator(device="cuda")
         gen.manual_seed(107)
         self.route = torch.randint(0, MOE_SOURCE_TOKENS, (T,), generator=gen, device="cuda", dtype=torch.int32)
-        self.a2 = gpu_normal(torch, (T, I), 102, outlier_cols=synth.outlier_channels(I, 0))
         self.g1 = gpu_t3(torch, (T, 2 * I), 105)             # dY of gate+up
         self.g2 = gpu_t3(torch, (T, H), 106)                 # dY of down
         # expert weights, quantized once (128x128 blocks never straddle experts):
@@ -421,7 +421,9 @@ class MoE:
             self.x_tok, off, rowwise=True, row_index=self.route))
         tm.run("gemm", "gate_up", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
             qa1.rowwise(), self.w1, off, 2 * I, torch.bfloat16, out=self.y1))
-        qa2 = tm.run("quant", "A2", e4m3_bytes(T, I, "tile", 2), lambda: grouped(self.a2))
+        # SwiGLU of the gate/up output fused into the down projection's quantizer
+        a2_bytes = 2.0 * T * 2 * I + e4m3_bytes(T, I, "tile", 2) - 2.0 * T * I
+        qa2 = tm.run("quant", "SwiGLU+A2", a2_bytes, lambda: fgs.swiglu_quantize_grouped(self.y1, off))
         tm.run("gemm", "down", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
             qa2.rowwise(), self.w2, off, H, torch.bfloat16, out=self.y2))
         # dgrad: dZ = dY2 W2 (2048 outputs, contraction over 7168), dH = dY1 W1

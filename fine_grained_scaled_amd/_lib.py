@@ -23,6 +23,7 @@ EXPORTS = (
     "fgs_grouped_gemm_block_scaled",
     "fgs_quantize_grouped_colwise",
     "fgs_grouped_colwise_blocks",
+    "fgs_swiglu_quantize_grouped",
     "fgs_grouped_wgrad_block_scaled",
     "fgs_gemm_tile_policy",
     "fgs_workspace_bytes",
@@ -70,6 +71,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_quantize_grouped_colwise.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_int32, P, P, P, I64, P, P]
     lib.fgs_grouped_colwise_blocks.argtypes = [I64, ctypes.c_int32]
+    lib.fgs_swiglu_quantize_grouped.argtypes = [P, I64, I64, I64, P, ctypes.c_int32, P, P, P, P, I64, P, P]
     lib.fgs_grouped_colwise_blocks.restype = I64
     lib.fgs_grouped_wgrad_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_tile_policy.argtypes = [ctypes.c_int]
@@ -80,7 +82,8 @@ def load() -> ctypes.CDLL:
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
                  "fgs_gemm_block_scaled", "fgs_grouped_gemm_block_scaled",
-                 "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled"):
+                 "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",
+                 "fgs_swiglu_quantize_grouped"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -323,6 +323,40 @@ int fgs_quantize_grouped_colwise(const void* x, int64_t rows, int64_t cols, int6
                       "quantize_grouped_colwise launch");
 }
 
+int fgs_swiglu_quantize_grouped(const void* gate_up, int64_t rows, int64_t inter, int64_t ld,
+                                const int32_t* group_offsets, int32_t G, uint16_t* h,
+                                uint8_t* q, float* scales, uint8_t* qT, int64_t ldqT, float* scalesT,
+                                void* stream)
+{
+    if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
+    if (inter < 0) return fail(FGS_ERR_INVALID_ARG, "inter must be >= 0");
+    int st = check_bf16_source(gate_up, rows, 2 * inter, ld);
+    if (st != FGS_OK) return st;
+    if (inter % 8) return fail(FGS_ERR_UNSUPPORTED, "inter must be a multiple of 8 (16-byte halves)");
+    if (rows == 0 || inter == 0 || G == 0 || (!q && !qT && !h)) return ok();
+    if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
+    if (h && !aligned(h, 16)) return fail(FGS_ERR_UNSUPPORTED, "h must be 16-byte aligned");
+    if (qT && !scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
+    const int64_t blocks = fgs_grouped_colwise_blocks(rows, G);
+    if (blocks > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many token blocks");
+    if ((inter + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "inter too large (%lld)", (long long)inter);
+    if (qT) {
+        if (ldqT < 128 * blocks)
+            return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,
+                        (long long)(128 * blocks));
+        if (ldqT % 16) return fail(FGS_ERR_UNSUPPORTED, "ldqT must be a multiple of 16");
+        if (!aligned(qT, 16) || !aligned(scalesT, 4)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
+    }
+    if (q) {
+        if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
+        if (inter % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs inter %% 128 == 0 (inter = %lld)", (long long)inter);
+        if (!aligned(q, 16) || !aligned(scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "q must be 16-byte and scales 4-byte aligned");
+    }
+    fgs::QuantGroupedArgs a{gate_up, rows, inter, ld, nullptr, 0, group_offsets, G, q, scales, qT, ldqT, scalesT, 1, h};
+    return hip_status(fgs::launch_quant_grouped_colwise(a, static_cast<hipStream_t>(stream)),
+                      "swiglu_quantize_grouped launch");
+}
+
 int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
                                    int32_t G, int64_t total_T, int64_t M, int64_t N,
                                    void* C, int64_t ldc, int out_dtype, void* stream)

@@ -36,6 +36,8 @@ struct QuantGroupedArgs {
     uint8_t* qT;
     int64_t ldqT;
     float* scalesT;
+    int swiglu;                     // x is a gate/up output [rows x 2*cols]; quantize its SwiGLU
+    uint16_t* h_out;                // swiglu: optional BF16 activation [rows x cols]
 };
 hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t stream);
 

@@ -74,6 +74,29 @@ __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
     return quant8_vals(xb, b);
 }
 
+// SwiGLU of one BF16 (gate, up) pair: h = silu(g) * u in FP32, rounded to
+// BF16 (nearest even, by the hardware converter).  The logistic factor is
+// formed from exp(-|g|) <= 1 on both sides of zero, so it never overflows:
+// 1 / (1 + e) for g >= 0, e / (1 + e) for g < 0.
+__device__ __forceinline__ uint32_t swiglu_bf16_bits(uint32_t gb, uint32_t ub)
+{
+    const float g = as_f32(gb), u = as_f32(ub);
+    const float e = expf(-__builtin_fabsf(g));
+    const float d = 1.0f + e;
+    const float sig = (g >= 0.0f) ? 1.0f / d : e / d;
+    const float h = (g * sig) * u;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)h);
+}
+
+// Eight SwiGLU activations from the gate and up vectors of one row.
+__device__ __forceinline__ uint4 swiglu8(const uint4& g, const uint4& u)
+{
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = swiglu_bf16_bits(val_bits(g, j), val_bits(u, j));
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
 // GROUPED (TILE mode only): the rows are split into groups (MoE experts,
 // rows offsets[g] .. offsets[g+1]-1), and the column-wise tiles run along the
 // rows of one group only.  Group g's transposed codes take the 128-column
@@ -85,16 +108,21 @@ __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
 // qT, no effect on the amax).  With row_index, logical row t is source row
 // row_index[t] of x (the MoE dispatch gather, fused so the permuted BF16
 // copy is never written); an index outside [0, src_rows) reads as zeros.
-template <int MODE, bool GROUPED>   // MODE: FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
+// SWIGLU (GROUPED only): x holds a gate/up GEMM output [rows x 2*cols] and
+// the quantized matrix is its SwiGLU activation, computed on the load (with
+// its BF16 values optionally stored to h_out [rows x cols]), so the
+// activation is never written and read back before the down projection.
+template <int MODE, bool GROUPED, bool SWIGLU = false>   // MODE: FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, float* __restrict__ scales,
     uint8_t* __restrict__ qT, float* __restrict__ scalesT,
     const uint32_t* __restrict__ tensor_amax,
     const int32_t* __restrict__ offsets, int32_t G, int64_t ldqT,
-    const int32_t* __restrict__ row_index, int64_t src_rows)
+    const int32_t* __restrict__ row_index, int64_t src_rows, uint16_t* __restrict__ h_out)
 {
     static_assert(!GROUPED || MODE == FGS_SCALE_TILE_1x128, "groups take 1x128 tiles");
+    static_assert(!SWIGLU || GROUPED, "the SwiGLU prologue belongs to the grouped quantizer");
     __shared__ uint32_t red[4][TB];
     __shared__ __align__(16) uint8_t tbuf[TB][TB + TPAD];
     __shared__ int s_group;
@@ -148,10 +176,20 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
                 ok = src >= 0 && src < src_rows;
             }
         }
-        if (ok)
-            v[u] = *reinterpret_cast<const uint4*>(x + src * ldx + col);
-        else
-            v[u] = make_uint4(0, 0, 0, 0);
+        if constexpr (SWIGLU) {
+            if (ok) {
+                const uint16_t* xr = x + src * ldx + col;
+                v[u] = swiglu8(*reinterpret_cast<const uint4*>(xr), *reinterpret_cast<const uint4*>(xr + cols));
+                if (h_out) *reinterpret_cast<uint4*>(h_out + row * cols + col) = v[u];
+            } else {
+                v[u] = make_uint4(0, 0, 0, 0);
+            }
+        } else {
+            if (ok)
+                v[u] = *reinterpret_cast<const uint4*>(x + src * ldx + col);
+            else
+                v[u] = make_uint4(0, 0, 0, 0);
+        }
     }
 
     // ---------------- shared (block / tensor) scale --------------------
@@ -317,11 +355,11 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
     switch (a.mode) {
     case FGS_SCALE_TILE_1x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     case FGS_SCALE_BLOCK_128x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     case FGS_SCALE_TENSOR: {
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
@@ -331,7 +369,7 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
         hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
                            x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TENSOR, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0, nullptr, 0);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     }
     default:
@@ -345,10 +383,16 @@ hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t s
     // every group owns at most floor(rows / 128) + G blocks in total
     const int64_t nblk = a.rows / TB + a.G, nbc = (a.cols + TB - 1) / TB;
     if (a.G == 0 || a.rows == 0 || nbc == 0) return hipSuccess;
-    hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true>), dim3((unsigned)nblk, (unsigned)nbc),
-                       dim3(256), 0, stream, static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ldx,
-                       a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets, a.G, a.ldqT,
-                       a.row_index, a.src_rows);
+    const dim3 grid((unsigned)nblk, (unsigned)nbc);
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    if (a.swiglu)
+        hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true, true>), grid, dim3(256), 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets,
+                           a.G, a.ldqT, a.row_index, a.src_rows, a.h_out);
+    else
+        hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true>), grid, dim3(256), 0, stream,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets,
+                           a.G, a.ldqT, a.row_index, a.src_rows, nullptr);
     return hipGetLastError();
 }
 

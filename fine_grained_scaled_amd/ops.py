@@ -319,6 +319,39 @@ def quantize_grouped_colwise(x: torch.Tensor, group_offsets: torch.Tensor,
     return Quantized(q, s, qT, sT, SCALE_TILE_1x128)
 
 
+def swiglu_quantize_grouped(gate_up: torch.Tensor, group_offsets: torch.Tensor, rowwise: bool = True,
+                            colwise: bool = True, return_h: bool = False):
+    """SwiGLU of a gate/up GEMM output [T x 2*I] (gate | up halves) fused
+    into the grouped 1x128 quantizer: the row-wise codes feed the down
+    projection's forward, the per-expert transposed codes its wgrad.
+    Returns the Quantized outputs, and the BF16 activation [T x I] too when
+    return_h (rows of no group are left unwritten)."""
+    rows, cols2, ld = _bf16_matrix(gate_up)
+    _need_gpu(group_offsets)
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or not group_offsets.is_contiguous():
+        raise TypeError("group_offsets must be a contiguous 1-D int32 tensor")
+    if cols2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    inter = cols2 // 2
+    G = group_offsets.numel() - 1
+    nb = grouped_colwise_blocks(rows, G)
+    dev = gate_up.device
+    q = s = qT = sT = h = None
+    if rowwise:
+        q = torch.empty((rows, inter), dtype=torch.uint8, device=dev)
+        s = torch.empty(((inter + 127) // 128, rows), dtype=torch.float32, device=dev)
+    if colwise:
+        qT = torch.empty((inter, 128 * nb), dtype=torch.uint8, device=dev)
+        sT = torch.empty((nb, inter), dtype=torch.float32, device=dev)
+    if return_h:
+        h = torch.empty((rows, inter), dtype=torch.bfloat16, device=dev)
+    check(_lib.load().fgs_swiglu_quantize_grouped(
+        _ptr(gate_up), rows, inter, ld, _ptr(group_offsets), G, _ptr(h), _ptr(q), _ptr(s),
+        _ptr(qT), 128 * nb, _ptr(sT), _stream()))
+    qq = Quantized(q, s, qT, sT, SCALE_TILE_1x128)
+    return (qq, h) if return_h else qq
+
+
 def grouped_wgrad_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, total_T: int,
                                out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """MoE weight gradients: C_g [M x N] = sum over group g's tokens of

@@ -280,6 +280,31 @@ int fgs_quantize_grouped_colwise(const void *x, int64_t rows, int64_t cols, int6
                                  uint8_t *q, float *scales,
                                  uint8_t *qT, int64_t ldqT, float *scalesT, void *stream);
 
+/*
+ * fgs_swiglu_quantize_grouped -- the SwiGLU activation between the two
+ *   expert GEMMs fused into the grouped quantizer of the down projection's
+ *   operands, so the activation is never written and read back in BF16.
+ *   [DSV3] "Mixed precision framework" (the expert GEMMs run in FP8); the
+ *   activation itself is not on the pages: SwiGLU is the DeepSeek-V3
+ *   expert's, computed here in FP32 before the FP8 cast.
+ * gate_up  BF16 [rows x 2*inter], row stride ld (multiple of 8; inter a
+ *          multiple of 8): the gate/up GEMM output, gate = columns
+ *          0..inter-1, up = columns inter..2*inter-1.
+ * The quantized matrix is h [rows x inter] with
+ *   h = BF16_RNE(fl32(fl32(g * sig) * u)), sig = 1 / (1 + e) for g >= 0 and
+ *   e / (1 + e) for g < 0, e = expf(-|g|), everything in FP32 (expf to
+ *   within a few ulp), so h is within one BF16 ulp of the exact SwiGLU; the
+ *   codes are exactly the 1x128 quantization of that h.
+ * h (optional, NULL skips it): BF16 [rows x inter] of the rows a valid group
+ *   covers (for a backward pass that wants it).
+ * group_offsets, G, q / scales, qT / ldqT / scalesT: as for
+ *   fgs_quantize_grouped_colwise with cols = inter (no gather).
+ */
+int fgs_swiglu_quantize_grouped(const void *gate_up, int64_t rows, int64_t inter, int64_t ld,
+                                const int32_t *group_offsets, int32_t G, uint16_t *h,
+                                uint8_t *q, float *scales, uint8_t *qT, int64_t ldqT, float *scalesT,
+                                void *stream);
+
 /* Number of 128-token blocks of the per-group column-wise layout for rows
  * tokens in G groups: floor(rows/128) + G (0 for negative arguments). */
 int64_t fgs_grouped_colwise_blocks(int64_t rows, int32_t G);

@@ -198,6 +198,22 @@ def test_grouped_colwise_validation(lib):
     assert call(x=NULL, idx=FAKE, src=100) == _lib.FGS_ERR_INVALID_ARG
 
 
+def test_swiglu_quantize_validation(lib):
+    S = NULL
+    f = lib.fgs_swiglu_quantize_grouped
+
+    def call(rows=300, inter=256, ld=512, offs=FAKE, G=4, h=NULL, q=FAKE, s=FAKE, qT=FAKE, ldq=128 * 6, sT=FAKE):
+        return f(FAKE, rows, inter, ld, offs, G, h, q, s, qT, ldq, sT, S)
+    assert call(G=-1) == _lib.FGS_ERR_INVALID_ARG
+    assert call(ld=300) == _lib.FGS_ERR_INVALID_ARG                    # ld < 2 * inter
+    assert call(inter=252, ld=504) == _lib.FGS_ERR_UNSUPPORTED         # inter % 8
+    assert call(inter=200, ld=400) == _lib.FGS_ERR_UNSUPPORTED         # row-wise needs inter % 128
+    assert call(offs=NULL) == _lib.FGS_ERR_INVALID_ARG
+    assert call(ldq=128 * 5) == _lib.FGS_ERR_INVALID_ARG
+    assert call(q=NULL, s=NULL, qT=NULL, sT=NULL) == _lib.FGS_OK        # nothing to write
+    assert call(G=0) == _lib.FGS_OK
+
+
 def test_grouped_wgrad_validation(lib):
     S = NULL
     g = lib.fgs_grouped_wgrad_block_scaled

@@ -305,3 +305,61 @@ def test_invalid_offsets_stay_in_bounds(fgs):
     for g in (1, 3, 5):
         assert not cc[g].any(), g
     assert np.all(np.isfinite(cc))
+
+
+# --------------------------------------------- SwiGLU fused into the quant --
+def _bf16_adjacent(a_bits, b_bits):
+    """Equal or neighbouring BF16 numbers (ordered bit patterns)."""
+    def key(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(key(a_bits) - key(b_bits)) <= 1
+
+
+def _check_swiglu(fgs, gu_bits, offs, rowwise, sample_cols=None):
+    inter = gu_bits.shape[1] // 2
+    off_t = torch.from_numpy(offs).cuda()
+    qq, h = fgs.swiglu_quantize_grouped(synth.to_torch_bf16(gu_bits).cuda(), off_t, rowwise=rowwise,
+                                        colwise=True, return_h=True)
+    torch.cuda.synchronize()
+    T = gu_bits.shape[0]
+    covered = np.zeros(T, dtype=bool)
+    for g in range(len(offs) - 1):
+        covered[offs[g]:offs[g + 1]] = True
+    hb = h.cpu().view(torch.int16).numpy().view(np.uint16)
+    # the activation: within one BF16 step of the exactly rounded SwiGLU
+    ref = oracle.swiglu_bf16(gu_bits, inter)
+    adj = _bf16_adjacent(hb[covered], ref[covered])
+    assert adj.all(), f"{int((~adj).sum())} activations off by more than one BF16 step"
+    # the codes: exactly the oracle's quantization of that activation
+    cols = np.arange(inter) if sample_cols is None else sample_cols
+    hsel = np.ascontiguousarray(hb[:, cols])
+    res = oracle.quant_e4m3_grouped_colwise(hsel, offs)
+    qT = qq.qT[torch.from_numpy(cols).cuda()].cpu().numpy()
+    sT = qq.scalesT[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    for g, kb, n in _blocks_of(offs):
+        qo, so = res[g]
+        assert np.array_equal(qT[:, 128 * kb:128 * kb + qo.shape[1]], qo), g
+        assert np.array_equal(sT[kb:kb + n].T.view(np.uint32), so.view(np.uint32)), g
+    if rowwise:
+        qr, sr = oracle.quant_e4m3(hb, "tile")
+        assert np.array_equal(qq.q.cpu().numpy()[covered], qr[covered])
+        assert np.array_equal(qq.scales.cpu().numpy()[:, covered].T.view(np.uint32), sr[covered].view(np.uint32))
+
+
+@pytest.mark.parametrize("inter,rowwise", [(256, True), (200, False)])
+def test_swiglu_quantize_ragged(fgs, inter, rowwise):
+    """Gate/up outputs with x50 outlier channels (|g| up to ~200, both tails
+    of the logistic), ragged and empty experts."""
+    offs = _offsets(COUNTS)
+    _check_swiglu(fgs, synth.activations(int(offs[-1]), 2 * inter, seed=inter), offs, rowwise)
+
+
+def test_swiglu_quantize_deepseek_moe_sampled(fgs):
+    """DeepSeek-V3 down-projection input at full size: 32768 routed rows of
+    the gate/up output [x 4096], 256 Zipf experts; every activation checked,
+    the codes on sampled columns."""
+    counts = synth.expert_counts(32768, 256, 1.1, seed=0)
+    offs = _offsets(counts)
+    gu = synth.activations(int(offs[-1]), 2 * 2048, seed=91)
+    _check_swiglu(fgs, gu, offs, rowwise=True, sample_cols=sample_rows(2048, seed=3))
