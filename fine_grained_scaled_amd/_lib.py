@@ -21,6 +21,8 @@ EXPORTS = (
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
     "fgs_grouped_gemm_block_scaled",
+    "fgs_gemm_block_scaled_fp8out",
+    "fgs_grouped_gemm_block_scaled_fp8out",
     "fgs_quantize_grouped_colwise",
     "fgs_grouped_colwise_blocks",
     "fgs_swiglu_quantize_grouped",
@@ -69,6 +71,8 @@ def load() -> ctypes.CDLL:
     OP = ctypes.POINTER(FgsOperand)
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_gemm_block_scaled_fp8out.argtypes = [OP, OP, I64, I64, I64, P, I64, P, P, P]
+    lib.fgs_grouped_gemm_block_scaled_fp8out.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, P, P, P]
     lib.fgs_quantize_grouped_colwise.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_int32, P, P, P, I64, P, P]
     lib.fgs_grouped_colwise_blocks.argtypes = [I64, ctypes.c_int32]
     lib.fgs_swiglu_quantize_grouped.argtypes = [P, I64, I64, I64, P, ctypes.c_int32, P, P, P, P, I64, P, P]
@@ -83,7 +87,8 @@ def load() -> ctypes.CDLL:
     for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
                  "fgs_gemm_block_scaled", "fgs_grouped_gemm_block_scaled",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",
-                 "fgs_swiglu_quantize_grouped"):
+                 "fgs_swiglu_quantize_grouped", "fgs_gemm_block_scaled_fp8out",
+                 "fgs_grouped_gemm_block_scaled_fp8out"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -231,16 +231,16 @@ static bool is_fp32_mode(int m)
     return m == FGS_SCALE_TENSOR || m == FGS_SCALE_TILE_1x128 || m == FGS_SCALE_BLOCK_128x128;
 }
 
-int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
-                          void* C, int64_t ldc, int out_dtype, void* stream)
+static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                     void* C, int64_t ldc, int out_dtype, uint8_t* q_out, float* s_out, void* stream)
 {
-    int st = check_gemm_common(A, B, M, N, K, C, ldc, out_dtype);
+    int st = check_gemm_common(A, B, M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
     if (st != FGS_OK) return st;
     if (M == 0 || N == 0) return ok();
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
     // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0};
+    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (A->elem != FGS_ELEM_E2M1 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
         if (A->scale_mode == FGS_SCALE_BLOCK_128x128)
@@ -257,12 +257,37 @@ int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M,
                 A->elem, A->scale_mode, B->scale_mode);
 }
 
-int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
-                                  int32_t G, int64_t total_M, int64_t N, int64_t K,
-                                  void* C, int64_t ldc, int out_dtype, void* stream)
+int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                          void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream);
+}
+
+// E4M3-output launches: validated like the BF16-out GEMM (C may be NULL);
+// the codes and scales need N % 128 == 0.
+static int check_fp8_out(int64_t N, void*& C, int64_t& ldc, uint8_t* q_out, float* s_out)
+{
+    if (!q_out || !s_out) return fail(FGS_ERR_INVALID_ARG, "q_out and scales_out are required");
+    if (N % 128) return fail(FGS_ERR_UNSUPPORTED, "the E4M3 output needs N %% 128 == 0 (N = %lld)", (long long)N);
+    if (!aligned(q_out, 4) || !aligned(s_out, 4)) return fail(FGS_ERR_UNSUPPORTED, "q_out and scales_out must be 4-byte aligned");
+    if (!C) ldc = N;      // no BF16 output: the common checks see a valid stride
+    return FGS_OK;
+}
+
+int fgs_gemm_block_scaled_fp8out(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                                 void* C, int64_t ldc, uint8_t* q_out, float* scales_out, void* stream)
+{
+    int st = check_fp8_out(N, C, ldc, q_out, scales_out);
+    if (st != FGS_OK) return st;
+    return gemm_impl(A, B, M, N, K, C, ldc, FGS_OUT_BF16, q_out, scales_out, stream);
+}
+
+static int grouped_impl(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets, int32_t G,
+                        int64_t total_M, int64_t N, int64_t K, void* C, int64_t ldc, int out_dtype,
+                        uint8_t* q_out, float* s_out, void* stream)
 {
     if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
-    int st = check_gemm_common(A, B, total_M, N, K, C, ldc, out_dtype);
+    int st = check_gemm_common(A, B, total_M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
     if (st != FGS_OK) return st;
     if (total_M == 0 || N == 0 || G == 0) return ok();
     if (!group_offsets) return fail(FGS_ERR_INVALID_ARG, "group_offsets is NULL");
@@ -271,8 +296,24 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, co
     if (total_M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
     const int64_t tiles = ((total_M + 127) / 128 + G) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G};
+    fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 0, 0, q_out, s_out};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_gemm_block_scaled launch");
+}
+
+int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                  int32_t G, int64_t total_M, int64_t N, int64_t K,
+                                  void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return grouped_impl(A, B, group_offsets, G, total_M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream);
+}
+
+int fgs_grouped_gemm_block_scaled_fp8out(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                         int32_t G, int64_t total_M, int64_t N, int64_t K, void* C, int64_t ldc,
+                                         uint8_t* q_out, float* scales_out, void* stream)
+{
+    int st = check_fp8_out(N, C, ldc, q_out, scales_out);
+    if (st != FGS_OK) return st;
+    return grouped_impl(A, B, group_offsets, G, total_M, N, K, C, ldc, FGS_OUT_BF16, q_out, scales_out, stream);
 }
 
 int64_t fgs_grouped_colwise_blocks(int64_t rows, int32_t G)

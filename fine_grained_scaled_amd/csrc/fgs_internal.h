@@ -91,6 +91,8 @@ struct GemmArgs {
     int32_t G;
     int group_k;                    // groups split the contraction (MoE wgrad)
     int64_t T;                      // group_k: tokens the offsets index
+    uint8_t* q_out;                 // BF16 out: also 1x128 E4M3 codes of the output, or nullptr
+    float* s_out;                   //   their scales [N/128][M]
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).

@@ -122,6 +122,8 @@ struct GemmParams {
     int64_t b_group_stride;       // elements between groups of B codes
     int64_t sb_group_stride;      // floats between groups of B block scales
     int32_t tiles_m, tiles_n;
+    uint8_t* q_out;               // BF16-out launches: 1x128 E4M3 codes of the BF16 output, or nullptr
+    float* s_out;                 //   and their scales [N/128][M]
 };
 
 // FP16 x FP16 MFMA, 32x32 outputs, 16-deep K, FP32 accumulate.
@@ -773,6 +775,58 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
     }
 
+    // ------------------------------------------- E4M3 output (optional) --
+    // The BF16-rounded outputs quantized in 1x128 tiles along N for the next
+    // layer (the online rule of the quantizers: s = fl32(amax / 448), code =
+    // E4M3_RNE(fl32(y / s))).  A tile row's 128 columns live in two waves
+    // (wn, wn ^ 1), 32 values per lane and 64 per lane pair (l, l ^ 32): the
+    // row maxima meet in the LDS stages, free once the K loop's last barrier
+    // has passed.  Launches with q_out need N % 128 == 0.
+    if constexpr (OUT_BF16 && GROUP != GROUP_K) {
+        if (p.q_out) {
+            uint32_t* rmax = reinterpret_cast<uint32_t*>(smem);      // [BM][NWN] |BF16| bits
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                uint32_t mx = 0;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                        const uint32_t h23 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        mx = max(mx, max(max(h01 & 0x7FFFu, (h01 >> 16) & 0x7FFFu),
+                                         max(h23 & 0x7FFFu, (h23 >> 16) & 0x7FFFu)));
+                    }
+                mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+                if (l < 32) rmax[(WM * wm + 32 * i + l) * NWN + wn] = mx;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int r = WM * wm + 32 * i + (l & 31);
+                const int64_t m = m0 + r;
+                const E4M3Block b = e4m3_block_from_amax_bits(max(rmax[r * NWN + wn], rmax[r * NWN + (wn ^ 1)]));
+                if (m < m_end) {
+                    if (l < 32 && (wn & 1) == 0) p.s_out[((n0 + 64 * wn) / 128) * p.M + m] = b.s;
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int64_t n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
+                            const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                            const uint32_t h23 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                            uint32_t c4 = 0x7F7F7F7Fu;
+                            if (!b.nan)
+                                c4 = e4m3_pack4(e4m3_quotient_bits(h01 << 16, b), e4m3_quotient_bits(h01 & 0xFFFF0000u, b),
+                                                e4m3_quotient_bits(h23 << 16, b), e4m3_quotient_bits(h23 & 0xFFFF0000u, b));
+                            if (n + 3 < p.N) *reinterpret_cast<uint32_t*>(p.q_out + m * p.N + n) = c4;
+                        }
+                }
+            }
+            if (!p.C) return;
+        }
+    }
+
     // ------------------------------------------------------ epilogue --
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
@@ -920,6 +974,8 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.offsets = a.group_offsets;
     p.G = a.G;
     p.T = a.T;
+    p.q_out = a.q_out;
+    p.s_out = a.s_out;
     if (a.M == 0 || a.N == 0) return hipSuccess;
     const bool bf16 = a.out_bf16 != 0;
     if (a.group_k) {

@@ -249,6 +249,52 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
     return out
 
 
+def gemm_block_scaled_fp8out(A: Operand, B: Operand, bf16_out: bool = True, K: Optional[int] = None):
+    """gemm_block_scaled with BF16 output whose epilogue also quantizes it in
+    1x128 tiles along N (the next layer's A operand).  Returns (Quantized
+    with q [M x N] and scales [N/128][M], the BF16 C or None)."""
+    _need_gpu(A.data, B.data, A.scales, B.scales)
+    M, N = A.data.shape[0], B.data.shape[0]
+    if K is None:
+        K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
+    _check_operand(A, M, K, "A")
+    _check_operand(B, N, K, "B")
+    dev = A.data.device
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if bf16_out else None
+    q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    s = torch.empty(((N + 127) // 128, M), dtype=torch.float32, device=dev)
+    a, b = A.c_struct(), B.c_struct()
+    check(_lib.load().fgs_gemm_block_scaled_fp8out(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(c),
+                                                   N, _ptr(q), _ptr(s), _stream()))
+    return Quantized(q, s, None, None, SCALE_TILE_1x128), c
+
+
+def grouped_gemm_block_scaled_fp8out(A: Operand, B: Operand, group_offsets: torch.Tensor, N: int,
+                                     bf16_out: bool = True, K: Optional[int] = None):
+    """grouped_gemm_block_scaled with BF16 output and the 1x128 E4M3 codes of
+    that output from the same epilogue (rows of no group are not written)."""
+    _need_gpu(A.data, B.data, group_offsets)
+    if group_offsets.dtype != torch.int32:
+        raise TypeError("group_offsets must be int32")
+    total_M = A.data.shape[0]
+    G = group_offsets.numel() - 1
+    if K is None:
+        K = A.data.shape[1]
+    _check_operand(A, total_M, K, "A")
+    if B.scale_mode != SCALE_BLOCK_128x128 or B.data.shape[0] < G * N:
+        raise ValueError("B must hold G x N rows of codes with 128x128 block scales")
+    _check_operand(B, N, K, "B", groups=G)
+    dev = A.data.device
+    c = torch.empty((total_M, N), dtype=torch.bfloat16, device=dev) if bf16_out else None
+    q = torch.empty((total_M, N), dtype=torch.uint8, device=dev)
+    s = torch.empty(((N + 127) // 128, total_M), dtype=torch.float32, device=dev)
+    a, b = A.c_struct(), B.c_struct()
+    check(_lib.load().fgs_grouped_gemm_block_scaled_fp8out(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
+                                                           G, total_M, N, K, _ptr(c), N, _ptr(q), _ptr(s),
+                                                           _stream()))
+    return Quantized(q, s, None, None, SCALE_TILE_1x128), c
+
+
 def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, N: int,
                               out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
                               K: Optional[int] = None) -> torch.Tensor:

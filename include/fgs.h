@@ -330,6 +330,29 @@ int fgs_grouped_wgrad_block_scaled(const fgs_operand *A, const fgs_operand *B,
                                    int64_t M, int64_t N, void *C, int64_t ldc, int out_dtype,
                                    void *stream);
 
+/*
+ * fgs_gemm_block_scaled_fp8out / fgs_grouped_gemm_block_scaled_fp8out --
+ *   the GEMMs above with BF16 output, whose epilogue also quantizes that BF16
+ *   output in 1x128 tiles along N for the next layer: the next GEMM's A
+ *   operand without a BF16 round trip.   [DSV3] "Fine-grained
+ *   quantization", "Online quantization" (the same rule as
+ *   fgs_quantize_blockwise's row-wise TILE_1x128 output, applied to the
+ *   BF16-rounded C).
+ * C may be NULL (no BF16 output; ldc is then ignored).
+ * q_out      E4M3 [M x N] (dense, 4-byte aligned); scales_out FP32
+ *            [N/128][M] (the TILE_1x128 layout for R = M, K = N).  The
+ *            grouped form writes the rows its groups cover.
+ * Needs N % 128 == 0.  Other arguments and supported operands as for the
+ * BF16-output GEMMs.
+ */
+int fgs_gemm_block_scaled_fp8out(const fgs_operand *A, const fgs_operand *B,
+                                 int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
+                                 uint8_t *q_out, float *scales_out, void *stream);
+int fgs_grouped_gemm_block_scaled_fp8out(const fgs_operand *A, const fgs_operand *B,
+                                         const int32_t *group_offsets, int32_t G,
+                                         int64_t total_M, int64_t N, int64_t K, void *C, int64_t ldc,
+                                         uint8_t *q_out, float *scales_out, void *stream);
+
 /* Workgroup tile of the GEMMs whose operands carry one scale for all of K
  * (per-tensor x per-tensor E4M3, NVFP4): FGS_TILE_AUTO (default) picks per
  * problem from the tile counts and the device's compute units,
