@@ -25,7 +25,11 @@ under "workloads" (per-kernel throughput against the roofline): the tiny
 blockwise GEMM, the Llama-3-8B layers in the hybrid delayed-scaling recipe
 (per-tensor scales from an amax history, E5M2 gradients), the DeepSeek-V3
 MoE grouped GEMMs (forward, dgrad and wgrad), MXFP8 at Llama-3.1-405B
-shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes.
+shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes; and the headline
+step and the MXFP8 layers again with their GEMMs on the FP8 matrix
+instructions (fgs_gemm_block_scaled_fp8mma: FP8 accumulation inside the
+instruction with FP32 promotion per 128-K block, MX scales applied by the
+instruction; a looser error bound than the exact headline GEMM).
 
 Prints ONE JSON line on stdout; per-kernel breakdowns go to stderr.
 """
@@ -159,6 +163,7 @@ def gpu_t3(torch, shape, seed):
 # --------------------------------------------------------------------------
 class Llama8B:
     name = "llama3_8b_linears"
+    fp8_mma = False
 
     def __init__(self, torch, fgs, synth):
         self.torch, self.fgs = torch, fgs
@@ -231,12 +236,21 @@ class Llama8B:
                              lambda: fgs.quantize_blockwise(dY, amode, rowwise=True, colwise=True))
                 f = 2.0 * LLAMA8B_M * N * K
                 o = self.out
+                mma = self.fp8_mma
                 tm.run("gemm", lab + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                    qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(rname, name, "y")]))
+                    qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(rname, name, "y")], fp8_mma=mma))
                 tm.run("gemm", lab + "/dgrad", f, lambda: fgs.gemm_block_scaled(
-                    qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(rname, name, "dx")]))
+                    qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(rname, name, "dx")], fp8_mma=mma))
                 tm.run("gemm", lab + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                    qdy.colwise(), qx.colwise(), torch.float32, out=o[(rname, name, "dw")]))
+                    qdy.colwise(), qx.colwise(), torch.float32, out=o[(rname, name, "dw")], fp8_mma=mma))
+
+
+class Llama8BFp8Mma(Llama8B):
+    """The headline step with every GEMM on the FP8 matrix instructions
+    (fgs_gemm_block_scaled_fp8mma: the pages' own accumulation design, a
+    looser error bound than the exact default)."""
+    name = "llama3_8b_linears_fp8_mfma"
+    fp8_mma = True
 
 
 # --------------------------------------------------------------------------
@@ -445,6 +459,7 @@ class MoE:
 # --------------------------------------------------------------------------
 class MX405B:
     name = "llama31_405b_mxfp8"
+    fp8_mma = False
 
     def __init__(self, torch, fgs, synth):
         self.torch, self.fgs = torch, fgs
@@ -472,10 +487,18 @@ class MX405B:
             qdy = tm.run("quant", name + "/dY", mx_bytes(MX_M, N, 1),
                          lambda: fgs.quantize_mx(dY, rowwise=False, colwise=True))
             f = 2.0 * MX_M * N * K
+            mma = self.fp8_mma
             tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")]))
+                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")], fp8_mma=mma))
             tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")]))
+                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")], fp8_mma=mma))
+
+
+class MX405BFp8Mma(MX405B):
+    """MXFP8 with the E8M0 scales applied by the scaled FP8 matrix
+    instruction (fgs_gemm_block_scaled_fp8mma)."""
+    name = "llama31_405b_mxfp8_fp8_mfma"
+    fp8_mma = True
 
 
 # --------------------------------------------------------------------------
@@ -524,7 +547,7 @@ class NV12B:
 
 
 WORKLOADS = {"llama3_8b": Llama8B, "hybrid8b": Hybrid8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B,
-             "nv12b": NV12B}
+             "nv12b": NV12B, "llama3_8b_fp8mma": Llama8BFp8Mma, "mx405b_fp8mma": MX405BFp8Mma}
 
 
 def measure(torch, wl, steps, warmup):
@@ -549,6 +572,7 @@ def kind_report(kinds, steps):
     if "gemm" in kinds:
         f, t, n = kinds["gemm"]
         out["gemm"] = {"TFLOP/s": round(f / t / 1e12, 2), "frac_fp16_mfma_peak": round(f / t / 1e12 / PEAK_FP16_MFMA, 4),
+                       "frac_fp8_mfma_peak": round(f / t / 1e12 / PEAK_FP8_MFMA, 4),
                        "ms_per_step": round(t / steps * 1e3, 4)}
     if "quant" in kinds:
         b, t, n = kinds["quant"]
@@ -711,7 +735,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="llama3_8b,hybrid8b,tiny,moe,mx405b,nv12b",
+    ap.add_argument("--workloads", default="llama3_8b,hybrid8b,tiny,moe,mx405b,nv12b,llama3_8b_fp8mma,mx405b_fp8mma",
                     help="comma list of " + ",".join(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

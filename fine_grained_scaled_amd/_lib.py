@@ -20,6 +20,7 @@ EXPORTS = (
     "fgs_quantize_mx",
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
+    "fgs_gemm_block_scaled_fp8mma",
     "fgs_grouped_gemm_block_scaled",
     "fgs_gemm_block_scaled_fp8out",
     "fgs_grouped_gemm_block_scaled_fp8out",
@@ -70,6 +71,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_quantize_nvfp4.argtypes = [P, I64, I64, I64, I32, U64, I32, U64, P, P, P, P, P, P, SZ, P]
     OP = ctypes.POINTER(FgsOperand)
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_gemm_block_scaled_fp8mma.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8out.argtypes = [OP, OP, I64, I64, I64, P, I64, P, P, P]
     lib.fgs_grouped_gemm_block_scaled_fp8out.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, P, P, P]
@@ -85,7 +87,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
-                 "fgs_gemm_block_scaled", "fgs_grouped_gemm_block_scaled",
+                 "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_fp8mma", "fgs_grouped_gemm_block_scaled",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",
                  "fgs_swiglu_quantize_grouped", "fgs_gemm_block_scaled_fp8out",
                  "fgs_grouped_gemm_block_scaled_fp8out"):

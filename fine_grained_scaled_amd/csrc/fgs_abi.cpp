@@ -232,7 +232,8 @@ static bool is_fp32_mode(int m)
 }
 
 static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
-                     void* C, int64_t ldc, int out_dtype, uint8_t* q_out, float* s_out, void* stream)
+                     void* C, int64_t ldc, int out_dtype, uint8_t* q_out, float* s_out, void* stream,
+                     bool fp8_mma = false)
 {
     int st = check_gemm_common(A, B, M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
     if (st != FGS_OK) return st;
@@ -240,8 +241,10 @@ static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int6
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
     // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out};
+    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out, fp8_mma ? 1 : 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fp8_mma && (A->elem == FGS_ELEM_E2M1 || B->elem == FGS_ELEM_E2M1))
+        return fail(FGS_ERR_UNSUPPORTED, "the FP8 matrix-instruction GEMM takes E4M3 / E5M2 operands only");
     if (A->elem != FGS_ELEM_E2M1 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
         if (A->scale_mode == FGS_SCALE_BLOCK_128x128)
             return fail(FGS_ERR_UNSUPPORTED, "A with 128x128 block scales is not supported (use TILE_1x128 or TENSOR)");
@@ -261,6 +264,12 @@ int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M,
                           void* C, int64_t ldc, int out_dtype, void* stream)
 {
     return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream);
+}
+
+int fgs_gemm_block_scaled_fp8mma(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                                 void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream, true);
 }
 
 // E4M3-output launches: validated like the BF16-out GEMM (C may be NULL);

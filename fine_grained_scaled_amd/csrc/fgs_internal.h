@@ -93,6 +93,7 @@ struct GemmArgs {
     int64_t T;                      // group_k: tokens the offsets index
     uint8_t* q_out;                 // BF16 out: also 1x128 E4M3 codes of the output, or nullptr
     float* s_out;                   //   their scales [N/128][M]
+    int fp8_mma;                    // dense only: accumulate on the FP8 matrix instructions
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).

@@ -132,6 +132,21 @@ __device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// FP8 x FP8 MFMA, 32x32 outputs, 64-deep K, FP32 accumulate, with E8M0
+// operand scales (127 = x1).  Formats (FA, FB): 0 = E4M3, 1 = E5M2.  Lane l
+// holds row l % 32 and 32 codes (8 registers); both operands take the same K
+// order.  The instruction's two 32-element scale blocks are bytes 0-15 of
+// both lane halves (scaled by the byte of lane half 0) and bytes 16-31 of
+// both halves (lane half 1's byte): measured on gfx950 with one nonzero code
+// per position and distinct scales per lane half.
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
 // 16 E4M3 codes (one 16-byte LDS read) -> two exact FP16 8-vectors: bytes
 // 0..7 feed one MFMA k-step, bytes 8..15 the next.
 __device__ __forceinline__ void decode16(const uint4 v, f16x8& lo, f16x8& hi)
@@ -255,7 +270,12 @@ struct Lds {
 enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
 
 // ELEMS (FP8 per-tensor operands only): bit 0 = A is E5M2, bit 1 = B is E5M2.
-template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP, int ELEMS = 0>
+// MMA8: accumulate on the FP8 matrix instructions (v_mfma_scale_*_f8f6f4)
+// instead of the exact FP16/BF16 decode: the codes go from LDS straight into
+// the MFMA, MX scales are applied by the instruction, and the 1x128 / 128x128
+// promotion stays as above.  The instruction's own sum is not exact (see the
+// header), so its results are bounded more loosely than the default path's.
+template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP, int ELEMS = 0, bool MMA8 = false>
 __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel(GemmParams p)
 {
     constexpr int NWM = S::NWM, NWN = S::NWN;
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
     uint32_t a_sw_next[TI], b_sw_next[TJ];
     uint32_t ea[TI], eb = 0;
-    if constexpr (MX) {
+    if constexpr (MX && !MMA8) {
         // one tile row per thread: A rows 0 .. BM-1, then B rows (rows past
         // the end clamped; they only feed outputs that are never stored)
         if (t == 0) s_mx_eb = 0;
@@ -523,6 +543,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
 #pragma unroll
         for (int i = 0; i < TI; ++i) ea[i] = s_mx_ref[WM * wm + 32 * i + (l & 31)];
         eb = s_mx_eb;
+    }
+    if constexpr (MX) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc);
 #pragma unroll
@@ -667,6 +689,42 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                             for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
                     }
                 }
+            } else if constexpr (MMA8) {
+                // two 64-deep k-steps; lane half h holds chunk 4*s2 + h of its
+                // row in bytes 0-15 and chunk 4*s2 + 2 + h in bytes 16-31, so
+                // the instruction's first scale block is MX block 2*s2 (chunks
+                // 4*s2, 4*s2 + 1) and its second MX block 2*s2 + 1; lane half
+                // h supplies the scale of block 2*s2 + h.  Same for A and B.
+                constexpr int FB = (ELEMS & 2) ? 1 : 0, FA = (ELEMS & 1) ? 1 : 0;
+    #pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int c0 = ((4 * s2 + half) ^ swz) << 4, c1 = ((4 * s2 + 2 + half) ^ swz) << 4;
+                    i32x8 af[TI], bf[TJ];
+                    int ea8[TI], eb8[TJ];
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j) {
+                        const uint4 x = *reinterpret_cast<const uint4*>(lb + 32 * j * ROW + c0);
+                        const uint4 y = *reinterpret_cast<const uint4*>(lb + 32 * j * ROW + c1);
+                        bf[j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                        eb8[j] = MX ? (int)((b_sw[j] >> (8 * (2 * s2 + half))) & 0xFFu) : 127;
+                    }
+    #pragma unroll
+                    for (int i = 0; i < TI; ++i) {
+                        const uint4 x = *reinterpret_cast<const uint4*>(la + 32 * i * ROW + c0);
+                        const uint4 y = *reinterpret_cast<const uint4*>(la + 32 * i * ROW + c1);
+                        af[i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                        ea8[i] = MX ? (int)((a_sw[i] >> (8 * (2 * s2 + half))) & 0xFFu) : 127;
+                    }
+    #pragma unroll
+                    for (int i = 0; i < TI; ++i)
+    #pragma unroll
+                        for (int j = 0; j < TJ; ++j) {
+                            if constexpr (PROMOTE)
+                                part[i][j] = mfma8<FB, FA>(bf[j], af[i], part[i][j], eb8[j], ea8[i]);
+                            else
+                                acc[i][j] = mfma8<FB, FA>(bf[j], af[i], acc[i][j], eb8[j], ea8[i]);
+                        }
+                }
             } else
     #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -749,7 +807,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         __syncthreads();
     }
 
-    if constexpr (MX) {
+    if constexpr (MX && !MMA8) {
         // 2^(E_A + E_B - 254) by exponent arithmetic (exact up to FP32
         // overflow or underflow); NaN rows and columns
 #pragma unroll
@@ -765,7 +823,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                     acc[i][j][r] = (rnan || s_mx_nan[BM + cn]) ? __builtin_nanf("") : v;
                 }
         }
-    } else if constexpr (!PROMOTE) {
+    } else if constexpr (!PROMOTE && !MX) {
         const float f = NV ? p.tsA[0] * p.tsB[0] : p.sA[0] * sBp[0];
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -864,7 +922,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
 }
 
-template <class S, int AMODE, int BMODE, int GROUP, int ELEMS = 0>
+template <class S, int AMODE, int BMODE, int GROUP, int ELEMS = 0, bool MMA8 = false>
 hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
     p.tiles_n = (int32_t)((a.N + S::BN - 1) / S::BN);
@@ -873,8 +931,8 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128>::STAGE;
-    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS>
-                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS>;
+    auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS, MMA8>
+                  : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS, MMA8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -902,44 +960,51 @@ bool prefer_wide(const GemmArgs& a)
 }
 
 // Modes without promotion (one scale per operand for all of K: per-tensor
-// E4M3, NVFP4) keep 128 accumulators per lane and can take the wide tile; the
-// promoted modes hold partial sums too and take the 256 x 128 tile.
+// E4M3, NVFP4, and MX on the exact path) keep 128 accumulators per lane and
+// can take the wide tile; the promoted modes hold partial sums too and take
+// the 256 x 128 tile.  MMA8: the same modes on the FP8 matrix instructions
+// (NVFP4's E4M3 block scales have no FP8-instruction form and are rejected).
+template <bool MMA8>
 hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
     using D = ShapeDense;
+    using W = ShapeWide;
+    constexpr int NONE = GROUP_NONE;
     const bool wide = prefer_wide(a);
     const int amode = a.A.scale_mode, bmode = a.B.scale_mode;
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_NONE>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_NONE>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, GROUP_NONE>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, NONE, 0, MMA8>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, NONE, 0, MMA8>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, NONE, 0, MMA8>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0) {
-        if (wide) return launch_modes<ShapeWide, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, GROUP_NONE>(p, a, bf16, s);
-        return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, GROUP_NONE>(p, a, bf16, s);
+        if (wide) return launch_modes<W, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, NONE, 0, MMA8>(p, a, bf16, s);
+        return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, NONE, 0, MMA8>(p, a, bf16, s);
     } else if (amode == FGS_SCALE_NV16_E4M3 && bmode == FGS_SCALE_NV16_E4M3) {
-        if (wide) return launch_modes<ShapeWide, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, GROUP_NONE>(p, a, bf16, s);
-        return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, GROUP_NONE>(p, a, bf16, s);
+        if constexpr (!MMA8) {
+            if (wide) return launch_modes<W, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, NONE>(p, a, bf16, s);
+            return launch_modes<D, FGS_SCALE_NV16_E4M3, FGS_SCALE_NV16_E4M3, NONE>(p, a, bf16, s);
+        }
     } else if (amode == FGS_SCALE_TENSOR) {
         if (bmode == FGS_SCALE_TENSOR) {
             const int elems = (a.A.elem == FGS_ELEM_E5M2 ? 1 : 0) | (a.B.elem == FGS_ELEM_E5M2 ? 2 : 0);
-            using T = std::integral_constant<int, FGS_SCALE_TENSOR>;
+            constexpr int T = FGS_SCALE_TENSOR;
             switch (elems) {
             case 1:
-                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 1>(p, a, bf16, s);
-                return launch_modes<D, T::value, T::value, GROUP_NONE, 1>(p, a, bf16, s);
+                if (wide) return launch_modes<W, T, T, NONE, 1, MMA8>(p, a, bf16, s);
+                return launch_modes<D, T, T, NONE, 1, MMA8>(p, a, bf16, s);
             case 2:
-                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 2>(p, a, bf16, s);
-                return launch_modes<D, T::value, T::value, GROUP_NONE, 2>(p, a, bf16, s);
+                if (wide) return launch_modes<W, T, T, NONE, 2, MMA8>(p, a, bf16, s);
+                return launch_modes<D, T, T, NONE, 2, MMA8>(p, a, bf16, s);
             case 3:
-                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE, 3>(p, a, bf16, s);
-                return launch_modes<D, T::value, T::value, GROUP_NONE, 3>(p, a, bf16, s);
+                if (wide) return launch_modes<W, T, T, NONE, 3, MMA8>(p, a, bf16, s);
+                return launch_modes<D, T, T, NONE, 3, MMA8>(p, a, bf16, s);
             default:
-                if (wide) return launch_modes<ShapeWide, T::value, T::value, GROUP_NONE>(p, a, bf16, s);
-                return launch_modes<D, T::value, T::value, GROUP_NONE>(p, a, bf16, s);
+                if (wide) return launch_modes<W, T, T, NONE, 0, MMA8>(p, a, bf16, s);
+                return launch_modes<D, T, T, NONE, 0, MMA8>(p, a, bf16, s);
             }
         }
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, GROUP_NONE>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, GROUP_NONE>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, NONE, 0, MMA8>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, NONE, 0, MMA8>(p, a, bf16, s);
     }
     return hipErrorInvalidValue;
 }
@@ -978,6 +1043,7 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.s_out = a.s_out;
     if (a.M == 0 || a.N == 0) return hipSuccess;
     const bool bf16 = a.out_bf16 != 0;
+    if (a.fp8_mma && (a.group_k || a.group_offsets || a.q_out)) return hipErrorInvalidValue;   // dense only
     if (a.group_k) {
         if (a.G == 0) return hipSuccess;
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_TILE_1x128)
@@ -995,7 +1061,8 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
             return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(p, a, bf16, stream);
         return hipErrorInvalidValue;
     }
-    return dispatch_dense(p, a, bf16, stream);
+    if (a.fp8_mma) return dispatch_dense<true>(p, a, bf16, stream);
+    return dispatch_dense<false>(p, a, bf16, stream);
 }
 
 // MXFP8 and NVFP4 operands take the same kernel (decode and scale handling

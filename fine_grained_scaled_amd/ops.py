@@ -230,8 +230,12 @@ def _out_code(out_dtype):
 
 
 def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
-                      out: Optional[torch.Tensor] = None, K: Optional[int] = None) -> torch.Tensor:
-    """C[M x N] = sum_k A^[m, k] * B^[n, k] over scaled low-precision operands."""
+                      out: Optional[torch.Tensor] = None, K: Optional[int] = None,
+                      fp8_mma: bool = False) -> torch.Tensor:
+    """C[M x N] = sum_k A^[m, k] * B^[n, k] over scaled low-precision operands.
+    fp8_mma=True runs fgs_gemm_block_scaled_fp8mma: the FP8 matrix
+    instructions with promotion per 128-K block (FP8 operands only; a looser
+    error bound than the exact default)."""
     _need_gpu(A.data, B.data, A.scales, B.scales)
     M, N = A.data.shape[0], B.data.shape[0]
     if K is None:
@@ -244,8 +248,8 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
     if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] < M or out.shape[1] < N or out.stride(1) != 1:
         raise ValueError("out must be a [M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
-    check(_lib.load().fgs_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), M, N, K,
-                                            _ptr(out), out.stride(0), code, _stream()))
+    fn = _lib.load().fgs_gemm_block_scaled_fp8mma if fp8_mma else _lib.load().fgs_gemm_block_scaled
+    check(fn(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0), code, _stream()))
     return out
 
 

@@ -218,6 +218,31 @@ int fgs_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
                           void *C, int64_t ldc, int out_dtype, void *stream);
 
 /*
+ * fgs_gemm_block_scaled_fp8mma -- the same product on the FP8 matrix
+ *   instructions, as the pages' own design does it: the FP8 codes go to the
+ *   matrix unit as they are, its partial sums over each 128-deep K block are
+ *   promoted into FP32 accumulators with sA * sB (1x128 / 128x128 scales),
+ *   and MX E8M0 scales are applied by the scaled instruction itself.
+ *   [DSV3] "Increasing accumulation precision" (limited accumulation inside
+ *   the matrix unit, promotion to FP32 at a fixed interval); [NEMO] MXFP8.
+ * Arguments, layouts, ownership and errors as fgs_gemm_block_scaled, for
+ *   the E4M3 / E5M2 operand pairs it lists (FP32-scaled and MX32_E8M0);
+ *   E2M1 operands return FGS_ERR_UNSUPPORTED.
+ * Accuracy: the instruction adds each group of 8 consecutive products with
+ *   about 13 bits below the largest of them, an error of at most
+ *   2^-10 * sum |a_k b_k| per group; with the FP32 sums that follow,
+ *   |C - C_ref| <= 2^-9 * sum_k |a_k b_k| + 1e-6 for K <= 65536 (FP32
+ *   output; BF16 output adds one BF16 ulp).  This is looser than the 1e-5
+ *   bound of fgs_gemm_block_scaled, which stays the exact default.
+ * MX: a scale byte of 0xFF (NaN) is passed to the instruction unchanged;
+ *   products whose scales leave the FP32 range overflow or underflow as the
+ *   instruction does (the default GEMM rescales them exactly).
+ */
+int fgs_gemm_block_scaled_fp8mma(const fgs_operand *A, const fgs_operand *B,
+                                 int64_t M, int64_t N, int64_t K,
+                                 void *C, int64_t ldc, int out_dtype, void *stream);
+
+/*
  * fgs_grouped_gemm_block_scaled -- MoE expert GEMMs: for each group g,
  *   rows group_offsets[g] .. group_offsets[g+1]-1 of A times B_g^T.
  *   [DSV3] "Mixed precision framework" (expert GEMMs in FP8, gating kept in

@@ -261,3 +261,21 @@ def test_binding_rejects_mis_sized_operands():
     for op in bad:
         with pytest.raises((ValueError, TypeError)):
             ops._check_operand(op, M, K, "A")
+
+
+def test_gemm_fp8mma_validation(lib):
+    """The FP8 matrix-instruction GEMM validates like the default GEMM and
+    rejects E2M1 operands (their E4M3 block scales have no FP8-instruction
+    form) before any HIP call."""
+    S = NULL
+    g = lib.fgs_gemm_block_scaled_fp8mma
+    r = ctypes.byref
+    a, b = _op(mode=1), _op(mode=2)
+    assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # K % 128
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 64, 0, S) == _lib.FGS_ERR_INVALID_ARG       # ldc < N
+    assert g(r(_op(mode=2)), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED   # A block
+    an, bn = _op(elem=1, mode=4, ts=FAKE), _op(elem=1, mode=4, ts=FAKE)
+    assert g(r(an), r(bn), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert b"E4M3 / E5M2" in lib.fgs_last_error()
+    assert g(r(_op(elem=2, mode=1)), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a), r(b), 0, 128, 256, NULL, 128, 0, S) == _lib.FGS_OK                     # empty

@@ -1,0 +1,220 @@
+"""GPU parity of the FP8 matrix-instruction GEMM (fgs_gemm_block_scaled_fp8mma)
+against the oracle's FP64 product of the dequantized operands.
+
+"Can you explain the role of FP8 precision in DeepSeek-V3 training",
+section "Increasing accumulation precision": the matrix unit's own FP8 sums
+are limited, and partial sums are promoted to FP32 at a fixed interval (here
+one 128-deep K block).  "Accelerating FP8 training performance with the
+NVIDIA NeMo framework": MXFP8, whose E8M0 scales the scaled instruction
+applies itself.
+
+The bound is derived from the instruction's accumulation, not the 1e-5 bound
+of the exact default GEMM: each group of 8 consecutive products is summed
+with about 13 bits below the largest of them (error <= 8 * 2^-13 * max|p| <=
+2^-10 * sum|p| per group); the FP32 sums after it add at most
+(K/8 + K/128) * 2^-24 * S, below 2^-10 * S for K <= 65536.  So
+|C - C_ref| <= 2^-9 * S + 1e-6 (FP32 out); BF16 out adds one BF16 ulp.
+A K pairing or scale mapping mistake gives errors of order S and fails it.
+Operands are quantized by the oracle and uploaded.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fine_grained_scaled_amd import synth
+
+from _helpers import _bf16_ulp, gemm_within_fp32_bound, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+MODE_CODE = {"tensor": 0, "tile": 1, "block": 2}
+BOUND = 2.0 ** -9
+
+
+@pytest.fixture(scope="module")
+def fgs():
+    import fine_grained_scaled_amd as m
+    return m
+
+
+def e4m3_operand(fgs, bits, mode, colwise=False, rows=None):
+    q, s = oracle.quant_e4m3(bits, mode, colwise=colwise)
+    s_abi = np.ascontiguousarray(s.T) if mode == "tile" else (s if mode == "block" else s.reshape(1))
+    if rows is None:
+        deq = oracle.dequant_e4m3(q, s, mode)
+    elif mode == "tile":
+        deq = oracle.dequant_e4m3(q[rows], s[rows], mode)
+    elif mode == "tensor":
+        deq = oracle.dequant_e4m3(q[rows], s, mode)
+    else:
+        deq = oracle.dequant_e4m3(q, s, mode)[rows]
+    op = fgs.Operand(torch.from_numpy(q).cuda(), torch.from_numpy(np.ascontiguousarray(s_abi)).cuda(),
+                     MODE_CODE[mode])
+    return op, deq
+
+
+def mx_operand(fgs, bits, colwise=False, rows=None):
+    q, s = oracle.quant_mx(bits, colwise=colwise)
+    deq = oracle.dequant_mx(q if rows is None else q[rows], s if rows is None else s[rows])
+    return fgs.Operand(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), fgs.SCALE_MX32_E8M0), deq
+
+
+def tensor_operand(fgs, bits, elem):
+    hist = [np.float32(np.abs(oracle.bf16_bits_to_f32(bits)).max())]     # this tensor's own amax
+    q, s, _ = oracle.quant_delayed(bits, elem, hist)
+    code = fgs.ELEM_E5M2 if elem == "e5m2" else fgs.ELEM_E4M3
+    op = fgs.Operand(torch.from_numpy(q).cuda(), torch.tensor([s], dtype=torch.float32, device="cuda"),
+                     fgs.SCALE_TENSOR, code)
+    return op, oracle.dequant_tensor(q, s, elem)
+
+
+def check(fgs, A, B, ah, bh, out, rows=None):
+    """Runs the FP8-instruction GEMM and checks the derived bound; returns
+    the worst err / S (for the report) ."""
+    c = fgs.gemm_block_scaled(A, B, out, fp8_mma=True)
+    torch.cuda.synchronize()
+    c = c.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        c = c[rows]
+    cref, sref = oracle.gemm_ref(ah, bh)
+    err = np.abs(c - cref)
+    bound = BOUND * sref + 1e-6
+    if out == torch.bfloat16:
+        bound = bound + _bf16_ulp(cref)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{int(bad.sum())} outputs outside 2^-9*S: worst err/S = {float((err / np.maximum(sref, 1e-30)).max())}"
+    return float((err / np.maximum(sref, 1e-30)).max())
+
+
+MODES = [("tile", "block"), ("tile", "tile"), ("tensor", "tensor"), ("tile", "tensor"),
+         ("tensor", "block"), ("tensor", "tile")]
+
+
+@pytest.mark.parametrize("amode,bmode", MODES)
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (1, 1, 128), (257, 129, 256), (520, 777, 384)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_fp8mma_modes_ragged(fgs, amode, bmode, M, N, K, out):
+    A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=M + K), amode)
+    B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=N + K), bmode)
+    check(fgs, A, B, ah, bh, out)
+
+
+def test_fp8mma_adversarial_promotion(fgs):
+    """Every 128-K block of A has its own scale in 2^-20 .. 2^20: without the
+    per-block FP32 promotion of sA * sB the result would be off by orders of
+    magnitude."""
+    M, N, K = 128, 256, 1024
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=7, outliers=False)).copy()
+    for kb in range(K // 128):
+        a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
+    A, ah = e4m3_operand(fgs, synth.f32_to_bf16_bits(a), "tile")
+    B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=8), "block")
+    check(fgs, A, B, ah, bh, torch.float32)
+
+
+@pytest.mark.parametrize("ea,eb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("M,N,K", [(257, 129, 256), (520, 777, 384)])
+def test_fp8mma_e5m2_operands(fgs, ea, eb, M, N, K):
+    """Per-tensor operands in either FP8 format (the E4M3/E5M2 hybrid): the
+    instruction takes each operand's format directly."""
+    a = synth.gradients(M, K, seed=M) if ea == "e5m2" else synth.activations(M, K, seed=M)
+    b = synth.gradients(N, K, seed=N + 1) if eb == "e5m2" else synth.weights(N, K, seed=N + 1)
+    A, ah = tensor_operand(fgs, a, ea)
+    B, bh = tensor_operand(fgs, b, eb)
+    check(fgs, A, B, ah, bh, torch.float32)
+    check(fgs, A, B, ah, bh, torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (257, 129, 256), (256, 384, 1024)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_fp8mma_mx_ragged(fgs, M, N, K, out):
+    A, ah = mx_operand(fgs, synth.activations(M, K, seed=M + 3, outliers=False))
+    B, bh = mx_operand(fgs, synth.weights(N, K, seed=N + 5))
+    check(fgs, A, B, ah, bh, out)
+
+
+def test_fp8mma_mx_exponent_spread(fgs):
+    """Every 32-block of both operands scaled by its own power of two in
+    2^-40 .. 2^40: a scale byte applied to the wrong 32 codes (the other lane
+    half, the other k-step, the other operand) is off by up to 2^80."""
+    M, N, K = 256, 256, 512
+    rng = np.random.default_rng(21)
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=22, outliers=False)).copy()
+    b = oracle.bf16_bits_to_f32(synth.weights(N, K, seed=23)).copy()
+    a *= np.repeat(np.ldexp(1.0, rng.integers(-40, 41, (M, K // 32))), 32, axis=1).astype(np.float32)
+    b *= np.repeat(np.ldexp(1.0, rng.integers(-40, 41, (N, K // 32))), 32, axis=1).astype(np.float32)
+    A, ah = mx_operand(fgs, synth.f32_to_bf16_bits(a))
+    B, bh = mx_operand(fgs, synth.f32_to_bf16_bits(b))
+    check(fgs, A, B, ah, bh, torch.float32)
+
+
+@pytest.mark.parametrize("policy", ["narrow", "wide"])
+def test_fp8mma_tile_policies(fgs, policy):
+    """Per-tensor and MX operands on either workgroup tile."""
+    M, N, K = 520, 777, 384
+    prev = fgs.gemm_tile_policy(policy)
+    try:
+        A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=30), "tensor")
+        B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=31), "tensor")
+        check(fgs, A, B, ah, bh, torch.float32)
+        A, ah = mx_operand(fgs, synth.activations(M, K, seed=30, outliers=False))
+        B, bh = mx_operand(fgs, synth.weights(N, K, seed=31))
+        check(fgs, A, B, ah, bh, torch.bfloat16)
+    finally:
+        fgs.gemm_tile_policy(prev)
+
+
+def test_fp8mma_determinism(fgs):
+    A, _ = e4m3_operand(fgs, synth.activations(512, 1024, seed=3), "tile")
+    B, _ = e4m3_operand(fgs, synth.weights(768, 1024, seed=4), "block")
+    c1 = fgs.gemm_block_scaled(A, B, fp8_mma=True)
+    c2 = fgs.gemm_block_scaled(A, B, fp8_mma=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+def test_fp8mma_rejects_nvfp4(fgs):
+    x = synth.to_torch_bf16(synth.activations(128, 256, seed=1)).cuda()
+    nv = fgs.quantize_nvfp4(x)
+    with pytest.raises(fgs.FgsError, match="E4M3 / E5M2"):
+        fgs.gemm_block_scaled(nv.rowwise(), nv.rowwise(), fp8_mma=True)
+
+
+def test_fp8mma_less_accurate_than_exact(fgs):
+    """The reason this path is not the default: on the outlier-channel
+    activations its error is larger than the exact GEMM's, which meets
+    1e-5 * S + 1e-6 on the same operands."""
+    M, N, K = 512, 512, 2048
+    A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=40), "tile")
+    B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=41), "block")
+    cref, sref = oracle.gemm_ref(ah, bh)
+    c_exact = fgs.gemm_block_scaled(A, B).cpu().numpy().astype(np.float64)
+    c_mma = fgs.gemm_block_scaled(A, B, fp8_mma=True).cpu().numpy().astype(np.float64)
+    ok, _ = gemm_within_fp32_bound(c_exact, cref, sref)
+    assert ok
+    e_exact = float((np.abs(c_exact - cref) / sref).max())
+    e_mma = float((np.abs(c_mma - cref) / sref).max())
+    print(f"max |C - C_ref| / S: exact {e_exact:.3g}, FP8 instructions {e_mma:.3g}")
+    assert e_mma <= BOUND
+    assert e_mma > e_exact
+
+
+@pytest.mark.parametrize("orient", ["fwd", "wgrad"])
+def test_fp8mma_llama3_8b_qkv_sampled(fgs, orient):
+    """Llama-3-8B QKV projection at full size (M = 8192 tokens, K = 4096,
+    N = 6144), blockwise recipe as the bench times it: fwd (1x128 x 128x128,
+    BF16 out) and wgrad (dY^T x X^T, both 1x128 along the 8192 tokens, FP32
+    out); rows {0, 127, one hashed} of every 128-row tile."""
+    M, K, N = 8192, 4096, 6144
+    if orient == "fwd":
+        a_bits, b_bits = synth.activations(M, K, seed=0), synth.weights(N, K, seed=0)
+        amode, bmode, a_col, b_col, out = "tile", "block", False, False, torch.bfloat16
+    else:
+        a_bits, b_bits = synth.gradients(M, N, seed=0), synth.activations(M, K, seed=0)
+        amode, bmode, a_col, b_col, out = "tile", "tile", True, True, torch.float32
+    rows_total = a_bits.shape[1] if a_col else a_bits.shape[0]
+    rs = sample_rows(rows_total)
+    A, ah = e4m3_operand(fgs, a_bits, amode, colwise=a_col, rows=rs)
+    B, bh = e4m3_operand(fgs, b_bits, bmode, colwise=b_col)
+    check(fgs, A, B, ah, bh, out, rows=rs)
