@@ -99,11 +99,14 @@ int fgs_gemm_tile_policy(int policy)
     return fgs::set_gemm_tile_policy(policy);
 }
 
+// The tensor-amax passes keep one partial per amax workgroup (4 bytes for
+// TENSOR mode, 8 for NVFP4's two orientations), up to two workgroups per
+// compute unit: 4 KiB covers 256 compute units at full speed.
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols)
 {
     (void)rows;
     (void)cols;
-    return 256;
+    return 4096;
 }
 
 int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
@@ -129,7 +132,7 @@ int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ld
         if (!workspace || workspace_bytes < 4) return fail(FGS_ERR_INVALID_ARG, "TENSOR mode needs a workspace of >= 4 bytes");
         if (!aligned(workspace, 4)) return fail(FGS_ERR_UNSUPPORTED, "workspace must be 4-byte aligned");
     }
-    fgs::QuantE4M3Args a{x, rows, cols, ldx, mode, q, scales, qT, scalesT, workspace};
+    fgs::QuantE4M3Args a{x, rows, cols, ldx, mode, q, scales, qT, scalesT, workspace, workspace_bytes};
     return hip_status(fgs::launch_quant_e4m3(a, static_cast<hipStream_t>(stream)), "quantize_blockwise launch");
 }
 
@@ -197,7 +200,7 @@ int fgs_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, int64_t ldx,
         if (!aligned(qT, 16)) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte aligned");
     }
     fgs::QuantNVFP4Args a{x, rows, cols, ldx, rht_mask, rht_seed, round == FGS_ROUND_STOCHASTIC, sr_seed,
-                          q, scales, qT, scalesT, tensor_scale, workspace};
+                          q, scales, qT, scalesT, tensor_scale, workspace, workspace_bytes};
     return hip_status(fgs::launch_quant_nvfp4(a, static_cast<hipStream_t>(stream)), "quantize_nvfp4 launch");
 }
 

@@ -18,7 +18,8 @@ struct QuantE4M3Args {
     float* scales;
     uint8_t* qT;
     float* scalesT;
-    void* workspace;   // >= 4 bytes for TENSOR mode
+    void* workspace;   // TENSOR mode: one uint32 amax partial per amax workgroup
+    size_t workspace_bytes;
 };
 hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream);
 
@@ -76,7 +77,8 @@ struct QuantNVFP4Args {
     uint8_t* qT;
     uint8_t* scalesT;
     float* tensor_scale;
-    void* workspace;   // >= 8 bytes
+    void* workspace;   // two uint32 amax partials per amax workgroup
+    size_t workspace_bytes;
 };
 hipError_t launch_quant_nvfp4(const QuantNVFP4Args& a, hipStream_t stream);
 

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, float* __restrict__ scales,
     uint8_t* __restrict__ qT, float* __restrict__ scalesT,
-    const uint32_t* __restrict__ tensor_amax,
+    const uint32_t* __restrict__ tensor_amax, int32_t n_amax,
     const int32_t* __restrict__ offsets, int32_t G, int64_t ldqT,
     const int32_t* __restrict__ row_index, int64_t src_rows, uint16_t* __restrict__ h_out)
 {
@@ -208,7 +208,15 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
             if (qT) scalesT[blockIdx.x * ((rows + TB - 1) / TB) + blockIdx.y] = shared_b.s;
         }
     } else if constexpr (MODE == FGS_SCALE_TENSOR) {
-        shared_b = e4m3_block_from_amax_bits(tensor_amax[0]);
+        // the tensor amax: the max of the amax pass's per-workgroup partials
+        // (read after this block's own loads are in flight)
+        uint32_t m = 0;
+        for (int i = t; i < n_amax; i += 256) m = max(m, tensor_amax[i]);
+        m = max_xor32(max_xor16(max_lanes16(m)));
+        if (l == 0) red[w][0] = m;
+        __syncthreads();
+        m = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
+        shared_b = e4m3_block_from_amax_bits(m);
         if (t == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
             if (scales) scales[0] = shared_b.s;
             if (scalesT) scalesT[0] = shared_b.s;
@@ -296,9 +304,11 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     }
 }
 
-// Tensor amax (|BF16| bits) of a 128 x 128-block grid: persistent over the
-// blocks with stride gridDim.x, the next block's rows loaded before the
-// current ones are reduced; one atomic per workgroup.
+// Tensor amax (|BF16| bits) of a 128 x 128-block grid, as one partial per
+// workgroup (out[blockIdx.x]; the cast kernel takes the max of the
+// gridDim.x partials, so no same-address atomics and no clearing pass):
+// persistent over the blocks with stride gridDim.x, the next block's rows loaded before the
+// current ones are reduced.
 __global__ __launch_bounds__(256) void amax_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     int64_t nbr, int64_t nbc, uint32_t* __restrict__ out)
@@ -333,15 +343,7 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(
     m = max_xor32(max_xor16(max_lanes16(m)));
     if (l == 0) red[w] = m;
     __syncthreads();
-    if (t == 0) {
-        m = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(out, m);
-    }
-}
-
-__global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v)
-{
-    if ((int)threadIdx.x < n) p[threadIdx.x] = v;
+    if (t == 0) out[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 } // namespace
@@ -355,21 +357,25 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
     switch (a.mode) {
     case FGS_SCALE_TILE_1x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0, nullptr);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, 0, nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     case FGS_SCALE_BLOCK_128x128:
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_BLOCK_128x128, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, nullptr, 0, 0, nullptr, 0, nullptr);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, 0, nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     case FGS_SCALE_TENSOR: {
+        // amax workgroups: two per compute unit (each keeps two blocks of
+        // loads in flight), at most one per 4-byte workspace slot
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, amax, 1, 0u);
-        const int64_t nblk = nbr * nbc, cap = (int64_t)device_cus() * 8;
-        const unsigned g = (unsigned)(nblk < cap ? nblk : cap);
-        hipLaunchKernelGGL(amax_bf16_kernel, dim3(g), block, 0, stream,
+        int64_t g = nbr * nbc;
+        const int64_t cap = (int64_t)device_cus() * 2, slots = (int64_t)(a.workspace_bytes / 4);
+        if (g > cap) g = cap;
+        if (g > slots) g = slots;
+        hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)g), block, 0, stream,
                            x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TENSOR, false>), grid, block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, nullptr, 0, 0, nullptr, 0, nullptr);
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, (int32_t)g,
+                           nullptr, 0, 0, nullptr, 0, nullptr);
         break;
     }
     default:
@@ -387,11 +393,11 @@ hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t s
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (a.swiglu)
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true, true>), grid, dim3(256), 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, 0, a.group_offsets,
                            a.G, a.ldqT, a.row_index, a.src_rows, a.h_out);
     else
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true>), grid, dim3(256), 0, stream,
-                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, a.group_offsets,
+                           x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, nullptr, 0, a.group_offsets,
                            a.G, a.ldqT, a.row_index, a.src_rows, nullptr);
     return hipGetLastError();
 }

@@ -25,8 +25,8 @@
 // fmix32 being MurmurHash3's 32-bit finalizer.
 //
 // Two kernels: a tensor-amax pass (both orientations from one read, one
-// atomic max per workgroup and orientation into the workspace) and the
-// quantize pass.  One workgroup (256 threads, 4 waves) owns a 128 x 128
+// partial per workgroup and orientation in the workspace) and the quantize
+// pass, which takes the max of the partials.  One workgroup (256 threads, 4 waves) owns a 128 x 128
 // tile of x; thread t (wave w, lane l) holds the 8 x 8 sub-block with
 // columns 8*(l & 15) .. +7 and rows 8*(4w + (l >> 4)) .. +7.  A row-wise
 // 16-chunk spans lanes l, l ^ 1; a column-wise one spans lanes l, l ^ 16.
@@ -309,8 +309,8 @@ __device__ __forceinline__ uint32_t bf16_amax8_bits(const uint4& v)
 // Tensor amax of both orientations (of the transformed values where the
 // transform applies).  Persistent over 128 x 128 tiles with stride
 // gridDim.x, the next tile's rows loaded before the current one is reduced;
-// one atomic max per workgroup and orientation, a few per CU in all (one
-// per tile made the atomics on the two words the bottleneck).
+// each workgroup stores its two maxima to ws[2 * blockIdx.x + o] (o = 0
+// row-wise, 1 column-wise): no same-address atomics, no clearing pass.
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     int rht_mask, uint32_t sign_mask, uint32_t* __restrict__ ws)
@@ -379,10 +379,7 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
         red[1][w] = mcol;
     }
     __syncthreads();
-    if (t < 2) {
-        const uint32_t m = max(max(red[t][0], red[t][1]), max(red[t][2], red[t][3]));
-        atomicMax(ws + t, m);
-    }
+    if (t < 2) ws[2 * blockIdx.x + t] = max(max(red[t][0], red[t][1]), max(red[t][2], red[t][3]));
 }
 
 // ---------------------------------------------------------------- pass 2 --
@@ -392,9 +389,10 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     int rht_mask, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
     uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ qT, uint8_t* __restrict__ scalesT,
-    float* __restrict__ tensor_scale, const uint32_t* __restrict__ ws)
+    float* __restrict__ tensor_scale, const uint32_t* __restrict__ ws, int32_t n_amax)
 {
     __shared__ __align__(16) uint8_t tbuf[TB][TB / 2 + TPAD];
+    __shared__ uint32_t s_red[2][4];
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int cg = l & 15, rg = 4 * w + (l >> 4);
     const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
@@ -403,8 +401,22 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     uint4 v[8];
     load_tile(x, rows, cols, ldx, r0, col, rg, col_ok, v);
 
-    const TensorScale ts_row = tensor_scale_from(ws[0]);
-    const TensorScale ts_col = tensor_scale_from(ws[1]);
+    // tensor amax of each orientation: the max of the amax pass's partials
+    // (read after this tile's loads are in flight)
+    uint32_t mr = 0, mc = 0;
+    for (int i = t; i < n_amax; i += 256) {
+        mr = max(mr, ws[2 * i]);
+        mc = max(mc, ws[2 * i + 1]);
+    }
+    mr = max_xor32(max_xor16(max_lanes16(mr)));
+    mc = max_xor32(max_xor16(max_lanes16(mc)));
+    if (l == 0) {
+        s_red[0][w] = mr;
+        s_red[1][w] = mc;
+    }
+    __syncthreads();
+    const TensorScale ts_row = tensor_scale_from(max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3])));
+    const TensorScale ts_col = tensor_scale_from(max(max(s_red[1][0], s_red[1][1]), max(s_red[1][2], s_red[1][3])));
     // SR: the hash's seed rounds per row of this thread
     uint32_t midr[8], ilo[8];
     if constexpr (SR) {
@@ -506,11 +518,6 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     }
 }
 
-__global__ void nvfp4_clear_kernel(uint32_t* ws)
-{
-    if (threadIdx.x < 2) ws[threadIdx.x] = 0u;
-}
-
 // Sign mask of the random Hadamard transform: bit j set <=> d_j = -1, with
 // d_j from bit 0 of fmix32(j ^ key), key = fmix32(lo32(seed) ^ fmix32(hi32(seed))).
 uint32_t host_fmix32(uint32_t h)
@@ -541,17 +548,21 @@ hipError_t launch_quant_nvfp4(const QuantNVFP4Args& a, hipStream_t stream)
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     uint32_t* ws = static_cast<uint32_t*>(a.workspace);
     const uint32_t mask = rht_sign_mask(a.rht_seed);
-    hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, ws);
-    const int64_t nblk = nbr * nbc, cap = (int64_t)device_cus() * 8;
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)(nblk < cap ? nblk : cap)), block, 0, stream,
+    // amax workgroups: two per compute unit, at most one per 8-byte
+    // workspace slot (two partials each)
+    int64_t g = nbr * nbc;
+    const int64_t cap = (int64_t)device_cus() * 2, slots = (int64_t)(a.workspace_bytes / 8);
+    if (g > cap) g = cap;
+    if (g > slots) g = slots;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)g), block, 0, stream,
                        x, a.rows, a.cols, a.ldx, a.rht_mask, mask, ws);
     const uint32_t slo = (uint32_t)a.sr_seed, shi = (uint32_t)(a.sr_seed >> 32);
     if (a.stochastic)
         hipLaunchKernelGGL(nvfp4_quant_kernel<true>, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask,
-                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws);
+                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws, (int32_t)g);
     else
         hipLaunchKernelGGL(nvfp4_quant_kernel<false>, grid, block, 0, stream, x, a.rows, a.cols, a.ldx, a.rht_mask,
-                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws);
+                           mask, slo, shi, a.q, a.scales, a.qT, a.scalesT, a.tensor_scale, ws, (int32_t)g);
     return hipGetLastError();
 }
 

@@ -91,9 +91,11 @@ class Quantized:
 
 
 def quantize_blockwise(x: torch.Tensor, mode: str = "tile", rowwise: bool = True,
-                       colwise: bool = False) -> Quantized:
+                       colwise: bool = False, workspace: Optional[torch.Tensor] = None) -> Quantized:
     """Online FP32-scaled E4M3 quantization (1x128 tiles, 128x128 blocks or
-    one per-tensor scale); row-wise and/or transposed (column-wise) outputs."""
+    one per-tensor scale); row-wise and/or transposed (column-wise) outputs.
+    workspace: optional uint8 device scratch for the per-tensor amax pass
+    (default: fgs_workspace_bytes() bytes)."""
     rows, cols, ldx = _bf16_matrix(x)
     m = MODES[mode]
     dev = x.device
@@ -114,10 +116,13 @@ def quantize_blockwise(x: torch.Tensor, mode: str = "tile", rowwise: bool = True
             sT = torch.empty(((cols + 127) // 128, (rows + 127) // 128), dtype=torch.float32, device=dev)
         else:
             sT = torch.empty(1, dtype=torch.float32, device=dev)
-    ws = _workspace(dev) if m == SCALE_TENSOR else None
+    ws = None
+    if m == SCALE_TENSOR:
+        ws = _workspace(dev) if workspace is None else workspace
+        _need_gpu(ws)
     check(_lib.load().fgs_quantize_blockwise(
         _ptr(x), rows, cols, ldx, m, _ptr(q), _ptr(s), _ptr(qT), _ptr(sT),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream()))
     return Quantized(q, s, qT, sT, m)
 
 
@@ -160,9 +165,11 @@ def quantize_mx(x: torch.Tensor, rowwise: bool = True, colwise: bool = False) ->
 
 def quantize_nvfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
                    rht_mask: int = 0, rht_seed: int = 0, stochastic: bool = False,
-                   sr_seed: int = 0) -> Quantized:
+                   sr_seed: int = 0, workspace: Optional[torch.Tensor] = None) -> Quantized:
     """NVFP4: packed E2M1 codes, E4M3 scale per 16 elements, FP32 tensor
-    scale; optional random Hadamard transform and stochastic rounding."""
+    scale; optional random Hadamard transform and stochastic rounding.
+    workspace: optional uint8 device scratch for the tensor-amax pass
+    (default: fgs_workspace_bytes() bytes)."""
     rows, cols, ldx = _bf16_matrix(x)
     dev = x.device
     q = s = qT = sT = None
@@ -173,11 +180,12 @@ def quantize_nvfp4(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
         qT = torch.empty((cols, (rows + 1) // 2), dtype=torch.uint8, device=dev)
         sT = torch.empty((cols, (rows + 15) // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(2, dtype=torch.float32, device=dev)
-    ws = _workspace(dev)
+    ws = _workspace(dev) if workspace is None else workspace
+    _need_gpu(ws)
     check(_lib.load().fgs_quantize_nvfp4(
         _ptr(x), rows, cols, ldx, rht_mask, rht_seed & (2**64 - 1),
         ROUND_STOCHASTIC if stochastic else ROUND_RNE, sr_seed & (2**64 - 1),
-        _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), _ptr(ts), _ptr(ws), ws.numel(), _stream()))
+        _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), _ptr(ts), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return Quantized(q, s, qT, sT, SCALE_NV16_E4M3, ELEM_E2M1, ts)
 
 

@@ -110,9 +110,12 @@ typedef struct {
  *   TILE re-quantizes each 128-row column segment from the BF16 source
  *   (the wgrad operand); BLOCK and TENSOR transpose the row-wise codes and
  *   scale grid (the 128x128 grid and a single scale are transpose-invariant).
- * Both outputs come from one read of x.  TENSOR mode needs a workspace of
- *   fgs_workspace_bytes() bytes (device, 4-byte aligned) for the tensor amax;
- *   TILE/BLOCK ignore it.
+ * Both outputs come from one read of x.  TENSOR mode needs a device
+ *   workspace (4-byte aligned, at least 4 bytes; its contents are scratch):
+ *   the amax pass stores one 4-byte partial per workgroup and the cast pass
+ *   takes their max.  fgs_workspace_bytes() bytes let it run two amax
+ *   workgroups per compute unit; a smaller workspace runs fewer (same
+ *   result).  TILE/BLOCK ignore it.
  * rows and cols may be 0 (nothing is enqueued).
  */
 int fgs_quantize_blockwise(const void *x, int64_t rows, int64_t cols, int64_t ldx,
@@ -174,7 +177,10 @@ int fgs_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  * Column-wise (needs rows % 128 == 0): qT [cols x rows/2], scalesT u8
  *   [cols][rows/16].
  * tensor_scale  device FP32 [2]: [0] row-wise s_t, [1] column-wise s_t.
- * workspace     fgs_workspace_bytes() bytes of device memory.
+ * workspace     device scratch, 4-byte aligned, at least 8 bytes: two 4-byte
+ *               amax partials per amax workgroup (fgs_workspace_bytes()
+ *               bytes give two workgroups per compute unit; fewer bytes,
+ *               fewer workgroups, same result).
  */
 int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
                        int rht_mask, uint64_t rht_seed, int round, uint64_t sr_seed,

@@ -145,3 +145,20 @@ def test_quant_strided_input(fgs):
     qt, st = oracle.quant_e4m3(sub, "tile", colwise=True)
     assert np.array_equal(r.q.cpu().numpy(), q) and np.array_equal(r.scales.cpu().numpy().T, s)
     assert np.array_equal(r.qT.cpu().numpy(), qt) and np.array_equal(r.scalesT.cpu().numpy().T, st)
+
+
+@pytest.mark.parametrize("ws_bytes", [4, 12, 4096])
+def test_tensor_mode_workspace_sizes(fgs, ws_bytes):
+    """The per-tensor amax pass keeps one partial per workgroup in the
+    workspace; any size from one slot up gives the oracle's codes and scale
+    (a 4-byte workspace runs one amax workgroup over every tile).  The
+    workspace starts as garbage: no pass may rely on it being cleared."""
+    bits = synth.activations(1024, 1536, seed=11)
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    r = fgs.quantize_blockwise(_dev(bits), "tensor", rowwise=True, colwise=True, workspace=ws)
+    torch.cuda.synchronize()
+    q, s = oracle.quant_e4m3(bits, "tensor")
+    qt, _ = oracle.quant_e4m3(bits, "tensor", colwise=True)
+    assert np.array_equal(r.q.cpu().numpy(), q)
+    assert np.array_equal(r.qT.cpu().numpy(), qt)
+    assert r.scales.cpu().numpy().view(np.uint32)[0] == np.asarray(s, dtype=np.float32).reshape(-1).view(np.uint32)[0]

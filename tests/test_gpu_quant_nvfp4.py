@@ -32,10 +32,11 @@ def _bits_f32(a):
     return np.asarray(a, dtype=np.float32).view(np.uint32)
 
 
-def _check(fgs, bits, rht_mask, stochastic, rowwise=True, colwise=True, rht_seed=RHT_SEED, sr_seed=SR_SEED):
+def _check(fgs, bits, rht_mask, stochastic, rowwise=True, colwise=True, rht_seed=RHT_SEED, sr_seed=SR_SEED,
+           workspace=None):
     x = synth.to_torch_bf16(bits).to("cuda")
     r = fgs.quantize_nvfp4(x, rowwise=rowwise, colwise=colwise, rht_mask=rht_mask, rht_seed=rht_seed,
-                           stochastic=stochastic, sr_seed=sr_seed)
+                           stochastic=stochastic, sr_seed=sr_seed, workspace=workspace)
     torch.cuda.synchronize()
     ts = r.tensor_scale.cpu().numpy()
     for side, on in ((0, rowwise), (1, colwise)):
@@ -145,3 +146,14 @@ def test_nvfp4_wgrad_gradient_full_size_sampled(fgs):
         q, s = oracle.quant_nvfp4_rows(valsT[c:c + 1], t1, True, SR_SEED, idx_base=int(c), idx_cs=N)
         assert np.array_equal(r.qT[int(c)].cpu().numpy(), q[0])
         assert np.array_equal(r.scalesT[int(c)].cpu().numpy(), s[0])
+
+
+@pytest.mark.parametrize("ws_bytes", [8, 24, 4096])
+def test_nvfp4_workspace_sizes(fgs, ws_bytes):
+    """The tensor-amax pass keeps two partials per workgroup in the
+    workspace; any size from one slot pair up gives the oracle's result (an
+    8-byte workspace runs one amax workgroup over every tile).  The
+    workspace starts as garbage: no pass may rely on it being cleared."""
+    bits = synth.gradients(768, 1024, seed=44)
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    _check(fgs, bits, 2, True, workspace=ws)
