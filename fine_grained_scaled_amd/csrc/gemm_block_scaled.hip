@@ -147,6 +147,18 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
+// FP8 x FP8 MFMA, 16x16 outputs, 128-deep K (one whole scale block), unit
+// scales, from zero: the block's partial sums in one instruction.  Lane l
+// holds row l % 16 and 32 codes of K (lane group l / 16); output lane l
+// holds column l % 16 of rows 4 * (l / 16) .. +3.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int FA, int FB>
+__device__ __forceinline__ f32x4 mfma8_k128(const i32x8& a, const i32x8& b)
+{
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, FA, FB, 0, 127, 0, 127);
+}
+
 // 16 E4M3 codes (one 16-byte LDS read) -> two exact FP16 8-vectors: bytes
 // 0..7 feed one MFMA k-step, bytes 8..15 the next.
 __device__ __forceinline__ void decode16(const uint4 v, f16x8& lo, f16x8& hi)
@@ -258,11 +270,12 @@ using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
 
-template <class S, int ROW, bool B_TILE>
+template <class S, int ROW, bool B_TILE, bool A_TILE = false>
 struct Lds {
     static constexpr int A_BYTES = S::BM * ROW;
     static constexpr int B_BYTES = S::BN * ROW;
-    static constexpr int STAGE = A_BYTES + B_BYTES + (B_TILE ? S::BN * 4 : 0);   // + B 1x128 scales of the block
+    static constexpr int SB_BYTES = B_TILE ? S::BN * 4 : 0;                    // B 1x128 scales of the block
+    static constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES + (A_TILE ? S::BM * 4 : 0);   // + A 1x128 scales
 };
 
 // Tile schedules: one dense problem; MoE groups of rows (each with its own
@@ -289,15 +302,24 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                              AMODE != FGS_SCALE_NV16_E4M3 && AMODE != FGS_SCALE_MX32_E8M0;
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
     constexpr bool MX = AMODE == FGS_SCALE_MX32_E8M0;
+    // promoted modes on the FP8 instructions at the 256 x 256 tile: 16x16x128
+    // instructions, each one scale block, promoted as soon as it is formed,
+    // so no partial-sum array has to live across the block (it would not fit
+    // beside 128 accumulators at two waves per SIMD)
+    constexpr bool MMA16 = MMA8 && PROMOTE && TI == 4;
+    // MMA16 with 1x128 A scales stages them in LDS with the codes (eight
+    // rows per lane would not fit in registers)
+    constexpr bool A_LDS = MMA16 && AMODE == FGS_SCALE_TILE_1x128;
     constexpr bool NV = AMODE == FGS_SCALE_NV16_E4M3;
     // staged row: 128 K-elements = 128 bytes (E4M3) or 64 bytes (E2M1)
     constexpr int ROW = NV ? 64 : 128;
     constexpr int CPR = ROW / 16;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
     constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
-    using L = Lds<S, ROW, B_TILE>;
+    using L = Lds<S, ROW, B_TILE, A_LDS>;
     static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN % 128 != 0), "128x128 B blocks need 128-aligned tiles");
     static_assert(BN / 64 <= NW, "B 1x128 scale staging needs BN / 64 waves");
+    static_assert(!A_LDS || BM / 64 <= NW, "A 1x128 scale staging needs BM / 64 waves");
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
@@ -456,6 +478,10 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
     int64_t sb_col = n0 + 64 * (w % (BN / 64)) + l;   // B 1x128 scales: waves 0 .. BN/64-1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
+    // A 1x128 scales (A_LDS): waves NW - BM/64 .. NW-1 stage 64 rows each
+    constexpr int SAW0 = NW - BM / 64;
+    int64_t sa_row = m0 + 64 * ((w - SAW0) & (BM / 64 - 1)) + l;
+    sa_row = sa_row < m_end ? sa_row : m_end - 1;
 
     // Rows of the tile that exist; a wave-instruction whose rows all lie past
     // them is not issued (its LDS rows only feed outputs that are never
@@ -475,6 +501,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             if (B_ROWS * w + RPI * u < b_live) g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
         if constexpr (B_TILE)
             if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
+        if constexpr (A_LDS)
+            if (w >= SAW0) g2lds4(sAp + kb * p.M + sa_row, st + L::A_BYTES + L::B_BYTES + L::SB_BYTES + 256 * (w - SAW0));
     };
 
     // rows of this lane's accumulators: m = m0 + WM*wm + 32*i + (l & 31)
@@ -568,7 +596,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // prologue: block 0 -> stage 0
     if (nkb > 0) stage_block(0, 0);
     float sa_next[TI];
-    if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
+    if constexpr (AMODE == FGS_SCALE_TILE_1x128 && !A_LDS) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) sa_next[i] = nkb > 0 ? sAp[am[i]] : 0.0f;
     }
@@ -592,7 +620,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         // scales of this block (prefetched one block ahead)
         float sa[TI];
 #pragma unroll
-        for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 ? sa_next[i] : 1.0f;
+        for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 && !A_LDS ? sa_next[i] : 1.0f;
         const float sb_blk = sb_next;
         uint32_t a_sw[TI], b_sw[TJ], a_nw[TI][2], b_nw[TJ][2];
         if constexpr (NV) {
@@ -609,7 +637,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         }
         if (more) {
             stage_block(kb + 1, cur ^ 1);
-            if constexpr (AMODE == FGS_SCALE_TILE_1x128) {
+            if constexpr (AMODE == FGS_SCALE_TILE_1x128 && !A_LDS) {
 #pragma unroll
                 for (int i = 0; i < TI; ++i) sa_next[i] = sAp[(kb + 1) * p.M + am[i]];
             }
@@ -640,7 +668,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
 
             f32x16 part[TI][TJ];
-            if constexpr (PROMOTE) {
+            if constexpr (PROMOTE && !MMA16) {
     #pragma unroll
                 for (int i = 0; i < TI; ++i)
     #pragma unroll
@@ -687,6 +715,59 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                         for (int i = 0; i < TI; ++i)
     #pragma unroll
                             for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
+                    }
+                }
+            } else if constexpr (MMA16) {
+                // 16x16 output tiles: A sub-tile a (rows 16 a ..) x B sub-tile
+                // b (columns 16 b ..) lands in acc[a / 2][b / 2] floats
+                // 4 (2 (a % 2) + b % 2) .. +3.  Lane group g = l / 16 holds
+                // chunk g in bytes 0-15 and chunk 4 + g in bytes 16-31 of its
+                // row, for A and B alike.
+                constexpr int FB = (ELEMS & 2) ? 1 : 0, FA = (ELEMS & 1) ? 1 : 0;
+                const int r16 = l & 15, g4 = l >> 4;
+                const int sw16 = (r16 >> SH) & (CPR - 1);
+                const int c0 = (g4 ^ sw16) << 4, c1 = ((4 + g4) ^ sw16) << 4;
+                const uint8_t* la16 = st + (WM * wm + r16) * ROW;
+                const uint8_t* lb16 = st + L::A_BYTES + (64 * wn + r16) * ROW;
+                i32x8 bfr[2 * TJ];
+    #pragma unroll
+                for (int b = 0; b < 2 * TJ; ++b) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(lb16 + 16 * b * ROW + c0);
+                    const uint4 y = *reinterpret_cast<const uint4*>(lb16 + 16 * b * ROW + c1);
+                    bfr[b] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                }
+                const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
+                const float fb = BMODE == FGS_SCALE_TENSOR ? sBp[0] : (BMODE == FGS_SCALE_BLOCK_128x128 ? sb_blk : 1.0f);
+                // B 1x128 scales of this lane's columns 64 wn + 16 b + 4 g4 .. +3
+                float4 sbt[B_TILE ? 2 * TJ : 1];
+                if constexpr (B_TILE) {
+                    const float* ssb = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES);
+    #pragma unroll
+                    for (int b = 0; b < 2 * TJ; ++b)
+                        sbt[b] = *reinterpret_cast<const float4*>(ssb + 64 * wn + 16 * b + 4 * g4);
+                }
+    #pragma unroll
+                for (int a = 0; a < 2 * TI; ++a) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c0);
+                    const uint4 y = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c1);
+                    const i32x8 afr = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                    float fa = sa_t;
+                    if constexpr (A_LDS)
+                        fa = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES + L::SB_BYTES)[WM * wm + 16 * a + r16];
+    #pragma unroll
+                    for (int b = 0; b < 2 * TJ; ++b) {
+                        const f32x4 pb = mfma8_k128<FB, FA>(bfr[b], afr);
+                        const int sub = 4 * (2 * (a & 1) + (b & 1));
+                        f32x16& ac = acc[a >> 1][b >> 1];
+                        if constexpr (B_TILE) {
+                            const float sbv[4] = {sbt[b].x, sbt[b].y, sbt[b].z, sbt[b].w};
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) ac[sub + e] = __builtin_fmaf(pb[e], fa * sbv[e], ac[sub + e]);
+                        } else {
+                            const float f = fa * fb;
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) ac[sub + e] = __builtin_fmaf(pb[e], f, ac[sub + e]);
+                        }
                     }
                 }
             } else if constexpr (MMA8) {
@@ -768,7 +849,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 }
             }
 
-            if constexpr (PROMOTE) {
+            if constexpr (PROMOTE && !MMA16) {
                 const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
                 const float sb_t = BMODE == FGS_SCALE_TENSOR ? sBp[0] : 1.0f;
                 if constexpr (B_TILE) {
@@ -840,7 +921,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // (wn, wn ^ 1), 32 values per lane and 64 per lane pair (l, l ^ 32): the
     // row maxima meet in the LDS stages, free once the K loop's last barrier
     // has passed.  Launches with q_out need N % 128 == 0.
-    if constexpr (OUT_BF16 && GROUP != GROUP_K) {
+    if constexpr (OUT_BF16 && GROUP != GROUP_K && !MMA16) {
         if (p.q_out) {
             uint32_t* rmax = reinterpret_cast<uint32_t*>(smem);      // [BM][NWN] |BF16| bits
 #pragma unroll
@@ -886,15 +967,21 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     }
 
     // ------------------------------------------------------ epilogue --
+    // acc[i][j] floats 4q .. 4q+3 are four consecutive columns of one row:
+    // 32x32 tiles: row 32 i + l % 32, columns 32 j + 8 q + 4 (l / 32) ..;
+    // 16x16 tiles (MMA16): row 32 i + 16 (q / 2) + l % 16, columns
+    // 32 j + 16 (q % 2) + 4 (l / 16) ..
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-        const int64_t m = m0 + WM * wm + 32 * i + (l & 31);
-        if (m >= m_end) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
+                const int64_t m = MMA16 ? m0 + WM * wm + 32 * i + 16 * (q >> 1) + (l & 15)
+                                        : m0 + WM * wm + 32 * i + (l & 31);
+                if (m >= m_end) continue;
+                const int64_t n = MMA16 ? n0 + 64 * wn + 32 * j + 16 * (q & 1) + 4 * (l >> 4)
+                                        : n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
                 if constexpr (OUT_BF16) {
                     uint16_t* C = static_cast<uint16_t*>(p.C) + c_off + m * p.ldc + n;
                     const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
@@ -930,7 +1017,8 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUP == GROUP_M ? a.G : 0));
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
-    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128>::STAGE;
+    constexpr bool a_lds = MMA8 && S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
+    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds>::STAGE;
     auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS, MMA8>
                   : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS, MMA8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -972,10 +1060,22 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
     constexpr int NONE = GROUP_NONE;
     const bool wide = prefer_wide(a);
     const int amode = a.A.scale_mode, bmode = a.B.scale_mode;
+    // promoted modes: the 256 x 128 tile, or on the FP8 instructions either
+    // tile (16x16x128 instructions at 256 x 256)
+    constexpr int TL = FGS_SCALE_TILE_1x128, BL = FGS_SCALE_BLOCK_128x128, TN = FGS_SCALE_TENSOR;
+    auto promoted = [&](auto am, auto bm) -> hipError_t {
+        constexpr int A_ = decltype(am)::value, B_ = decltype(bm)::value;
+        if constexpr (MMA8)
+            if (wide) return launch_modes<W, A_, B_, NONE, 0, true>(p, a, bf16, s);
+        return launch_modes<D, A_, B_, NONE, 0, MMA8>(p, a, bf16, s);
+    };
+    using IC_TL = std::integral_constant<int, TL>;
+    using IC_BL = std::integral_constant<int, BL>;
+    using IC_TN = std::integral_constant<int, TN>;
     if (amode == FGS_SCALE_TILE_1x128) {
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, NONE, 0, MMA8>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, NONE, 0, MMA8>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TENSOR) return launch_modes<D, FGS_SCALE_TILE_1x128, FGS_SCALE_TENSOR, NONE, 0, MMA8>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return promoted(IC_TL{}, IC_BL{});
+        if (bmode == FGS_SCALE_TILE_1x128) return promoted(IC_TL{}, IC_TL{});
+        if (bmode == FGS_SCALE_TENSOR) return promoted(IC_TL{}, IC_TN{});
     } else if (amode == FGS_SCALE_MX32_E8M0 && bmode == FGS_SCALE_MX32_E8M0) {
         if (wide) return launch_modes<W, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, NONE, 0, MMA8>(p, a, bf16, s);
         return launch_modes<D, FGS_SCALE_MX32_E8M0, FGS_SCALE_MX32_E8M0, NONE, 0, MMA8>(p, a, bf16, s);
@@ -1003,8 +1103,8 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
                 return launch_modes<D, T, T, NONE, 0, MMA8>(p, a, bf16, s);
             }
         }
-        if (bmode == FGS_SCALE_BLOCK_128x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_BLOCK_128x128, NONE, 0, MMA8>(p, a, bf16, s);
-        if (bmode == FGS_SCALE_TILE_1x128) return launch_modes<D, FGS_SCALE_TENSOR, FGS_SCALE_TILE_1x128, NONE, 0, MMA8>(p, a, bf16, s);
+        if (bmode == FGS_SCALE_BLOCK_128x128) return promoted(IC_TN{}, IC_BL{});
+        if (bmode == FGS_SCALE_TILE_1x128) return promoted(IC_TN{}, IC_TL{});
     }
     return hipErrorInvalidValue;
 }

@@ -100,17 +100,43 @@ def test_fp8mma_modes_ragged(fgs, amode, bmode, M, N, K, out):
     check(fgs, A, B, ah, bh, out)
 
 
-def test_fp8mma_adversarial_promotion(fgs):
+@pytest.mark.parametrize("policy", ["narrow", "wide"])
+def test_fp8mma_adversarial_promotion(fgs, policy):
     """Every 128-K block of A has its own scale in 2^-20 .. 2^20: without the
     per-block FP32 promotion of sA * sB the result would be off by orders of
-    magnitude."""
+    magnitude.  Both workgroup tiles (32x32x64 instructions with a partial-sum
+    array, or 16x16x128 instructions promoted one by one)."""
     M, N, K = 128, 256, 1024
     a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=7, outliers=False)).copy()
     for kb in range(K // 128):
         a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
     A, ah = e4m3_operand(fgs, synth.f32_to_bf16_bits(a), "tile")
     B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=8), "block")
-    check(fgs, A, B, ah, bh, torch.float32)
+    prev = fgs.gemm_tile_policy(policy)
+    try:
+        check(fgs, A, B, ah, bh, torch.float32)
+    finally:
+        fgs.gemm_tile_policy(prev)
+
+
+PROMOTED = [("tile", "block"), ("tile", "tile"), ("tile", "tensor"), ("tensor", "block"), ("tensor", "tile")]
+
+
+@pytest.mark.parametrize("amode,bmode", PROMOTED)
+@pytest.mark.parametrize("M,N,K", [(257, 129, 256), (520, 777, 384), (1000, 600, 512)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_fp8mma_promoted_wide_tile(fgs, amode, bmode, M, N, K, out):
+    """The promoted modes on the 256 x 256 tile (16x16x128 instructions, A
+    1x128 scales staged in LDS), forced on ragged shapes the automatic choice
+    would give the narrow tile; the result equals the narrow tile's to the
+    same bound."""
+    A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=M + 2 * K), amode)
+    B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=N + 2 * K), bmode)
+    prev = fgs.gemm_tile_policy("wide")
+    try:
+        check(fgs, A, B, ah, bh, out)
+    finally:
+        fgs.gemm_tile_policy(prev)
 
 
 @pytest.mark.parametrize("ea,eb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
