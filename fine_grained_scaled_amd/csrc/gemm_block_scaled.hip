@@ -270,12 +270,14 @@ using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
 
-template <class S, int ROW, bool B_TILE, bool A_TILE = false>
+template <class S, int ROW, bool B_TILE, bool A_TILE = false, bool MXS = false>
 struct Lds {
     static constexpr int A_BYTES = S::BM * ROW;
     static constexpr int B_BYTES = S::BN * ROW;
     static constexpr int SB_BYTES = B_TILE ? S::BN * 4 : 0;                    // B 1x128 scales of the block
-    static constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES + (A_TILE ? S::BM * 4 : 0);   // + A 1x128 scales
+    static constexpr int SA_BYTES = A_TILE ? S::BM * 4 : 0;                    // A 1x128 scales
+    static constexpr int MXS_OFF = A_BYTES + B_BYTES + SB_BYTES + SA_BYTES;     // MX: the block's E8M0 word
+    static constexpr int STAGE = MXS_OFF + (MXS ? (S::BM + S::BN) * 4 : 0);    //   of every A, then B row
 };
 
 // Tile schedules: one dense problem; MoE groups of rows (each with its own
@@ -316,10 +318,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int CPR = ROW / 16;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
     constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
-    using L = Lds<S, ROW, B_TILE, A_LDS>;
+    using L = Lds<S, ROW, B_TILE, A_LDS, MX>;
     static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN % 128 != 0), "128x128 B blocks need 128-aligned tiles");
     static_assert(BN / 64 <= NW, "B 1x128 scale staging needs BN / 64 waves");
     static_assert(!A_LDS || BM / 64 <= NW, "A 1x128 scale staging needs BM / 64 waves");
+    static_assert(!MX || (BM + BN) / 64 <= NW, "MX scale staging needs (BM + BN) / 64 waves");
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
@@ -482,6 +485,19 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int SAW0 = NW - BM / 64;
     int64_t sa_row = m0 + 64 * ((w - SAW0) & (BM / 64 - 1)) + l;
     sa_row = sa_row < m_end ? sa_row : m_end - 1;
+    // MX: wave w < (BM + BN) / 64 stages the 128-K block's E8M0 word (four
+    // scale bytes) of tile row 64 w + l: A rows first, then B rows (clamped)
+    const uint8_t* mx_src = nullptr;
+    if constexpr (MX) {
+        const int rr = 64 * w + l;
+        if (rr < BM) {
+            const int64_t r = m0 + rr < m_end ? m0 + rr : m_end - 1;
+            mx_src = reinterpret_cast<const uint8_t*>(p.sA) + r * (p.K / 32);
+        } else {
+            const int64_t r = n0 + rr - BM < p.N ? n0 + rr - BM : p.N - 1;
+            mx_src = reinterpret_cast<const uint8_t*>(sBp) + r * (p.K / 32);
+        }
+    }
 
     // Rows of the tile that exist; a wave-instruction whose rows all lie past
     // them is not issued (its LDS rows only feed outputs that are never
@@ -503,6 +519,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
         if constexpr (A_LDS)
             if (w >= SAW0) g2lds4(sAp + kb * p.M + sa_row, st + L::A_BYTES + L::B_BYTES + L::SB_BYTES + 256 * (w - SAW0));
+        if constexpr (MX)
+            if (w < (BM + BN) / 64) g2lds4(mx_src + 4 * kb, st + L::MXS_OFF + 256 * w);
     };
 
     // rows of this lane's accumulators: m = m0 + WM*wm + 32*i + (l & 31)
@@ -540,7 +558,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         const int64_t n = n0 + 64 * wn + 32 * j + (l & 31);
         bn[j] = n < p.N ? n : p.N - 1;
     }
-    uint32_t a_sw_next[TI], b_sw_next[TJ];
     uint32_t ea[TI], eb = 0;
     if constexpr (MX && !MMA8) {
         // one tile row per thread: A rows 0 .. BM-1, then B rows (rows past
@@ -571,12 +588,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
 #pragma unroll
         for (int i = 0; i < TI; ++i) ea[i] = s_mx_ref[WM * wm + 32 * i + (l & 31)];
         eb = s_mx_eb;
-    }
-    if constexpr (MX) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc);
     }
     // NVFP4 scales: the eight E4M3 bytes of a fragment row's 128-K block are
     // two aligned 32-bit words (16-blocks 0-3 and 4-7)
@@ -629,12 +640,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
 #pragma unroll
             for (int j = 0; j < TJ; ++j) { b_nw[j][0] = b_nw_next[j][0]; b_nw[j][1] = b_nw_next[j][1]; }
         }
-        if constexpr (MX) {
-#pragma unroll
-            for (int i = 0; i < TI; ++i) a_sw[i] = a_sw_next[i];
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) b_sw[j] = b_sw_next[j];
-        }
         if (more) {
             stage_block(kb + 1, cur ^ 1);
             if constexpr (AMODE == FGS_SCALE_TILE_1x128 && !A_LDS) {
@@ -654,18 +659,20 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                     for (int h = 0; h < 2; ++h)
                         b_nw_next[j][h] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksn + 8 * (kb + 1) + 4 * h);
             }
-            if constexpr (MX) {
-#pragma unroll
-                for (int i = 0; i < TI; ++i) a_sw_next[i] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksc + 4 * (kb + 1));
-#pragma unroll
-                for (int j = 0; j < TJ; ++j) b_sw_next[j] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksc + 4 * (kb + 1));
-            }
         }
 
         if (wave_live) {
             const uint8_t* st = smem + cur * L::STAGE;
             const uint8_t* la = st + (WM * wm + (l & 31)) * ROW;
             const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
+            if constexpr (MX) {
+                // this block's E8M0 words of the lane's A and B rows (staged)
+                const uint32_t* mxw = reinterpret_cast<const uint32_t*>(st + L::MXS_OFF);
+    #pragma unroll
+                for (int i = 0; i < TI; ++i) a_sw[i] = mxw[WM * wm + 32 * i + (l & 31)];
+    #pragma unroll
+                for (int j = 0; j < TJ; ++j) b_sw[j] = mxw[BM + 64 * wn + 32 * j + (l & 31)];
+            }
 
             f32x16 part[TI][TJ];
             if constexpr (PROMOTE && !MMA16) {
@@ -1018,7 +1025,8 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
     constexpr bool a_lds = MMA8 && S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
-    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds>::STAGE;
+    const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds,
+                                       AMODE == FGS_SCALE_MX32_E8M0>::STAGE;
     auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS, MMA8>
                   : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS, MMA8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -1029,9 +1037,11 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
 }
 
 // The wide tile does twice the work of the 256 x 128 one in about 1.85x its
-// time (measured on the Llama-3-8B shapes), but halves the tile count, so a
-// problem whose wide tiles fill the last round poorly runs faster on the
-// narrow tile: compare rounds x time per round.
+// time on the exact path (measured on the Llama-3-8B shapes; 1.6-1.7 on
+// 8192 x 28672 x 4096) and about 1.6x on the FP8 instructions (1.45-1.65 on
+// that shape), but halves the tile count, so a problem whose wide tiles fill
+// the last round poorly runs faster on the narrow tile: compare rounds x
+// time per round.
 std::atomic<int> g_tile_policy{FGS_TILE_AUTO};
 
 bool prefer_wide(const GemmArgs& a)
@@ -1042,7 +1052,7 @@ bool prefer_wide(const GemmArgs& a)
     const int64_t tm = (a.M + ShapeWide::BM - 1) / ShapeWide::BM;
     const int64_t wide = tm * ((a.N + ShapeWide::BN - 1) / ShapeWide::BN);
     const int64_t narrow = ((a.M + ShapeDense::BM - 1) / ShapeDense::BM) * ((a.N + ShapeDense::BN - 1) / ShapeDense::BN);
-    const double t_wide = 1.85 * (double)((wide + cus - 1) / cus);
+    const double t_wide = (a.fp8_mma ? 1.6 : 1.85) * (double)((wide + cus - 1) / cus);
     const double t_narrow = (double)((narrow + cus - 1) / cus);
     return t_wide <= t_narrow;
 }
