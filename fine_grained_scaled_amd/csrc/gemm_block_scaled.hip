@@ -270,14 +270,17 @@ using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
 
-template <class S, int ROW, bool B_TILE, bool A_TILE = false, bool MXS = false>
+// SCW: scale words per tile row and K block staged with the codes (MX: the
+// four E8M0 bytes; NVFP4: the eight E4M3 bytes as two words); word h of tile
+// row rr (A rows, then B rows) at SCW_OFF + 4 (h (BM + BN) + rr).
+template <class S, int ROW, bool B_TILE, bool A_TILE = false, int SCW = 0>
 struct Lds {
     static constexpr int A_BYTES = S::BM * ROW;
     static constexpr int B_BYTES = S::BN * ROW;
     static constexpr int SB_BYTES = B_TILE ? S::BN * 4 : 0;                    // B 1x128 scales of the block
     static constexpr int SA_BYTES = A_TILE ? S::BM * 4 : 0;                    // A 1x128 scales
-    static constexpr int MXS_OFF = A_BYTES + B_BYTES + SB_BYTES + SA_BYTES;     // MX: the block's E8M0 word
-    static constexpr int STAGE = MXS_OFF + (MXS ? (S::BM + S::BN) * 4 : 0);    //   of every A, then B row
+    static constexpr int SCW_OFF = A_BYTES + B_BYTES + SB_BYTES + SA_BYTES;
+    static constexpr int STAGE = SCW_OFF + SCW * (S::BM + S::BN) * 4;
 };
 
 // Tile schedules: one dense problem; MoE groups of rows (each with its own
@@ -318,11 +321,12 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int CPR = ROW / 16;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per DMA wave-instruction (1 KiB)
     constexpr int SH = CPR == 8 ? 1 : 2;     // swizzle: slot = chunk ^ ((row >> SH) & (CPR - 1))
-    using L = Lds<S, ROW, B_TILE, A_LDS, MX>;
+    constexpr int SCW = MX ? 1 : (NV ? 2 : 0);    // block-scale words per tile row staged in LDS
+    using L = Lds<S, ROW, B_TILE, A_LDS, SCW>;
     static_assert(!(BMODE == FGS_SCALE_BLOCK_128x128 && BN % 128 != 0), "128x128 B blocks need 128-aligned tiles");
     static_assert(BN / 64 <= NW, "B 1x128 scale staging needs BN / 64 waves");
     static_assert(!A_LDS || BM / 64 <= NW, "A 1x128 scale staging needs BM / 64 waves");
-    static_assert(!MX || (BM + BN) / 64 <= NW, "MX scale staging needs (BM + BN) / 64 waves");
+    static_assert((BM + BN) % 64 == 0, "scale-word staging takes 64 tile rows per wave-instruction");
 
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_scan[NT];
@@ -485,18 +489,30 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int SAW0 = NW - BM / 64;
     int64_t sa_row = m0 + 64 * ((w - SAW0) & (BM / 64 - 1)) + l;
     sa_row = sa_row < m_end ? sa_row : m_end - 1;
-    // MX: wave w < (BM + BN) / 64 stages the 128-K block's E8M0 word (four
-    // scale bytes) of tile row 64 w + l: A rows first, then B rows (clamped)
-    const uint8_t* mx_src = nullptr;
-    if constexpr (MX) {
-        const int rr = 64 * w + l;
+    // MX / NVFP4 block scales: wave-instruction u (of SC_INSTR per stage,
+    // wave w issuing u = w, w + NW, ..) stages word u / (tile rows / 64) of
+    // the 128-K block's scale bytes of tile rows 64 (u % (rows / 64)) + l,
+    // A rows first, then B rows (clamped), so the fragment loop reads its
+    // scales from LDS instead of one scattered 4-byte global load per lane.
+    constexpr int SC_ROWS = BM + BN, SC_INSTR = SCW * SC_ROWS / 64;
+    constexpr int SC_PER_W = SCW ? (SC_INSTR + NW - 1) / NW : 1;
+    const int64_t sc_row_bytes = MX ? p.K / 32 : p.K / 16;     // scale bytes of a row
+    const uint8_t* sc_src[SC_PER_W];
+    int sc_dst[SC_PER_W];
+#pragma unroll
+    for (int k = 0; k < SC_PER_W; ++k) {
+        const int u = w + NW * k, blk = u % (SC_ROWS / 64), h = u / (SC_ROWS / 64);
+        const int rr = 64 * blk + l;
+        const uint8_t* base;
         if (rr < BM) {
             const int64_t r = m0 + rr < m_end ? m0 + rr : m_end - 1;
-            mx_src = reinterpret_cast<const uint8_t*>(p.sA) + r * (p.K / 32);
+            base = reinterpret_cast<const uint8_t*>(p.sA) + r * sc_row_bytes;
         } else {
             const int64_t r = n0 + rr - BM < p.N ? n0 + rr - BM : p.N - 1;
-            mx_src = reinterpret_cast<const uint8_t*>(sBp) + r * (p.K / 32);
+            base = reinterpret_cast<const uint8_t*>(sBp) + r * sc_row_bytes;
         }
+        sc_src[k] = base + 4 * h;
+        sc_dst[k] = L::SCW_OFF + 4 * (h * SC_ROWS + 64 * blk);
     }
 
     // Rows of the tile that exist; a wave-instruction whose rows all lie past
@@ -519,8 +535,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
         if constexpr (A_LDS)
             if (w >= SAW0) g2lds4(sAp + kb * p.M + sa_row, st + L::A_BYTES + L::B_BYTES + L::SB_BYTES + 256 * (w - SAW0));
-        if constexpr (MX)
-            if (w < (BM + BN) / 64) g2lds4(mx_src + 4 * kb, st + L::MXS_OFF + 256 * w);
+        if constexpr (SCW > 0) {
+#pragma unroll
+            for (int k = 0; k < SC_PER_W; ++k)
+                if (w + NW * k < SC_INSTR) g2lds4(sc_src[k] + 4 * SCW * kb, st + sc_dst[k]);
+        }
     };
 
     // rows of this lane's accumulators: m = m0 + WM*wm + 32*i + (l & 31)
@@ -590,19 +609,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         eb = s_mx_eb;
     }
     // NVFP4 scales: the eight E4M3 bytes of a fragment row's 128-K block are
-    // two aligned 32-bit words (16-blocks 0-3 and 4-7)
-    const int64_t ksn = p.K / 16;
-    uint32_t a_nw_next[TI][2], b_nw_next[TJ][2];
-    if constexpr (NV) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) a_nw_next[i][h] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksn + 4 * h);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) b_nw_next[j][h] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksn + 4 * h);
-    }
+    // two aligned 32-bit words (16-blocks 0-3 and 4-7), staged in LDS
 
     // prologue: block 0 -> stage 0
     if (nkb > 0) stage_block(0, 0);
@@ -634,12 +641,6 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         for (int i = 0; i < TI; ++i) sa[i] = AMODE == FGS_SCALE_TILE_1x128 && !A_LDS ? sa_next[i] : 1.0f;
         const float sb_blk = sb_next;
         uint32_t a_sw[TI], b_sw[TJ], a_nw[TI][2], b_nw[TJ][2];
-        if constexpr (NV) {
-#pragma unroll
-            for (int i = 0; i < TI; ++i) { a_nw[i][0] = a_nw_next[i][0]; a_nw[i][1] = a_nw_next[i][1]; }
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) { b_nw[j][0] = b_nw_next[j][0]; b_nw[j][1] = b_nw_next[j][1]; }
-        }
         if (more) {
             stage_block(kb + 1, cur ^ 1);
             if constexpr (AMODE == FGS_SCALE_TILE_1x128 && !A_LDS) {
@@ -647,31 +648,28 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 for (int i = 0; i < TI; ++i) sa_next[i] = sAp[(kb + 1) * p.M + am[i]];
             }
             if constexpr (BMODE == FGS_SCALE_BLOCK_128x128) sb_next = sBp[sb_row * nkb + kb + 1];
-            if constexpr (NV) {
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        a_nw_next[i][h] = *reinterpret_cast<const uint32_t*>(sA8 + am[i] * ksn + 8 * (kb + 1) + 4 * h);
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        b_nw_next[j][h] = *reinterpret_cast<const uint32_t*>(sB8 + bn[j] * ksn + 8 * (kb + 1) + 4 * h);
-            }
         }
 
         if (wave_live) {
             const uint8_t* st = smem + cur * L::STAGE;
             const uint8_t* la = st + (WM * wm + (l & 31)) * ROW;
             const uint8_t* lb = st + L::A_BYTES + (64 * wn + (l & 31)) * ROW;
-            if constexpr (MX) {
-                // this block's E8M0 words of the lane's A and B rows (staged)
-                const uint32_t* mxw = reinterpret_cast<const uint32_t*>(st + L::MXS_OFF);
+            if constexpr (SCW > 0) {
+                // this block's scale words of the lane's A and B rows (staged)
+                const uint32_t* scw = reinterpret_cast<const uint32_t*>(st + L::SCW_OFF);
     #pragma unroll
-                for (int i = 0; i < TI; ++i) a_sw[i] = mxw[WM * wm + 32 * i + (l & 31)];
+                for (int h = 0; h < SCW; ++h) {
     #pragma unroll
-                for (int j = 0; j < TJ; ++j) b_sw[j] = mxw[BM + 64 * wn + 32 * j + (l & 31)];
+                    for (int i = 0; i < TI; ++i) {
+                        const uint32_t v = scw[h * SC_ROWS + WM * wm + 32 * i + (l & 31)];
+                        if constexpr (MX) a_sw[i] = v; else a_nw[i][h] = v;
+                    }
+    #pragma unroll
+                    for (int j = 0; j < TJ; ++j) {
+                        const uint32_t v = scw[h * SC_ROWS + BM + 64 * wn + 32 * j + (l & 31)];
+                        if constexpr (MX) b_sw[j] = v; else b_nw[j][h] = v;
+                    }
+                }
             }
 
             f32x16 part[TI][TJ];
@@ -1025,8 +1023,9 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
     constexpr bool a_lds = MMA8 && S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
+    constexpr int scw = AMODE == FGS_SCALE_MX32_E8M0 ? 1 : (AMODE == FGS_SCALE_NV16_E4M3 ? 2 : 0);   // the kernel's SCW
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds,
-                                       AMODE == FGS_SCALE_MX32_E8M0>::STAGE;
+                                       scw>::STAGE;
     auto k = bf16 ? gemm_block_scaled_kernel<S, AMODE, BMODE, true, GROUP, ELEMS, MMA8>
                   : gemm_block_scaled_kernel<S, AMODE, BMODE, false, GROUP, ELEMS, MMA8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
