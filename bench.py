@@ -697,7 +697,7 @@ def read_gemm_traffic():
 
 def cpu_baseline():
     """The oracle, untuned, on a bounded sample of the headline workload: the
-    QKV layer (K = 4096, N = 6144) with M cut to 512 tokens, both recipes:
+    QKV layer (K = 4096, N = 6144) with M cut to 1024 tokens, both recipes:
     oracle quantization of X, W, dY (row-wise and column-wise) and the three
     FP64 GEMMs.  Reported in the metric's unit (GEMM TFLOP/s of the sample)."""
     import oracle
@@ -707,7 +707,7 @@ def cpu_baseline():
         blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:
         blas = 1
-    K, N, Ms = 4096, 6144, 512
+    K, N, Ms = 4096, 6144, 1024
     x = synth.activations(LLAMA8B_M, K, seed=0, row_range=(0, Ms))
     w = synth.weights(N, K, seed=0, tag=synth.TAG_W + 16)
     dy = synth.gradients(LLAMA8B_M, N, seed=0, row_range=(0, Ms))
