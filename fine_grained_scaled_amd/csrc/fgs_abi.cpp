@@ -64,6 +64,8 @@ int check_operand(const fgs_operand* op, const char* name, int64_t rows, int64_t
     const int64_t ld_bytes = op->elem == FGS_ELEM_E2M1 ? op->ld / 2 : op->ld;
     if (op->elem == FGS_ELEM_E2M1 && (op->ld & 1)) return fail(FGS_ERR_UNSUPPORTED, "%s.ld must be even for E2M1", name);
     if (ld_bytes % 16) return fail(FGS_ERR_UNSUPPORTED, "%s row stride must be a multiple of 16 bytes", name);
+    // the GEMM addresses a tile's rows by 32-bit offsets from its first row
+    if (ld_bytes >= ((int64_t)1 << 24)) return fail(FGS_ERR_UNSUPPORTED, "%s row stride must be below 2^24 bytes", name);
     if (!aligned(op->data, 16)) return fail(FGS_ERR_UNSUPPORTED, "%s.data must be 16-byte aligned", name);
     if (!aligned(op->scales, 4)) return fail(FGS_ERR_UNSUPPORTED, "%s.scales must be 4-byte aligned", name);
     return FGS_OK;

@@ -77,8 +77,8 @@ constexpr int BK = 128;      // K block: the scale block and the promotion inter
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef const __attribute__((address_space(1))) void* gbl_ptr;
 
-// Direct global->LDS loads.  dst is the wave's LDS span base (wave-uniform,
-// passed in M0); lane i writes bytes [size*i, size*(i+1)) of it.  They are
+// Direct global->LDS loads.  The LDS destination is the wave's span base
+// (wave-uniform, passed in M0); lane i writes bytes [size*i, size*(i+1)) of it.  They are
 // issued from inline assembly on purpose: seen as LDS writes, the compiler
 // would make every later LDS read wait for the loads to land (it cannot tell
 // that they fill the other stage of the ring), which serialises the next
@@ -91,10 +91,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p)
 {
     return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)p));
 }
-__device__ __forceinline__ void g2lds16(const void* src, void* dst_wave_base)
+// 16 bytes per lane from a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// per-lane byte offset (the global instructions' saddr form), to the LDS
+// address lds_addr (uniform): a K block's code loads need no per-lane
+// address arithmetic, only scalar adds.
+__device__ __forceinline__ void g2lds16_s(const void* sbase, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_offset(dst_wave_base)) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+// a wave-uniform pointer, held in SGPRs
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ void g2lds4(const void* src, void* dst_wave_base)
 {
@@ -467,22 +479,30 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     constexpr int A_INSTR = A_ROWS / RPI, B_INSTR = B_ROWS / RPI;
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the wave count");
     const int srow = l / CPR, sslot = l % CPR;
-    const uint8_t* a_src[A_INSTR];
-    const uint8_t* b_src[B_INSTR];
+    // per-lane byte offsets from the tile's first A / B row (row clamped,
+    // < 256 rows x a row stride below 2^24 bytes, so 32 bits), and the
+    // tile's uniform bases; a K block adds kb * ROW to the bases
+    uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int u = 0; u < A_INSTR; ++u) {
         const int lr = A_ROWS * w + RPI * u + srow;
         int64_t r = m0 + lr;
         r = r < m_end ? r : m_end - 1;
-        a_src[u] = Ap + r * p.lda + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
+        a_off[u] = (uint32_t)((r - m0) * p.lda) + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
 #pragma unroll
     for (int u = 0; u < B_INSTR; ++u) {
         const int lr = B_ROWS * w + RPI * u + srow;
         int64_t r = n0 + lr;
         r = r < p.N ? r : p.N - 1;
-        b_src[u] = Bp + r * p.ldb + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
+        b_off[u] = (uint32_t)((r - n0) * p.ldb) + 16 * (sslot ^ ((lr >> SH) & (CPR - 1)));
     }
+    const uint8_t* a_base = uniform_ptr(Ap + m0 * p.lda);
+    const uint8_t* b_base = uniform_ptr(Bp + n0 * p.ldb);
+    // LDS addresses (M0) of the stages and of this wave's A and B rows
+    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t lds_a = __builtin_amdgcn_readfirstlane((uint32_t)(A_ROWS * w * ROW));
+    const uint32_t lds_b = __builtin_amdgcn_readfirstlane((uint32_t)(L::A_BYTES + B_ROWS * w * ROW));
     int64_t sb_col = n0 + 64 * (w % (BN / 64)) + l;   // B 1x128 scales: waves 0 .. BN/64-1 stage 64 each
     sb_col = sb_col < p.N ? sb_col : p.N - 1;
     // A 1x128 scales (A_LDS): waves NW - BM/64 .. NW-1 stage 64 rows each
@@ -525,12 +545,13 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     auto stage_block = [&](int64_t kb, int stage) {
         uint8_t* st = smem + stage * L::STAGE;
         const int64_t ko = kb * ROW;
+        const uint32_t lst = lds0 + (uint32_t)(stage * L::STAGE);
 #pragma unroll
         for (int u = 0; u < A_INSTR; ++u)
-            if (A_ROWS * w + RPI * u < a_live) g2lds16(a_src[u] + ko, st + (A_ROWS * w + RPI * u) * ROW);
+            if (A_ROWS * w + RPI * u < a_live) g2lds16_s(a_base + ko, a_off[u], lst + lds_a + RPI * u * ROW);
 #pragma unroll
         for (int u = 0; u < B_INSTR; ++u)
-            if (B_ROWS * w + RPI * u < b_live) g2lds16(b_src[u] + ko, st + L::A_BYTES + (B_ROWS * w + RPI * u) * ROW);
+            if (B_ROWS * w + RPI * u < b_live) g2lds16_s(b_base + ko, b_off[u], lst + lds_b + RPI * u * ROW);
         if constexpr (B_TILE)
             if (w < BN / 64) g2lds4(sBp + kb * p.N + sb_col, st + L::A_BYTES + L::B_BYTES + 256 * w);
         if constexpr (A_LDS)

@@ -279,3 +279,14 @@ def test_gemm_fp8mma_validation(lib):
     assert b"E4M3 / E5M2" in lib.fgs_last_error()
     assert g(r(_op(elem=2, mode=1)), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
     assert g(r(a), r(b), 0, 128, 256, NULL, 128, 0, S) == _lib.FGS_OK                     # empty
+
+
+def test_gemm_rejects_row_strides_of_2_pow_24_bytes(lib):
+    """Tile rows are addressed by 32-bit offsets from the tile's first row,
+    so operand row strides must stay below 2^24 bytes."""
+    S = NULL
+    r = ctypes.byref
+    a_big, b = _op(mode=1, ld=1 << 24), _op(mode=2)
+    for g in (lib.fgs_gemm_block_scaled, lib.fgs_gemm_block_scaled_fp8mma):
+        assert g(r(a_big), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+        assert b"2^24" in lib.fgs_last_error()
