@@ -26,7 +26,7 @@ blockwise GEMM, the Llama-3-8B layers in the hybrid delayed-scaling recipe
 (per-tensor scales from an amax history, E5M2 gradients), the DeepSeek-V3
 MoE grouped GEMMs (forward, dgrad and wgrad), MXFP8 at Llama-3.1-405B
 shapes (one GPU's share) and NVFP4 at 12B-hybrid shapes; and the headline
-step and the MXFP8 layers again with their GEMMs on the FP8 matrix
+step, the MXFP8 layers and the MoE step again with their GEMMs on the FP8 matrix
 instructions (fgs_gemm_block_scaled_fp8mma: FP8 accumulation inside the
 instruction with FP32 promotion per 128-K block, MX scales applied by the
 instruction; a looser error bound than the exact headline GEMM).
@@ -334,6 +334,7 @@ class Tiny:
 # --------------------------------------------------------------------------
 class MoE:
     name = "deepseek_v3_moe_grouped"
+    fp8_mma = False
 
     def __init__(self, torch, fgs, synth):
         import numpy as np
@@ -395,15 +396,19 @@ class MoE:
         active = int((self.counts > 0).sum())
         return MOE_TOKENS * K * (1 + 4 / 128) + active * N * K * (1 + 4 / 16384) + 2 * MOE_TOKENS * N
 
+    def mfma_peak(self):
+        """The matrix rate the GEMMs run at: FP16 (exact decode) or FP8."""
+        return PEAK_FP8_MFMA if self.fp8_mma else PEAK_FP16_MFMA
+
     def roofline_seconds(self, N, K):
-        """Sum over experts of max(MFMA time at the FP16 peak, HBM time)."""
+        """Sum over experts of max(MFMA time at the matrix peak, HBM time)."""
         t = 0.0
         for c in self.counts:
             if c == 0:
                 continue
             fl = 2.0 * c * N * K
             by = c * K * (1 + 4 / 128) + N * K * (1 + 4 / 16384) + 2 * c * N
-            t += max(fl / (PEAK_FP16_MFMA * 1e12), by / (PEAK_HBM * 1e9))
+            t += max(fl / (self.mfma_peak() * 1e12), by / (PEAK_HBM * 1e9))
         return t
 
     def wgrad_bytes(self, M, N):
@@ -413,18 +418,19 @@ class MoE:
         return (M + N) * MOE_TOKENS * (1 + 4 / 128) + MOE_EXPERTS * 4.0 * M * N
 
     def wgrad_roofline_seconds(self, M, N):
-        """Sum over experts of max(MFMA time at the FP16 peak, HBM time)."""
+        """Sum over experts of max(MFMA time at the matrix peak, HBM time)."""
         t = 0.0
         for c in self.counts:
             fl = 2.0 * c * M * N
             by = (M + N) * c * (1 + 4 / 128) + 4.0 * M * N
-            t += max(fl / (PEAK_FP16_MFMA * 1e12), by / (PEAK_HBM * 1e9))
+            t += max(fl / (self.mfma_peak() * 1e12), by / (PEAK_HBM * 1e9))
         return t
 
     def step(self, tm):
         torch, fgs = self.torch, self.fgs
         T, H, I = MOE_TOKENS, MOE_HIDDEN, MOE_INTER
         off = self.offsets
+        mma = self.fp8_mma
         # each input is read once for its row-wise codes (fwd / dgrad) and its
         # per-expert transposed codes (wgrad)
         grouped = lambda x: fgs.quantize_grouped_colwise(x, off, rowwise=True)
@@ -434,24 +440,30 @@ class MoE:
         qa1 = tm.run("quant", "A1", a1_bytes, lambda: fgs.quantize_grouped_colwise(
             self.x_tok, off, rowwise=True, row_index=self.route))
         tm.run("gemm", "gate_up", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
-            qa1.rowwise(), self.w1, off, 2 * I, torch.bfloat16, out=self.y1))
+            qa1.rowwise(), self.w1, off, 2 * I, torch.bfloat16, out=self.y1, fp8_mma=mma))
         # SwiGLU of the gate/up output fused into the down projection's quantizer
         a2_bytes = 2.0 * T * 2 * I + e4m3_bytes(T, I, "tile", 2) - 2.0 * T * I
         qa2 = tm.run("quant", "SwiGLU+A2", a2_bytes, lambda: fgs.swiglu_quantize_grouped(self.y1, off))
         tm.run("gemm", "down", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
-            qa2.rowwise(), self.w2, off, H, torch.bfloat16, out=self.y2))
+            qa2.rowwise(), self.w2, off, H, torch.bfloat16, out=self.y2, fp8_mma=mma))
         # dgrad: dZ = dY2 W2 (2048 outputs, contraction over 7168), dH = dY1 W1
         qg2 = tm.run("quant", "dY2", e4m3_bytes(T, H, "tile", 2), lambda: grouped(self.g2))
         tm.run("gemm", "down_dgrad", 2.0 * T * H * I, lambda: fgs.grouped_gemm_block_scaled(
-            qg2.rowwise(), self.w2t, off, I, torch.bfloat16, out=self.dx2))
+            qg2.rowwise(), self.w2t, off, I, torch.bfloat16, out=self.dx2, fp8_mma=mma))
         qg1 = tm.run("quant", "dY1", e4m3_bytes(T, 2 * I, "tile", 2), lambda: grouped(self.g1))
         tm.run("gemm", "gate_up_dgrad", 2.0 * T * 2 * I * H, lambda: fgs.grouped_gemm_block_scaled(
-            qg1.rowwise(), self.w1t, off, H, torch.bfloat16, out=self.dx1))
+            qg1.rowwise(), self.w1t, off, H, torch.bfloat16, out=self.dx1, fp8_mma=mma))
         # wgrad: dW2_g = dY2_g^T Z_g [7168 x 2048], dW1_g = dY1_g^T X_g [4096 x 7168]
         tm.run("gemm", "down_wgrad", 2.0 * T * H * I, lambda: fgs.grouped_wgrad_block_scaled(
-            qg2.colwise(), qa2.colwise(), off, T, torch.float32, out=self.dw2))
+            qg2.colwise(), qa2.colwise(), off, T, torch.float32, out=self.dw2, fp8_mma=mma))
         tm.run("gemm", "gate_up_wgrad", 2.0 * T * 2 * I * H, lambda: fgs.grouped_wgrad_block_scaled(
-            qg1.colwise(), qa1.colwise(), off, T, torch.float32, out=self.dw1))
+            qg1.colwise(), qa1.colwise(), off, T, torch.float32, out=self.dw1, fp8_mma=mma))
+
+
+class MoEFp8Mma(MoE):
+    """The MoE step with its grouped GEMMs on the FP8 matrix instructions."""
+    name = "deepseek_v3_moe_grouped_fp8_mfma"
+    fp8_mma = True
 
 
 # --------------------------------------------------------------------------
@@ -547,7 +559,8 @@ class NV12B:
 
 
 WORKLOADS = {"llama3_8b": Llama8B, "hybrid8b": Hybrid8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B,
-             "nv12b": NV12B, "llama3_8b_fp8mma": Llama8BFp8Mma, "mx405b_fp8mma": MX405BFp8Mma}
+             "nv12b": NV12B, "llama3_8b_fp8mma": Llama8BFp8Mma, "mx405b_fp8mma": MX405BFp8Mma,
+             "moe_fp8mma": MoEFp8Mma}
 
 
 def measure(torch, wl, steps, warmup):
@@ -735,7 +748,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="llama3_8b,hybrid8b,tiny,moe,mx405b,nv12b,llama3_8b_fp8mma,mx405b_fp8mma",
+    ap.add_argument("--workloads", default="llama3_8b,hybrid8b,tiny,moe,mx405b,nv12b,llama3_8b_fp8mma,mx405b_fp8mma,moe_fp8mma",
                     help="comma list of " + ",".join(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -22,6 +22,8 @@ EXPORTS = (
     "fgs_gemm_block_scaled",
     "fgs_gemm_block_scaled_fp8mma",
     "fgs_grouped_gemm_block_scaled",
+    "fgs_grouped_gemm_block_scaled_fp8mma",
+    "fgs_grouped_wgrad_block_scaled_fp8mma",
     "fgs_gemm_block_scaled_fp8out",
     "fgs_grouped_gemm_block_scaled_fp8out",
     "fgs_quantize_grouped_colwise",
@@ -73,6 +75,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8mma.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_grouped_gemm_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8out.argtypes = [OP, OP, I64, I64, I64, P, I64, P, P, P]
     lib.fgs_grouped_gemm_block_scaled_fp8out.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, P, P, P]
     lib.fgs_quantize_grouped_colwise.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_int32, P, P, P, I64, P, P]
@@ -80,6 +83,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_swiglu_quantize_grouped.argtypes = [P, I64, I64, I64, P, ctypes.c_int32, P, P, P, P, I64, P, P]
     lib.fgs_grouped_colwise_blocks.restype = I64
     lib.fgs_grouped_wgrad_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_grouped_wgrad_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_tile_policy.argtypes = [ctypes.c_int]
     lib.fgs_gemm_tile_policy.restype = ctypes.c_int
     lib.fgs_workspace_bytes.argtypes = [I64, I64]
@@ -88,6 +92,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
                  "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_fp8mma", "fgs_grouped_gemm_block_scaled",
+                 "fgs_grouped_gemm_block_scaled_fp8mma", "fgs_grouped_wgrad_block_scaled_fp8mma",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",
                  "fgs_swiglu_quantize_grouped", "fgs_gemm_block_scaled_fp8out",
                  "fgs_grouped_gemm_block_scaled_fp8out"):

@@ -298,7 +298,7 @@ int fgs_gemm_block_scaled_fp8out(const fgs_operand* A, const fgs_operand* B, int
 
 static int grouped_impl(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets, int32_t G,
                         int64_t total_M, int64_t N, int64_t K, void* C, int64_t ldc, int out_dtype,
-                        uint8_t* q_out, float* s_out, void* stream)
+                        uint8_t* q_out, float* s_out, void* stream, bool fp8_mma = false)
 {
     if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
     int st = check_gemm_common(A, B, total_M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
@@ -310,7 +310,8 @@ static int grouped_impl(const fgs_operand* A, const fgs_operand* B, const int32_
     if (total_M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
     const int64_t tiles = ((total_M + 127) / 128 + G) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 0, 0, q_out, s_out};
+    fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 0, 0, q_out, s_out,
+                    fp8_mma ? 1 : 0};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_gemm_block_scaled launch");
 }
 
@@ -319,6 +320,13 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, co
                                   void* C, int64_t ldc, int out_dtype, void* stream)
 {
     return grouped_impl(A, B, group_offsets, G, total_M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream);
+}
+
+int fgs_grouped_gemm_block_scaled_fp8mma(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                         int32_t G, int64_t total_M, int64_t N, int64_t K,
+                                         void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return grouped_impl(A, B, group_offsets, G, total_M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream, true);
 }
 
 int fgs_grouped_gemm_block_scaled_fp8out(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
@@ -412,9 +420,9 @@ int fgs_swiglu_quantize_grouped(const void* gate_up, int64_t rows, int64_t inter
                       "swiglu_quantize_grouped launch");
 }
 
-int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
-                                   int32_t G, int64_t total_T, int64_t M, int64_t N,
-                                   void* C, int64_t ldc, int out_dtype, void* stream)
+static int wgrad_impl(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                      int32_t G, int64_t total_T, int64_t M, int64_t N,
+                      void* C, int64_t ldc, int out_dtype, void* stream, bool fp8_mma)
 {
     if (G < 0) return fail(FGS_ERR_INVALID_ARG, "G must be >= 0");
     if (total_T < 0) return fail(FGS_ERR_INVALID_ARG, "total_T must be >= 0");
@@ -432,8 +440,23 @@ int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, c
     if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return fail(FGS_ERR_UNSUPPORTED, "sizes too large");
     const int64_t tiles = (int64_t)G * ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, M, N, Kcap, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 1, total_T};
+    fgs::GemmArgs a{*A, *B, M, N, Kcap, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 1, total_T,
+                    nullptr, nullptr, fp8_mma ? 1 : 0};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_wgrad_block_scaled launch");
+}
+
+int fgs_grouped_wgrad_block_scaled(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                   int32_t G, int64_t total_T, int64_t M, int64_t N,
+                                   void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return wgrad_impl(A, B, group_offsets, G, total_T, M, N, C, ldc, out_dtype, stream, false);
+}
+
+int fgs_grouped_wgrad_block_scaled_fp8mma(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets,
+                                          int32_t G, int64_t total_T, int64_t M, int64_t N,
+                                          void* C, int64_t ldc, int out_dtype, void* stream)
+{
+    return wgrad_impl(A, B, group_offsets, G, total_T, M, N, C, ldc, out_dtype, stream, true);
 }
 
 } // extern "C"

@@ -1173,22 +1173,28 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.s_out = a.s_out;
     if (a.M == 0 || a.N == 0) return hipSuccess;
     const bool bf16 = a.out_bf16 != 0;
-    if (a.fp8_mma && (a.group_k || a.group_offsets || a.q_out)) return hipErrorInvalidValue;   // dense only
+    if (a.fp8_mma && a.q_out) return hipErrorInvalidValue;   // no E4M3-output epilogue on the FP8 instructions
     if (a.group_k) {
         if (a.G == 0) return hipSuccess;
-        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_TILE_1x128)
-            // 128 x 128 tiles, two workgroups per CU: most experts hold one or
-            // two 128-token blocks, so each tile is mostly its 64 KiB of FP32
-            // output, and two resident workgroups overlap one's stores with the
-            // other's loads and MFMAs (1.4x the 256 x 128 tile on DeepSeek-V3)
+        // 128 x 128 tiles, two workgroups per CU: most experts hold one or
+        // two 128-token blocks, so each tile is mostly its 64 KiB of FP32
+        // output, and two resident workgroups overlap one's stores with the
+        // other's loads and MFMAs (1.4x the 256 x 128 tile on DeepSeek-V3)
+        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_TILE_1x128) {
+            if (a.fp8_mma)
+                return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_K, 0, true>(p, a, bf16, stream);
             return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_TILE_1x128, GROUP_K>(p, a, bf16, stream);
+        }
         return hipErrorInvalidValue;
     }
     if (a.group_offsets) {
         p.b_group_stride = a.N * a.B.ld;
         p.sb_group_stride = ((a.N + 127) / 128) * (a.K / BK);
-        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128)
+        if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128) {
+            if (a.fp8_mma)
+                return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, true>(p, a, bf16, stream);
             return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(p, a, bf16, stream);
+        }
         return hipErrorInvalidValue;
     }
     if (a.fp8_mma) return dispatch_dense<true>(p, a, bf16, stream);

@@ -309,9 +309,10 @@ def grouped_gemm_block_scaled_fp8out(A: Operand, B: Operand, group_offsets: torc
 
 def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, N: int,
                               out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
-                              K: Optional[int] = None) -> torch.Tensor:
+                              K: Optional[int] = None, fp8_mma: bool = False) -> torch.Tensor:
     """MoE expert GEMMs: rows offsets[g]..offsets[g+1] of A times B_g^T.
-    B.data is [G*N x K] (groups contiguous); group_offsets is int32 [G+1] on the GPU."""
+    B.data is [G*N x K] (groups contiguous); group_offsets is int32 [G+1] on the GPU.
+    fp8_mma=True runs fgs_grouped_gemm_block_scaled_fp8mma (FP8 instructions)."""
     _need_gpu(A.data, B.data, group_offsets)
     if group_offsets.dtype != torch.int32:
         raise TypeError("group_offsets must be int32")
@@ -329,8 +330,10 @@ def grouped_gemm_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tenso
     if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] < total_M or out.shape[1] < N or out.stride(1) != 1:
         raise ValueError("out must be a [total_M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
-    check(_lib.load().fgs_grouped_gemm_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
-                                                    G, total_M, N, K, _ptr(out), out.stride(0), code, _stream()))
+    lib = _lib.load()
+    fn = lib.fgs_grouped_gemm_block_scaled_fp8mma if fp8_mma else lib.fgs_grouped_gemm_block_scaled
+    check(fn(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets), G, total_M, N, K, _ptr(out), out.stride(0),
+             code, _stream()))
     return out
 
 
@@ -411,10 +414,12 @@ def swiglu_quantize_grouped(gate_up: torch.Tensor, group_offsets: torch.Tensor, 
 
 
 def grouped_wgrad_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tensor, total_T: int,
-                               out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                               out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                               fp8_mma: bool = False) -> torch.Tensor:
     """MoE weight gradients: C_g [M x N] = sum over group g's tokens of
     A^[m, t] B^[n, t], for operands from quantize_grouped_colwise (A of dY,
-    B of X) over total_T tokens.  Returns [G x M x N]; empty groups get 0."""
+    B of X) over total_T tokens.  Returns [G x M x N]; empty groups get 0.
+    fp8_mma=True runs fgs_grouped_wgrad_block_scaled_fp8mma (FP8 instructions)."""
     _need_gpu(A.data, B.data, group_offsets)
     if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1:
         raise TypeError("group_offsets must be a 1-D int32 tensor")
@@ -435,7 +440,8 @@ def grouped_wgrad_block_scaled(A: Operand, B: Operand, group_offsets: torch.Tens
         raise ValueError("out must be a [G x M x N] tensor of out_dtype, rows contiguous, "
                          "matrices M * ldc elements apart")
     a, b = A.c_struct(), B.c_struct()
-    check(_lib.load().fgs_grouped_wgrad_block_scaled(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets),
-                                                     G, total_T, M, N, _ptr(out), out.stride(1), code,
-                                                     _stream()))
+    lib = _lib.load()
+    fn = lib.fgs_grouped_wgrad_block_scaled_fp8mma if fp8_mma else lib.fgs_grouped_wgrad_block_scaled
+    check(fn(ctypes.byref(a), ctypes.byref(b), _ptr(group_offsets), G, total_T, M, N, _ptr(out), out.stride(1),
+             code, _stream()))
     return out

@@ -267,6 +267,20 @@ int fgs_grouped_gemm_block_scaled(const fgs_operand *A, const fgs_operand *B,
                                   void *C, int64_t ldc, int out_dtype, void *stream);
 
 /*
+ * fgs_grouped_gemm_block_scaled_fp8mma -- the grouped (MoE) GEMM above on
+ *   the FP8 matrix instructions, promoted to FP32 once per 128-deep K block,
+ *   for callers who accept that accumulation (see
+ *   fgs_gemm_block_scaled_fp8mma).   [DSV3] "Increasing accumulation
+ *   precision".  Arguments, layouts, ownership and errors as
+ *   fgs_grouped_gemm_block_scaled.  Accuracy: |C - C_ref| <= 2^-9 *
+ *   sum_k |a_k b_k| + 1e-6 per group (FP32 output; BF16 adds one BF16 ulp).
+ */
+int fgs_grouped_gemm_block_scaled_fp8mma(const fgs_operand *A, const fgs_operand *B,
+                                         const int32_t *group_offsets, int32_t G,
+                                         int64_t total_M, int64_t N, int64_t K,
+                                         void *C, int64_t ldc, int out_dtype, void *stream);
+
+/*
  * fgs_quantize_grouped_colwise -- the MoE weight-gradient operands: per-group
  *   transposed 1x128 E4M3 quantization.   [DSV3] "Fine-grained
  *   quantization", "Online quantization", "Mixed precision framework" (the
@@ -360,6 +374,19 @@ int fgs_grouped_wgrad_block_scaled(const fgs_operand *A, const fgs_operand *B,
                                    const int32_t *group_offsets, int32_t G, int64_t total_T,
                                    int64_t M, int64_t N, void *C, int64_t ldc, int out_dtype,
                                    void *stream);
+
+/*
+ * fgs_grouped_wgrad_block_scaled_fp8mma -- the per-expert weight gradient
+ *   above on the FP8 matrix instructions, promoted to FP32 once per
+ *   128-token block.   [DSV3] "Increasing accumulation precision".
+ *   Arguments, layouts, ownership and errors as
+ *   fgs_grouped_wgrad_block_scaled.  Accuracy: |dW_g - ref| <= 2^-9 *
+ *   sum_t |a_t b_t| + 1e-6 (FP32 output; BF16 adds one BF16 ulp).
+ */
+int fgs_grouped_wgrad_block_scaled_fp8mma(const fgs_operand *A, const fgs_operand *B,
+                                          const int32_t *group_offsets, int32_t G, int64_t total_T,
+                                          int64_t M, int64_t N, void *C, int64_t ldc, int out_dtype,
+                                          void *stream);
 
 /*
  * fgs_gemm_block_scaled_fp8out / fgs_grouped_gemm_block_scaled_fp8out --

@@ -290,3 +290,21 @@ def test_gemm_rejects_row_strides_of_2_pow_24_bytes(lib):
     for g in (lib.fgs_gemm_block_scaled, lib.fgs_gemm_block_scaled_fp8mma):
         assert g(r(a_big), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
         assert b"2^24" in lib.fgs_last_error()
+
+
+def test_grouped_fp8mma_validation(lib):
+    """The grouped FP8-instruction entry points validate like their exact
+    counterparts (before any HIP call)."""
+    S = NULL
+    r = ctypes.byref
+    a, b = _op(mode=1), _op(mode=2)
+    g = lib.fgs_grouped_gemm_block_scaled_fp8mma
+    assert g(r(a), r(b), FAKE, -1, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(_op(mode=0)), FAKE, 4, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a), r(b), FAKE, 0, 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_OK
+    w = lib.fgs_grouped_wgrad_block_scaled_fp8mma
+    ld = 128 * (2 + 4)
+    wa, wb = _op(mode=1, ld=ld), _op(mode=1, ld=ld)
+    assert w(r(wa), r(wb), FAKE, -1, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
+    assert w(r(wa), r(_op(mode=2, ld=ld)), FAKE, 4, 300, 128, 128, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED
+    assert w(r(wa), r(wb), FAKE, 0, 300, 128, 128, NULL, 128, 0, S) == _lib.FGS_OK

@@ -244,3 +244,91 @@ def test_fp8mma_llama3_8b_qkv_sampled(fgs, orient):
     A, ah = e4m3_operand(fgs, a_bits, amode, colwise=a_col, rows=rs)
     B, bh = e4m3_operand(fgs, b_bits, bmode, colwise=b_col)
     check(fgs, A, B, ah, bh, out, rows=rs)
+
+
+# ------------------------------------------------------------ grouped (MoE) --
+def _within(got, cref, sref, out):
+    err = np.abs(got - cref)
+    bound = BOUND * sref + 1e-6
+    if out == torch.bfloat16:
+        bound = bound + _bf16_ulp(cref)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{int(bad.sum())} outputs outside 2^-9*S"
+
+
+@pytest.mark.parametrize("dgrad", [False, True])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_fp8mma_grouped_ragged(fgs, dgrad, out):
+    """MoE expert GEMMs on the FP8 instructions: ragged groups (1, 3, 130,
+    200, 257 rows, two empty), 1x128 A x per-expert 128x128 B; with dgrad the
+    experts' B is the transpose of a forward weight, quantized column-wise.
+    Rows of no group keep their sentinel."""
+    counts = np.array([1, 0, 3, 130, 200, 0, 257])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total, G, N, K = int(offs[-1]), len(counts), 200, 384
+    a_bits = synth.gradients(total, K, seed=5) if dgrad else synth.activations(total, K, seed=5)
+    A, ah = e4m3_operand(fgs, a_bits, "tile")
+    qs, ss, bhs = [], [], []
+    for g in range(G):
+        if dgrad:
+            q, s = oracle.quant_e4m3(synth.weights(K, N, seed=50 + g), "block", colwise=True)
+        else:
+            q, s = oracle.quant_e4m3(synth.weights(N, K, seed=50 + g), "block")
+        qs.append(q)
+        ss.append(s)
+        bhs.append(oracle.dequant_e4m3(q, s, "block"))
+    B = fgs.Operand(torch.from_numpy(np.concatenate(qs)).cuda(),
+                    torch.from_numpy(np.concatenate([s[None] for s in ss])).cuda(), 2)
+    c = torch.full((total, N), 3.0, dtype=out, device="cuda")
+    fgs.grouped_gemm_block_scaled(A, B, torch.from_numpy(offs).cuda(), N, out_dtype=out, out=c, fp8_mma=True)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy().astype(np.float64)
+    cref, sref = oracle.grouped_gemm_ref(ah, bhs, offs)
+    _within(got, cref, sref, out)
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_fp8mma_grouped_wgrad(fgs, out):
+    """The per-expert weight gradient on the FP8 instructions: ragged experts
+    (two empty, whose dW must be zero), the contraction over each expert's
+    tokens with a partial last 128-token tile."""
+    counts = np.array([1, 3, 0, 130, 200, 0, 257])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T, G, M, N = int(offs[-1]), len(counts), 328, 200
+    dy = synth.gradients(T, M, seed=8)
+    x = synth.activations(T, N, seed=9)
+    off_t = torch.from_numpy(offs).cuda()
+    qa = fgs.quantize_grouped_colwise(synth.to_torch_bf16(dy).cuda(), off_t)
+    qb = fgs.quantize_grouped_colwise(synth.to_torch_bf16(x).cuda(), off_t)
+    c = torch.full((G, M, N), 3.0, dtype=out, device="cuda")
+    fgs.grouped_wgrad_block_scaled(qa.colwise(), qb.colwise(), off_t, T, out_dtype=out, out=c, fp8_mma=True)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy().astype(np.float64)
+    ah = [oracle.dequant_e4m3(q, s, "tile") for q, s in oracle.quant_e4m3_grouped_colwise(dy, offs)]
+    bh = [oracle.dequant_e4m3(q, s, "tile") for q, s in oracle.quant_e4m3_grouped_colwise(x, offs)]
+    cref, sref = oracle.grouped_wgrad_ref(ah, bh)
+    for g in range(G):
+        if counts[g] == 0:
+            assert not got[g].any(), f"empty expert {g} not zero"
+    _within(got, cref, sref, out)
+
+
+def test_fp8mma_grouped_many_experts(fgs):
+    """64 experts with Zipf(1.1) counts over 4096 rows, N = 512, K = 1024 (a
+    DeepSeek-V3-like mix of long and short groups at test size)."""
+    counts = synth.expert_counts(tokens=4096, experts=64, seed=4)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total, G, N, K = int(offs[-1]), len(counts), 512, 1024
+    A, ah = e4m3_operand(fgs, synth.activations(total, K, seed=6), "tile")
+    qs, ss, bhs = [], [], []
+    for g in range(G):
+        q, s = oracle.quant_e4m3(synth.weights(N, K, seed=200 + g), "block")
+        qs.append(q)
+        ss.append(s)
+        bhs.append(oracle.dequant_e4m3(q, s, "block"))
+    B = fgs.Operand(torch.from_numpy(np.concatenate(qs)).cuda(),
+                    torch.from_numpy(np.concatenate([s[None] for s in ss])).cuda(), 2)
+    c = fgs.grouped_gemm_block_scaled(A, B, torch.from_numpy(offs).cuda(), N, out_dtype=torch.float32, fp8_mma=True)
+    torch.cuda.synchronize()
+    cref, sref = oracle.grouped_gemm_ref(ah, bhs, offs)
+    _within(c.cpu().numpy().astype(np.float64), cref, sref, torch.float32)
