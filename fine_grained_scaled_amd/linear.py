@@ -17,7 +17,10 @@ with the operands quantized by the recipe:
 X is quantized once in the forward pass for both of its uses (row-wise for
 Y, column-wise along the tokens for dW), W once for Y and dX, dY once in the
 backward pass for dX and dW.  Y and dX are BF16, dW is FP32.  Shapes: the
-token count and both feature counts must be multiples of 128.
+token count and both feature counts must be multiples of 128.  fp8_mma=True
+runs the three products on the FP8 matrix instructions (partial sums
+promoted to FP32 per 128-deep block, section "Increasing accumulation
+precision") instead of the exact FP16 decode.
 """
 from __future__ import annotations
 
@@ -54,11 +57,11 @@ def _quant(t: torch.Tensor, role: str, recipe: str, state: Optional[DelayedState
 
 class _FP8LinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, w, recipe, state):
+    def forward(ctx, x, w, recipe, state, fp8_mma):
         qx = _quant(x, "x", recipe, state)
         qw = _quant(w.to(torch.bfloat16).contiguous(), "w", recipe, state)
-        y = ops.gemm_block_scaled(qx.rowwise(), qw.rowwise(), torch.bfloat16)
-        ctx.qx, ctx.qw, ctx.recipe, ctx.state = qx, qw, recipe, state
+        y = ops.gemm_block_scaled(qx.rowwise(), qw.rowwise(), torch.bfloat16, fp8_mma=fp8_mma)
+        ctx.qx, ctx.qw, ctx.recipe, ctx.state, ctx.fp8_mma = qx, qw, recipe, state, fp8_mma
         ctx.w_dtype = w.dtype
         return y
 
@@ -68,15 +71,16 @@ class _FP8LinearFn(torch.autograd.Function):
         qdy = _quant(dy, "dy", ctx.recipe, ctx.state)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            dx = ops.gemm_block_scaled(qdy.rowwise(), ctx.qw.colwise(), torch.bfloat16)
+            dx = ops.gemm_block_scaled(qdy.rowwise(), ctx.qw.colwise(), torch.bfloat16, fp8_mma=ctx.fp8_mma)
         if ctx.needs_input_grad[1]:
-            dw = ops.gemm_block_scaled(qdy.colwise(), ctx.qx.colwise(), torch.float32).to(ctx.w_dtype)
+            dw = ops.gemm_block_scaled(qdy.colwise(), ctx.qx.colwise(), torch.float32,
+                                       fp8_mma=ctx.fp8_mma).to(ctx.w_dtype)
         ctx.qx = ctx.qw = None
-        return dx, dw, None, None
+        return dx, dw, None, None, None
 
 
 def fp8_linear(x: torch.Tensor, w: torch.Tensor, recipe: str = "blockwise",
-               state: Optional[DelayedState] = None) -> torch.Tensor:
+               state: Optional[DelayedState] = None, fp8_mma: bool = False) -> torch.Tensor:
     """Y = X W^T with the recipe's scaled FP8 operands in forward and backward.
     x: [T x K] (any float dtype; cast to BF16), w: [N x K] (FP32 master or
     BF16; quantized from its BF16 cast, dW returned in w's dtype); returns
@@ -91,7 +95,7 @@ def fp8_linear(x: torch.Tensor, w: torch.Tensor, recipe: str = "blockwise",
     N = w.shape[0]
     if T % 128 or K % 128 or N % 128:
         raise ValueError(f"tokens ({T}), in ({K}) and out ({N}) features must be multiples of 128")
-    return _FP8LinearFn.apply(x.to(torch.bfloat16).contiguous(), w, recipe, state)
+    return _FP8LinearFn.apply(x.to(torch.bfloat16).contiguous(), w, recipe, state, fp8_mma)
 
 
 class Linear(torch.nn.Module):
@@ -99,16 +103,17 @@ class Linear(torch.nn.Module):
     The weight is an FP32 master copy; its BF16 cast is quantized each step."""
 
     def __init__(self, in_features: int, out_features: int, recipe: str = "blockwise",
-                 device=None, history: int = 16):
+                 device=None, history: int = 16, fp8_mma: bool = False):
         super().__init__()
         if recipe not in RECIPES:
             raise ValueError(f"recipe must be one of {RECIPES}")
         self.recipe = recipe
+        self.fp8_mma = fp8_mma
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, dtype=torch.float32, device=device))
         torch.nn.init.normal_(self.weight, std=in_features ** -0.5)
         self.state = DelayedState(self.weight.device, history) if recipe == "delayed" else None
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         shape = x.shape
-        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.recipe, self.state)
+        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.recipe, self.state, self.fp8_mma)
         return y.reshape(*shape[:-1], self.weight.shape[0])

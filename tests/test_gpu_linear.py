@@ -84,7 +84,7 @@ def test_linear_rejects_unaligned_shapes(fgs):
         layer(torch.zeros((100, 256), dtype=torch.bfloat16, device="cuda"))
 
 
-def _train(fgs, recipe, steps=120, T=1024, D=256, H=512, seed=0):
+def _train(fgs, recipe, steps=120, T=1024, D=256, H=512, seed=0, fp8_mma=False):
     """Student MLP D -> H -> D (GELU) regressing a fixed random teacher on
     Gaussian inputs; Adam, MSE.  recipe None: FP32 torch layers."""
     torch.manual_seed(seed)
@@ -98,8 +98,8 @@ def _train(fgs, recipe, steps=120, T=1024, D=256, H=512, seed=0):
         torch.nn.init.normal_(l1.weight, std=D ** -0.5)
         torch.nn.init.normal_(l2.weight, std=H ** -0.5)
     else:
-        l1 = fgs.Linear(D, H, recipe=recipe, device="cuda")
-        l2 = fgs.Linear(H, D, recipe=recipe, device="cuda")
+        l1 = fgs.Linear(D, H, recipe=recipe, device="cuda", fp8_mma=fp8_mma)
+        l2 = fgs.Linear(H, D, recipe=recipe, device="cuda", fp8_mma=fp8_mma)
     opt = torch.optim.Adam(list(l1.parameters()) + list(l2.parameters()), lr=2e-3)
     losses = []
     for s in range(steps):
@@ -119,14 +119,40 @@ def _train(fgs, recipe, steps=120, T=1024, D=256, H=512, seed=0):
 def test_toy_training_tracks_fp32(fgs):
     """Every recipe learns (the loss falls by 4x in 120 steps; FP32: ~7x)
     and ends within 25% of the FP32 run's final loss (mean of the last 10
-    steps)."""
+    steps); so does the blockwise recipe with its products on the FP8
+    matrix instructions (promotion per 128-deep block)."""
     ref = _train(fgs, None)
     tail = lambda a: float(a[-10:].mean())
     print(f"fp32: first {ref[0]:.4f} last-10 {tail(ref):.4f}")
     assert tail(ref) < ref[0] / 4
-    for recipe in ("blockwise", "per_tensor", "delayed"):
-        got = _train(fgs, recipe)
+    for recipe, mma in (("blockwise", False), ("per_tensor", False), ("delayed", False), ("blockwise", True)):
+        got = _train(fgs, recipe, fp8_mma=mma)
+        recipe = recipe + (" on FP8 instructions" if mma else "")
         print(f"{recipe}: first {got[0]:.4f} last-10 {tail(got):.4f}")
         assert np.all(np.isfinite(got)), recipe
         assert tail(got) < got[0] / 4, (recipe, got[0], tail(got))
         assert tail(got) < 1.25 * tail(ref), (recipe, tail(got), tail(ref))
+
+
+def test_linear_fp8_mma_products_within_derived_bound(fgs):
+    """The layer with fp8_mma=True: Y, dX and dW against the oracle's
+    blockwise products within the FP8-instruction bound 2^-9 * S + 1e-6
+    (plus one BF16 ulp for the BF16 outputs)."""
+    from _helpers import _bf16_ulp
+    T, K, N = 256, 384, 256
+    layer = fgs.Linear(K, N, recipe="blockwise", device="cuda", fp8_mma=True)
+    x = synth.to_torch_bf16(synth.activations(T, K, seed=30)).cuda().requires_grad_(True)
+    dy = synth.to_torch_bf16(synth.gradients(T, N, seed=31)).cuda()
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xb, wb, dyb = _bits(x), _bits(layer.weight), _bits(dy)
+    none = np.zeros(16, F32)
+    cases = [(y.detach(), _deq(xb, "blockwise", "x", False, none), _deq(wb, "blockwise", "w", False, none), True),
+             (x.grad, _deq(dyb, "blockwise", "dy", False, none), _deq(wb, "blockwise", "w", True, none), True),
+             (layer.weight.grad, _deq(dyb, "blockwise", "dy", True, none), _deq(xb, "blockwise", "x", True, none), False)]
+    for got, a, b, bf16 in cases:
+        cref, sref = oracle.gemm_ref(a, b)
+        err = np.abs(got.float().cpu().numpy().astype(np.float64) - cref)
+        bound = 2.0 ** -9 * sref + 1e-6 + (_bf16_ulp(cref) if bf16 else 0.0)
+        assert np.all(err <= bound)
