@@ -708,6 +708,27 @@ def read_gemm_traffic():
     return summary
 
 
+def gpu_clocks():
+    """Current shader and memory clock levels of the first AMD GPU, read from
+    the amdgpu driver's DPM tables in sysfs (the level marked '*'); plain file
+    reads, no child process.  None where the files are absent."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+            out = {}
+            for key in ("sclk", "mclk"):
+                with open(os.path.join(dev, f"pp_dpm_{key}")) as f:
+                    cur = [ln.split(":", 1)[1].strip(" *\n") for ln in f if ln.rstrip().endswith("*")]
+                out[key] = cur[0] if cur else None
+            return out
+        except (OSError, IndexError):
+            continue
+    return None
+
+
 def cpu_baseline():
     """The oracle, untuned, on a bounded sample of the headline workload: the
     QKV layer (K = 4096, N = 6144) with M cut to 1024 tokens, both recipes:
@@ -792,7 +813,9 @@ def main():
     names = [n for n in args.workloads.split(",") if n]
 
     head = Llama8B(torch, fgs, synth)
+    clocks_before = gpu_clocks()
     wall, kinds, _ = measure(torch, head, args.steps, args.warmup)
+    clocks_after = gpu_clocks()
     ms = wall * 1e3 / args.steps
     value = head.flops() / (wall / args.steps) / 1e12
     rep = kind_report(kinds, args.steps)
@@ -874,6 +897,7 @@ def main():
         "quant": rep.get("quant"),
         "workloads": extra,
         "cpu_baseline": cpu,
+        "clocks": {"before": clocks_before, "after": clocks_after},
     }
     print(json.dumps(out), flush=True)
 
