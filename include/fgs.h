@@ -28,7 +28,8 @@
  *    E5M2 = OCP E5M2 byte (0x7B = 57344); E2M1 = OCP FP4 nibble, two per
  *    byte, element 2j in the low nibble.
  *  - Quantization is online: every scale comes from the amax of the data
- *    being quantized in this call.  FP32-scaled blocks use
+ *    being quantized in this call (except fgs_quantize_delayed, whose scale
+ *    comes from an amax history).  FP32-scaled blocks use
  *    scale = fl32(amax / 448) and code = E4M3_RNE_SAT(fl32(x / scale));
  *    an all-zero block gets scale 1 and signed-zero codes; a block holding
  *    NaN/Inf gets scale NaN and NaN codes.
@@ -37,7 +38,11 @@
  *    returns a message (thread-local).  A kernel launch failure returns
  *    FGS_ERR_HIP; a fault inside a kernel surfaces at the caller's next
  *    synchronisation.
- *  - Pointers must be 16-byte aligned; row strides are in elements.
+ *  - Pointers must be 16-byte aligned; row strides are in elements.  GEMM
+ *    operand row strides must stay below 2^24 bytes.
+ *  - GEMMs sum exact products in FP32 (the codes are decoded exactly to
+ *    FP16/BF16 for the matrix unit), except the *_fp8mma entry points,
+ *    which use the FP8 matrix instructions and a looser error bound.
  */
 #ifndef FGS_H
 #define FGS_H
