@@ -171,6 +171,13 @@ __device__ __forceinline__ f32x4 mfma8_k128(const i32x8& a, const i32x8& b)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, FA, FB, 0, 127, 0, 127);
 }
 
+// FP16 x FP16 MFMA, 16x16 outputs, 32-deep K, FP32 accumulate (lane l holds
+// row l % 16 and the 8 values of K of lane group l / 16).
+__device__ __forceinline__ f32x4 mfma16x16(const f16x8& a, const f16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // 16 E4M3 codes (one 16-byte LDS read) -> two exact FP16 8-vectors: bytes
 // 0..7 feed one MFMA k-step, bytes 8..15 the next.
 __device__ __forceinline__ void decode16(const uint4 v, f16x8& lo, f16x8& hi)
@@ -319,11 +326,13 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                              AMODE != FGS_SCALE_NV16_E4M3 && AMODE != FGS_SCALE_MX32_E8M0;
     constexpr bool B_TILE = BMODE == FGS_SCALE_TILE_1x128;
     constexpr bool MX = AMODE == FGS_SCALE_MX32_E8M0;
-    // promoted modes on the FP8 instructions at the 256 x 256 tile: 16x16x128
-    // instructions, each one scale block, promoted as soon as it is formed,
+    // promoted modes at the 256 x 256 tile: 16x16 output tiles whose partial
+    // sums over one scale block are formed and promoted one tile at a time,
     // so no partial-sum array has to live across the block (it would not fit
-    // beside 128 accumulators at two waves per SIMD)
-    constexpr bool MMA16 = MMA8 && PROMOTE && TI == 4;
+    // beside 128 accumulators at two waves per SIMD).  On the FP8
+    // instructions one 16x16x128 MFMA is the block; on the exact path four
+    // chained 16x16x32 FP16 MFMAs, the B fragments decoded once per block.
+    constexpr bool MMA16 = PROMOTE && TI == 4;
     // MMA16 with 1x128 A scales stages them in LDS with the codes (eight
     // rows per lane would not fit in registers)
     constexpr bool A_LDS = MMA16 && AMODE == FGS_SCALE_TILE_1x128;
@@ -755,12 +764,20 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 const int c0 = (g4 ^ sw16) << 4, c1 = ((4 + g4) ^ sw16) << 4;
                 const uint8_t* la16 = st + (WM * wm + r16) * ROW;
                 const uint8_t* lb16 = st + L::A_BYTES + (64 * wn + r16) * ROW;
-                i32x8 bfr[2 * TJ];
+                // FP8: the codes as they are; exact: decoded to FP16 once per
+                // block, k-step s of lane group g = its codes 8 s .. 8 s + 7
+                i32x8 bfr[MMA8 ? 2 * TJ : 1];
+                f16x8 bfh[MMA8 ? 1 : 2 * TJ][4];
     #pragma unroll
                 for (int b = 0; b < 2 * TJ; ++b) {
                     const uint4 x = *reinterpret_cast<const uint4*>(lb16 + 16 * b * ROW + c0);
                     const uint4 y = *reinterpret_cast<const uint4*>(lb16 + 16 * b * ROW + c1);
-                    bfr[b] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                    if constexpr (MMA8) {
+                        bfr[b] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                    } else {
+                        decode16(x, bfh[b][0], bfh[b][1]);
+                        decode16(y, bfh[b][2], bfh[b][3]);
+                    }
                 }
                 const float sa_t = AMODE == FGS_SCALE_TENSOR ? p.sA[0] : 1.0f;
                 const float fb = BMODE == FGS_SCALE_TENSOR ? sBp[0] : (BMODE == FGS_SCALE_BLOCK_128x128 ? sb_blk : 1.0f);
@@ -776,13 +793,27 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 for (int a = 0; a < 2 * TI; ++a) {
                     const uint4 x = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c0);
                     const uint4 y = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c1);
-                    const i32x8 afr = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                    i32x8 afr;
+                    f16x8 afh[4];
+                    if constexpr (MMA8) {
+                        afr = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+                    } else {
+                        decode16(x, afh[0], afh[1]);
+                        decode16(y, afh[2], afh[3]);
+                    }
                     float fa = sa_t;
                     if constexpr (A_LDS)
                         fa = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES + L::SB_BYTES)[WM * wm + 16 * a + r16];
     #pragma unroll
                     for (int b = 0; b < 2 * TJ; ++b) {
-                        const f32x4 pb = mfma8_k128<FB, FA>(bfr[b], afr);
+                        f32x4 pb;
+                        if constexpr (MMA8) {
+                            pb = mfma8_k128<FB, FA>(bfr[b], afr);
+                        } else {
+                            pb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+                            for (int k4 = 0; k4 < 4; ++k4) pb = mfma16x16(bfh[b][k4], afh[k4], pb);
+                        }
                         const int sub = 4 * (2 * (a & 1) + (b & 1));
                         f32x16& ac = acc[a >> 1][b >> 1];
                         if constexpr (B_TILE) {
@@ -1043,7 +1074,7 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUP == GROUP_M ? a.G : 0));
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
-    constexpr bool a_lds = MMA8 && S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
+    constexpr bool a_lds = S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
     constexpr int scw = AMODE == FGS_SCALE_MX32_E8M0 ? 1 : (AMODE == FGS_SCALE_NV16_E4M3 ? 2 : 0);   // the kernel's SCW
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds,
                                        scw>::STAGE;
@@ -1090,13 +1121,15 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
     constexpr int NONE = GROUP_NONE;
     const bool wide = prefer_wide(a);
     const int amode = a.A.scale_mode, bmode = a.B.scale_mode;
-    // promoted modes: the 256 x 128 tile, or on the FP8 instructions either
-    // tile (16x16x128 instructions at 256 x 256)
+    // promoted modes: the 256 x 128 tile, or the 256 x 256 tile of 16x16
+    // output tiles (FP8 instructions: every mode; exact path: not with 1x128
+    // B scales, whose four scale factors per lane and tile would not fit in
+    // registers beside the held FP16 B fragments)
     constexpr int TL = FGS_SCALE_TILE_1x128, BL = FGS_SCALE_BLOCK_128x128, TN = FGS_SCALE_TENSOR;
     auto promoted = [&](auto am, auto bm) -> hipError_t {
         constexpr int A_ = decltype(am)::value, B_ = decltype(bm)::value;
-        if constexpr (MMA8)
-            if (wide) return launch_modes<W, A_, B_, NONE, 0, true>(p, a, bf16, s);
+        if constexpr (MMA8 || B_ != FGS_SCALE_TILE_1x128)
+            if (wide) return launch_modes<W, A_, B_, NONE, 0, MMA8>(p, a, bf16, s);
         return launch_modes<D, A_, B_, NONE, 0, MMA8>(p, a, bf16, s);
     };
     using IC_TL = std::integral_constant<int, TL>;

@@ -307,3 +307,36 @@ def test_grouped_deepseek_moe_sampled(fgs, N, K):
     # an unsampled row of a zero-weight expert is exactly zero
     other = int(offs[1])
     assert float(c[other].float().abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("amode,bmode", [("tile", "block"), ("tile", "tensor"), ("tensor", "block")])
+@pytest.mark.parametrize("M,N,K", [(257, 129, 256), (520, 777, 384), (1000, 600, 512)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_promoted_wide_tile(fgs, amode, bmode, M, N, K, out):
+    """The promoted modes on the 256 x 256 tile (16x16 output tiles: four
+    chained 16x16x32 FP16 MFMAs per scale block, promoted one tile at a time;
+    A 1x128 scales staged in LDS), forced on ragged shapes the automatic choice
+    would give the 256 x 128 tile: the same bound."""
+    A, ah = oracle_operand(fgs, synth.activations(M, K, seed=M + 3 * K), amode)
+    B, bh = oracle_operand(fgs, synth.weights(N, K, seed=N + 3 * K), bmode)
+    prev = fgs.gemm_tile_policy("wide")
+    try:
+        _run_and_check(fgs, A, B, ah, bh, out)
+    finally:
+        fgs.gemm_tile_policy(prev)
+
+
+def test_gemm_promoted_wide_tile_adversarial_promotion(fgs):
+    """Per-128-K-block A scales spanning 2^-20 .. 2^20 on the 256 x 256
+    promoted tile."""
+    M, N, K = 128, 256, 1024
+    a = oracle.bf16_bits_to_f32(synth.activations(M, K, seed=7, outliers=False)).copy()
+    for kb in range(K // 128):
+        a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
+    A, ah = oracle_operand(fgs, synth.f32_to_bf16_bits(a), "tile")
+    B, bh = oracle_operand(fgs, synth.weights(N, K, seed=8), "block")
+    prev = fgs.gemm_tile_policy("wide")
+    try:
+        _run_and_check(fgs, A, B, ah, bh, torch.float32)
+    finally:
+        fgs.gemm_tile_policy(prev)
