@@ -897,38 +897,18 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                     for (int b = 0; b < 2 * TJ; ++b)
                         sbt[b] = *reinterpret_cast<const float4*>(ssb + 64 * wn + 16 * b + 4 * g4);
                 }
+                if constexpr (MMA8) {
     #pragma unroll
                 for (int a = 0; a < 2 * TI; ++a) {
                     const uint4 x = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c0);
                     const uint4 y = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c1);
-                    i32x8 afr;
-                    f16x8 afh[4];
-                    if constexpr (MMA8) {
-                        afr = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-                    } else {
-                        decode16(x, afh[0], afh[1]);
-                        decode16(y, afh[2], afh[3]);
-                    }
+                    const i32x8 afr = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
                     float fa = sa_t;
                     if constexpr (A_LDS)
                         fa = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES + L::SB_BYTES)[WM * wm + 16 * a + r16];
     #pragma unroll
                     for (int b = 0; b < 2 * TJ; ++b) {
-                        f32x4 pb;
-                        if constexpr (MMA8) {
-                            pb = mfma8_k128<FB, FA>(bfr[b], afr);
-                        } else {
-                            // the chain runs at raised wave priority: of the
-                            // two waves on a SIMD, the one with matrix work
-                            // ready issues first, and the other's decode and
-                            // promotion instructions fill the gaps (measured
-                            // 2-3% faster than one priority)
-                            pb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                            __builtin_amdgcn_s_setprio(1);
-    #pragma unroll
-                            for (int k4 = 0; k4 < 4; ++k4) pb = mfma16x16(bfh[b][k4], afh[k4], pb);
-                            __builtin_amdgcn_s_setprio(0);
-                        }
+                        const f32x4 pb = mfma8_k128<FB, FA>(bfr[b], afr);
                         const int sub = 4 * (2 * (a & 1) + (b & 1));
                         f32x16& ac = acc[a >> 1][b >> 1];
                         if constexpr (B_TILE) {
@@ -941,6 +921,59 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                             for (int e = 0; e < 4; ++e) ac[sub + e] = __builtin_fmaf(pb[e], f, ac[sub + e]);
                         }
                     }
+                }
+                } else {
+                // Exact: chain b of sub-tile a is four dependent 16x16x32
+                // FP16 MFMAs, and the vector work of the sub-tile rides
+                // between them, about two instructions per MFMA, in an order
+                // fixed by scheduling fences: under chain 0 the four FP16
+                // quarters of the A fragment are decoded, each just before
+                // the MFMA that takes it; under chain b > 0 the four sums of
+                // chain b - 1 are promoted (and under chain 1 also those of
+                // the previous sub-tile's last chain), one per MFMA, so no
+                // promotion waits on the chain it reads.
+                auto promote = [&](int a, int b, int e, const f32x4& v, float fa) {
+                    f32x16& ac = acc[a >> 1][b >> 1];
+                    const int sub = 4 * (2 * (a & 1) + (b & 1));
+                    float f;
+                    if constexpr (B_TILE) {
+                        const float sbv[4] = {sbt[b].x, sbt[b].y, sbt[b].z, sbt[b].w};
+                        f = fa * sbv[e];
+                    } else {
+                        f = fa * fb;
+                    }
+                    ac[sub + e] = __builtin_fmaf(v[e], f, ac[sub + e]);
+                };
+                f32x4 pq[2 * TJ], plast = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                float fa_prev = 0.0f;
+    #pragma unroll
+                for (int a = 0; a < 2 * TI; ++a) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c0);
+                    const uint4 y = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c1);
+                    float fa = sa_t;
+                    if constexpr (A_LDS)
+                        fa = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES + L::SB_BYTES)[WM * wm + 16 * a + r16];
+                    f16x8 afh[4];
+    #pragma unroll
+                    for (int b = 0; b < 2 * TJ; ++b) {
+    #pragma unroll
+                        for (int k4 = 0; k4 < 4; ++k4) {
+                            if (b == 0) {
+                                const uint4 v = k4 < 2 ? x : y;
+                                afh[k4] = decode8_fp8<false>((k4 & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y));
+                            }
+                            pq[b] = mfma16x16(bfh[b][k4], afh[k4], k4 == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : pq[b]);
+                            __builtin_amdgcn_sched_barrier(0);
+                            if (b >= 1) promote(a, b - 1, k4, pq[b - 1], fa);
+                            if (b == 1 && a >= 1) promote(a - 1, 2 * TJ - 1, k4, plast, fa_prev);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    plast = pq[2 * TJ - 1];
+                    fa_prev = fa;
+                }
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) promote(2 * TI - 1, 2 * TJ - 1, e, plast, fa_prev);
                 }
             } else if constexpr (MMA8) {
                 // two 64-deep k-steps; lane half h holds chunk 4*s2 + h of its
