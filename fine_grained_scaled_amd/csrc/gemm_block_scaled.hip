@@ -268,6 +268,17 @@ __device__ __forceinline__ void decode16(const uint4 v, float s, bf16x8& lo, bf1
     hi = bf16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
+// MXFP8: 8 E4M3 codes -> BF16 8-vector of code * s (the lower or upper half
+// of what decode16 with a scale returns for 16 codes).
+__device__ __forceinline__ bf16x8 decode8_mx(const uint2 v, float s)
+{
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // E8M0 helper: the converter scale 2^(c - ref) (c <= ref) as an FP32 power
 // of two, clamped at 2^-127 (exponent field 0, which the converters read as
 // 2^-127).
@@ -356,8 +367,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // instructions one 16x16x128 MFMA is the block; on the exact path four
     // chained 16x16x32 FP16 MFMAs, the B fragments decoded once per block.
     constexpr bool MMA16 = PROMOTE && TI == 4;
-    // per-tensor scales on the exact path: the software-pipelined K loop
-    constexpr bool PIPE_T = !PROMOTE && AMODE == FGS_SCALE_TENSOR && !MMA8;
+    // per-tensor and MX scales on the exact path: the software-pipelined K loop
+    constexpr bool PIPE = (AMODE == FGS_SCALE_TENSOR || AMODE == FGS_SCALE_MX32_E8M0) && !PROMOTE && !MMA8;
     // MMA16 with 1x128 A scales stages them in LDS with the codes (eight
     // rows per lane would not fit in registers)
     constexpr bool A_LDS = MMA16 && AMODE == FGS_SCALE_TILE_1x128;
@@ -687,9 +698,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // row lives in slot c ^ swz
     const int swz = (l >> SH) & (CPR - 1), half = l >> 5;
 
-    if constexpr (PIPE_T) {
-        // One scale per operand: no promotion, so a block is eight 32x32x16
-        // k-steps (ks, h) straight into the accumulators.  Lane half `half`
+    if constexpr (PIPE) {
+        // One scale per operand (or MX, whose block scales are applied in the
+        // decode relative to per-row and per-tile reference exponents): no
+        // promotion, so a block is eight 32x32x16 k-steps (ks, h) straight
+        // into the accumulators.  Lane half `half`
         // reads chunk 2 ks + half of its rows; bytes 0-7 feed k-step (ks, 0),
         // bytes 8-15 k-step (ks, 1).  The decode runs half a k-step ahead of
         // the matrix instructions, one operand fragment per MFMA: under the
@@ -704,28 +717,47 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         constexpr bool E5A = (ELEMS & 1) != 0, E5B = (ELEMS & 2) != 0;
         constexpr int NP = TI + TJ, NT = TI * TJ, LAG = NT > NP ? NT - NP : 1;
         static_assert(NP <= NT, "one fragment decode per MFMA");
-        f16x8 af[TI][2], bf[TJ][2];
+        using Frag = std::conditional_t<MX, bf16x8, f16x8>;
+        Frag af[TI][2], bf[TJ][2];
         uint4 raw[NP];
+        uint32_t sw[MX ? NP : 1] = {};   // MX: the fragments' rows' scale words of the block
+        auto rdsw = [&](int stage) {
+            if constexpr (MX) {
+                const uint32_t* scw = reinterpret_cast<const uint32_t*>(smem + stage * L::STAGE + L::SCW_OFF);
+#pragma unroll
+                for (int pc = 0; pc < NP; ++pc)
+                    sw[pc] = scw[pc < TI ? WM * wm + 32 * pc + (l & 31) : BM + 64 * wn + 32 * (pc - TI) + (l & 31)];
+            }
+        };
         auto rd = [&](int stage, int pc, int ks) -> uint4 {
             const uint8_t* st = smem + stage * L::STAGE;
             const uint8_t* q = pc < TI ? st + (WM * wm + (l & 31) + 32 * pc) * ROW
                                        : st + L::A_BYTES + (64 * wn + (l & 31) + 32 * (pc - TI)) * ROW;
             return *reinterpret_cast<const uint4*>(q + (((2 * ks + half) ^ swz) << 4));
         };
-        auto dec = [&](int pc, int h) {
+        // k-step (ks, h) of fragment pc from the chunk in raw[pc]
+        auto dec = [&](int pc, int h, int ks) {
             const uint2 v = h == 0 ? make_uint2(raw[pc].x, raw[pc].y) : make_uint2(raw[pc].z, raw[pc].w);
-            if (pc < TI) af[pc][h] = decode8_fp8<E5A>(v);
-            else bf[pc - TI][h] = decode8_fp8<E5B>(v);
+            if constexpr (MX) {
+                // k-steps (ks, 0) and (ks, 1) both lie in MX block ks of the row
+                const float sc = e8m0_rel((sw[pc] >> (8 * ks)) & 0xFFu, pc < TI ? ea[pc] : eb);
+                if (pc < TI) af[pc][h] = decode8_mx(v, sc);
+                else bf[pc - TI][h] = decode8_mx(v, sc);
+            } else {
+                if (pc < TI) af[pc][h] = decode8_fp8<E5A>(v);
+                else bf[pc - TI][h] = decode8_fp8<E5B>(v);
+            }
         };
         auto mma = [&](int t, int h) {
             const int i = t / TJ, j = t % TJ;
             acc[i][j] = mfma16(bf[j][h], af[i][h], acc[i][j]);
         };
         if (wave_live && nkb > 0) {
+            rdsw(0);
 #pragma unroll
             for (int pc = 0; pc < NP; ++pc) raw[pc] = rd(0, pc, 0);
 #pragma unroll
-            for (int pc = 0; pc < NP; ++pc) dec(pc, 0);
+            for (int pc = 0; pc < NP; ++pc) dec(pc, 0, 0);
         }
         for (int64_t kb = 0; kb < nkb; ++kb) {
             const int cur = (int)(kb & 1);
@@ -743,7 +775,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                         for (int t = 0; t < NT; ++t) {
                             mma(t, h);
                             if (t < NP) {
-                                dec(t, h ^ 1);
+                                dec(t, h ^ 1, h == 0 ? ks : ks + 1);
                                 if (h == 0 && ks + 1 < 4) raw[t] = rd(cur, t, ks + 1);
                             }
                             __builtin_amdgcn_sched_barrier(0);
@@ -753,17 +785,18 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             wait_lds_dma();
             __syncthreads();
             if (wave_live && more) {
+                rdsw(cur ^ 1);
 #pragma unroll
                 for (int pc = 0; pc < NP; ++pc) raw[pc] = rd(cur ^ 1, pc, 0);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     mma(t, 1);
                     const int pc = t - LAG;
-                    if (pc >= 0 && pc < NP) dec(pc, 0);
+                    if (pc >= 0 && pc < NP) dec(pc, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int pc = NT - LAG; pc < NP; ++pc) dec(pc, 0);
+                for (int pc = NT - LAG; pc < NP; ++pc) dec(pc, 0, 0);
             } else if (wave_live) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) mma(t, 1);
