@@ -1039,10 +1039,14 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                 };
                 f32x4 pq[2 * TJ], plast = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 float fa_prev = 0.0f;
+                // the next sub-tile's codes are read as soon as the last
+                // chain has taken the first two FP16 quarters, into their
+                // registers
+                uint4 xn = *reinterpret_cast<const uint4*>(la16 + c0);
+                uint4 yn = *reinterpret_cast<const uint4*>(la16 + c1);
     #pragma unroll
                 for (int a = 0; a < 2 * TI; ++a) {
-                    const uint4 x = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c0);
-                    const uint4 y = *reinterpret_cast<const uint4*>(la16 + 16 * a * ROW + c1);
+                    const uint4 x = xn, y = yn;
                     float fa = sa_t;
                     if constexpr (A_LDS)
                         fa = reinterpret_cast<const float*>(st + L::A_BYTES + L::B_BYTES + L::SB_BYTES)[WM * wm + 16 * a + r16];
@@ -1059,6 +1063,10 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
                             __builtin_amdgcn_sched_barrier(0);
                             if (b >= 1) promote(a, b - 1, k4, pq[b - 1], fa);
                             if (b == 1 && a >= 1) promote(a - 1, 2 * TJ - 1, k4, plast, fa_prev);
+                            if (b == 2 * TJ - 1 && k4 == 1 && a + 1 < 2 * TI) {
+                                xn = *reinterpret_cast<const uint4*>(la16 + 16 * (a + 1) * ROW + c0);
+                                yn = *reinterpret_cast<const uint4*>(la16 + 16 * (a + 1) * ROW + c1);
+                            }
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
