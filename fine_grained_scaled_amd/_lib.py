@@ -20,6 +20,7 @@ EXPORTS = (
     "fgs_quantize_mx",
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
+    "fgs_gemm_block_scaled_ex",
     "fgs_gemm_block_scaled_fp8mma",
     "fgs_grouped_gemm_block_scaled",
     "fgs_grouped_gemm_block_scaled_fp8mma",
@@ -30,7 +31,6 @@ EXPORTS = (
     "fgs_grouped_colwise_blocks",
     "fgs_swiglu_quantize_grouped",
     "fgs_grouped_wgrad_block_scaled",
-    "fgs_gemm_tile_policy",
     "fgs_workspace_bytes",
     "fgs_last_error",
     "fgs_version",
@@ -45,6 +45,15 @@ class FgsOperand(ctypes.Structure):
         ("scale_mode", ctypes.c_int32),
         ("scales", ctypes.c_void_p),
         ("tensor_scale", ctypes.c_void_p),
+    ]
+
+
+class FgsGemmOptions(ctypes.Structure):
+    _fields_ = [
+        ("tile", ctypes.c_int32),
+        ("fp8_mma", ctypes.c_int32),
+        ("q_out", ctypes.c_void_p),
+        ("scales_out", ctypes.c_void_p),
     ]
 
 
@@ -74,6 +83,7 @@ def load() -> ctypes.CDLL:
     OP = ctypes.POINTER(FgsOperand)
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8mma.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
+    lib.fgs_gemm_block_scaled_ex.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, ctypes.POINTER(FgsGemmOptions), P]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8out.argtypes = [OP, OP, I64, I64, I64, P, I64, P, P, P]
@@ -84,14 +94,13 @@ def load() -> ctypes.CDLL:
     lib.fgs_grouped_colwise_blocks.restype = I64
     lib.fgs_grouped_wgrad_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_wgrad_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
-    lib.fgs_gemm_tile_policy.argtypes = [ctypes.c_int]
-    lib.fgs_gemm_tile_policy.restype = ctypes.c_int
     lib.fgs_workspace_bytes.argtypes = [I64, I64]
     lib.fgs_workspace_bytes.restype = SZ
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
-                 "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_fp8mma", "fgs_grouped_gemm_block_scaled",
+                 "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_ex", "fgs_gemm_block_scaled_fp8mma",
+                 "fgs_grouped_gemm_block_scaled",
                  "fgs_grouped_gemm_block_scaled_fp8mma", "fgs_grouped_wgrad_block_scaled_fp8mma",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",
                  "fgs_swiglu_quantize_grouped", "fgs_gemm_block_scaled_fp8out",

@@ -1,7 +1,6 @@
 // fgs_abi.cpp -- the extern "C" entry points of libfgs: argument validation
 // (before any HIP call), error reporting, and dispatch to the launchers.
 // The operations themselves are documented in include/fgs.h.
-#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -75,15 +74,17 @@ int check_operand(const fgs_operand* op, const char* name, int64_t rows, int64_t
 
 namespace fgs {
 
+// A per-thread memo of a device property (no state shared between threads
+// or carried from one call's arguments into another's behaviour).
 int device_cus()
 {
-    static std::atomic<int> cached[64] = {};
+    thread_local int cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
+    int n = cached[dev];
     if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
+        cached[dev] = n;
     }
     return n;
 }
@@ -95,11 +96,6 @@ extern "C" {
 const char* fgs_last_error(void) { return g_last_error.c_str(); }
 
 const char* fgs_version(void) { return "fgs 0.1.0 (gfx950)"; }
-
-int fgs_gemm_tile_policy(int policy)
-{
-    return fgs::set_gemm_tile_policy(policy);
-}
 
 // The tensor-amax passes keep one partial per amax workgroup (4 bytes for
 // TENSOR mode, 8 for NVFP4's two orientations), up to two workgroups per
@@ -237,18 +233,33 @@ static bool is_fp32_mode(int m)
 }
 
 static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
-                     void* C, int64_t ldc, int out_dtype, uint8_t* q_out, float* s_out, void* stream,
-                     bool fp8_mma = false)
+                     void* C, int64_t ldc, int out_dtype, const fgs_gemm_options& o, void* stream)
 {
+    if (o.tile != FGS_TILE_AUTO && o.tile != FGS_TILE_NARROW && o.tile != FGS_TILE_WIDE)
+        return fail(FGS_ERR_INVALID_ARG, "tile %d is not FGS_TILE_AUTO, FGS_TILE_NARROW or FGS_TILE_WIDE", o.tile);
+    if (o.fp8_mma != 0 && o.fp8_mma != 1) return fail(FGS_ERR_INVALID_ARG, "fp8_mma must be 0 or 1 (got %d)", o.fp8_mma);
+    uint8_t* q_out = o.q_out;
+    float* s_out = o.scales_out;
+    if (q_out || s_out) {
+        // the E4M3-output epilogue: BF16 accumulation output, C optional,
+        // codes and scales need N % 128 == 0
+        if (!q_out || !s_out) return fail(FGS_ERR_INVALID_ARG, "q_out and scales_out are required together");
+        if (out_dtype != FGS_OUT_BF16) return fail(FGS_ERR_INVALID_ARG, "the E4M3 output needs out_dtype FGS_OUT_BF16");
+        if (o.fp8_mma) return fail(FGS_ERR_UNSUPPORTED, "the E4M3 output is not available on the FP8 matrix instructions");
+        if (N % 128) return fail(FGS_ERR_UNSUPPORTED, "the E4M3 output needs N %% 128 == 0 (N = %lld)", (long long)N);
+        if (!aligned(q_out, 4) || !aligned(s_out, 4)) return fail(FGS_ERR_UNSUPPORTED, "q_out and scales_out must be 4-byte aligned");
+        if (!C) ldc = N;      // no BF16 output: the common checks see a valid stride
+    }
     int st = check_gemm_common(A, B, M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
     if (st != FGS_OK) return st;
     if (M == 0 || N == 0) return ok();
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
     // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
-    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out, fp8_mma ? 1 : 0};
+    fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out, o.fp8_mma,
+                    o.tile};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (fp8_mma && (A->elem == FGS_ELEM_E2M1 || B->elem == FGS_ELEM_E2M1))
+    if (o.fp8_mma && (A->elem == FGS_ELEM_E2M1 || B->elem == FGS_ELEM_E2M1))
         return fail(FGS_ERR_UNSUPPORTED, "the FP8 matrix-instruction GEMM takes E4M3 / E5M2 operands only");
     if (A->elem != FGS_ELEM_E2M1 && is_fp32_mode(A->scale_mode) && is_fp32_mode(B->scale_mode)) {
         if (A->scale_mode == FGS_SCALE_BLOCK_128x128)
@@ -265,16 +276,25 @@ static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int6
                 A->elem, A->scale_mode, B->scale_mode);
 }
 
+int fgs_gemm_block_scaled_ex(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                             void* C, int64_t ldc, int out_dtype, const fgs_gemm_options* opts, void* stream)
+{
+    const fgs_gemm_options o = opts ? *opts : fgs_gemm_options{};
+    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, o, stream);
+}
+
 int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
                           void* C, int64_t ldc, int out_dtype, void* stream)
 {
-    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream);
+    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, fgs_gemm_options{}, stream);
 }
 
 int fgs_gemm_block_scaled_fp8mma(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
                                  void* C, int64_t ldc, int out_dtype, void* stream)
 {
-    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, nullptr, nullptr, stream, true);
+    fgs_gemm_options o{};
+    o.fp8_mma = 1;
+    return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, o, stream);
 }
 
 // E4M3-output launches: validated like the BF16-out GEMM (C may be NULL);
@@ -291,9 +311,11 @@ static int check_fp8_out(int64_t N, void*& C, int64_t& ldc, uint8_t* q_out, floa
 int fgs_gemm_block_scaled_fp8out(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
                                  void* C, int64_t ldc, uint8_t* q_out, float* scales_out, void* stream)
 {
-    int st = check_fp8_out(N, C, ldc, q_out, scales_out);
-    if (st != FGS_OK) return st;
-    return gemm_impl(A, B, M, N, K, C, ldc, FGS_OUT_BF16, q_out, scales_out, stream);
+    if (!q_out || !scales_out) return fail(FGS_ERR_INVALID_ARG, "q_out and scales_out are required");
+    fgs_gemm_options o{};
+    o.q_out = q_out;
+    o.scales_out = scales_out;
+    return gemm_impl(A, B, M, N, K, C, ldc, FGS_OUT_BF16, o, stream);
 }
 
 static int grouped_impl(const fgs_operand* A, const fgs_operand* B, const int32_t* group_offsets, int32_t G,
@@ -311,7 +333,7 @@ static int grouped_impl(const fgs_operand* A, const fgs_operand* B, const int32_
     const int64_t tiles = ((total_M + 127) / 128 + G) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, total_M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 0, 0, q_out, s_out,
-                    fp8_mma ? 1 : 0};
+                    fp8_mma ? 1 : 0, FGS_TILE_AUTO};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_gemm_block_scaled launch");
 }
 
@@ -441,7 +463,7 @@ static int wgrad_impl(const fgs_operand* A, const fgs_operand* B, const int32_t*
     const int64_t tiles = (int64_t)G * ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, M, N, Kcap, C, ldc, out_dtype == FGS_OUT_BF16, group_offsets, G, 1, total_T,
-                    nullptr, nullptr, fp8_mma ? 1 : 0};
+                    nullptr, nullptr, fp8_mma ? 1 : 0, FGS_TILE_AUTO};
     return hip_status(fgs::launch_gemm_fp8(a, static_cast<hipStream_t>(stream)), "grouped_wgrad_block_scaled launch");
 }
 

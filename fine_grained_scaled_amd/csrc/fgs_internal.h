@@ -95,15 +95,12 @@ struct GemmArgs {
     int64_t T;                      // group_k: tokens the offsets index
     uint8_t* q_out;                 // BF16 out: also 1x128 E4M3 codes of the output, or nullptr
     float* s_out;                   //   their scales [N/128][M]
-    int fp8_mma;                    // dense only: accumulate on the FP8 matrix instructions
+    int fp8_mma;                    // accumulate on the FP8 matrix instructions
+    int tile;                       // dense only: FGS_TILE_AUTO | FGS_TILE_NARROW | FGS_TILE_WIDE
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).
 int device_cus();
-
-// GEMM tile policy (FGS_TILE_*), read at launch.
-int gemm_tile_policy();
-int set_gemm_tile_policy(int policy);
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t stream);

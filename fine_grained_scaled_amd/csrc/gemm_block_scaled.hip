@@ -56,7 +56,6 @@
 // chunk, 256 bytes) touches each of the 64 LDS banks once.  MFMA operands
 // are swapped (B fragment first) so each lane's 16 accumulators share one
 // row m: the 1x128 A scale is one value per lane and per sub-tile row.
-#include <atomic>
 #include <type_traits>
 
 #include "fgs_device.h"
@@ -1224,42 +1223,66 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // The BF16-rounded outputs quantized in 1x128 tiles along N for the next
     // layer (the online rule of the quantizers: s = fl32(amax / 448), code =
     // E4M3_RNE(fl32(y / s))).  A tile row's 128 columns live in two waves
-    // (wn, wn ^ 1), 32 values per lane and 64 per lane pair (l, l ^ 32): the
-    // row maxima meet in the LDS stages, free once the K loop's last barrier
-    // has passed.  Launches with q_out need N % 128 == 0.
-    if constexpr (OUT_BF16 && GROUP != GROUP_K && !MMA16) {
+    // (wn, wn ^ 1), 64 in each.  Rows are taken in row sets rs of the
+    // accumulator layout:
+    //  32x32 tiles: rs = i, lane row 32 i + l % 32; the row's 64 columns of
+    //    the wave lie in lanes l and l ^ 32, 32 values each (j, q, e);
+    //  16x16 tiles (MMA16): rs = 2 i + h, lane row 32 i + 16 h + l % 16; the
+    //    row's 64 columns lie in lanes l, l ^ 16, l ^ 32, l ^ 48, 16 values
+    //    each (j, quarter 2 h + c, e).
+    // The row maxima meet in the LDS stages, free once the K loop's last
+    // barrier has passed.  Launches with q_out need N % 128 == 0.
+    if constexpr (OUT_BF16 && GROUP != GROUP_K && !MMA8) {
         if (p.q_out) {
+            constexpr int RS = MMA16 ? 2 * TI : TI;      // row sets per lane
+            constexpr int QS = MMA16 ? 2 : 4;            // float quads per (row set, j)
+            auto lane_row = [&](int rs) -> int {
+                return MMA16 ? WM * wm + 32 * (rs >> 1) + 16 * (rs & 1) + (l & 15) : WM * wm + 32 * rs + (l & 31);
+            };
+            // float quad c (0 .. QS-1) of row set rs and sub-tile j, and its
+            // first column within the tile
+            auto quad = [&](int rs, int j, int c) -> float4 {
+                const f32x16& a = acc[MMA16 ? rs >> 1 : rs][j];
+                const int o = MMA16 ? 4 * (2 * (rs & 1) + c) : 4 * c;
+                return make_float4(a[o], a[o + 1], a[o + 2], a[o + 3]);
+            };
+            auto quad_col = [&](int j, int c) -> int {
+                return MMA16 ? 64 * wn + 32 * j + 16 * c + 4 * (l >> 4) : 64 * wn + 32 * j + 8 * c + 4 * (l >> 5);
+            };
             uint32_t* rmax = reinterpret_cast<uint32_t*>(smem);      // [BM][NWN] |BF16| bits
 #pragma unroll
-            for (int i = 0; i < TI; ++i) {
+            for (int rs = 0; rs < RS; ++rs) {
                 uint32_t mx = 0;
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                        const uint32_t h23 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    for (int c = 0; c < QS; ++c) {
+                        const float4 v = quad(rs, j, c);
+                        const uint32_t h01 = bf16x2_rne(v.x, v.y);
+                        const uint32_t h23 = bf16x2_rne(v.z, v.w);
                         mx = max(mx, max(max(h01 & 0x7FFFu, (h01 >> 16) & 0x7FFFu),
                                          max(h23 & 0x7FFFu, (h23 >> 16) & 0x7FFFu)));
                     }
-                mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-                if (l < 32) rmax[(WM * wm + 32 * i + l) * NWN + wn] = mx;
+                if constexpr (MMA16) mx = max_xor16(mx);
+                mx = max_xor32(mx);
+                if (l < (MMA16 ? 16 : 32)) rmax[lane_row(rs) * NWN + wn] = mx;
             }
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                const int r = WM * wm + 32 * i + (l & 31);
+            for (int rs = 0; rs < RS; ++rs) {
+                const int r = lane_row(rs);
                 const int64_t m = m0 + r;
                 const E4M3Block b = e4m3_block_from_amax_bits(max(rmax[r * NWN + wn], rmax[r * NWN + (wn ^ 1)]));
                 if (m < m_end) {
-                    if (l < 32 && (wn & 1) == 0) p.s_out[((n0 + 64 * wn) / 128) * p.M + m] = b.s;
+                    if (l < (MMA16 ? 16 : 32) && (wn & 1) == 0) p.s_out[((n0 + 64 * wn) / 128) * p.M + m] = b.s;
 #pragma unroll
                     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int64_t n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (l >> 5);
-                            const uint32_t h01 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                            const uint32_t h23 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        for (int c = 0; c < QS; ++c) {
+                            const float4 v = quad(rs, j, c);
+                            const int64_t n = n0 + quad_col(j, c);
+                            const uint32_t h01 = bf16x2_rne(v.x, v.y);
+                            const uint32_t h23 = bf16x2_rne(v.z, v.w);
                             uint32_t c4 = 0x7F7F7F7Fu;
                             if (!b.nan)
                                 c4 = e4m3_pack4(e4m3_quotient_bits(h01 << 16, b), e4m3_quotient_bits(h01 & 0xFFFF0000u, b),
@@ -1323,6 +1346,10 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUP == GROUP_M ? a.G : 0));
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
+    // the E4M3-output epilogue exists for BF16 output on the exact path of
+    // the row-grouped and dense schedules only; any other launch with q_out
+    // would leave it unwritten, so it is refused before launching
+    if (a.q_out && (!bf16 || MMA8 || GROUP == GROUP_K)) return hipErrorInvalidValue;
     constexpr bool a_lds = S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
     constexpr int scw = AMODE == FGS_SCALE_MX32_E8M0 ? 1 : (AMODE == FGS_SCALE_NV16_E4M3 ? 2 : 0);   // the kernel's SCW
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds,
@@ -1341,13 +1368,10 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
 // 8192 x 28672 x 4096) and about 1.6x on the FP8 instructions (1.45-1.65 on
 // that shape), but halves the tile count, so a problem whose wide tiles fill
 // the last round poorly runs faster on the narrow tile: compare rounds x
-// time per round.
-std::atomic<int> g_tile_policy{FGS_TILE_AUTO};
-
+// time per round.  The caller may force either tile (GemmArgs::tile).
 bool prefer_wide(const GemmArgs& a)
 {
-    const int policy = g_tile_policy.load(std::memory_order_relaxed);
-    if (policy != FGS_TILE_AUTO) return policy == FGS_TILE_WIDE;
+    if (a.tile != FGS_TILE_AUTO) return a.tile == FGS_TILE_WIDE;
     const int64_t cus = device_cus();   // one workgroup of either dense shape fills a CU's LDS
     const int64_t tm = (a.M + ShapeWide::BM - 1) / ShapeWide::BM;
     const int64_t wide = tm * ((a.N + ShapeWide::BN - 1) / ShapeWide::BN);
@@ -1422,14 +1446,6 @@ hipError_t dispatch_dense(const GemmParams& p, const GemmArgs& a, bool bf16, hip
 }
 
 } // namespace
-
-int gemm_tile_policy() { return g_tile_policy.load(); }
-
-int set_gemm_tile_policy(int policy)
-{
-    if (policy != FGS_TILE_AUTO && policy != FGS_TILE_NARROW && policy != FGS_TILE_WIDE) return -1;
-    return g_tile_policy.exchange(policy);
-}
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
 {

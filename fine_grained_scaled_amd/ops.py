@@ -218,15 +218,13 @@ def _check_operand(op: Operand, rows: int, K: int, name: str, groups: int = 1):
                          f"(got {op.scales.dtype}, {op.scales.numel()})")
 
 
-def gemm_tile_policy(policy: str) -> str:
-    """Set the workgroup tile of the single-scale GEMM modes ("auto",
-    "narrow" = 256 x 128, "wide" = 256 x 256); returns the previous one.
-    Results are bit-identical across policies."""
-    codes = {"auto": _lib.TILE_AUTO, "narrow": _lib.TILE_NARROW, "wide": _lib.TILE_WIDE}
-    if policy not in codes:
-        raise ValueError(f"tile policy must be one of {sorted(codes)}")
-    prev = _lib.load().fgs_gemm_tile_policy(codes[policy])
-    return {v: k for k, v in codes.items()}[prev]
+TILES = {"auto": _lib.TILE_AUTO, "narrow": _lib.TILE_NARROW, "wide": _lib.TILE_WIDE}
+
+
+def _tile_code(tile: str) -> int:
+    if tile not in TILES:
+        raise ValueError(f"tile must be one of {sorted(TILES)}")
+    return TILES[tile]
 
 
 def _out_code(out_dtype):
@@ -239,16 +237,20 @@ def _out_code(out_dtype):
 
 def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
                       out: Optional[torch.Tensor] = None, K: Optional[int] = None,
-                      fp8_mma: bool = False) -> torch.Tensor:
+                      fp8_mma: bool = False, tile: str = "auto") -> torch.Tensor:
     """C[M x N] = sum_k A^[m, k] * B^[n, k] over scaled low-precision operands.
-    fp8_mma=True runs fgs_gemm_block_scaled_fp8mma: the FP8 matrix
-    instructions with promotion per 128-K block (FP8 operands only; a looser
-    error bound than the exact default)."""
+    fp8_mma=True runs the FP8 matrix instructions with promotion per 128-K
+    block (FP8 operands only; a looser error bound than the exact default).
+    tile: "auto" (chosen per problem), "narrow" (256 x 128 outputs per
+    workgroup) or "wide" (256 x 256).  The defaults call
+    fgs_gemm_block_scaled / fgs_gemm_block_scaled_fp8mma, a forced tile
+    fgs_gemm_block_scaled_ex."""
     _need_gpu(A.data, B.data, A.scales, B.scales)
     M, N = A.data.shape[0], B.data.shape[0]
     if K is None:
         K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
     code = _out_code(out_dtype)
+    tcode = _tile_code(tile)
     _check_operand(A, M, K, "A")
     _check_operand(B, N, K, "B")
     if out is None:
@@ -256,19 +258,28 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
     if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] < M or out.shape[1] < N or out.stride(1) != 1:
         raise ValueError("out must be a [M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
-    fn = _lib.load().fgs_gemm_block_scaled_fp8mma if fp8_mma else _lib.load().fgs_gemm_block_scaled
-    check(fn(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0), code, _stream()))
+    lib = _lib.load()
+    if tcode == _lib.TILE_AUTO:
+        fn = lib.fgs_gemm_block_scaled_fp8mma if fp8_mma else lib.fgs_gemm_block_scaled
+        check(fn(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0), code, _stream()))
+    else:
+        opt = _lib.FgsGemmOptions(tcode, 1 if fp8_mma else 0, None, None)
+        check(lib.fgs_gemm_block_scaled_ex(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0),
+                                           code, ctypes.byref(opt), _stream()))
     return out
 
 
-def gemm_block_scaled_fp8out(A: Operand, B: Operand, bf16_out: bool = True, K: Optional[int] = None):
+def gemm_block_scaled_fp8out(A: Operand, B: Operand, bf16_out: bool = True, K: Optional[int] = None,
+                             tile: str = "auto"):
     """gemm_block_scaled with BF16 output whose epilogue also quantizes it in
     1x128 tiles along N (the next layer's A operand).  Returns (Quantized
-    with q [M x N] and scales [N/128][M], the BF16 C or None)."""
+    with q [M x N] and scales [N/128][M], the BF16 C or None).  tile as for
+    gemm_block_scaled (a forced tile calls fgs_gemm_block_scaled_ex)."""
     _need_gpu(A.data, B.data, A.scales, B.scales)
     M, N = A.data.shape[0], B.data.shape[0]
     if K is None:
         K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
+    tcode = _tile_code(tile)
     _check_operand(A, M, K, "A")
     _check_operand(B, N, K, "B")
     dev = A.data.device
@@ -276,8 +287,14 @@ def gemm_block_scaled_fp8out(A: Operand, B: Operand, bf16_out: bool = True, K: O
     q = torch.empty((M, N), dtype=torch.uint8, device=dev)
     s = torch.empty(((N + 127) // 128, M), dtype=torch.float32, device=dev)
     a, b = A.c_struct(), B.c_struct()
-    check(_lib.load().fgs_gemm_block_scaled_fp8out(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(c),
-                                                   N, _ptr(q), _ptr(s), _stream()))
+    lib = _lib.load()
+    if tcode == _lib.TILE_AUTO:
+        check(lib.fgs_gemm_block_scaled_fp8out(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(c),
+                                               N, _ptr(q), _ptr(s), _stream()))
+    else:
+        opt = _lib.FgsGemmOptions(tcode, 0, q.data_ptr(), s.data_ptr())
+        check(lib.fgs_gemm_block_scaled_ex(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(c), N, OUT_BF16,
+                                           ctypes.byref(opt), _stream()))
     return Quantized(q, s, None, None, SCALE_TILE_1x128), c
 
 

@@ -416,16 +416,42 @@ int fgs_grouped_gemm_block_scaled_fp8out(const fgs_operand *A, const fgs_operand
                                          int64_t total_M, int64_t N, int64_t K, void *C, int64_t ldc,
                                          uint8_t *q_out, float *scales_out, void *stream);
 
-/* Workgroup tile of the GEMMs whose operands carry one scale for all of K
- * (per-tensor x per-tensor E4M3, NVFP4): FGS_TILE_AUTO (default) picks per
- * problem from the tile counts and the device's compute units,
- * FGS_TILE_NARROW forces 256 x 128 outputs per workgroup, FGS_TILE_WIDE
- * 256 x 256.  Every output is accumulated in the same order either way, so
- * the results are bit-identical; only the speed differs.  Other modes ignore
- * the policy.  Process-wide; returns the previous policy, or -1 (nothing
- * changed) for an unknown value. */
+/*
+ * fgs_gemm_block_scaled_ex -- fgs_gemm_block_scaled with per-call options:
+ *   the workgroup tile, the matrix instructions, and the E4M3-output
+ *   epilogue.   [DSV3] "Mixed precision framework", "Increasing
+ *   accumulation precision"; [NEMO]; [NVFP4].
+ * opts     NULL, or a caller-owned host struct read during the call only.
+ *          NULL and an all-zero struct both mean: automatic tile, exact
+ *          path, no E4M3 output, i.e. fgs_gemm_block_scaled.
+ *   tile        FGS_TILE_AUTO picks the workgroup tile per problem from the
+ *               tile counts and the device's compute units; FGS_TILE_NARROW
+ *               forces 256 x 128 outputs per workgroup, FGS_TILE_WIDE
+ *               256 x 256.  Only the speed and the order of the FP32 sums
+ *               inside one 128-deep block differ: per-tensor E4M3/E5M2 and
+ *               NVFP4 results are bit-identical across tiles, and every mode
+ *               meets the accuracy bound on either tile.
+ *   fp8_mma     0: exact (codes decoded to FP16/BF16); 1: the FP8 matrix
+ *               instructions, as fgs_gemm_block_scaled_fp8mma (with its
+ *               looser bound).
+ *   q_out, scales_out  both NULL, or the E4M3-output epilogue of
+ *               fgs_gemm_block_scaled_fp8out (then out_dtype must be
+ *               FGS_OUT_BF16, C may be NULL, N % 128 == 0, and fp8_mma must
+ *               be 0).
+ * Other arguments, layouts, ownership and errors as fgs_gemm_block_scaled;
+ * an unknown tile or fp8_mma value returns FGS_ERR_INVALID_ARG.  The library
+ * keeps no state between calls: every choice is made from the arguments.
+ */
 enum { FGS_TILE_AUTO = 0, FGS_TILE_NARROW = 1, FGS_TILE_WIDE = 2 };
-int fgs_gemm_tile_policy(int policy);
+typedef struct {
+    int32_t tile;          /* FGS_TILE_*                                      */
+    int32_t fp8_mma;       /* 0 or 1                                          */
+    uint8_t *q_out;        /* device E4M3 [M x N] or NULL                     */
+    float *scales_out;     /* device FP32 [N/128][M] or NULL                  */
+} fgs_gemm_options;
+int fgs_gemm_block_scaled_ex(const fgs_operand *A, const fgs_operand *B,
+                             int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
+                             int out_dtype, const fgs_gemm_options *opts, void *stream);
 
 /* Device workspace needed by TENSOR-mode and NVFP4 quantization (bytes). */
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols);

@@ -38,18 +38,6 @@ def test_version_and_workspace(lib):
     assert lib.fgs_last_error() is not None
 
 
-def test_gemm_tile_policy_setter(lib):
-    """Host-side state only: set, read back through the return value, reject
-    unknown values without changing the policy."""
-    prev = lib.fgs_gemm_tile_policy(_lib.TILE_WIDE)
-    try:
-        assert lib.fgs_gemm_tile_policy(_lib.TILE_NARROW) == _lib.TILE_WIDE
-        assert lib.fgs_gemm_tile_policy(7) == -1
-        assert lib.fgs_gemm_tile_policy(_lib.TILE_AUTO) == _lib.TILE_NARROW
-    finally:
-        lib.fgs_gemm_tile_policy(prev)
-
-
 # Fake, 16-byte aligned, never-dereferenced addresses: every call below must
 # be rejected by validation, which happens before any HIP call.
 FAKE = ctypes.c_void_p(0x10000)
@@ -128,6 +116,33 @@ def test_gemm_validation(lib):
     assert g(r(a), r(b), big + 1, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED  # M too large
     assert g(r(a), r(b), big, big, 256, FAKE, big, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # 2^45 tiles
     assert b"tiles" in lib.fgs_last_error()
+
+
+def test_gemm_ex_options_validation(lib):
+    """The per-call options of fgs_gemm_block_scaled_ex: an unknown tile or
+    fp8_mma value, a half-given E4M3 output, the E4M3 output with FP32 C,
+    on the FP8 instructions or with N % 128 != 0 are rejected before any HIP
+    call; NULL options and an all-zero struct validate like the plain entry
+    point."""
+    S = NULL
+    a, b = _op(), _op(mode=2)
+    g = lib.fgs_gemm_block_scaled_ex
+    r = ctypes.byref
+    O = _lib.FgsGemmOptions
+    assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, None, S) == _lib.FGS_ERR_UNSUPPORTED    # K % 128, NULL opts
+    assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, r(O()), S) == _lib.FGS_ERR_UNSUPPORTED  # same, zero opts
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 0, r(O(3, 0, None, None)), S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 0, r(O(-1, 0, None, None)), S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 0, r(O(0, 2, None, None)), S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 1, r(O(0, 0, 0x10000, None)), S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 0, r(O(0, 0, 0x10000, 0x10000)), S) == _lib.FGS_ERR_INVALID_ARG
+    assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 1, r(O(2, 1, 0x10000, 0x10000)), S) == _lib.FGS_ERR_UNSUPPORTED
+    assert g(r(a), r(b), 128, 136, 256, FAKE, 136, 1, r(O(1, 0, 0x10000, 0x10000)), S) == _lib.FGS_ERR_UNSUPPORTED
+    # every valid tile with a K error still reaches the K check
+    for tile in (_lib.TILE_AUTO, _lib.TILE_NARROW, _lib.TILE_WIDE):
+        assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, r(O(tile, 0, None, None)), S) == _lib.FGS_ERR_UNSUPPORTED
+    # nothing to do: M = 0 succeeds with any valid option and launches nothing
+    assert g(r(a), r(b), 0, 128, 256, FAKE, 128, 0, r(O(2, 1, None, None)), S) == _lib.FGS_OK
 
 
 def test_grouped_validation(lib):

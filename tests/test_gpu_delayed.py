@@ -158,13 +158,8 @@ def test_e5m2_gemm_tile_policies_bit_identical(fgs, ea, eb):
     A, _ = _tensor_operand(fgs, a, ea, [1e-2])
     B, _ = _tensor_operand(fgs, b, eb, [0.1])
     res = {}
-    prev = fgs.gemm_tile_policy("narrow")
-    try:
-        for pol in ("narrow", "wide"):
-            fgs.gemm_tile_policy(pol)
-            res[pol] = fgs.gemm_block_scaled(A, B, torch.float32).cpu()
-    finally:
-        fgs.gemm_tile_policy(prev)
+    for tile in ("narrow", "wide"):
+        res[tile] = fgs.gemm_block_scaled(A, B, torch.float32, tile=tile).cpu()
     assert torch.equal(res["narrow"].view(torch.int32), res["wide"].view(torch.int32))
 
 

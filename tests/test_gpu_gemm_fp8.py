@@ -53,8 +53,8 @@ def oracle_operand(fgs, bits, mode, colwise=False, rows_for_ref=None):
     return op, deq
 
 
-def _run_and_check(fgs, A, B, a_hat, b_hat, out_dtype, rows=None):
-    c = fgs.gemm_block_scaled(A, B, out_dtype)
+def _run_and_check(fgs, A, B, a_hat, b_hat, out_dtype, rows=None, tile="auto"):
+    c = fgs.gemm_block_scaled(A, B, out_dtype, tile=tile)
     torch.cuda.synchronize()
     c = c.float().cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -101,14 +101,9 @@ def test_gemm_tile_policies_bit_identical(fgs, M, N, K, out):
     A, ah = oracle_operand(fgs, synth.activations(M, K, seed=M), "tensor")
     B, bh = oracle_operand(fgs, synth.weights(N, K, seed=N), "tensor")
     res = {}
-    prev = fgs.gemm_tile_policy("narrow")
-    try:
-        for pol in ("narrow", "wide"):
-            fgs.gemm_tile_policy(pol)
-            _run_and_check(fgs, A, B, ah, bh, out)
-            res[pol] = fgs.gemm_block_scaled(A, B, out).cpu()
-    finally:
-        fgs.gemm_tile_policy(prev)
+    for tile in ("narrow", "wide"):
+        _run_and_check(fgs, A, B, ah, bh, out, tile=tile)
+        res[tile] = fgs.gemm_block_scaled(A, B, out, tile=tile).cpu()
     assert torch.equal(res["narrow"].view(torch.uint8), res["wide"].view(torch.uint8))
 
 
@@ -319,11 +314,7 @@ def test_gemm_promoted_wide_tile(fgs, amode, bmode, M, N, K, out):
     would give the 256 x 128 tile: the same bound."""
     A, ah = oracle_operand(fgs, synth.activations(M, K, seed=M + 3 * K), amode)
     B, bh = oracle_operand(fgs, synth.weights(N, K, seed=N + 3 * K), bmode)
-    prev = fgs.gemm_tile_policy("wide")
-    try:
-        _run_and_check(fgs, A, B, ah, bh, out)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    _run_and_check(fgs, A, B, ah, bh, out, tile="wide")
 
 
 def test_gemm_promoted_wide_tile_adversarial_promotion(fgs):
@@ -335,8 +326,4 @@ def test_gemm_promoted_wide_tile_adversarial_promotion(fgs):
         a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
     A, ah = oracle_operand(fgs, synth.f32_to_bf16_bits(a), "tile")
     B, bh = oracle_operand(fgs, synth.weights(N, K, seed=8), "block")
-    prev = fgs.gemm_tile_policy("wide")
-    try:
-        _run_and_check(fgs, A, B, ah, bh, torch.float32)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    _run_and_check(fgs, A, B, ah, bh, torch.float32, tile="wide")

@@ -69,10 +69,10 @@ def tensor_operand(fgs, bits, elem):
     return op, oracle.dequant_tensor(q, s, elem)
 
 
-def check(fgs, A, B, ah, bh, out, rows=None):
+def check(fgs, A, B, ah, bh, out, rows=None, tile="auto"):
     """Runs the FP8-instruction GEMM and checks the derived bound; returns
     the worst err / S (for the report) ."""
-    c = fgs.gemm_block_scaled(A, B, out, fp8_mma=True)
+    c = fgs.gemm_block_scaled(A, B, out, fp8_mma=True, tile=tile)
     torch.cuda.synchronize()
     c = c.float().cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -112,11 +112,7 @@ def test_fp8mma_adversarial_promotion(fgs, policy):
         a[:, kb * 128:(kb + 1) * 128] *= np.float32(2.0 ** (5 * kb - 20))
     A, ah = e4m3_operand(fgs, synth.f32_to_bf16_bits(a), "tile")
     B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=8), "block")
-    prev = fgs.gemm_tile_policy(policy)
-    try:
-        check(fgs, A, B, ah, bh, torch.float32)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    check(fgs, A, B, ah, bh, torch.float32, tile=policy)
 
 
 PROMOTED = [("tile", "block"), ("tile", "tile"), ("tile", "tensor"), ("tensor", "block"), ("tensor", "tile")]
@@ -132,11 +128,7 @@ def test_fp8mma_promoted_wide_tile(fgs, amode, bmode, M, N, K, out):
     same bound."""
     A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=M + 2 * K), amode)
     B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=N + 2 * K), bmode)
-    prev = fgs.gemm_tile_policy("wide")
-    try:
-        check(fgs, A, B, ah, bh, out)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    check(fgs, A, B, ah, bh, out, tile="wide")
 
 
 @pytest.mark.parametrize("ea,eb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
@@ -179,16 +171,12 @@ def test_fp8mma_mx_exponent_spread(fgs):
 def test_fp8mma_tile_policies(fgs, policy):
     """Per-tensor and MX operands on either workgroup tile."""
     M, N, K = 520, 777, 384
-    prev = fgs.gemm_tile_policy(policy)
-    try:
-        A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=30), "tensor")
-        B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=31), "tensor")
-        check(fgs, A, B, ah, bh, torch.float32)
-        A, ah = mx_operand(fgs, synth.activations(M, K, seed=30, outliers=False))
-        B, bh = mx_operand(fgs, synth.weights(N, K, seed=31))
-        check(fgs, A, B, ah, bh, torch.bfloat16)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    A, ah = e4m3_operand(fgs, synth.activations(M, K, seed=30), "tensor")
+    B, bh = e4m3_operand(fgs, synth.weights(N, K, seed=31), "tensor")
+    check(fgs, A, B, ah, bh, torch.float32, tile=policy)
+    A, ah = mx_operand(fgs, synth.activations(M, K, seed=30, outliers=False))
+    B, bh = mx_operand(fgs, synth.weights(N, K, seed=31))
+    check(fgs, A, B, ah, bh, torch.bfloat16, tile=policy)
 
 
 def test_fp8mma_determinism(fgs):

@@ -66,6 +66,34 @@ def test_fp8out_dense(fgs, amode, bmode, M, N, K):
     assert torch.equal(qq2.q, qq.q) and torch.equal(qq2.scales.view(torch.int32), qq.scales.view(torch.int32))
 
 
+@pytest.mark.parametrize("amode,bmode", [("tile", "block"), ("tile", "tensor"), ("tensor", "block")])
+@pytest.mark.parametrize("M,N,K", [(520, 384, 384), (257, 768, 256), (8, 256, 128)])
+@pytest.mark.parametrize("bf16_out", [True, False])
+def test_fp8out_promoted_wide_tile(fgs, amode, bmode, M, N, K, bf16_out):
+    """The promoted modes forced onto the 256 x 256 tile, whose accumulators
+    are 16x16 output tiles (a row's 64 columns of a wave spread over four
+    lanes): the epilogue's codes and scales equal the oracle's 1x128
+    quantization of the BF16 C, with and without the BF16 output, and both
+    tiles give the same codes (where their BF16 outputs agree bit for bit)."""
+    A, ah = _e4m3_operand(fgs, synth.activations(M, K, seed=M + 11), amode)
+    B, bh = _e4m3_operand(fgs, synth.weights(N, K, seed=N + 13), bmode)
+    qq, c = fgs.gemm_block_scaled_fp8out(A, B, tile="wide")
+    torch.cuda.synchronize()
+    cref, sref = oracle.gemm_ref(ah, bh)
+    ok, nbad = gemm_within_bf16_bound(c.float().cpu().numpy().astype(np.float64), cref, sref)
+    assert ok, f"{nbad} BF16 outputs outside one ulp"
+    _check_codes(qq, _bits(c))
+    if not bf16_out:
+        qq2, c2 = fgs.gemm_block_scaled_fp8out(A, B, bf16_out=False, tile="wide")
+        torch.cuda.synchronize()
+        assert c2 is None
+        assert torch.equal(qq2.q, qq.q) and torch.equal(qq2.scales.view(torch.int32), qq.scales.view(torch.int32))
+    # the plain BF16 GEMM on the same tile gives the same C
+    c_plain = fgs.gemm_block_scaled(A, B, torch.bfloat16, tile="wide")
+    torch.cuda.synchronize()
+    assert torch.equal(c_plain.view(torch.int16), c.view(torch.int16))
+
+
 @pytest.mark.parametrize("policy", ["narrow", "wide"])
 def test_fp8out_per_tensor_both_tiles_and_nan_row(fgs, policy):
     """Per-tensor operands on either workgroup tile (the wide tile pairs the
@@ -78,12 +106,8 @@ def test_fp8out_per_tensor_both_tiles_and_nan_row(fgs, policy):
     q[77, 5] = 0x7F
     A = fgs.Operand(torch.from_numpy(q).cuda(), torch.from_numpy(s.reshape(1)).cuda(), 0)
     B, _ = _e4m3_operand(fgs, synth.weights(N, K, seed=4), "tensor")
-    prev = fgs.gemm_tile_policy(policy)
-    try:
-        qq, c = fgs.gemm_block_scaled_fp8out(A, B)
-        torch.cuda.synchronize()
-    finally:
-        fgs.gemm_tile_policy(prev)
+    qq, c = fgs.gemm_block_scaled_fp8out(A, B, tile=policy)
+    torch.cuda.synchronize()
     cb = _bits(c)
     _check_codes(qq, cb)
     assert np.all(qq.q.cpu().numpy()[77] == 0x7F) and np.all(np.isnan(qq.scales.cpu().numpy()[:, 77]))

@@ -32,8 +32,8 @@ def mx_operand(fgs, bits, colwise=False, rows=None):
     return op, deq
 
 
-def _check(fgs, A, B, ah, bh, out, rows=None):
-    c = fgs.gemm_block_scaled(A, B, out)
+def _check(fgs, A, B, ah, bh, out, rows=None, tile="auto"):
+    c = fgs.gemm_block_scaled(A, B, out, tile=tile)
     torch.cuda.synchronize()
     c = c.float().cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -97,12 +97,8 @@ def test_mx_gemm_nan_blocks(fgs, policy):
     b[131, 300] = np.nan
     A, ah = mx_operand(fgs, synth.f32_to_bf16_bits(a))
     B, bh = mx_operand(fgs, synth.f32_to_bf16_bits(b))
-    prev = fgs.gemm_tile_policy(policy)
-    try:
-        c = fgs.gemm_block_scaled(A, B, torch.float32)
-        torch.cuda.synchronize()
-    finally:
-        fgs.gemm_tile_policy(prev)
+    c = fgs.gemm_block_scaled(A, B, torch.float32, tile=policy)
+    torch.cuda.synchronize()
     c = c.cpu().numpy().astype(np.float64)
     cref, sref = oracle.gemm_ref(ah, bh)
     assert np.array_equal(np.isnan(c), np.isnan(cref))
@@ -118,12 +114,8 @@ def test_mx_gemm_tile_policies(fgs, policy):
     M, N, K = 520, 777, 384
     A, ah = mx_operand(fgs, synth.activations(M, K, seed=30, outliers=False))
     B, bh = mx_operand(fgs, synth.weights(N, K, seed=31))
-    prev = fgs.gemm_tile_policy(policy)
-    try:
-        _check(fgs, A, B, ah, bh, torch.float32)
-        _check(fgs, A, B, ah, bh, torch.bfloat16)
-    finally:
-        fgs.gemm_tile_policy(prev)
+    _check(fgs, A, B, ah, bh, torch.float32, tile=policy)
+    _check(fgs, A, B, ah, bh, torch.bfloat16, tile=policy)
 
 
 def test_mx_gemm_determinism(fgs):

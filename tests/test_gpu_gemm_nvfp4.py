@@ -39,8 +39,8 @@ def nv_operand(fgs, bits, colwise=False, rht=False, stochastic=False, rows=None)
     return op, deq
 
 
-def _check(fgs, A, B, ah, bh, out, rows=None):
-    c = fgs.gemm_block_scaled(A, B, out)
+def _check(fgs, A, B, ah, bh, out, rows=None, tile="auto"):
+    c = fgs.gemm_block_scaled(A, B, out, tile=tile)
     torch.cuda.synchronize()
     c = c.float().cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -68,14 +68,9 @@ def test_nvfp4_gemm_tile_policies_bit_identical(fgs, M, N, K):
     A, ah = nv_operand(fgs, synth.activations(M, K, seed=M + 3))
     B, bh = nv_operand(fgs, synth.weights(N, K, seed=N + 5))
     res = {}
-    prev = fgs.gemm_tile_policy("narrow")
-    try:
-        for pol in ("narrow", "wide"):
-            fgs.gemm_tile_policy(pol)
-            _check(fgs, A, B, ah, bh, torch.float32)
-            res[pol] = fgs.gemm_block_scaled(A, B, torch.float32).cpu()
-    finally:
-        fgs.gemm_tile_policy(prev)
+    for tile in ("narrow", "wide"):
+        _check(fgs, A, B, ah, bh, torch.float32, tile=tile)
+        res[tile] = fgs.gemm_block_scaled(A, B, torch.float32, tile=tile).cpu()
     assert torch.equal(res["narrow"].view(torch.uint8), res["wide"].view(torch.uint8))
 
 
