@@ -16,6 +16,7 @@ TILE_AUTO, TILE_NARROW, TILE_WIDE = 0, 1, 2
 
 EXPORTS = (
     "fgs_quantize_blockwise",
+    "fgs_quantize_blockwise_noalloc",
     "fgs_quantize_delayed",
     "fgs_quantize_mx",
     "fgs_quantize_nvfp4",
@@ -77,6 +78,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
     lib.fgs_quantize_blockwise.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P, SZ, P]
+    lib.fgs_quantize_blockwise_noalloc.argtypes = [P, I64, I64, I64, I32, P, P, P, P, P]
     lib.fgs_quantize_delayed.argtypes = [P, I64, I64, I64, I32, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
     lib.fgs_quantize_mx.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     lib.fgs_quantize_nvfp4.argtypes = [P, I64, I64, I64, I32, U64, I32, U64, P, P, P, P, P, P, SZ, P]
@@ -98,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.fgs_workspace_bytes.restype = SZ
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
-    for name in ("fgs_quantize_blockwise", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
+    for name in ("fgs_quantize_blockwise", "fgs_quantize_blockwise_noalloc", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
                  "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_ex", "fgs_gemm_block_scaled_fp8mma",
                  "fgs_grouped_gemm_block_scaled",
                  "fgs_grouped_gemm_block_scaled_fp8mma", "fgs_grouped_wgrad_block_scaled_fp8mma",

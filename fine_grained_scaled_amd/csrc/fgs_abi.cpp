@@ -107,15 +107,15 @@ size_t fgs_workspace_bytes(int64_t rows, int64_t cols)
     return 4096;
 }
 
-int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
-                           uint8_t* q, float* scales, uint8_t* qT, float* scalesT,
-                           void* workspace, size_t workspace_bytes, void* stream)
+// Arguments of fgs_quantize_blockwise apart from its workspace.
+static int check_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                           uint8_t* q, float* scales, uint8_t* qT, float* scalesT)
 {
     if (mode != FGS_SCALE_TENSOR && mode != FGS_SCALE_TILE_1x128 && mode != FGS_SCALE_BLOCK_128x128)
         return fail(FGS_ERR_INVALID_ARG, "mode %d is not TENSOR, TILE_1x128 or BLOCK_128x128", mode);
     int st = check_bf16_source(x, rows, cols, ldx);
     if (st != FGS_OK) return st;
-    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
+    if (rows == 0 || cols == 0 || (!q && !qT)) return FGS_OK;
     if (q) {
         if (!scales) return fail(FGS_ERR_INVALID_ARG, "scales is NULL while q is given");
         if (cols % 128) return fail(FGS_ERR_UNSUPPORTED, "row-wise output needs cols %% 128 == 0 (cols = %lld)", (long long)cols);
@@ -126,12 +126,41 @@ int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ld
         if (rows % 128) return fail(FGS_ERR_UNSUPPORTED, "column-wise output needs rows %% 128 == 0 (rows = %lld)", (long long)rows);
         if (!aligned(qT, 16) || (scalesT && !aligned(scalesT, 4))) return fail(FGS_ERR_UNSUPPORTED, "qT must be 16-byte and scalesT 4-byte aligned");
     }
+    return FGS_OK;
+}
+
+int fgs_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                           uint8_t* q, float* scales, uint8_t* qT, float* scalesT,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_blockwise(x, rows, cols, ldx, mode, q, scales, qT, scalesT);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
     if (mode == FGS_SCALE_TENSOR) {
         if (!workspace || workspace_bytes < 4) return fail(FGS_ERR_INVALID_ARG, "TENSOR mode needs a workspace of >= 4 bytes");
         if (!aligned(workspace, 4)) return fail(FGS_ERR_UNSUPPORTED, "workspace must be 4-byte aligned");
     }
     fgs::QuantE4M3Args a{x, rows, cols, ldx, mode, q, scales, qT, scalesT, workspace, workspace_bytes};
     return hip_status(fgs::launch_quant_e4m3(a, static_cast<hipStream_t>(stream)), "quantize_blockwise launch");
+}
+
+int fgs_quantize_blockwise_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                                   uint8_t* q, float* scales, uint8_t* qT, float* scalesT, void* stream)
+{
+    int st = check_blockwise(x, rows, cols, ldx, mode, q, scales, qT, scalesT);
+    if (st != FGS_OK) return st;
+    if (rows == 0 || cols == 0 || (!q && !qT)) return ok();
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (mode == FGS_SCALE_TENSOR) {
+        // the library's own 4 KiB per device: the amax pass runs at most one
+        // workgroup per 4-byte slot, so every input size fits it
+        hipError_t e = fgs::quant_scratch(&ws, &ws_bytes);
+        if (e != hipSuccess) return hip_status(e, "quantize_blockwise_noalloc: scratch address");
+        if (ws_bytes < 4) return fail(FGS_ERR_UNSUPPORTED, "scratch of %zu bytes is below one amax slot", ws_bytes);
+    }
+    fgs::QuantE4M3Args a{x, rows, cols, ldx, mode, q, scales, qT, scalesT, ws, ws_bytes};
+    return hip_status(fgs::launch_quant_e4m3(a, static_cast<hipStream_t>(stream)), "quantize_blockwise_noalloc launch");
 }
 
 int fgs_quantize_delayed(const void* x, int64_t rows, int64_t cols, int64_t ldx, int elem,

@@ -23,6 +23,11 @@ struct QuantE4M3Args {
 };
 hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream);
 
+// The library's own device scratch for the per-tensor amax partials on the
+// current device (a fixed 4 KiB array per device, its address resolved once
+// per device): the workspace of fgs_quantize_blockwise_noalloc.
+hipError_t quant_scratch(void** ptr, size_t* bytes);
+
 // Per-group column-wise 1x128 quantization (plus the optional row-wise
 // output of the grouped rows), TILE mode only.
 struct QuantGroupedArgs {

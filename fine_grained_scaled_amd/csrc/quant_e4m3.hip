@@ -17,10 +17,21 @@
 // the block / tensor scale) and the column-wise codes (128x1 tiles along the
 // source rows, the wgrad operand, or the transposed block/tensor codes),
 // the latter transposed through LDS so every store is a full 128-byte row.
+#include <mutex>
+
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
 namespace fgs {
+
+// Scratch of the allocation-free per-tensor quantization
+// (fgs_quantize_blockwise_noalloc): the amax pass's per-workgroup partials,
+// one 4-byte slot per amax workgroup.  Every GPU the library runs on holds
+// its own copy until the process ends.  Host code never passes this name to
+// a kernel (on the host it is a stand-in, not a device address): the
+// per-device address comes from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = 4 * 1024;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
 
 namespace {
 
@@ -382,6 +393,29 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, resolved once per
+// device (with that device current) and kept.
+hipError_t quant_scratch(void** ptr, size_t* bytes)
+{
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static void* addr[kMaxDevices];
+    static hipError_t status[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
+        void* p = nullptr;
+        status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        addr[dev] = p;
+    });
+    if (status[dev] != hipSuccess) return status[dev];
+    *ptr = addr[dev];
+    *bytes = kScratchBytes;
+    return hipSuccess;
 }
 
 hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t stream)

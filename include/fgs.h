@@ -129,6 +129,28 @@ int fgs_quantize_blockwise(const void *x, int64_t rows, int64_t cols, int64_t ld
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fgs_quantize_blockwise_noalloc -- fgs_quantize_blockwise without a
+ *   workspace argument, for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid allocation).  It calls no allocator: TENSOR mode keeps its amax
+ *   partials in the library's own device scratch, a fixed 4 KiB array per
+ *   GPU (1024 four-byte slots) that each GPU holds until the process ends.
+ *   The amax pass runs at most one workgroup per slot whatever the input
+ *   size, so no input is too large for it.  The first call on a device
+ *   resolves that array's address on the device (a HIP call, after the
+ *   argument checks); a failure there returns FGS_ERR_HIP.
+ * Arguments, layouts, results, ownership and errors as fgs_quantize_blockwise
+ *   (the results are bit-identical).  Every slot a call reads is written by
+ *   the same call first, so nothing carried over from an earlier call
+ *   matters; but calls that overlap on one GPU (on different streams, or
+ *   from different threads) share the array and race: the caller orders
+ *   them.  TILE and BLOCK modes use no scratch.
+ */
+int fgs_quantize_blockwise_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int mode, uint8_t *q, float *scales,
+                                   uint8_t *qT, float *scalesT, void *stream);
+
+/*
  * fgs_quantize_delayed -- per-tensor DELAYED scaling to E4M3 or E5M2: the
  *   scale comes from the amaxes of earlier steps, the recipe that online
  *   scaling replaces, and E5M2 gives the hybrid recipe (E4M3 forward, E5M2
