@@ -18,7 +18,13 @@ weight blocks).  For every layer and recipe the step runs
   wgrad dW = dY^T X   (FP32 out)
 `value` is the step's GEMM FLOPs over its wall time (quantization
 included) in TFLOP/s.  Inputs are seeded synthetic BF16 tensors resident in
-HBM before timing starts.
+HBM before timing starts: every layer has its own X, W and dY, and four
+copies of that set (7 GB) sit at distinct addresses, step s reading copy
+s mod 4, so no step finds its inputs in the 256 MB last-level cache (MALL)
+from the step before.  The line reports the median, p10 and p90 step time,
+the rate of every GEMM kernel instantiation (named as profilers print it)
+with the dominant one as the roofline, and the quantizers against the HBM
+peak and against the read and copy rates of in-tree streaming kernels.
 
 The other workloads of the path are measured in the same run and reported
 under "workloads" (per-kernel throughput against the roofline): the tiny
@@ -60,6 +66,8 @@ COUNTER_PROFILE = os.path.join("profiles", "counters_llama3_8b_linears.md")
 GEMM_SOURCES = [os.path.join("fine_grained_scaled_amd", "csrc", f)
                 for f in ("gemm_block_scaled.hip", "fgs_device.h", "fgs_internal.h")]
 CALIBRATION_BYTES = 1 << 30
+HBM_LIB = os.path.join(ROOT, "fine_grained_scaled_amd", "libfgs_hbm.so")
+INPUT_SETS = 4
 
 LLAMA8B_M = 8192
 LLAMA8B_LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672), ("down", 14336, 4096)]
@@ -111,14 +119,21 @@ def nvfp4_bytes(rows, cols, outputs):
 # (the stream the library launches on)
 # --------------------------------------------------------------------------
 class Timer:
+    """HIP events around each launch on torch's current stream (the stream
+    the library launches on).  kname: a callable naming the kernel
+    instantiation a GEMM launch runs (asked once per label)."""
+
     def __init__(self, torch, enabled=True):
         self.torch = torch
         self.enabled = enabled
         self.rec = []
+        self.names = {}
 
-    def run(self, kind, label, units, fn):
+    def run(self, kind, label, units, fn, kname=None):
         if not self.enabled:
             return fn()
+        if kname is not None and label not in self.names:
+            self.names[label] = kname()
         e0 = self.torch.cuda.Event(enable_timing=True)
         e1 = self.torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -127,15 +142,26 @@ class Timer:
         self.rec.append((kind, label, units, e0, e1))
         return r
 
+    def times(self):
+        """[(kind, label, units, seconds, kernel name or None)]"""
+        return [(k, lab, u, e0.elapsed_time(e1) * 1e-3, self.names.get(lab)) for k, lab, u, e0, e1 in self.rec]
+
     def summary(self):
         kinds, labels = {}, {}
-        for kind, label, units, e0, e1 in self.rec:
-            t = e0.elapsed_time(e1) * 1e-3
+        for kind, label, units, t, _ in self.times():
             u, s, n = kinds.get(kind, (0.0, 0.0, 0))
             kinds[kind] = (u + units, s + t, n + 1)
             u, s, n = labels.get((kind, label), (0.0, 0.0, 0))
             labels[(kind, label)] = (u + units, s + t, n + 1)
         return kinds, labels
+
+
+def dense_gemm(tm, fgs, label, A, B, dt, out, fp8_mma=False):
+    """One timed dense GEMM launch, recorded with its FLOPs and the name of
+    the kernel instantiation it runs."""
+    f = 2.0 * A.data.shape[0] * B.data.shape[0] * A.data.shape[1] * (2 if A.elem == fgs.ELEM_E2M1 else 1)
+    return tm.run("gemm", label, f, lambda: fgs.gemm_block_scaled(A, B, dt, out=out, fp8_mma=fp8_mma),
+                  kname=lambda: fgs.gemm_kernel_name(A, B, dt, fp8_mma=fp8_mma))
 
 
 def gpu_normal(torch, shape, seed, sigma=1.0, outlier_cols=None):
@@ -165,39 +191,60 @@ class Llama8B:
     name = "llama3_8b_linears"
     fp8_mma = False
 
-    def __init__(self, torch, fgs, synth):
+    def __init__(self, torch, fgs, synth, sets=INPUT_SETS):
         self.torch, self.fgs = torch, fgs
         t0 = time.time()
-        self.x, self.w, self.dy, self.out = {}, {}, {}, {}
+        self.out = {}
+        base = {}
         for i, (name, K, N) in enumerate(LLAMA8B_LAYERS):
-            if K not in self.x:
-                self.x[K] = synth.to_torch_bf16(synth.activations(LLAMA8B_M, K, seed=0)).cuda()
-            self.w[name] = synth.to_torch_bf16(synth.weights(N, K, seed=0, tag=synth.TAG_W + 16 * (1 + i))).cuda()
-            if N not in self.dy:
-                self.dy[N] = synth.to_torch_bf16(synth.gradients(LLAMA8B_M, N, seed=0)).cuda()
+            # every layer its own seeded X, W and dY (tags per layer)
+            x = synth.activations(LLAMA8B_M, K, seed=0, tag=synth.TAG_A + 16 * (1 + i))
+            w = synth.weights(N, K, seed=0, tag=synth.TAG_W + 16 * (1 + i))
+            dy = synth.gradients(LLAMA8B_M, N, seed=0, tag=synth.TAG_DY + 16 * (1 + i))
+            base[name] = tuple(synth.to_torch_bf16(v).cuda() for v in (x, w, dy))
             for rname, _, _ in RECIPES:
                 self.out[(rname, name, "y")] = torch.empty((LLAMA8B_M, N), dtype=torch.bfloat16, device="cuda")
                 self.out[(rname, name, "dx")] = torch.empty((LLAMA8B_M, K), dtype=torch.bfloat16, device="cuda")
                 self.out[(rname, name, "dw")] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        # copies of the input set at distinct addresses, read in rotation
+        self.sets = [base] + [{n: tuple(t.clone() for t in v) for n, v in base.items()} for _ in range(sets - 1)]
+        self.step_no = 0
         torch.cuda.synchronize()
-        log(f"[bench] {self.name}: inputs generated and uploaded in {time.time() - t0:.1f} s")
+        nbytes = sum(t.numel() * t.element_size() for st in self.sets for v in st.values() for t in v)
+        log(f"[bench] {self.name}: inputs generated and uploaded in {time.time() - t0:.1f} s "
+            f"({len(self.sets)} input sets, {nbytes / 2**30:.2f} GiB)")
+
+    def input_bytes(self):
+        return sum(t.numel() * t.element_size() for st in self.sets for v in st.values() for t in v)
 
     def flops(self):
         return len(RECIPES) * sum(3 * 2.0 * LLAMA8B_M * N * K for _, K, N in LLAMA8B_LAYERS)
 
-    def gemm_bytes(self):
-        """Algorithmic HBM bytes of the step's GEMMs: every operand code, scale
-        and output element once."""
-        tot = 0.0
-        for _, amode, wmode in RECIPES:
-            for _, K, N in LLAMA8B_LAYERS:
+    def gemm_launches(self):
+        """(label, M, N, K, A scale mode, B scale mode, out dtype) of every GEMM
+        launch of one step: fwd X W^T, dgrad dY W, wgrad dY^T X."""
+        torch = self.torch
+        out = []
+        for rname, amode, wmode in RECIPES:
+            for name, K, N in LLAMA8B_LAYERS:
                 M = LLAMA8B_M
-                sc = lambda r, c, mode: 4.0 * (r * c / 128 if mode == "tile" else
-                                               r * c / 16384 if mode == "block" else 1)
-                tot += M * K + N * K + sc(M, K, amode) + sc(N, K, wmode) + 2.0 * M * N      # fwd
-                tot += M * N + N * K + sc(M, N, amode) + sc(N, K, wmode) + 2.0 * M * K      # dgrad
-                tot += M * N + M * K + sc(M, N, amode) + sc(M, K, amode) + 4.0 * N * K      # wgrad
-        return tot
+                out.append((f"{rname}/{name}/fwd", M, N, K, amode, wmode, torch.bfloat16))
+                out.append((f"{rname}/{name}/dgrad", M, K, N, amode, wmode, torch.bfloat16))
+                out.append((f"{rname}/{name}/wgrad", N, K, M, amode, amode, torch.float32))
+        return out
+
+    @staticmethod
+    def gemm_bytes_one(M, N, K, amode, bmode, out_bytes):
+        """Algorithmic HBM bytes of one GEMM launch: operand codes and scales
+        once, the output once."""
+        sc = lambda r, c, mode: 4.0 * (r * c / 128 if mode == "tile" else
+                                       r * c / 16384 if mode == "block" else 1)
+        return M * K + N * K + sc(M, K, amode) + sc(N, K, bmode) + out_bytes * M * N
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of the step's GEMMs."""
+        return sum(self.gemm_bytes_one(M, N, K, am, bm, 2 if dt == self.torch.bfloat16 else 4)
+                   for _, M, N, K, am, bm, dt in self.gemm_launches())
 
     def gemm_only(self, steps):
         """Quantize once, then run only the step's GEMM launches `steps` times."""
@@ -205,9 +252,10 @@ class Llama8B:
         ops = []
         for rname, amode, wmode in RECIPES:
             for name, K, N in LLAMA8B_LAYERS:
-                qx = fgs.quantize_blockwise(self.x[K], amode, rowwise=True, colwise=True)
-                qw = fgs.quantize_blockwise(self.w[name], wmode, rowwise=True, colwise=True)
-                qdy = fgs.quantize_blockwise(self.dy[N], amode, rowwise=True, colwise=True)
+                X, W, dY = self.sets[0][name]
+                qx = fgs.quantize_blockwise(X, amode, rowwise=True, colwise=True)
+                qw = fgs.quantize_blockwise(W, wmode, rowwise=True, colwise=True)
+                qdy = fgs.quantize_blockwise(dY, amode, rowwise=True, colwise=True)
                 o = self.out
                 ops.append((qx.rowwise(), qw.rowwise(), torch.bfloat16, o[(rname, name, "y")]))
                 ops.append((qdy.rowwise(), qw.colwise(), torch.bfloat16, o[(rname, name, "dx")]))
@@ -222,11 +270,16 @@ class Llama8B:
         log(f"[bench] GEMM launches only: {dt / steps * 1e3:.2f} ms per step, "
             f"{self.flops() / (dt / steps) / 1e12:.1f} TFLOP/s")
 
+    def gemm(self, tm, label, A, B, dt, out):
+        dense_gemm(tm, self.fgs, label, A, B, dt, out, self.fp8_mma)
+
     def step(self, tm):
         torch, fgs = self.torch, self.fgs
+        inputs = self.sets[self.step_no % len(self.sets)]
+        self.step_no += 1
         for rname, amode, wmode in RECIPES:
             for name, K, N in LLAMA8B_LAYERS:
-                X, W, dY = self.x[K], self.w[name], self.dy[N]
+                X, W, dY = inputs[name]
                 lab = f"{rname}/{name}"
                 qx = tm.run("quant", lab + "/X", e4m3_bytes(LLAMA8B_M, K, amode),
                             lambda: fgs.quantize_blockwise(X, amode, rowwise=True, colwise=True))
@@ -234,15 +287,10 @@ class Llama8B:
                             lambda: fgs.quantize_blockwise(W, wmode, rowwise=True, colwise=True))
                 qdy = tm.run("quant", lab + "/dY", e4m3_bytes(LLAMA8B_M, N, amode),
                              lambda: fgs.quantize_blockwise(dY, amode, rowwise=True, colwise=True))
-                f = 2.0 * LLAMA8B_M * N * K
                 o = self.out
-                mma = self.fp8_mma
-                tm.run("gemm", lab + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                    qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(rname, name, "y")], fp8_mma=mma))
-                tm.run("gemm", lab + "/dgrad", f, lambda: fgs.gemm_block_scaled(
-                    qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(rname, name, "dx")], fp8_mma=mma))
-                tm.run("gemm", lab + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                    qdy.colwise(), qx.colwise(), torch.float32, out=o[(rname, name, "dw")], fp8_mma=mma))
+                self.gemm(tm, lab + "/fwd", qx.rowwise(), qw.rowwise(), torch.bfloat16, o[(rname, name, "y")])
+                self.gemm(tm, lab + "/dgrad", qdy.rowwise(), qw.colwise(), torch.bfloat16, o[(rname, name, "dx")])
+                self.gemm(tm, lab + "/wgrad", qdy.colwise(), qx.colwise(), torch.float32, o[(rname, name, "dw")])
 
 
 class Llama8BFp8Mma(Llama8B):
@@ -266,11 +314,10 @@ class Hybrid8B:
         self.torch, self.fgs = torch, fgs
         self.x, self.w, self.dy, self.out, self.hist = {}, {}, {}, {}, {}
         for i, (name, K, N) in enumerate(LLAMA8B_LAYERS):
-            if K not in self.x:
-                self.x[K] = gpu_normal(torch, (LLAMA8B_M, K), 300 + i, outlier_cols=synth.outlier_channels(K, 0))
+            # every layer its own X, W and dY
+            self.x[name] = gpu_normal(torch, (LLAMA8B_M, K), 300 + i, outlier_cols=synth.outlier_channels(K, 0))
             self.w[name] = gpu_normal(torch, (N, K), 310 + i, sigma=0.02)
-            if N not in self.dy:
-                self.dy[N] = gpu_t3(torch, (LLAMA8B_M, N), 320 + i)
+            self.dy[name] = gpu_t3(torch, (LLAMA8B_M, N), 320 + i)
             for role in ("x", "w", "dy"):
                 self.hist[(name, role)] = torch.zeros(self.HISTORY, dtype=torch.float32, device="cuda")
             self.out[(name, "y")] = torch.empty((LLAMA8B_M, N), dtype=torch.bfloat16, device="cuda")
@@ -287,20 +334,16 @@ class Hybrid8B:
         slot = self.step_no % self.HISTORY
         self.step_no += 1
         for name, K, N in LLAMA8B_LAYERS:
-            X, W, dY, h, o = self.x[K], self.w[name], self.dy[N], self.hist, self.out
+            X, W, dY, h, o = self.x[name], self.w[name], self.dy[name], self.hist, self.out
             qx = tm.run("quant", name + "/X", 4.0 * LLAMA8B_M * K, lambda: fgs.quantize_delayed(
                 X, h[(name, "x")], slot, "e4m3", rowwise=True, colwise=True))
             qw = tm.run("quant", name + "/W", 4.0 * N * K, lambda: fgs.quantize_delayed(
                 W, h[(name, "w")], slot, "e4m3", rowwise=True, colwise=True))
             qdy = tm.run("quant", name + "/dY", 4.0 * LLAMA8B_M * N, lambda: fgs.quantize_delayed(
                 dY, h[(name, "dy")], slot, "e5m2", rowwise=True, colwise=True))
-            f = 2.0 * LLAMA8B_M * N * K
-            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=o[(name, "y")]))
-            tm.run("gemm", name + "/dgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.rowwise(), qw.colwise(), torch.bfloat16, out=o[(name, "dx")]))
-            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.colwise(), qx.colwise(), torch.float32, out=o[(name, "dw")]))
+            dense_gemm(tm, fgs, name + "/fwd", qx.rowwise(), qw.rowwise(), torch.bfloat16, o[(name, "y")])
+            dense_gemm(tm, fgs, name + "/dgrad", qdy.rowwise(), qw.colwise(), torch.bfloat16, o[(name, "dx")])
+            dense_gemm(tm, fgs, name + "/wgrad", qdy.colwise(), qx.colwise(), torch.float32, o[(name, "dw")])
 
 
 # --------------------------------------------------------------------------
@@ -322,8 +365,7 @@ class Tiny:
         fgs = self.fgs
         qa = tm.run("quant", "A", e4m3_bytes(128, 256, "tile", 1), lambda: fgs.quantize_blockwise(self.a, "tile"))
         qb = tm.run("quant", "B", e4m3_bytes(256, 256, "block", 1), lambda: fgs.quantize_blockwise(self.b, "block"))
-        tm.run("gemm", "fwd", self.flops(), lambda: fgs.gemm_block_scaled(
-            qa.rowwise(), qb.rowwise(), self.torch.float32, out=self.c))
+        dense_gemm(tm, fgs, "fwd", qa.rowwise(), qb.rowwise(), self.torch.float32, self.c)
 
 
 # --------------------------------------------------------------------------
@@ -478,8 +520,7 @@ class MX405B:
         t0 = time.time()
         self.x, self.w, self.dy, self.out = {}, {}, {}, {}
         for i, (name, K, N) in enumerate(MX_LAYERS):
-            if K not in self.x:
-                self.x[K] = gpu_normal(torch, (MX_M, K), 200 + i)
+            self.x[name] = gpu_normal(torch, (MX_M, K), 200 + i)      # every layer its own X
             self.w[name] = gpu_normal(torch, (N, K), 210 + i, sigma=0.02)
             self.dy[name] = gpu_normal(torch, (MX_M, N), 220 + i)
             self.out[(name, "y")] = torch.empty((MX_M, N), dtype=torch.bfloat16, device="cuda")
@@ -493,17 +534,14 @@ class MX405B:
     def step(self, tm):
         torch, fgs = self.torch, self.fgs
         for name, K, N in MX_LAYERS:
-            X, W, dY = self.x[K], self.w[name], self.dy[name]
+            X, W, dY = self.x[name], self.w[name], self.dy[name]
             qx = tm.run("quant", name + "/X", mx_bytes(MX_M, K, 2), lambda: fgs.quantize_mx(X, rowwise=True, colwise=True))
             qw = tm.run("quant", name + "/W", mx_bytes(N, K, 1), lambda: fgs.quantize_mx(W))
             qdy = tm.run("quant", name + "/dY", mx_bytes(MX_M, N, 1),
                          lambda: fgs.quantize_mx(dY, rowwise=False, colwise=True))
-            f = 2.0 * MX_M * N * K
             mma = self.fp8_mma
-            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")], fp8_mma=mma))
-            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")], fp8_mma=mma))
+            dense_gemm(tm, fgs, name + "/fwd", qx.rowwise(), qw.rowwise(), torch.bfloat16, self.out[(name, "y")], mma)
+            dense_gemm(tm, fgs, name + "/wgrad", qdy.colwise(), qx.colwise(), torch.float32, self.out[(name, "dw")], mma)
 
 
 class MX405BFp8Mma(MX405B):
@@ -549,13 +587,9 @@ class NV12B:
             qdy = tm.run("quant", name + "/dY", nvfp4_bytes(NV_M, N, 2), lambda: fgs.quantize_nvfp4(
                 dY, rowwise=True, colwise=True, rht_mask=2, rht_seed=self.rht_seed,
                 stochastic=True, sr_seed=self.sr_seed))
-            f = 2.0 * NV_M * N * K
-            tm.run("gemm", name + "/fwd", f, lambda: fgs.gemm_block_scaled(
-                qx.rowwise(), qw.rowwise(), torch.bfloat16, out=self.out[(name, "y")]))
-            tm.run("gemm", name + "/dgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.rowwise(), qw.colwise(), torch.bfloat16, out=self.out[(name, "dx")]))
-            tm.run("gemm", name + "/wgrad", f, lambda: fgs.gemm_block_scaled(
-                qdy.colwise(), qx.colwise(), torch.float32, out=self.out[(name, "dw")]))
+            dense_gemm(tm, fgs, name + "/fwd", qx.rowwise(), qw.rowwise(), torch.bfloat16, self.out[(name, "y")])
+            dense_gemm(tm, fgs, name + "/dgrad", qdy.rowwise(), qw.colwise(), torch.bfloat16, self.out[(name, "dx")])
+            dense_gemm(tm, fgs, name + "/wgrad", qdy.colwise(), qx.colwise(), torch.float32, self.out[(name, "dw")])
 
 
 WORKLOADS = {"llama3_8b": Llama8B, "hybrid8b": Hybrid8B, "tiny": Tiny, "moe": MoE, "mx405b": MX405B,
@@ -564,20 +598,34 @@ WORKLOADS = {"llama3_8b": Llama8B, "hybrid8b": Hybrid8B, "tiny": Tiny, "moe": Mo
 
 
 def measure(torch, wl, steps, warmup):
+    """W untimed warm-up steps, then exactly `steps` timed steps between two
+    device synchronisations; an event at every step boundary gives the
+    per-step times."""
     for _ in range(warmup):
         wl.step(Timer(torch, enabled=False))
     torch.cuda.synchronize()
     tm = Timer(torch)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    marks[0].record()
+    for i in range(steps):
         wl.step(tm)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_s = [marks[i].elapsed_time(marks[i + 1]) * 1e-3 for i in range(steps)]
     kinds, labels = tm.summary()
     for (kind, label), (u, t, n) in labels.items():
         rate = f"{u / t / 1e12:8.1f} TFLOP/s" if kind == "gemm" else f"{u / t / 1e9:8.1f} GB/s"
-        log(f"  {wl.name:28s} {label:24s} {t / n * 1e6:9.1f} us  {rate}")
-    return wall, kinds, labels
+        log(f"  {wl.name:28s} {label:24s} {t / n * 1e6:9.1f} us  {rate}  {tm.names.get(label, '')}")
+    return wall, kinds, labels, step_s, tm
+
+
+def step_stats(step_s):
+    import numpy as np
+    v = np.asarray(step_s) * 1e3
+    return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4), "mean": round(float(v.mean()), 4), "n": int(v.size)}
 
 
 def kind_report(kinds, steps):
@@ -592,6 +640,111 @@ def kind_report(kinds, steps):
         out["quant"] = {"GB/s": round(b / t / 1e9, 1), "frac_hbm_peak": round(b / t / 1e9 / PEAK_HBM, 4),
                         "ms_per_step": round(t / steps * 1e3, 4)}
     return out
+
+
+def instantiation_report(tm, steps):
+    """Every GEMM kernel instantiation of a workload: launches per step, FLOPs
+    per launch, average and median launch time, rate and its fraction of the
+    matrix peak its instructions run at (FP8 for the FP8-instruction path, else
+    FP16), and its share of the workload's GEMM time; sorted by share."""
+    import numpy as np
+    groups = {}
+    for kind, label, units, t, name in tm.times():
+        if kind != "gemm":
+            continue
+        g = groups.setdefault(name or label, {"flop": 0.0, "t": [], "labels": []})
+        g["flop"] += units
+        g["t"].append(t)
+        if label not in g["labels"]:
+            g["labels"].append(label)
+    total = sum(sum(g["t"]) for g in groups.values()) or 1.0
+    rows = []
+    for name, g in groups.items():
+        n, tt = len(g["t"]), sum(g["t"])
+        rate = g["flop"] / tt / 1e12
+        peak = PEAK_FP8_MFMA if name.endswith("true>") else PEAK_FP16_MFMA
+        rows.append({"kernel": name, "launches_per_step": round(n / steps, 3),
+                     "flop_per_launch": round(g["flop"] / n), "avg_us": round(tt / n * 1e6, 2),
+                     "median_us": round(float(np.median(g["t"])) * 1e6, 2), "TFLOP/s": round(rate, 2),
+                     "peak": peak, "frac_peak": round(rate / peak, 4), "share_of_gemm_time": round(tt / total, 4),
+                     "launches": g["labels"]})
+    rows.sort(key=lambda r: -r["share_of_gemm_time"])
+    return rows
+
+
+def quant_report(tm, steps, ceilings):
+    """Quantizer rates per role (recipe / tensor, over the layers) and in
+    total, against the HBM peak and the measured streaming ceilings."""
+    groups = {}
+    for kind, label, units, t, _ in tm.times():
+        if kind != "quant":
+            continue
+        parts = label.split("/")
+        key = "/".join([parts[0], parts[-1]]) if len(parts) > 2 else label
+        b, tt = groups.get(key, (0.0, 0.0))
+        groups[key] = (b + units, tt + t)
+    out = {}
+    for key, (b, tt) in sorted(groups.items()):
+        r = b / tt / 1e9
+        e = {"GB/s": round(r, 1), "frac_hbm_peak": round(r / PEAK_HBM, 4), "ms_per_step": round(tt / steps * 1e3, 4)}
+        if ceilings:
+            e["frac_copy_ceiling"] = round(r / ceilings["copy_GB/s"], 4)
+            e["frac_read_ceiling"] = round(r / ceilings["read_GB/s"], 4)
+        out[key] = e
+    return out
+
+
+def hbm_ceilings(torch, nbytes=1 << 30, reps=8):
+    """What HBM sustains for this chip, measured by the in-tree streaming
+    kernels (libfgs_hbm.so): a 1 GiB read reduced to one word per workgroup,
+    and a 1 GiB copy (read + write bytes counted); each the best over the
+    kernel variants (unroll depth, non-temporal access) and 1, 2, 4 or 8
+    workgroups per compute unit, median of `reps` launches."""
+    import ctypes
+    import numpy as np
+    if not os.path.exists(HBM_LIB):
+        return None
+    lib = ctypes.CDLL(HBM_LIB)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.fgs_hbm_read_grid.argtypes = [I32]
+    lib.fgs_hbm_read.argtypes = [P, I64, P, I32, I32, P]
+    lib.fgs_hbm_copy.argtypes = [P, P, I64, I32, I32, P]
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = {}
+    for per_cu in (1, 2, 4, 8):
+        out = torch.empty(lib.fgs_hbm_read_grid(per_cu), dtype=torch.int32, device="cuda")
+        for variant in range(lib.fgs_hbm_variants()):
+            for kind in ("read", "copy"):
+                ts = []
+                for r in range(reps + 2):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    if kind == "read":
+                        rc = lib.fgs_hbm_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                              per_cu, variant, stream)
+                    else:
+                        rc = lib.fgs_hbm_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                              nbytes, per_cu, variant, stream)
+                    e1.record()
+                    if rc != 0:
+                        raise RuntimeError(f"streaming kernel returned {rc}")
+                    torch.cuda.synchronize()
+                    if r >= 2:
+                        ts.append(e0.elapsed_time(e1) * 1e-3)
+                moved = nbytes * (1 if kind == "read" else 2)
+                rate = moved / float(np.median(ts)) / 1e9
+                if rate > best.get(kind, (0.0,))[0]:
+                    best[kind] = (rate, per_cu, variant)
+    del src, dst
+    return {"read_GB/s": round(best["read"][0], 1), "read_config": {"workgroups_per_cu": best["read"][1],
+                                                                    "variant": best["read"][2]},
+            "copy_GB/s": round(best["copy"][0], 1), "copy_config": {"workgroups_per_cu": best["copy"][1],
+                                                                    "variant": best["copy"][2]},
+            "bytes": nbytes, "frac_hbm_peak_read": round(best["read"][0] / PEAK_HBM, 4),
+            "frac_hbm_peak_copy": round(best["copy"][0] / PEAK_HBM, 4)}
 
 
 # --------------------------------------------------------------------------
@@ -627,8 +780,9 @@ def _counter_rows(d, counter):
 
 
 def write_counter_profile(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command):
-    """Summarise FETCH_SIZE / WRITE_SIZE runs of one headline step (and of the
-    1 GiB copy that calibrates both counters) into COUNTER_PROFILE."""
+    """Summarise FETCH_SIZE / WRITE_SIZE runs of the headline step (and of the
+    1 GiB copy that calibrates both counters) into COUNTER_PROFILE, per kernel
+    instantiation."""
     fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
     cf, cw = _counter_rows(cal_fetch_dir, "FETCH_SIZE"), _counter_rows(cal_write_dir, "WRITE_SIZE")
     copy = [k for k in cf if "copyBuffer" in k]
@@ -639,27 +793,20 @@ def write_counter_profile(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, co
     f_write = kib / (sum(cw[copy[0]]) / len(cw[copy[0]]))
     lines = ["| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (calibrated) |",
              "|---|---:|---:|---:|---:|"]
-    g_n, g_bytes, g_fetch, g_write = 0, 0.0, 0.0, 0.0
+    kernels = {}
     for k in sorted(fetch):
         fv, wv = fetch[k], write.get(k, [])
         if len(fv) != len(wv):
             raise SystemExit(f"dispatch counts differ for {k}: {len(fv)} vs {len(wv)}")
         af, aw = sum(fv) / len(fv), sum(wv) / len(wv)
-        by = 1024.0 * (af * f_fetch + aw * f_write)
-        lines.append(f"| `{k}` | {len(fv)} | {af:.1f} | {aw:.1f} | {by / 1e6:.2f} MB |")
-        if k.startswith("gemm_block_scaled_kernel"):
-            g_n += len(fv)
-            g_fetch += 1024.0 * f_fetch * sum(fv)
-            g_write += 1024.0 * f_write * sum(wv)
-    if g_n == 0:
+        fb, wb = 1024.0 * af * f_fetch, 1024.0 * aw * f_write
+        lines.append(f"| `{k}` | {len(fv)} | {af:.1f} | {aw:.1f} | {(fb + wb) / 1e6:.2f} MB |")
+        kernels[k] = {"dispatches": len(fv), "fetch_bytes_per_dispatch": round(fb), "write_bytes_per_dispatch": round(wb),
+                      "traffic_bytes_per_dispatch": round(fb + wb)}
+    if not any(k.startswith("gemm_block_scaled_kernel") for k in kernels):
         raise SystemExit("no gemm_block_scaled_kernel dispatches in the counter runs")
-    launches_per_step = 3 * len(LLAMA8B_LAYERS) * len(RECIPES)
-    alg = Llama8B.gemm_bytes(None) / launches_per_step
-    summary = {"source_digest": gemm_source_digest(), "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
-               "gemm_launches": g_n, "gemm_fetch_bytes_per_launch": round(g_fetch / g_n),
-               "gemm_write_bytes_per_launch": round(g_write / g_n),
-               "gemm_traffic_bytes_per_launch": round((g_fetch + g_write) / g_n),
-               "gemm_algorithmic_bytes_per_launch": round(alg)}
+    summary = {"source_digest": gemm_source_digest(), "fetch_factor": round(f_fetch, 4),
+               "write_factor": round(f_write, 4), "kernels": kernels}
     text = [
         "# HBM traffic of the headline step's kernels (rocprofv3 counters)",
         "",
@@ -675,13 +822,8 @@ def write_counter_profile(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, co
         "",
         *lines,
         "",
-        f"GEMM kernel, average over its {g_n} dispatches (one step: {launches_per_step} launches): "
-        f"{summary['gemm_traffic_bytes_per_launch'] / 1e6:.1f} MB of HBM traffic per launch against "
-        f"{alg / 1e6:.1f} MB algorithmic (operand codes, scales and output once), ratio "
-        f"{summary['gemm_traffic_bytes_per_launch'] / alg:.2f}.",
-        "",
         "Machine-readable summary (read by bench.py; `source_digest` is the SHA-256 prefix of the GEMM kernel's "
-        "sources when the counters were taken):",
+        "sources when the counters were taken, and bench.py reports traffic only while they still match):",
         "",
         "```json",
         json.dumps(summary),
@@ -690,12 +832,13 @@ def write_counter_profile(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, co
     ]
     with open(os.path.join(ROOT, COUNTER_PROFILE), "w") as f:
         f.write("\n".join(text))
-    log(f"[bench] wrote {COUNTER_PROFILE}: {summary}")
+    log(f"[bench] wrote {COUNTER_PROFILE}")
 
 
-def read_gemm_traffic():
-    """HBM bytes per GEMM launch from COUNTER_PROFILE, or None when the file
-    is missing or the kernel's sources changed since the counters were taken."""
+def read_kernel_traffic(kernel):
+    """HBM bytes per dispatch of one kernel instantiation from
+    COUNTER_PROFILE, or None when the file is missing, holds no such kernel,
+    or the GEMM kernel's sources changed since the counters were taken."""
     try:
         with open(os.path.join(ROOT, COUNTER_PROFILE)) as f:
             text = f.read()
@@ -705,7 +848,7 @@ def read_gemm_traffic():
         return None
     if summary.get("source_digest") != gemm_source_digest():
         return None
-    return summary
+    return summary.get("kernels", {}).get(kernel)
 
 
 def gpu_clocks():
@@ -729,39 +872,98 @@ def gpu_clocks():
     return None
 
 
-def cpu_baseline():
-    """The oracle, untuned, on a bounded sample of the headline workload: the
-    QKV layer (K = 4096, N = 6144) with M cut to 1024 tokens, both recipes:
-    oracle quantization of X, W, dY (row-wise and column-wise) and the three
-    FP64 GEMMs.  Reported in the metric's unit (GEMM TFLOP/s of the sample)."""
-    import oracle
-    from fine_grained_scaled_amd import synth
+def _cpu_info():
+    model = None
     try:
-        from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas = 1
-    K, N, Ms = 4096, 6144, 1024
-    x = synth.activations(LLAMA8B_M, K, seed=0, row_range=(0, Ms))
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def _host_threads():
+    """The host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS where that is set (the GPU machine's CPU share)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        n = min(n, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        pass
+    return max(1, n)
+
+
+def _oracle_quant(pool, bits, mode, colwise, chunks):
+    """The oracle's FP32-scaled E4M3 quantization of `bits`, split into
+    128-row chunks run in parallel (bit-identical to one call: 1x128 tiles,
+    128x128 blocks and the column-wise 128x1 tiles never cross a 128-row
+    boundary; per-tensor scaling takes the tensor amax first, then quantizes
+    each chunk with that amax as its only history entry, which is the same
+    scale)."""
+    import numpy as np
+    import oracle
+    rows = bits.shape[0]
+    step = max(128, -(-rows // chunks) // 128 * 128)
+    bounds = [(r, min(rows, r + step)) for r in range(0, rows, step)]
+    axis = 1 if colwise else 0
+    if mode == "tensor":
+        am = max(pool.map(lambda b: int(np.max(bits[b[0]:b[1]] & 0x7FFF)), bounds))
+        hist = np.array([am << 16], dtype=np.uint32).view(np.float32)
+        parts = list(pool.map(lambda b: oracle.quant_delayed(bits[b[0]:b[1]], "e4m3", hist, colwise=colwise), bounds))
+        return np.concatenate([p[0] for p in parts], axis=axis), np.array([[parts[0][1]]], dtype=np.float32)
+    parts = list(pool.map(lambda b: oracle.quant_e4m3(bits[b[0]:b[1]], mode, colwise=colwise), bounds))
+    return np.concatenate([p[0] for p in parts], axis=axis), np.concatenate([p[1] for p in parts], axis=axis)
+
+
+def _oracle_sample(x, w, dy, threads):
+    """One pass of the oracle over the sample: X, W, dY quantized row- and
+    column-wise in both recipes, dequantized, and the three FP64 products."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with ThreadPoolExecutor(max_workers=threads) as pool, threadpool_limits(threads):
+        for _, amode, wmode in RECIPES:
+            qx, sx = _oracle_quant(pool, x, amode, False, threads)
+            qxt, sxt = _oracle_quant(pool, x, amode, True, threads)
+            qw, sw = _oracle_quant(pool, w, wmode, False, threads)
+            qwt, swt = _oracle_quant(pool, w, wmode, True, threads)
+            qd, sd = _oracle_quant(pool, dy, amode, False, threads)
+            qdt, sdt = _oracle_quant(pool, dy, amode, True, threads)
+            oracle.gemm_ref(oracle.dequant_e4m3(qx, sx, amode), oracle.dequant_e4m3(qw, sw, wmode))
+            oracle.gemm_ref(oracle.dequant_e4m3(qd, sd, amode), oracle.dequant_e4m3(qwt, swt, wmode))
+            oracle.gemm_ref(oracle.dequant_e4m3(qdt, sdt, amode), oracle.dequant_e4m3(qxt, sxt, amode))
+
+
+def cpu_baseline(tokens=512):
+    """The oracle, untuned, on a bounded sample of the headline workload: the
+    QKV layer (K = 4096, N = 6144) with M cut to `tokens` tokens, both
+    recipes: oracle quantization of X, W, dY (row-wise and column-wise,
+    plain C, run in 128-row chunks on every host thread) and the three FP64
+    numpy GEMMs (BLAS on every host thread); then the same on one thread.
+    Reported in the metric's unit (GEMM TFLOP/s of the sample)."""
+    from fine_grained_scaled_amd import synth
+    K, N = 4096, 6144
+    x = synth.activations(LLAMA8B_M, K, seed=0, tag=synth.TAG_A + 16, row_range=(0, tokens))
     w = synth.weights(N, K, seed=0, tag=synth.TAG_W + 16)
-    dy = synth.gradients(LLAMA8B_M, N, seed=0, row_range=(0, Ms))
+    dy = synth.gradients(LLAMA8B_M, N, seed=0, tag=synth.TAG_DY + 16, row_range=(0, tokens))
+    flops = len(RECIPES) * 3 * 2.0 * tokens * N * K
+    threads = _host_threads()
     t0 = time.perf_counter()
-    for _, amode, wmode in RECIPES:
-        qx, sx = oracle.quant_e4m3(x, amode)
-        qxt, sxt = oracle.quant_e4m3(x, amode, colwise=True)
-        qw, sw = oracle.quant_e4m3(w, wmode)
-        qwt, swt = oracle.quant_e4m3(w, wmode, colwise=True)
-        qd, sd = oracle.quant_e4m3(dy, amode)
-        qdt, sdt = oracle.quant_e4m3(dy, amode, colwise=True)
-        oracle.gemm_ref(oracle.dequant_e4m3(qx, sx, amode), oracle.dequant_e4m3(qw, sw, wmode))
-        oracle.gemm_ref(oracle.dequant_e4m3(qd, sd, amode), oracle.dequant_e4m3(qwt, swt, wmode))
-        oracle.gemm_ref(oracle.dequant_e4m3(qdt, sdt, amode), oracle.dequant_e4m3(qxt, sxt, amode))
+    _oracle_sample(x, w, dy, threads)
     dt = time.perf_counter() - t0
-    flops = len(RECIPES) * 3 * 2.0 * Ms * N * K
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
-            "sample": (f"QKV layer (K=4096, N=6144) with M={Ms} of 8192 tokens, both recipes: oracle quantization "
-                       f"(single-threaded C) of X, W, dY row- and column-wise + 3 FP64 numpy GEMMs "
-                       f"({blas} BLAS threads); {dt:.1f} s wall")}
+    t0 = time.perf_counter()
+    _oracle_sample(x, w, dy, 1)
+    dt1 = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"QKV layer (K=4096, N=6144) with M={tokens} of 8192 tokens, both recipes: oracle "
+                       f"quantization (plain C in 128-row chunks) of X, W, dY row- and column-wise, dequantization "
+                       f"and 3 FP64 numpy GEMMs per recipe; {threads} host threads, {dt:.1f} s wall"),
+            "seconds": round(dt, 2),
+            "single_thread": {"value": round(flops / dt1 / 1e12, 6), "seconds": round(dt1, 2)},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_info()}
 
 
 def main():
@@ -812,24 +1014,42 @@ def main():
     log(f"[bench] device {torch.cuda.get_device_name(0)}; steps {args.steps} warmup {args.warmup}")
     names = [n for n in args.workloads.split(",") if n]
 
+    ceilings = hbm_ceilings(torch)
+    log(f"[bench] HBM ceilings (in-tree streaming kernels): {ceilings}")
+
     head = Llama8B(torch, fgs, synth)
     clocks_before = gpu_clocks()
-    wall, kinds, _ = measure(torch, head, args.steps, args.warmup)
+    wall, kinds, _, step_s, tm = measure(torch, head, args.steps, args.warmup)
     clocks_after = gpu_clocks()
     ms = wall * 1e3 / args.steps
     value = head.flops() / (wall / args.steps) / 1e12
     rep = kind_report(kinds, args.steps)
+    inst = instantiation_report(tm, args.steps)
+    quant = dict(rep.get("quant") or {})
+    if ceilings:
+        quant["frac_copy_ceiling"] = round(quant["GB/s"] / ceilings["copy_GB/s"], 4)
+        quant["frac_read_ceiling"] = round(quant["GB/s"] / ceilings["read_GB/s"], 4)
+    quant["roles"] = quant_report(tm, args.steps, ceilings)
     log(f"[bench] {head.name}: step {ms:.2f} ms, {value:.1f} TFLOP/s; {rep}")
+    for r in inst:
+        log(f"[bench]   {r['kernel']}: {r['launches_per_step']} launches/step, {r['avg_us']} us avg, "
+            f"{r['TFLOP/s']} TFLOP/s = {r['frac_peak']} of peak, {r['share_of_gemm_time']} of GEMM time")
 
     extra = {}
     for n in names:
         if n == "llama3_8b":
             continue
         wl = WORKLOADS[n](torch, fgs, synth)
-        w_wall, w_kinds, w_labels = measure(torch, wl, args.steps, args.warmup)
+        w_wall, w_kinds, w_labels, w_steps, w_tm = measure(torch, wl, args.steps, args.warmup)
         r = kind_report(w_kinds, args.steps)
         r["ms_per_step"] = round(w_wall * 1e3 / args.steps, 4)
+        r["step_ms"] = step_stats(w_steps)
         r["step_TFLOP/s"] = round(wl.flops() / (w_wall / args.steps) / 1e12, 2)
+        if not isinstance(wl, MoE):
+            r["instantiations"] = [{k: v for k, v in e.items() if k != "launches"}
+                                   for e in instantiation_report(w_tm, args.steps)]
+        if ceilings and "quant" in r:
+            r["quant"]["frac_copy_ceiling"] = round(r["quant"]["GB/s"] / ceilings["copy_GB/s"], 4)
         if isinstance(wl, MoE):
             f, t, _ = w_kinds["gemm"]
             # forward (gate/up N=4096 K=7168, down N=7168 K=2048) and dgrad
@@ -843,16 +1063,17 @@ def main():
             roof_w = sum(wl.wgrad_roofline_seconds(m, n) for m, n in wshapes)
             by = sum(wl.gemm_bytes(n, k) for n, k in shapes) + sum(wl.wgrad_bytes(m, n) for m, n in wshapes)
             gemm_s = t / args.steps
-            r["gemm"]["roofline_ms"] = round((roof_rows + roof_w) * 1e3, 4)
-            r["gemm"]["frac_roofline"] = round((roof_rows + roof_w) / gemm_s, 4)
+            r["gemm"]["roofline_ms"] = round(float(roof_rows + roof_w) * 1e3, 4)
+            r["gemm"]["frac_roofline"] = round(float(roof_rows + roof_w) / gemm_s, 4)
             r["gemm"]["GB/s"] = round(by / gemm_s / 1e9, 1)
             tw = sum(tt for (kind, lab), (_, tt, _) in w_labels.items() if kind == "gemm" and "wgrad" in lab)
             tw /= args.steps
             wby = sum(wl.wgrad_bytes(m, n) for m, n in wshapes)
-            r["gemm"]["roofline_ms"] = float(r["gemm"]["roofline_ms"])
-            r["gemm"]["frac_roofline"] = float(r["gemm"]["frac_roofline"])
             r["wgrad"] = {"ms_per_step": round(tw * 1e3, 4), "roofline_ms": round(float(roof_w) * 1e3, 4),
                           "frac_roofline": round(float(roof_w) / tw, 4), "GB/s": round(wby / tw / 1e9, 1)}
+            tr = gemm_s - tw
+            r["fwd_dgrad"] = {"ms_per_step": round(tr * 1e3, 4), "roofline_ms": round(float(roof_rows) * 1e3, 4),
+                              "frac_roofline": round(float(roof_rows) / tr, 4)}
         log(f"[bench] {wl.name}: {r}")
         extra[wl.name] = r
         del wl
@@ -862,17 +1083,21 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample (CPU) ...")
         cpu = cpu_baseline()
-        log(f"[bench] oracle sample: {cpu['value']} TFLOP/s; {cpu['sample']}")
+        log(f"[bench] oracle sample: {cpu['value']} TFLOP/s; {cpu['sample']}; one thread "
+            f"{cpu['single_thread']['value']} TFLOP/s ({cpu['single_thread']['seconds']} s)")
 
     g = rep["gemm"]
-    counters = read_gemm_traffic()
-    traffic = None
-    if counters is not None:
-        traffic = counters["gemm_traffic_bytes_per_launch"]
-        log(f"[bench] GEMM HBM traffic {traffic / 1e6:.1f} MB per launch ({COUNTER_PROFILE}); algorithmic "
-            f"{counters['gemm_algorithmic_bytes_per_launch'] / 1e6:.1f} MB")
-    else:
-        log(f"[bench] no GEMM traffic: {COUNTER_PROFILE} missing or taken on other kernel sources")
+    dom = inst[0]
+    # algorithmic bytes per launch of the dominant instantiation (its launches'
+    # operand codes, scales and output, once each), and the HBM traffic its
+    # dispatches made in the committed counter runs of the same sources
+    shapes = {lab: (M, N, K, am, bm, dt) for lab, M, N, K, am, bm, dt in head.gemm_launches()}
+    dl = [shapes[lab] for lab in dom["launches"]]
+    alg = sum(head.gemm_bytes_one(M, N, K, am, bm, 2 if dt == torch.bfloat16 else 4) for M, N, K, am, bm, dt in dl) / len(dl)
+    tr = read_kernel_traffic(dom["kernel"])
+    traffic = tr["traffic_bytes_per_dispatch"] if tr else None
+    if traffic is None:
+        log(f"[bench] no traffic for {dom['kernel']}: {COUNTER_PROFILE} missing, without it, or taken on other sources")
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -881,20 +1106,29 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats(step_s),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3 codes, fp16 mfma, fp32 accumulate",
         "data": "synthetic (seeded BF16: activations N(0,1) with x50 outlier channels, weights N(0,0.02), "
-                "gradients Student-t(3) std 1e-3)",
+                "gradients Student-t(3) std 1e-3; each layer its own tensors, "
+                f"{len(head.sets)} input sets in rotation, {head.input_bytes() / 2**30:.2f} GiB)",
         "config": {"workload": "llama3-8b linear layers fwd+dgrad+wgrad, blockwise 1x128/128x128 and per-tensor E4M3",
                    "tokens": LLAMA8B_M, "layers": {n: [K, N] for n, K, N in LLAMA8B_LAYERS},
-                   "recipes": [r[0] for r in RECIPES], "step_gemm_tflop": round(head.flops() / 1e12, 4)},
-        "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP16_MFMA, "unit": "TFLOP/s",
-                     "frac": g["frac_fp16_mfma_peak"], "traffic": traffic,
-                     "kernel": "gemm_block_scaled (all GEMM launches of the step)",
-                     "frac_of_fp8_peak": round(g["TFLOP/s"] / PEAK_FP8_MFMA, 4)},
-        "quant": rep.get("quant"),
+                   "recipes": [r[0] for r in RECIPES], "step_gemm_tflop": round(head.flops() / 1e12, 4),
+                   "input_sets": len(head.sets)},
+        "roofline": {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": PEAK_FP16_MFMA, "unit": "TFLOP/s",
+                     "frac": round(dom["TFLOP/s"] / PEAK_FP16_MFMA, 4), "traffic": traffic,
+                     "kernel": dom["kernel"], "launches_per_step": dom["launches_per_step"],
+                     "flop_per_launch": dom["flop_per_launch"], "avg_launch_us": dom["avg_us"],
+                     "share_of_gemm_time": dom["share_of_gemm_time"],
+                     "algorithmic_bytes_per_launch": round(alg),
+                     "frac_of_fp8_peak": round(dom["TFLOP/s"] / PEAK_FP8_MFMA, 4)},
+        "gemm": dict(g, instantiations=[{k: v for k, v in e.items() if k != "launches"} for e in inst],
+                     dominant=dom["kernel"]),
+        "quant": quant,
+        "hbm_ceiling": ceilings,
         "workloads": extra,
         "cpu_baseline": cpu,
         "clocks": {"before": clocks_before, "after": clocks_after},

@@ -3,7 +3,9 @@
 Every .hip / .cpp file under csrc/ is compiled separately (in parallel) and
 linked into fine_grained_scaled_amd/libfgs.so.  All device code is built with
 -ffp-contract=off (every fused multiply-add in the kernels is explicit) and
-without packed-FP32 instruction selection.
+without packed-FP32 instruction selection.  The benchmark's HBM-ceiling
+kernels (bench_kernels/) are linked into libfgs_hbm.so, outside the product
+library.
 """
 from __future__ import annotations
 
@@ -15,6 +17,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libfgs.so")
+HBM_SRC = os.path.join(HERE, "bench_kernels")
+HBM_LIB_PATH = os.path.join(HERE, "libfgs_hbm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,18 +41,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile and link libfgs.so; returns its path.  Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(objs, path):
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile and link libfgs.so (and the benchmark's libfgs_hbm.so);
+    returns the path of libfgs.so.  Always recompiles."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    hbm = sorted(glob.glob(os.path.join(HBM_SRC, "*.hip")))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs + hbm))
+    _link(objs[:len(srcs)], LIB_PATH)
+    if hbm:
+        _link(objs[len(srcs):], HBM_LIB_PATH)
     return LIB_PATH
 
 

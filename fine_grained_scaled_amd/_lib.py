@@ -22,6 +22,7 @@ EXPORTS = (
     "fgs_quantize_nvfp4",
     "fgs_gemm_block_scaled",
     "fgs_gemm_block_scaled_ex",
+    "fgs_gemm_kernel_name",
     "fgs_gemm_block_scaled_fp8mma",
     "fgs_grouped_gemm_block_scaled",
     "fgs_grouped_gemm_block_scaled_fp8mma",
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.fgs_gemm_block_scaled.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8mma.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_ex.argtypes = [OP, OP, I64, I64, I64, P, I64, I32, ctypes.POINTER(FgsGemmOptions), P]
+    lib.fgs_gemm_kernel_name.argtypes = [OP, OP, I64, I64, I64, I32, ctypes.POINTER(FgsGemmOptions), ctypes.c_char_p,
+                                         SZ]
     lib.fgs_grouped_gemm_block_scaled.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_grouped_gemm_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_gemm_block_scaled_fp8out.argtypes = [OP, OP, I64, I64, I64, P, I64, P, P, P]
@@ -101,7 +104,8 @@ def load() -> ctypes.CDLL:
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_blockwise_noalloc", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",
-                 "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_ex", "fgs_gemm_block_scaled_fp8mma",
+                 "fgs_gemm_block_scaled", "fgs_gemm_block_scaled_ex", "fgs_gemm_kernel_name",
+                 "fgs_gemm_block_scaled_fp8mma",
                  "fgs_grouped_gemm_block_scaled",
                  "fgs_grouped_gemm_block_scaled_fp8mma", "fgs_grouped_wgrad_block_scaled_fp8mma",
                  "fgs_quantize_grouped_colwise", "fgs_grouped_wgrad_block_scaled",

@@ -262,7 +262,8 @@ static bool is_fp32_mode(int m)
 }
 
 static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
-                     void* C, int64_t ldc, int out_dtype, const fgs_gemm_options& o, void* stream)
+                     void* C, int64_t ldc, int out_dtype, const fgs_gemm_options& o, void* stream,
+                     char* name = nullptr, size_t name_len = 0)
 {
     if (o.tile != FGS_TILE_AUTO && o.tile != FGS_TILE_NARROW && o.tile != FGS_TILE_WIDE)
         return fail(FGS_ERR_INVALID_ARG, "tile %d is not FGS_TILE_AUTO, FGS_TILE_NARROW or FGS_TILE_WIDE", o.tile);
@@ -281,12 +282,15 @@ static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int6
     }
     int st = check_gemm_common(A, B, M, N, K, C ? C : static_cast<void*>(q_out), ldc, out_dtype);
     if (st != FGS_OK) return st;
-    if (M == 0 || N == 0) return ok();
+    if (M == 0 || N == 0) {
+        if (name) name[0] = '\0';      // nothing would be launched
+        return ok();
+    }
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
     // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
     fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out, o.fp8_mma,
-                    o.tile};
+                    o.tile, name, name_len};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (o.fp8_mma && (A->elem == FGS_ELEM_E2M1 || B->elem == FGS_ELEM_E2M1))
         return fail(FGS_ERR_UNSUPPORTED, "the FP8 matrix-instruction GEMM takes E4M3 / E5M2 operands only");
@@ -310,6 +314,19 @@ int fgs_gemm_block_scaled_ex(const fgs_operand* A, const fgs_operand* B, int64_t
 {
     const fgs_gemm_options o = opts ? *opts : fgs_gemm_options{};
     return gemm_impl(A, B, M, N, K, C, ldc, out_dtype, o, stream);
+}
+
+int fgs_gemm_kernel_name(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,
+                         int out_dtype, const fgs_gemm_options* opts, char* name, size_t len)
+{
+    if (!name || len < 2) return fail(FGS_ERR_INVALID_ARG, "name must hold at least 2 bytes");
+    const fgs_gemm_options o = opts ? *opts : fgs_gemm_options{};
+    // validated as the launch would be, with a stand-in output address that
+    // is never written (nothing is launched)
+    void* c_stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+    const int st = gemm_impl(A, B, M, N, K, o.q_out ? nullptr : c_stand_in, N, out_dtype, o, nullptr, name, len);
+    if (st != FGS_OK) name[0] = '\0';
+    return st;
 }
 
 int fgs_gemm_block_scaled(const fgs_operand* A, const fgs_operand* B, int64_t M, int64_t N, int64_t K,

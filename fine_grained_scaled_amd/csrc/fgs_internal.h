@@ -102,6 +102,8 @@ struct GemmArgs {
     float* s_out;                   //   their scales [N/128][M]
     int fp8_mma;                    // accumulate on the FP8 matrix instructions
     int tile;                       // dense only: FGS_TILE_AUTO | FGS_TILE_NARROW | FGS_TILE_WIDE
+    char* name_out;                 // non-null: write the kernel instantiation's name instead of launching
+    size_t name_len;
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).

@@ -56,6 +56,7 @@
 // chunk, 256 bytes) touches each of the 64 LDS banks once.  MFMA operands
 // are swapped (B fragment first) so each lane's 16 accumulators share one
 // row m: the 1x128 A scale is one value per lane and per sub-tile row.
+#include <cstdio>
 #include <type_traits>
 
 #include "fgs_device.h"
@@ -1350,6 +1351,13 @@ hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t 
     // the row-grouped and dense schedules only; any other launch with q_out
     // would leave it unwritten, so it is refused before launching
     if (a.q_out && (!bf16 || MMA8 || GROUP == GROUP_K)) return hipErrorInvalidValue;
+    if (a.name_out) {
+        // the instantiation, as profilers print it without namespaces and
+        // arguments
+        snprintf(a.name_out, a.name_len, "gemm_block_scaled_kernel<Shape<%d, %d, %d>, %d, %d, %s, %d, %d, %s>",
+                 S::NWM, S::NWN, S::TI, AMODE, BMODE, bf16 ? "true" : "false", GROUP, ELEMS, MMA8 ? "true" : "false");
+        return hipSuccess;
+    }
     constexpr bool a_lds = S::TI == 4 && AMODE == FGS_SCALE_TILE_1x128;   // the kernel's A_LDS
     constexpr int scw = AMODE == FGS_SCALE_MX32_E8M0 ? 1 : (AMODE == FGS_SCALE_NV16_E4M3 ? 2 : 0);   // the kernel's SCW
     const size_t lds = 2 * (size_t)Lds<S, AMODE == FGS_SCALE_NV16_E4M3 ? 64 : 128, BMODE == FGS_SCALE_TILE_1x128, a_lds,

@@ -269,6 +269,22 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
     return out
 
 
+def gemm_kernel_name(A: Operand, B: Operand, out_dtype=torch.float32, K: Optional[int] = None,
+                     fp8_mma: bool = False, tile: str = "auto") -> str:
+    """Name of the kernel instantiation gemm_block_scaled(A, B, out_dtype,
+    fp8_mma=..., tile=...) launches, as profilers print it (nothing is
+    launched)."""
+    M, N = A.data.shape[0], B.data.shape[0]
+    if K is None:
+        K = A.data.shape[1] * (2 if A.elem == ELEM_E2M1 else 1)
+    a, b = A.c_struct(), B.c_struct()
+    opt = _lib.FgsGemmOptions(_tile_code(tile), 1 if fp8_mma else 0, None, None)
+    buf = ctypes.create_string_buffer(256)
+    check(_lib.load().fgs_gemm_kernel_name(ctypes.byref(a), ctypes.byref(b), M, N, K, _out_code(out_dtype),
+                                           ctypes.byref(opt), buf, len(buf)))
+    return buf.value.decode()
+
+
 def gemm_block_scaled_fp8out(A: Operand, B: Operand, bf16_out: bool = True, K: Optional[int] = None,
                              tile: str = "auto"):
     """gemm_block_scaled with BF16 output whose epilogue also quantizes it in

@@ -475,6 +475,22 @@ int fgs_gemm_block_scaled_ex(const fgs_operand *A, const fgs_operand *B,
                              int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
                              int out_dtype, const fgs_gemm_options *opts, void *stream);
 
+/*
+ * fgs_gemm_kernel_name -- the kernel instantiation that
+ *   fgs_gemm_block_scaled_ex(A, B, M, N, K, C, ldc, out_dtype, opts, ...)
+ *   would launch, named as profilers print it (without namespaces and
+ *   arguments, e.g. "gemm_block_scaled_kernel<Shape<2, 4, 4>, 1, 2, true,
+ *   0, 0, false>"), so timings and counters can be matched to launches.
+ *   Nothing is launched and no HIP call is made beyond reading the current
+ *   device's compute-unit count.
+ * name     host buffer of len >= 2 bytes; receives a NUL-terminated string
+ *          (truncated to len - 1 characters; "" when M or N is 0).
+ * Returns what the GEMM call would return for these operands, shapes and
+ * options (an argument error leaves name empty).
+ */
+int fgs_gemm_kernel_name(const fgs_operand *A, const fgs_operand *B, int64_t M, int64_t N, int64_t K,
+                         int out_dtype, const fgs_gemm_options *opts, char *name, size_t len);
+
 /* Device workspace needed by TENSOR-mode and NVFP4 quantization (bytes). */
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols);
 

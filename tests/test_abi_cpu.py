@@ -145,6 +145,34 @@ def test_gemm_ex_options_validation(lib):
     assert g(r(a), r(b), 0, 128, 256, FAKE, 128, 0, r(O(2, 1, None, None)), S) == _lib.FGS_OK
 
 
+def test_gemm_kernel_name(lib):
+    """The instantiation query launches nothing (fake addresses are fine) and
+    names what the GEMM call would run: the forced tiles, the 256 x 128 tile
+    for 1x128 B scales, the FP8-instruction flag, BF16 out; "" for an empty
+    problem; an argument error returns the GEMM's status and an empty name."""
+    import ctypes as C
+    O = _lib.FgsGemmOptions
+    buf = C.create_string_buffer(256)
+
+    def name(M, N, K, am, bm, out=0, tile=0, mma=0, elem=0):
+        a, b = _op(ld=K, mode=am, elem=elem), _op(ld=K, mode=bm, elem=elem)
+        st = lib.fgs_gemm_kernel_name(C.byref(a), C.byref(b), M, N, K, out, C.byref(O(tile, mma, None, None)), buf, 256)
+        return st, buf.value.decode()
+
+    st, n = name(512, 512, 256, 1, 2, tile=_lib.TILE_NARROW)
+    assert st == _lib.FGS_OK and n == "gemm_block_scaled_kernel<Shape<4, 2, 2>, 1, 2, false, 0, 0, false>"
+    assert name(512, 512, 256, 1, 2, tile=_lib.TILE_WIDE)[1].startswith("gemm_block_scaled_kernel<Shape<2, 4, 4>, 1, 2,")
+    assert name(8192, 6144, 4096, 1, 1, tile=_lib.TILE_WIDE)[1].startswith("gemm_block_scaled_kernel<Shape<4, 2, 2>, 1, 1")
+    assert name(512, 512, 256, 0, 0, out=1, tile=_lib.TILE_WIDE)[1].endswith(", 0, 0, true, 0, 0, false>")
+    assert name(512, 512, 256, 1, 2, mma=1)[1].endswith(", 0, 0, true>")
+    assert name(512, 512, 256, 3, 3, tile=_lib.TILE_NARROW)[1] == \
+        "gemm_block_scaled_kernel<Shape<4, 2, 2>, 3, 3, false, 0, 0, false>"
+    assert name(0, 512, 256, 1, 2) == (_lib.FGS_OK, "")
+    assert name(512, 512, 200, 1, 2) == (_lib.FGS_ERR_UNSUPPORTED, "")
+    assert lib.fgs_gemm_kernel_name(C.byref(_op()), C.byref(_op(mode=2)), 128, 128, 256, 0, None, buf, 1) == \
+        _lib.FGS_ERR_INVALID_ARG
+
+
 def test_grouped_validation(lib):
     S = NULL
     g = lib.fgs_grouped_gemm_block_scaled
