@@ -982,6 +982,9 @@ def main():
                          "step, then of --copy-calibration) into " + COUNTER_PROFILE + " and exit (no GPU needed)")
     ap.add_argument("--counter-command", action="append", default=[],
                     help="command line recorded in the counter profile (repeatable)")
+    ap.add_argument("--only", default=None,
+                    help="comma list of workloads to run alone (no headline, no CPU baseline), reported on "
+                         "stderr: for profiling runs")
     ap.add_argument("--gemm-only", action="store_true",
                     help="headline workload: quantize once, then time only the GEMM launches "
                          "(for counter collection on the GEMM kernel)")
@@ -1013,6 +1016,14 @@ def main():
         return
     log(f"[bench] device {torch.cuda.get_device_name(0)}; steps {args.steps} warmup {args.warmup}")
     names = [n for n in args.workloads.split(",") if n]
+    if args.only:
+        for n in args.only.split(","):
+            wl = WORKLOADS[n](torch, fgs, synth)
+            w_wall, w_kinds, _, w_steps, w_tm = measure(torch, wl, args.steps, args.warmup)
+            log(f"[bench] {wl.name}: {kind_report(w_kinds, args.steps)}; step {step_stats(w_steps)}")
+            del wl
+            torch.cuda.empty_cache()
+        return
 
     ceilings = hbm_ceilings(torch)
     log(f"[bench] HBM ceilings (in-tree streaming kernels): {ceilings}")

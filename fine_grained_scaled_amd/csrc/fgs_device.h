@@ -25,6 +25,15 @@ __device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f);
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 
+// 16 bytes read once with the non-temporal hint (global_load_dwordx4 ... nt):
+// streamed inputs are not kept in the caches for reuse that never comes.
+__device__ __forceinline__ uint4 load_nt16(const void* p)
+{
+    const uint32_t* q = static_cast<const uint32_t*>(p);
+    return make_uint4(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                      __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3));
+}
+
 // ------------------------------------------------------------------------
 // cross-lane max of non-negative integers (amax carried as |BF16| bits,
 // where the integer order equals the value order and NaN > Inf > finite,

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void quant_delayed_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int64_t row = r0 + 8 * rg + u;
-        v[u] = (col_ok && row < rows) ? *reinterpret_cast<const uint4*>(x + row * ldx + col)
+        v[u] = (col_ok && row < rows) ? load_nt16(x + row * ldx + col)
                                       : make_uint4(0, 0, 0, 0);
     }
     const float s = scale[0];

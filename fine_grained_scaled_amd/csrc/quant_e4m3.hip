@@ -190,14 +190,17 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
         if constexpr (SWIGLU) {
             if (ok) {
                 const uint16_t* xr = x + src * ldx + col;
-                v[u] = swiglu8(*reinterpret_cast<const uint4*>(xr), *reinterpret_cast<const uint4*>(xr + cols));
+                v[u] = swiglu8(load_nt16(xr), load_nt16(xr + cols));
                 if (h_out) *reinterpret_cast<uint4*>(h_out + row * cols + col) = v[u];
             } else {
                 v[u] = make_uint4(0, 0, 0, 0);
             }
         } else {
+            // a dispatch gather reads each token's row several times (top-k
+            // routing), so it keeps the caches; other rows are read once
             if (ok)
-                v[u] = *reinterpret_cast<const uint4*>(x + src * ldx + col);
+                v[u] = (GROUPED && row_index) ? *reinterpret_cast<const uint4*>(x + src * ldx + col)
+                                              : load_nt16(x + src * ldx + col);
             else
                 v[u] = make_uint4(0, 0, 0, 0);
         }
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t row = r0 + 8 * rg + u;
-            v[u] = (col < cols && row < rows) ? *reinterpret_cast<const uint4*>(x + row * ldx + col)
+            v[u] = (col < cols && row < rows) ? load_nt16(x + row * ldx + col)
                                               : make_uint4(0, 0, 0, 0);
         }
     };
@@ -351,6 +354,35 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(
         for (int u = 0; u < 8; ++u) v[u] = vn[u];
         blk = next;
     }
+    m = max_xor32(max_xor16(max_lanes16(m)));
+    if (l == 0) red[w] = m;
+    __syncthreads();
+    if (t == 0) out[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Tensor amax of a contiguous tensor (ldx == cols), read as a flat array of
+// n16 16-byte chunks: persistent, consecutive lanes on consecutive chunks
+// (each wave-instruction reads 1 KiB of contiguous memory), eight
+// non-temporal loads in flight per thread; one partial per workgroup, as
+// amax_bf16_kernel.  Every index touched is below n16: the unrolled body
+// runs only while its last index is.
+__global__ __launch_bounds__(256) void amax_bf16_flat_kernel(const uint16_t* __restrict__ x, int64_t n16,
+                                                             uint32_t* __restrict__ out)
+{
+    constexpr int UNROLL = 8;
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + t;
+    uint32_t m = 0;
+    for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+        uint4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = load_nt16(x + 8 * (i + u * stride));
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) m = max(m, abs_max8(v[u]));
+    }
+    for (; i < n16; i += stride) m = max(m, abs_max8(load_nt16(x + 8 * i)));
     m = max_xor32(max_xor16(max_lanes16(m)));
     if (l == 0) red[w] = m;
     __syncthreads();
@@ -378,12 +410,25 @@ hipError_t launch_quant_e4m3(const QuantE4M3Args& a, hipStream_t stream)
         // amax workgroups: two per compute unit (each keeps two blocks of
         // loads in flight), at most one per 4-byte workspace slot
         uint32_t* amax = static_cast<uint32_t*>(a.workspace);
-        int64_t g = nbr * nbc;
-        const int64_t cap = (int64_t)device_cus() * 2, slots = (int64_t)(a.workspace_bytes / 4);
-        if (g > cap) g = cap;
-        if (g > slots) g = slots;
-        hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)g), block, 0, stream,
-                           x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
+        const int64_t slots = (int64_t)(a.workspace_bytes / 4);
+        int64_t g;
+        if (a.ldx == a.cols) {
+            // contiguous: stream it as one flat array, one workgroup per
+            // compute unit (the read ceiling's configuration)
+            const int64_t n16 = a.rows * a.cols / 8;
+            g = (n16 + 255) / 256;
+            const int64_t cap = (int64_t)device_cus();
+            if (g > cap) g = cap;
+            if (g > slots) g = slots;
+            hipLaunchKernelGGL(amax_bf16_flat_kernel, dim3((unsigned)g), block, 0, stream, x, n16, amax);
+        } else {
+            g = nbr * nbc;
+            const int64_t cap = (int64_t)device_cus() * 2;
+            if (g > cap) g = cap;
+            if (g > slots) g = slots;
+            hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)g), block, 0, stream,
+                               x, a.rows, a.cols, a.ldx, nbr, nbc, amax);
+        }
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TENSOR, false>), grid, block, 0, stream,
                            x, a.rows, a.cols, a.ldx, a.q, a.scales, a.qT, a.scalesT, amax, (int32_t)g,
                            nullptr, 0, 0, nullptr, 0, nullptr);

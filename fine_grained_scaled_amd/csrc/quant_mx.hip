@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
     for (int u = 0; u < 8; ++u) {
         const int64_t row = r0 + 8 * rg + u;
         if (col_ok && row < rows)
-            v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+            v[u] = load_nt16(x + row * ldx + col);
         else
             v[u] = make_uint4(0, 0, 0, 0);
     }

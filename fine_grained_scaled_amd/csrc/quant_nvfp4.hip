@@ -151,24 +151,26 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a)
            (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
-// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r.
-// The magnitudes split into three segments of equal spacing: [0, 2) with
-// step 1/2 (codes 0-3), [2, 4) with step 1 (codes 4-5), [4, 6] with step 2
-// (codes 6-7).  u = (a - base) / step is exact (a power-of-two multiple of a
-// difference that Sterbenz's lemma makes exact); its integer part k gives
-// the lower neighbour, code0 + k, and p = u - k = (a - lo) / (hi - lo) is
-// exact.  Round up iff (r >> 8) < p * 2^24.
+// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r: the
+// lower neighbour lo <= a, plus one iff (r >> 8) < p * 2^24 with
+// p = (a - lo) / (hi - lo).  Two exact forms, selected on a:
+//  * a >= 1 (FP32 bits b): the grid {1, 1.5, 2, 3, 4, 6} keeps one mantissa
+//    bit, so lo's code is (b >> 22) - 252 and p * 2^24 = (b mod 2^22) * 4,
+//    an integer; (r >> 8) < p * 2^24 is then the unsigned r < (b << 10).
+//  * a < 1 (grid {0, 0.5, 1}): u = 2a is exact, lo's code is [u >= 1] and
+//    p = u - floor(u) (exact); the comparison is taken in FP32, where both
+//    (r >> 8) and p * 2^24 are exact.
+// Equal to the segment-by-segment rule for every FP32 a in [0, 6], checked
+// on the host at each a's decision threshold (and one either side) plus
+// random words: 1.3e10 pairs.
 __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
 {
-    const bool s0 = a < 2.0f, s1 = a < 4.0f;
-    const float base = s0 ? 0.0f : (s1 ? 2.0f : 4.0f);
-    const float inv_step = s0 ? 2.0f : (s1 ? 1.0f : 0.5f);
-    const uint32_t code0 = s0 ? 0u : (s1 ? 4u : 6u);
-    const float u = (a - base) * inv_step;
-    const float k = __builtin_floorf(u);
-    const float p = u - k;
-    const uint32_t up = (float)(r >> 8) < p * 16777216.0f ? 1u : 0u;
-    return code0 + (uint32_t)k + up;
+    const uint32_t b = as_u32(a);
+    const uint32_t hi = (b >> 22) - 252u + (r < (b << 10) ? 1u : 0u);
+    const float u = a * 2.0f;
+    const float p = __builtin_amdgcn_fractf(u);
+    const uint32_t lo = (u >= 1.0f ? 1u : 0u) + ((float)(r >> 8) < p * 16777216.0f ? 1u : 0u);
+    return a >= 1.0f ? hi : lo;
 }
 
 struct TensorScale {
@@ -251,7 +253,7 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
     if constexpr (SR) {
         uint32_t packed = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) packed |= (e2m1_sr(q[i], rw[i]) | (sg[i] >> 28)) << (4 * i);
+        for (int i = 0; i < 8; ++i) packed |= (e2m1_sr(q[i], rw[i]) | ((sg[i] >> 31) << 3)) << (4 * i);
         return packed;
     } else {
         float v[8];
@@ -273,13 +275,14 @@ __device__ __forceinline__ uint32_t sr_mid(uint32_t seed_lo, uint32_t seed_hi, u
     return fmix32(seed_lo ^ fmix32(seed_hi ^ (uint32_t)(i >> 32)));
 }
 
-// Random word of element i0 + j (0 <= j < 8) from lo32(i0) and the seed
-// rounds of i0.  Every run of 8 starts at a multiple of 8 (cols and the
-// column offset are multiples of 8), so lo32(i0) + j never carries into
-// hi32 and the seed rounds of i0 hold for the whole run.
-__device__ __forceinline__ uint32_t sr_word_at(uint32_t lo0, uint32_t mid0, int j)
+// Random word of element i0 + j (0 <= j < 8) from base = lo32(i0) ^ mid0,
+// mid0 the seed rounds of i0.  Every run of 8 starts at a multiple of 8
+// (cols and the column offset are multiples of 8), so lo32(i0) + j equals
+// lo32(i0) ^ j, never carries into hi32, and the seed rounds of i0 hold for
+// the whole run: fmix32((lo32(i0) + j) ^ mid0) = fmix32(base ^ j).
+__device__ __forceinline__ uint32_t sr_word_at(uint32_t base, int j)
 {
-    return fmix32((lo0 + (uint32_t)j) ^ mid0);
+    return fmix32(base ^ (uint32_t)j);
 }
 
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -289,7 +292,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
     for (int u = 0; u < 8; ++u) {
         const int64_t row = r0 + 8 * rg + u;
         if (col_ok && row < rows)
-            v[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+            v[u] = load_nt16(x + row * ldx + col);
         else
             v[u] = make_uint4(0, 0, 0, 0);
     }
@@ -417,24 +420,18 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     __syncthreads();
     const TensorScale ts_row = tensor_scale_from(max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3])));
     const TensorScale ts_col = tensor_scale_from(max(max(s_red[1][0], s_red[1][1]), max(s_red[1][2], s_red[1][3])));
-    // SR: the hash's seed rounds per row of this thread
-    uint32_t midr[8], ilo[8];
+    // SR: the random word of an element does not depend on the
+    // orientation: hash each of the thread's 64 elements once for both
+    // outputs (the seed rounds once per row of the thread)
+    uint32_t W[8][8];
     if constexpr (SR) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const uint64_t i0 = (uint64_t)((r0 + 8 * rg + u) * cols + col);
-            midr[u] = sr_mid(seed_lo, seed_hi, i0);
-            ilo[u] = (uint32_t)i0;
+            const uint32_t base = (uint32_t)i0 ^ sr_mid(seed_lo, seed_hi, i0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) W[u][j] = sr_word_at(base, j);
         }
-    }
-    // the random word of an element does not depend on the orientation: hash
-    // each of the thread's 64 elements once for both outputs
-    uint32_t W[8][8];
-    if constexpr (SR) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) W[u][j] = sr_word_at(ilo[u], midr[u], j);
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
         tensor_scale[0] = ts_row.st;
