@@ -34,6 +34,22 @@ __device__ __forceinline__ uint4 load_nt16(const void* p)
                       __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3));
 }
 
+// 8 and 16 bytes written with the non-temporal hint: streamed outputs.
+__device__ __forceinline__ void store_nt8(void* p, const uint2& v)
+{
+    uint32_t* q = static_cast<uint32_t*>(p);
+    __builtin_nontemporal_store(v.x, q);
+    __builtin_nontemporal_store(v.y, q + 1);
+}
+__device__ __forceinline__ void store_nt16(void* p, const uint4& v)
+{
+    uint32_t* q = static_cast<uint32_t*>(p);
+    __builtin_nontemporal_store(v.x, q);
+    __builtin_nontemporal_store(v.y, q + 1);
+    __builtin_nontemporal_store(v.z, q + 2);
+    __builtin_nontemporal_store(v.w, q + 3);
+}
+
 // ------------------------------------------------------------------------
 // cross-lane max of non-negative integers (amax carried as |BF16| bits,
 // where the integer order equals the value order and NaN > Inf > finite,

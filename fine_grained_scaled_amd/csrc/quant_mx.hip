@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
             const uint2 codes = mx_code8(h, b);
             const int64_t row = r0 + 8 * rg + u;
             if (col_ok && row < rows) {
-                *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+                store_nt8(q + row * cols + col, codes);
                 if ((cg & 3) == 0) scales[row * nsc + col / 32] = (uint8_t)b.code;
             }
         }
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
             const int64_t orow = c0 + trow;
             if (orow < cols) {
                 const uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
-                *reinterpret_cast<uint4*>(qT + orow * rows + r0 + 16 * chunk) = d;
+                store_nt16(qT + orow * rows + r0 + 16 * chunk, d);
             }
         }
     }
