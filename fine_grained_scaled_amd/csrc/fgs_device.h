@@ -109,18 +109,21 @@ __device__ __forceinline__ uint32_t e4m3_code_abs(float a)
 }
 
 // ------------------------------------------------------------------------
-// Correctly rounded fl32(x / s) from a per-block reciprocal r = RN(1/s):
-// q0 = x*r, residual x - q0*s (exact with FMA), one correction step.  Equal
-// to IEEE division for every BF16 x with |x| <= amax and s = fl32(amax/448)
-// of a BF16 amax >= 2^-64 (checked exhaustively on the host, all 5.3e8
-// pairs); blocks with a smaller amax are pre-scaled by 2^64 on both sides,
-// which leaves the quotient unchanged.
+// fl32(x / s) from a per-block reciprocal r = RN(1/s): q0 = x*r, residual
+// e = q0*s - x (exact with FMA), one correction step q0 - e*r.  The signs
+// work out for either sign of x, -0 included (-0 gives q0 = -0, e = +0 and
+// -0 + -0 = -0).  For s = fl32(amax/448) of a BF16 amax >= 2^-64 and every
+// BF16 x with |x| <= amax, of either sign (all 1.07e9 pairs, checked on the
+// host), the result is IEEE x / s except for tiny x whose quotient lies
+// below 2^-40, far under the first E4M3 rounding point 2^-10, so every code
+// is that of the correctly rounded quotient.  Blocks with 0 < amax < 2^-64
+// are pre-scaled by 2^64 on both sides, which leaves the quotient unchanged.
 // ------------------------------------------------------------------------
 __device__ __forceinline__ float div_by_scale(float x, float s, float r)
 {
-    float q0 = x * r;
-    float res = __builtin_fmaf(-q0, s, x);
-    return __builtin_fmaf(res, r, q0);
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-e, r, q0);
 }
 
 // fl32(amax / 448) for a BF16-valued amax, by multiplication and one FMA
@@ -133,6 +136,18 @@ __device__ __forceinline__ float scale_from_amax_448(float amax)
     return __builtin_fmaf(e, inv448, s0);
 }
 
+// RN(1 / d) for the divisors d of the E4M3 block rule (d = fl32(amax / 448)
+// of a finite BF16 amax > 0, times 2^64 when amax < 2^-64, or 1): the
+// hardware reciprocal (within 1 ulp) and one Newton step.  Equal to IEEE
+// division for all 32639 such divisors (checked on gfx950); 1 and the other
+// powers of two come out exact.
+__device__ __forceinline__ float e4m3_scale_recip(float d)
+{
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
 // Per-block quantization constants of the FP32-scaled E4M3 rule.
 struct E4M3Block {
     float s;      // the block scale written out
@@ -141,6 +156,19 @@ struct E4M3Block {
     float r;      // RN(1 / sp)
     bool nan;     // amax non-finite: scale NaN, all codes 0x7F
 };
+
+// 0 < amax < 2^-64 (BF16 bits of 2^-64: 0x1F80): the pre-scaled blocks
+__device__ __forceinline__ bool e4m3_block_prescaled(uint32_t amax_bits16)
+{
+    return amax_bits16 - 1u < 0x1F7Fu;
+}
+
+// The block takes the NaN path or the pre-scale: true exactly when
+// e4m3_block_from_amax_bits gives nan or k != 1.
+__device__ __forceinline__ bool e4m3_block_special(uint32_t amax_bits16)
+{
+    return amax_bits16 >= 0x7F80u || e4m3_block_prescaled(amax_bits16);
+}
 
 __device__ __forceinline__ E4M3Block e4m3_block_from_amax_bits(uint32_t amax_bits16)
 {
@@ -153,9 +181,24 @@ __device__ __forceinline__ E4M3Block e4m3_block_from_amax_bits(uint32_t amax_bit
         return b;
     }
     b.s = (amax_bits16 == 0) ? 1.0f : scale_from_amax_448(amax);
-    b.k = (amax < 0x1p-64f) ? 0x1p64f : 1.0f;
+    // an all-zero block takes k = 1: every quotient of it is a signed zero
+    // with or without the pre-scale
+    b.k = e4m3_block_prescaled(amax_bits16) ? 0x1p64f : 1.0f;
     b.sp = b.s * b.k;
-    b.r = 1.0f / b.sp;   // IEEE division (hipcc keeps FP32 division correctly rounded)
+    b.r = e4m3_scale_recip(b.sp);
+    return b;
+}
+
+// The same constants for a block that e4m3_block_special rejects (finite,
+// not pre-scaled): no NaN or pre-scale selects.
+__device__ __forceinline__ E4M3Block e4m3_block_plain(uint32_t amax_bits16)
+{
+    E4M3Block b;
+    b.nan = false;
+    b.s = (amax_bits16 == 0) ? 1.0f : scale_from_amax_448(as_f32(amax_bits16 << 16));
+    b.k = 1.0f;
+    b.sp = b.s;
+    b.r = e4m3_scale_recip(b.sp);
     return b;
 }
 
@@ -169,30 +212,29 @@ __device__ __forceinline__ E4M3Block e4m3_block_from_amax_bits(uint32_t amax_bit
 // path).
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the first conversion writes the low half of a word whose high half the
+    // second one overwrites, so its old value is free: a's own bits, which
+    // die here, save a register move of zero
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)as_u32(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
 
-// fl32(x / s) of a block element given as FP32 bits: the correctly rounded
-// quotient of |x| (abs is a free source modifier) with the sign bit of x put
-// back (so -0 stays -0).  Blocks with amax < 2^-64 (b.k != 1) take the
-// pre-scaled form, a branch that real data does not enter.
+// fl32(x / s) of a block element given as FP32 bits (sign kept, -0
+// included).  Blocks with 0 < amax < 2^-64 (b.k != 1) take the pre-scaled
+// form (x * 2^64 is exact), a branch that real data does not enter.
 __device__ __forceinline__ float e4m3_quotient_bits(uint32_t xb, const E4M3Block& b)
 {
-    float a = __builtin_fabsf(as_f32(xb));
-    if (__builtin_expect(b.k != 1.0f, 0)) a *= b.k;
-    const float q = div_by_scale(a, b.sp, b.r);
-    return as_f32(as_u32(q) | (xb & 0x80000000u));
+    float x = as_f32(xb);
+    if (__builtin_expect(b.k != 1.0f, 0)) x *= b.k;
+    return div_by_scale(x, b.sp, b.r);
 }
 
-// code of one BF16 element (raw 16-bit pattern in the low half of h)
-__device__ __forceinline__ uint32_t e4m3_quant_bf16(uint32_t h, const E4M3Block& b)
+// The same quotient for a block with k == 1 and no NaN (the caller has
+// ruled out both, e.g. with e4m3_block_special over the whole wave).
+__device__ __forceinline__ float e4m3_quotient_plain(uint32_t xb, const E4M3Block& b)
 {
-    if (b.nan) return 0x7Fu;
-    float a = as_f32((h & 0x7FFFu) << 16) * b.k;
-    uint32_t c = e4m3_code_abs(div_by_scale(a, b.sp, b.r));
-    return c | ((h >> 8) & 0x80u);
+    return div_by_scale(as_f32(xb), b.sp, b.r);
 }
 
 } // namespace fgs

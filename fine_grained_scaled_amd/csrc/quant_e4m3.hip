@@ -18,6 +18,7 @@
 // source rows, the wgrad operand, or the transposed block/tensor codes),
 // the latter transposed through LDS so every store is a full 128-byte row.
 #include <mutex>
+#include <type_traits>
 
 #include "fgs_device.h"
 #include "fgs_internal.h"
@@ -68,21 +69,34 @@ __device__ __forceinline__ uint32_t val_bits(const uint4& v, int j)
 }
 
 // Codes of 8 values (FP32 bit patterns of BF16 numbers) of one block.
+// SPECIAL: the block may be non-finite or pre-scaled (per-lane tests);
+// without it the caller guarantees neither (the common, branch-free form).
+template <bool SPECIAL>
 __device__ __forceinline__ uint2 quant8_vals(const uint32_t xb[8], const E4M3Block& b)
 {
-    if (b.nan) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if constexpr (SPECIAL) {
+        if (b.nan) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    }
     float q[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = e4m3_quotient_bits(xb[j], b);
+    for (int j = 0; j < 8; ++j) q[j] = SPECIAL ? e4m3_quotient_bits(xb[j], b) : e4m3_quotient_plain(xb[j], b);
     return make_uint2(e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7]));
 }
 
+template <bool SPECIAL>
 __device__ __forceinline__ uint2 quant8(const uint4& v, const E4M3Block& b)
 {
     uint32_t xb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) xb[j] = val_bits(v, j);
-    return quant8_vals(xb, b);
+    return quant8_vals<SPECIAL>(xb, b);
+}
+
+// true on every lane when any lane of the wave passes true: a wave-uniform
+// branch condition
+__device__ __forceinline__ bool wave_any(bool p)
+{
+    return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
 // SwiGLU of one BF16 (gate, up) pair: h = silu(g) * u in FP32, rounded to
@@ -175,6 +189,8 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     const int64_t col = c0 + 8 * cg;
     const bool col_ok = col < cols;
 
+    // per-thread base of row 8*rg (u * stride is wave-uniform)
+    const uint16_t* const x_base = x + (r0 + 8 * rg) * ldx + col;
     uint4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
             // routing), so it keeps the caches; other rows are read once
             if (ok)
                 v[u] = (GROUPED && row_index) ? *reinterpret_cast<const uint4*>(x + src * ldx + col)
-                                              : load_nt16(x + src * ldx + col);
+                                              : load_nt16(x_base + u * ldx);
             else
                 v[u] = make_uint4(0, 0, 0, 0);
         }
@@ -240,24 +256,41 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
     // ---------------- row-wise output ---------------------------------
     if (q) {
         float srow[8];
+        uint32_t mrow[8];
+        bool special = false;
+        if constexpr (MODE == FGS_SCALE_TILE_1x128) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            E4M3Block b;
-            if constexpr (MODE == FGS_SCALE_TILE_1x128) {
-                b = e4m3_block_from_amax_bits(max_lanes16(abs_max8(v[u])));
-                srow[u] = b.s;
-            } else {
-                b = shared_b;
+            for (int u = 0; u < 8; ++u) {
+                mrow[u] = max_lanes16(abs_max8(v[u]));
+                special |= e4m3_block_special(mrow[u]);
             }
-            const int64_t row = r0 + 8 * rg + u;
-            uint2 codes = quant8(v[u], b);
-            if (col_ok && 8 * rg + u < live) {
-                // non-temporal stores measured faster for the grouped (MoE)
-                // layout and slower for the dense one
-                if constexpr (GROUPED) store_nt8(q + row * cols + col, codes);
-                else *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
-            }
+        } else {
+            special = shared_b.nan || shared_b.k != 1.0f;
         }
+        uint8_t* const q_base = q + (r0 + 8 * rg) * cols + col;
+        auto emit = [&](auto special_c) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                E4M3Block b;
+                if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+                    b = decltype(special_c)::value ? e4m3_block_from_amax_bits(mrow[u])
+                                                   : e4m3_block_plain(mrow[u]);
+                    srow[u] = b.s;
+                } else {
+                    b = shared_b;
+                }
+                const uint2 codes = quant8<decltype(special_c)::value>(v[u], b);
+                if (col_ok && 8 * rg + u < live) {
+                    uint8_t* dst = q_base + u * cols;
+                    // non-temporal stores measured faster for the grouped
+                    // (MoE) layout and slower for the dense one
+                    if constexpr (GROUPED) store_nt8(dst, codes);
+                    else *reinterpret_cast<uint2*>(dst) = codes;
+                }
+            }
+        };
+        if (wave_any(special)) emit(std::true_type{});
+        else emit(std::false_type{});
         if constexpr (MODE == FGS_SCALE_TILE_1x128) {
             if (cg == 0) {
                 float* dst = scales + (c0 / TB) * rows + r0 + 8 * rg;
@@ -270,7 +303,8 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
 
     // ---------------- column-wise (transposed) output ------------------
     if (qT) {
-        E4M3Block bcol[8];
+        uint32_t mcol[8];     // 1x128 mode: |BF16| amax bits of columns 8*cg + j
+        bool special = false;
         if constexpr (MODE == FGS_SCALE_TILE_1x128) {
             uint32_t cm[8];
 #pragma unroll
@@ -288,36 +322,52 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 8 * cg + j;
-                uint32_t m = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
-                bcol[j] = e4m3_block_from_amax_bits(m);
-            }
-            if (w == 0 && (l >> 4) == 0 && col_ok) {
-                float* dst = scalesT + tb * cols + col;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) dst[j] = bcol[j].s;
+                mcol[j] = max(max(red[0][c], red[1][c]), max(red[2][c], red[3][c]));
+                special |= e4m3_block_special(mcol[j]);
             }
         } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bcol[j] = shared_b;
+            special = shared_b.nan || shared_b.k != 1.0f;
         }
         // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+        auto emit = [&](auto special_c) {
+            constexpr bool SPECIAL = decltype(special_c)::value;
+            E4M3Block bcol[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t xb[8];
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (MODE == FGS_SCALE_TILE_1x128)
+                    bcol[j] = SPECIAL ? e4m3_block_from_amax_bits(mcol[j]) : e4m3_block_plain(mcol[j]);
+                else
+                    bcol[j] = shared_b;
+            }
+            if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+                if (w == 0 && (l >> 4) == 0 && col_ok) {
+                    float* dst = scalesT + tb * cols + col;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) xb[u] = val_bits(v[u], j);
-            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = quant8_vals(xb, bcol[j]);
-        }
+                    for (int j = 0; j < 8; ++j) dst[j] = bcol[j].s;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t xb[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) xb[u] = val_bits(v[u], j);
+                *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = quant8_vals<SPECIAL>(xb, bcol[j]);
+            }
+        };
+        if (wave_any(special)) emit(std::true_type{});
+        else emit(std::false_type{});
         __syncthreads();
         // 8 lanes write one 128-byte row of qT
+        const int chunk = t & 7;
+        uint8_t* const qT_base = qT + (c0 + (t >> 3)) * ldt + tc + 16 * chunk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int trow = 32 * i + (t >> 3), chunk = t & 7;
-            const int64_t orow = c0 + trow;
-            if (orow < cols) {
+            const int trow = 32 * i + (t >> 3);
+            if (c0 + trow < cols) {
                 uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
-                if constexpr (GROUPED) store_nt16(qT + orow * ldt + tc + 16 * chunk, d);
-                else *reinterpret_cast<uint4*>(qT + orow * ldt + tc + 16 * chunk) = d;
+                uint8_t* const dst = qT_base + 32 * i * ldt;
+                if constexpr (GROUPED) store_nt16(dst, d);
+                else *reinterpret_cast<uint4*>(dst) = d;
             }
         }
     }
