@@ -1296,6 +1296,44 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         }
     }
 
+    // ------------------------------------------ staged FP32 epilogue --
+    // MoE weight gradients: most experts hold one or two 128-token blocks,
+    // so a tile is mostly its 64 KiB of FP32 output.  Stored straight from
+    // the accumulator layout, each store instruction writes 32 bytes to each
+    // of 32 rows; through the LDS stages (free after the K loop's last
+    // barrier) each instruction writes two whole 512-byte rows.  Row r of
+    // the staged tile holds its 16-byte chunk c at slot c ^ (r & 31), so the
+    // column-wise writes and the row-wise reads both spread over the banks.
+    if constexpr (!OUT_BF16 && GROUP == GROUP_K && !MMA16) {
+        static_assert(BN == 128 && 2 * L::STAGE >= BM * BN * 4, "the FP32 tile must fit the two LDS stages");
+        // uniform over the workgroup: a full-width tile and 16-byte rows
+        if (n0 + BN <= p.N && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+            float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = WM * wm + 32 * i + (l & 31);
+                        const int c = 16 * wn + 8 * j + 2 * q + (l >> 5);
+                        *reinterpret_cast<float4*>(st + r * BN + 4 * (c ^ (r & 31))) =
+                            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    }
+            __syncthreads();
+            const int c = t & 31;
+            float* const Ct = static_cast<float*>(p.C) + c_off + m0 * p.ldc + n0 + 4 * c;
+#pragma unroll
+            for (int it = 0; it < BM / (NT / 32); ++it) {
+                const int r = (NT / 32) * it + (t >> 5);
+                if (m0 + r < m_end)
+                    *reinterpret_cast<float4*>(Ct + r * p.ldc) =
+                        *reinterpret_cast<const float4*>(st + r * BN + 4 * (c ^ (r & 31)));
+            }
+            return;
+        }
+    }
+
     // ------------------------------------------------------ epilogue --
     // acc[i][j] floats 4q .. 4q+3 are four consecutive columns of one row:
     // 32x32 tiles: row 32 i + l % 32, columns 32 j + 8 q + 4 (l / 32) ..;
