@@ -253,7 +253,8 @@ __device__ __forceinline__ void decode16_fp8(const uint4 v, f16x8& lo, f16x8& hi
 // MXFP8: 16 E4M3 codes of one 32-element block -> two BF16 8-vectors of
 // code * s, with s = 2^d (d <= 0) the block's scale relative to the
 // reference exponent; exact whenever code * s is a BF16 number (every code
-// for d >= -124).
+// for d >= -124; the GEMM's products need the stricter pair condition of
+// its MX prologue).
 __device__ __forceinline__ void decode16(const uint4 v, float s, bf16x8& lo, bf16x8& hi)
 {
     const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, false);
@@ -631,10 +632,15 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
     // MXFP8 scales.  A (per lane row m): E_A[m] = the largest E8M0 byte of
     // the row over all of K; B: one E_B for the tile (the largest byte of its
     // rows over all of K).  Every code is decoded as code * 2^(e - E) into
-    // BF16, exact whenever e - E >= -124, the FP16/BF16 matrix unit sums the
-    // exact products over all of K in FP32, and the epilogue multiplies by
-    // 2^(E_A + E_B - 254) (exact scaling), so no per-block promotion is
-    // needed.  NaN scale bytes (0xFF) are left out of the references and
+    // BF16 and the FP16/BF16 matrix unit sums the products over all of K in
+    // FP32; the epilogue multiplies by 2^(E_A + E_B - 254) (exact scaling),
+    // so no per-block promotion is needed.  Exact whenever every pair of
+    // blocks that meet has (e_A - E_A) + (e_B - E_B) >= -108: both decoded
+    // codes are then BF16 numbers and their product, at least
+    // 2^-9 2^-9 2^-108 = 2^-126, a normal FP32 number.  A pair further apart
+    // holds products below 448^2 2^-108 < 2^-90 reference units, and what it
+    // adds (rounded, flushed, or with the converter's scale saturated at
+    // 2^-127 for blocks more than 127 below the reference) stays below that.  NaN scale bytes (0xFF) are left out of the references and
     // flagged: their rows (A) and columns (B) of C are NaN, as in the
     // dequantized product.  The four bytes of a row's 128-K block are one
     // aligned 32-bit word.

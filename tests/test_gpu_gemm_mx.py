@@ -71,6 +71,66 @@ def test_mx_gemm_exponent_spread(fgs):
     _check(fgs, A, B, ah, bh, torch.float32)
 
 
+def _spread_operands(fgs, da, db, E=200, seed=41):
+    """A [64 x 256] and B [96 x 256] MX operands whose only pair of nonzero
+    blocks that meet is block 1.  Block 0 carries both references (scale
+    byte E): A's has codes, B's is all zeros, so it adds nothing.  Block 1's
+    scale byte lies da (A) and db (B) below E; its codes are positive (no
+    cancellation) and include the smallest subnormal E4M3 codes, so the
+    products reach down to 2^-18 2^(da+db) of the reference unit
+    2^(2E - 254).  Blocks 2-7 are zero."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 64, 96, 256
+    small = np.concatenate([np.arange(1, 16), rng.integers(1, 0x7F, 17)]).astype(np.uint8)
+
+    def operand(rows, d, ref_codes):
+        q = np.zeros((rows, K), dtype=np.uint8)
+        s = np.full((rows, K // 32), 127, dtype=np.uint8)
+        s[:, 0] = E
+        if ref_codes:
+            q[:, 0:32] = rng.integers(0x08, 0x7F, (rows, 32))
+        s[:, 1] = E + d
+        q[:, 32:64] = rng.permuted(np.tile(small, (rows, 1)), axis=1)
+        return q, s
+
+    qa, sa = operand(M, da, True)     # A block 0: the reference, meets B's zeros
+    qb, sb = operand(N, db, False)    # B block 0: the reference scale, zero codes
+    A = fgs.Operand(torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(), fgs.SCALE_MX32_E8M0)
+    B = fgs.Operand(torch.from_numpy(qb).cuda(), torch.from_numpy(sb).cuda(), fgs.SCALE_MX32_E8M0)
+    return A, B, oracle.dequant_mx(qa, sa), oracle.dequant_mx(qb, sb)
+
+
+@pytest.mark.parametrize("da,db", [(-54, -54), (-100, -8), (0, -108)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_mx_gemm_exponent_limit(fgs, da, db, out):
+    """At the exactness limit of the MX decode: block pairs whose exponents
+    lie da + db = -108 below the references (A: the row over all of K; B:
+    the tile's rows over all of K) decode to BF16 numbers and multiply to
+    normal FP32 numbers (the smallest, 2^-9 * 2^-9 * 2^-108 = 2^-126, is
+    reached), so the outputs, made of those products only, meet the
+    standard bound."""
+    A, B, ah, bh = _spread_operands(fgs, da, db)
+    _check(fgs, A, B, ah, bh, out)
+
+
+@pytest.mark.parametrize("da,db", [(-60, -60), (-130, 0), (-200, -40)])
+def test_mx_gemm_beyond_exponent_limit(fgs, da, db):
+    """Past the limit (da + db < -108, or a block more than 127 below its
+    reference, where the converter's power-of-two scale saturates at
+    2^-127): each such product of two codes is below 448^2 2^-108 < 2^-90
+    reference units, and what the kernel adds for it (rounded, flushed or
+    saturated) stays below 2^-90 units too, so every output is finite and
+    within the standard bound plus 32 2^-90 units per meeting block pair."""
+    A, B, ah, bh = _spread_operands(fgs, da, db)
+    c = fgs.gemm_block_scaled(A, B, torch.float32)
+    torch.cuda.synchronize()
+    c = c.cpu().numpy().astype(np.float64)
+    cref, sref = oracle.gemm_ref(ah, bh)
+    unit = 2.0 ** (2 * 200 - 254)
+    assert np.all(np.isfinite(c))
+    assert np.all(np.abs(c - cref) <= 1e-5 * sref + 1e-6 + 32 * 2.0 ** -90 * unit)
+
+
 def test_mx_gemm_zero_and_tiny_blocks(fgs):
     """All-zero 32-blocks (scale byte 127) next to blocks of tiny values."""
     M, N, K = 128, 128, 256
