@@ -137,8 +137,12 @@ __device__ __forceinline__ uint4 swiglu8(const uint4& g, const uint4& u)
 // the quantized matrix is its SwiGLU activation, computed on the load (with
 // its BF16 values optionally stored to h_out [rows x cols]), so the
 // activation is never written and read back before the down projection.
+// Occupancy: the 1x128 kernels hold sixteen block scales per thread; asked
+// for six (dense) or five (grouped) resident workgroups per CU they fit 80 or
+// 96 VGPRs without spilling (101 unconstrained: four workgroups).  The other
+// modes use 49.
 template <int MODE, bool GROUPED, bool SWIGLU = false>   // MODE: FGS_SCALE_TILE_1x128 | FGS_SCALE_BLOCK_128x128 | FGS_SCALE_TENSOR
-__global__ __launch_bounds__(256) void quant_e4m3_kernel(
+__global__ __launch_bounds__(256, GROUPED ? 5 : 6) void quant_e4m3_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, float* __restrict__ scales,
     uint8_t* __restrict__ qT, float* __restrict__ scalesT,
@@ -329,29 +333,24 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(
             special = shared_b.nan || shared_b.k != 1.0f;
         }
         // codes of column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+        // one column block's constants live at a time (eight at once cost
+        // the 1x128 kernel occupancy)
         auto emit = [&](auto special_c) {
             constexpr bool SPECIAL = decltype(special_c)::value;
-            E4M3Block bcol[8];
+            const bool scale_writer = w == 0 && (l >> 4) == 0 && col_ok;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                if constexpr (MODE == FGS_SCALE_TILE_1x128)
-                    bcol[j] = SPECIAL ? e4m3_block_from_amax_bits(mcol[j]) : e4m3_block_plain(mcol[j]);
-                else
-                    bcol[j] = shared_b;
-            }
-            if constexpr (MODE == FGS_SCALE_TILE_1x128) {
-                if (w == 0 && (l >> 4) == 0 && col_ok) {
-                    float* dst = scalesT + tb * cols + col;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) dst[j] = bcol[j].s;
+                E4M3Block b;
+                if constexpr (MODE == FGS_SCALE_TILE_1x128) {
+                    b = SPECIAL ? e4m3_block_from_amax_bits(mcol[j]) : e4m3_block_plain(mcol[j]);
+                    if (scale_writer) scalesT[tb * cols + col + j] = b.s;
+                } else {
+                    b = shared_b;
                 }
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
                 uint32_t xb[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) xb[u] = val_bits(v[u], j);
-                *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = quant8_vals<SPECIAL>(xb, bcol[j]);
+                *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) = quant8_vals<SPECIAL>(xb, b);
             }
         };
         if (wave_any(special)) emit(std::true_type{});
