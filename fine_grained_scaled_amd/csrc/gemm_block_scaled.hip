@@ -56,6 +56,8 @@
 // chunk, 256 bytes) touches each of the 64 LDS banks once.  MFMA operands
 // are swapped (B fragment first) so each lane's 16 accumulators share one
 // row m: the 1x128 A scale is one value per lane and per sub-tile row.
+#include <algorithm>
+#include <climits>
 #include <cstdio>
 #include <type_traits>
 
@@ -136,6 +138,7 @@ struct GemmParams {
     int32_t tiles_m, tiles_n;
     uint8_t* q_out;               // BF16-out launches: 1x128 E4M3 codes of the BF16 output, or nullptr
     float* s_out;                 //   and their scales [N/128][M]
+    int32_t grp_lo, grp_hi;       // row groups: this launch takes the groups of grp_lo <= rows < grp_hi
 };
 
 // FP16 x FP16 MFMA, 32x32 outputs, 16-deep K, FP32 accumulate.
@@ -323,6 +326,7 @@ struct Shape {
 using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
+constexpr int32_t kWideRows = 256;      // row groups this long take ShapeWide (exact path)
 
 // SCW: scale words per tile row and K block staged with the codes (MX: the
 // four E8M0 bytes; NVFP4: the eight E4M3 bytes as two words); word h of tile
@@ -437,7 +441,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
             int cnt = 0;
             if (g < p.G) {
                 const int32_t o0 = p.offsets[g], o1 = p.offsets[g + 1];
-                if (o0 >= 0 && o1 >= o0 && o1 <= p.M) cnt = (o1 - o0 + BM - 1) / BM;
+                if (o0 >= 0 && o1 >= o0 && o1 <= p.M && o1 - o0 >= p.grp_lo && o1 - o0 < p.grp_hi)
+                    cnt = (o1 - o0 + BM - 1) / BM;
             }
             return cnt;
         };
@@ -1387,8 +1392,16 @@ template <class S, int AMODE, int BMODE, int GROUP, int ELEMS = 0, bool MMA8 = f
 hipError_t launch_modes(GemmParams p, const GemmArgs& a, bool bf16, hipStream_t s)
 {
     p.tiles_n = (int32_t)((a.N + S::BN - 1) / S::BN);
-    // row groups: every group can add one partial m-tile
-    p.tiles_m = (int32_t)((a.M + S::BM - 1) / S::BM + (GROUP == GROUP_M ? a.G : 0));
+    // row groups: every group can add one partial m-tile; a launch that
+    // takes only groups of at least grp_lo rows holds at most M / grp_lo of
+    // them, one that takes groups below grp_hi rows at most
+    // ceil((grp_hi - 1) / BM) tiles per group
+    int64_t tm = (a.M + S::BM - 1) / S::BM;
+    if constexpr (GROUP == GROUP_M) {
+        tm += p.grp_lo > 0 ? std::min<int64_t>(a.G, a.M / p.grp_lo) : a.G;
+        if (p.grp_hi < INT32_MAX) tm = std::min<int64_t>(tm, (int64_t)a.G * ((p.grp_hi - 1 + S::BM - 1) / S::BM));
+    }
+    p.tiles_m = (int32_t)tm;
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * (GROUP == GROUP_K ? a.G : 1);
     const dim3 grid((unsigned)tiles);
     // the E4M3-output epilogue exists for BF16 output on the exact path of
@@ -1521,6 +1534,8 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
     p.T = a.T;
     p.q_out = a.q_out;
     p.s_out = a.s_out;
+    p.grp_lo = 0;
+    p.grp_hi = INT32_MAX;
     if (a.M == 0 || a.N == 0) return hipSuccess;
     const bool bf16 = a.out_bf16 != 0;
     if (a.fp8_mma && a.q_out) return hipErrorInvalidValue;   // no E4M3-output epilogue on the FP8 instructions
@@ -1543,7 +1558,19 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128) {
             if (a.fp8_mma)
                 return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, true>(p, a, bf16, stream);
-            return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(p, a, bf16, stream);
+            // Groups of at least kWideRows rows take the 256 x 256 tile with
+            // 16x16 output tiles, the smaller ones the 128 x 128 tile: two
+            // launches on the stream, each one's device schedule skipping the
+            // other's groups.  Measured per tile: long groups 1.11-1.16 PF
+            // on the 256 x 256 tile against 0.93-0.98 on the 128 x 128 one;
+            // groups of 16-64 rows stream their weights at 4.0-4.3 TB/s on
+            // the 128 x 128 tile, 3.3-3.4 on the 256 x 256 one.
+            GemmParams ps = p, pl = p;
+            ps.grp_hi = kWideRows;
+            pl.grp_lo = kWideRows;
+            const hipError_t e = launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(ps, a, bf16, stream);
+            if (e != hipSuccess) return e;
+            return launch_modes<ShapeWide, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(pl, a, bf16, stream);
         }
         return hipErrorInvalidValue;
     }
