@@ -1556,8 +1556,6 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
         p.b_group_stride = a.N * a.B.ld;
         p.sb_group_stride = ((a.N + 127) / 128) * (a.K / BK);
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128) {
-            if (a.fp8_mma)
-                return launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, true>(p, a, bf16, stream);
             // Groups of at least kWideRows rows take the 256 x 256 tile with
             // 16x16 output tiles, the smaller ones the 128 x 128 tile: two
             // launches on the stream, each one's device schedule skipping the
@@ -1565,12 +1563,17 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
             // on the 256 x 256 tile against 0.93-0.98 on the 128 x 128 one;
             // groups of 16-64 rows stream their weights at 4.0-4.3 TB/s on
             // the 128 x 128 tile, 3.3-3.4 on the 256 x 256 one.
+            // The FP8 matrix instructions take the same split.
             GemmParams ps = p, pl = p;
             ps.grp_hi = kWideRows;
             pl.grp_lo = kWideRows;
-            const hipError_t e = launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(ps, a, bf16, stream);
-            if (e != hipSuccess) return e;
-            return launch_modes<ShapeWide, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M>(pl, a, bf16, stream);
+            auto split = [&](auto mma8) -> hipError_t {
+                constexpr bool M8 = decltype(mma8)::value;
+                const hipError_t e = launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(ps, a, bf16, stream);
+                if (e != hipSuccess) return e;
+                return launch_modes<ShapeWide, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(pl, a, bf16, stream);
+            };
+            return a.fp8_mma ? split(std::true_type{}) : split(std::false_type{});
         }
         return hipErrorInvalidValue;
     }
