@@ -84,6 +84,42 @@ __device__ __forceinline__ uint2 delayed_code8(const uint32_t xb[8], float s)
                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
 }
 
+// The same codes for finite x and a scale in [2^-60, 2^60], without the
+// per-element IEEE division.  x is first clamped to +-t, t = fl32(2 fmax s):
+// a quotient beyond the clamp saturates either way, and within it the
+// quotient stays far from overflow.  The quotient is Markstein's correction
+// from r = RN(1/s): q0 = x r, e = q0 s - x (exact), q = q0 - e r.  For every
+// BF16 significand of x and every FP32 significand of s (all 2^31 pairs with
+// sign, x and s in [1, 2), checked on the host) it equals IEEE x / s, and
+// each step is exact under scaling by powers of two while its operands and
+// results stay normal.  They do wherever the code can differ from 0: there
+// |q| >= 2^-17 and s >= 2^-60, so |x| >= 2^-77 and the residual is exact.
+// The sign of x, -0 included, carries through the correction.
+template <bool E5M2>
+__device__ __forceinline__ uint2 delayed_code8_fast(const uint32_t xb[8], float s, float r, float t)
+{
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float x = __builtin_amdgcn_fmed3f(as_f32(xb[j]), -t, t);
+        const float q0 = x * r;
+        const float e = __builtin_fmaf(q0, s, -x);
+        y[j] = __builtin_fmaf(-e, r, q0);
+    }
+    if constexpr (E5M2) {
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            c[j] = ((as_u32(y[j]) >> 24) & 0x80u) | e5m2_code_abs(__builtin_fminf(__builtin_fabsf(y[j]), 57344.0f));
+        return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                          c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], -448.0f, 448.0f);
+        return make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
+    }
+}
+
 // One workgroup: s from the history, then the slot is cleared for this
 // step's amax (after every thread has read the history).
 __global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ hist, int32_t H, int32_t slot,
@@ -144,14 +180,27 @@ __global__ __launch_bounds__(256) void quant_delayed_kernel(
     if (l == 0) red[w] = m;
 
     // the codes of the thread's 8 x 8 values, computed once: row u is c[u]
-    // (byte j = column j); the column-wise output is their byte transpose
+    // (byte j = column j); the column-wise output is their byte transpose.
+    // m is the wave's amax: the branch is uniform across the wave.
     uint2 c[8];
+    if (s >= 0x1p-60f && s <= 0x1p60f && m < 0x7F80u) {
+        const float r = 1.0f / s;                        // IEEE division, once
+        const float t = (E5M2 ? 2.0f * 57344.0f : 2.0f * 448.0f) * s;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        uint32_t xb[8];
+        for (int u = 0; u < 8; ++u) {
+            uint32_t xb[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
-        c[u] = delayed_code8<E5M2>(xb, s);
+            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+            c[u] = delayed_code8_fast<E5M2>(xb, s, r, t);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            uint32_t xb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+            c[u] = delayed_code8<E5M2>(xb, s);
+        }
     }
     if (q) {
 #pragma unroll

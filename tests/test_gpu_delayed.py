@@ -85,6 +85,23 @@ def test_delayed_quant_special_values(fgs, elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("log2_scale", [-61, -60, 60, 61])
+def test_delayed_quant_scale_range_edges(fgs, elem, log2_scale):
+    """Scales on either side of the kernel's fast-path range [2^-60, 2^60]
+    (outside it every quotient takes the IEEE division): the history's max is
+    fmax * 2^log2_scale, so s is that power of two exactly, and x spans the
+    code range around it (with saturating outliers), zeros and -0 included."""
+    fmax = F32(57344.0) if elem == "e5m2" else F32(448.0)
+    xf = oracle.bf16_bits_to_f32(synth.activations(256, 256, seed=63 + log2_scale)).astype(np.float64)
+    xf[9, :] *= 1e5                 # saturates in either format
+    xf *= np.ldexp(1.0, log2_scale)
+    xf[7, :] = 0.0
+    xf[7, ::2] = -0.0
+    xb = synth.f32_to_bf16_bits(xf.astype(F32))
+    _check(fgs, xb, elem, [F32(np.ldexp(fmax, log2_scale)), F32(0.0)], 1)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 def test_delayed_rolling_window(fgs, elem):
     """Five steps on one device history of three entries (slot = step % 3):
     every step's codes, scale and history match the oracle run on the
