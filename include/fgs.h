@@ -225,9 +225,12 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *     sA * sB and added into FP32 accumulators once per block (promotion);
  *   E4M3 with MX32_E8M0 on both: each code decoded exactly to BF16 as
  *     code * 2^(e - E) (E the largest non-NaN scale exponent of the row (A)
- *     or of the workgroup tile's rows (B) over all of K; exact while
- *     e - E >= -124), BF16 MFMA with FP32 accumulation over all of K, then
- *     2^(E_A + E_B) applied by exponent arithmetic; a NaN scale byte makes
+ *     or of the workgroup tile's rows (B) over all of K), BF16 MFMA with
+ *     FP32 accumulation over all of K, then 2^(E_A + E_B) applied by
+ *     exponent arithmetic; exact while every pair of meeting blocks has
+ *     (e_A - E_A) + (e_B - E_B) >= -108 (each decoded code a BF16 number,
+ *     each product a normal FP32 number); a pair further apart adds less
+ *     than 2^-90 * 2^(E_A + E_B - 254) per product; a NaN scale byte makes
  *     its A row or B column of C NaN;
  *   E4M3 or E5M2 on each side with TENSOR on both (the delayed-scaling
  *     recipes; E5M2 gradients against E4M3 weights or activations): every
