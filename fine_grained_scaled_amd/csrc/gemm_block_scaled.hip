@@ -420,7 +420,11 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel
         // workgroups are dealt round-robin to the 8 XCDs: give each XCD a
         // contiguous range of the tile order so its L2 sees neighbouring tiles
         if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
-        const int GM = 8;
+        // the order runs down GM m-tiles, then to the next n-tile: with 32
+        // workgroups per XCD in flight, GM = 4 keeps about 4 A panels and 8
+        // B panels live in the XCD's L2 (on the Llama-3-8B step, same box:
+        // GM 4 1263-1287 TFLOP/s, 2 or 6 1255-1260, 8 1228-1276, 16 1184-1222)
+        const int GM = 4;
         const int group = id / (GM * p.tiles_n);
         const int first_m = group * GM;
         const int gsz = min(p.tiles_m - first_m, GM);
