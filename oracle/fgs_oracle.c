@@ -210,11 +210,14 @@ uint8_t orc_e2m1_encode_rne(float y)
 
 /*
  * Stochastic rounding to E2M1 with a 32-bit random word r.
- * READING [NVFP4 "How it works" names stochastic rounding only]: with
- * lo <= |y| < hi the two neighbouring magnitudes, round up iff
- * (r >> 8) < p * 2^24 where p = (|y| - lo) / (hi - lo).  p * 2^24 is an
- * exact integer-or-fraction in double; values already representable never
- * move.  |y| >= 6 saturates.
+ * READING [NVFP4 "How it works" names stochastic rounding only, not its
+ * resolution]: with lo <= |y| < hi the two neighbouring magnitudes and
+ * p = (|y| - lo) / (hi - lo), round up iff (r >> 10) < floor(p * 2^22).
+ * The 22 high bits of r are the uniform variate and p is resolved to 22
+ * bits, so P(up) = floor(p * 2^22) / 2^22: exactly p for |y| >= 1, where
+ * p * 2^22 is an integer, and less than 2^-22 below p for |y| < 1.  p and
+ * floor(p * 2^22) are exact in double.  Values already representable never
+ * move; |y| >= 6 saturates.
  */
 uint8_t orc_e2m1_encode_sr(float y, uint32_t r)
 {
@@ -231,7 +234,7 @@ uint8_t orc_e2m1_encode_sr(float y, uint32_t r)
         return sign | (uint8_t)i;
     hi = E2M1_MAG[i + 1];
     p = (a - lo) / (hi - lo);
-    if ((double)(r >> 8) < p * 16777216.0)
+    if ((double)(r >> 10) < floor(p * 4194304.0))
         return sign | (uint8_t)(i + 1);
     return sign | (uint8_t)i;
 }

@@ -91,6 +91,63 @@ def test_sr_keeps_representable_values():
     assert np.array_equal(tab[oracle.e2m1_encode(vals, words)], tab)
 
 
+# FP32 bit patterns across every E2M1 interval: plain fractions of a step,
+# values just above a grid point or just below the next, values with low
+# mantissa bits below 1 (where p * 2^22 is not an integer), the smallest
+# subnormal, and 3.4 (an inexact FP32 value)
+SR_BITS = [0x3DCCCCCD, 0x3E800001, 0x3EFFFFFF, 0x3F000001, 0x3F000003, 0x3F2AAAAB, 0x3F7FFFFF,
+           0x3F800001, 0x3FA00000, 0x3FD55555, 0x3FFFFFFF, 0x40200001, 0x4059999A, 0x409FFFFF,
+           0x40A00000, 0x40BFFFFF, 0x3A83126F, 0x00000001]
+SR_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+@pytest.mark.parametrize("bits", SR_BITS)
+def test_sr_up_count_over_all_variates(bits):
+    """Over every one of the 2^22 values of the variate (r >> 10; the low 10
+    bits of r random), SR rounds y up for exactly floor(p * 2^22) of them,
+    p = (|y| - lo) / (hi - lo) taken in exact rational arithmetic.  For
+    |y| >= 1 that count is p * 2^22 itself, so the mean of SR(y) over the
+    variates is y exactly; below 1 it falls short of y by less than 2^-22
+    of the grid step and never exceeds it."""
+    y = np.array([bits], dtype=np.uint32).view(np.float32)[0]
+    yq = Fraction(float(y))
+    lo = max(Fraction(v) for v in SR_GRID if Fraction(v) <= yq)
+    hi = min(Fraction(v) for v in SR_GRID if Fraction(v) > yq)
+    p = (yq - lo) / (hi - lo)
+    expect = math.floor(p * 2**22)
+    g = np.random.default_rng(bits)
+    k = np.arange(1 << 22, dtype=np.uint32)
+    r = (k << np.uint32(10)) | g.integers(0, 1024, k.size, dtype=np.uint64).astype(np.uint32)
+    tab = oracle.e2m1_decode_table()
+    for sign in (1.0, -1.0):
+        vals = tab[oracle.e2m1_encode(np.full(k.size, sign * y, dtype=np.float32), r)].astype(np.float64)
+        assert np.all((np.abs(vals) == float(lo)) | (np.abs(vals) == float(hi)))
+        assert int(np.sum(np.abs(vals) == float(hi))) == expect
+        mean = Fraction(int(round(abs(vals).sum() * 2)), 2 * 2**22)     # vals are multiples of 1/2
+        if yq >= 1:
+            assert mean == yq
+        else:
+            assert 0 <= yq - mean < (hi - lo) / 2**22
+
+
+def test_sr_decision_uses_the_high_22_bits_monotonically():
+    """The low 10 bits of r never change a code, the all-ones word never
+    rounds up, and a smaller variate rounds up wherever a larger one does."""
+    g = np.random.default_rng(3)
+    y = (g.uniform(0.0, 6.0, 200_000) * g.choice([1.0, 1e-3], 200_000)).astype(np.float32)
+    r = g.integers(0, 2**32, y.size, dtype=np.uint64).astype(np.uint32)
+    base = oracle.e2m1_encode(y, r)
+    low = g.integers(0, 1024, y.size, dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(oracle.e2m1_encode(y, r ^ low), base)
+    down = oracle.e2m1_encode(y, np.full(y.size, 0xFFFFFFFF, np.uint32))
+    tab = oracle.e2m1_decode_table()
+    assert np.all(np.abs(tab[down]) <= np.abs(y))                     # all-ones: the lower neighbour
+    smaller = ((r >> np.uint32(10)) // np.uint32(3)) << np.uint32(10)
+    up = base != down
+    assert np.all(oracle.e2m1_encode(y, smaller)[up] == base[up])
+    assert 0.2 < up.mean() < 0.8
+
+
 def test_sr_words_uniform_and_seeded():
     n = 1 << 20
     idx = np.arange(n, dtype=np.uint64)
