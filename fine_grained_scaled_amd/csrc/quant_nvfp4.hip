@@ -19,8 +19,9 @@
 // (-1 where bit j of sign_mask is set), four butterfly stages with strides
 // 1, 2, 4, 8 ((a, b) -> (a + b, a - b) in FP32), then the exact factor 1/4.
 // Stochastic rounding of |y| between neighbours lo < hi: round up iff
-// (r >> 8) < p * 2^24 with p = (|y| - lo) / (hi - lo) (exact), where the
-// random word of source element i (row * cols + col of x) is
+// (r >> 10) < floor(p * 2^22) with p = (|y| - lo) / (hi - lo) (the 22 high
+// bits of r against p resolved to 22 bits), where the random word of
+// source element i (row * cols + col of x) is
 // r = fmix32(lo32(i) ^ fmix32(lo32(seed) ^ fmix32(hi32(seed) ^ hi32(i)))),
 // fmix32 being MurmurHash3's 32-bit finalizer.
 //
@@ -68,13 +69,16 @@ __device__ __forceinline__ float xor16(float v)
 
 // Random Hadamard transform of the 16-chunk whose elements 8*hpos .. 8*hpos+7
 // this lane holds (the partner lane holds the other 8), without the final
-// factor 1/4: z holds d (.) x on entry (the signs are applied to the packed
-// BF16 pairs, see rht_pair_signs) and 4 * (H d x) on return.  The caller
-// folds the exact 1/4 into the block amax and the divisor.  sgn is +1 for
-// hpos 0 and -1 for hpos 1: the stride-8 stage is other + sgn * z, one FMA
-// whose product by +-1 is exact.
+// factor 1/4: z holds d (.) x on entry, negated on the hpos 1 lane (the
+// signs are applied to the packed BF16 pairs, see rht_pair_signs), and
+// 4 * (H d x) on return.  The caller folds the exact 1/4 into the block amax
+// and the divisor.  The three in-lane stages carry the negation through
+// exactly (nearest rounding is symmetric), so the stride-8 stage is
+// z + s * partner with s = -1 on hpos 0 (giving a + b) and +1 on hpos 1
+// (giving a - b), one FMA whose product by +-1 is exact.  Row-wise the
+// partner is the neighbouring lane, read through a DPP operand of the FMA.
 template <bool ROWWISE>
-__device__ __forceinline__ void rht16x4(float z[8], float sgn)
+__device__ __forceinline__ void rht16x4(float z[8], float s)
 {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
@@ -88,23 +92,25 @@ __device__ __forceinline__ void rht16x4(float z[8], float sgn)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float other = ROWWISE ? xor1(z[i]) : xor16(z[i]);
-        z[i] = __builtin_fmaf(sgn, z[i], other);
+        z[i] = __builtin_fmaf(other, s, z[i]);
     }
 }
 
-// XOR masks that apply the RHT signs to packed BF16 pairs.  Row-wise chunks
-// run along the 8 columns of a lane (positions 8*hpos + j, pair k = columns
-// 2k, 2k+1); column-wise chunks run along its 8 rows (position 8*hpos + u,
-// the same sign for every column of row u).
+// XOR masks that apply the RHT signs to packed BF16 pairs, and negate every
+// element on the hpos 1 lane (see rht16x4).  Row-wise chunks run along the
+// 8 columns of a lane (positions 8*hpos + j, pair k = columns 2k, 2k+1);
+// column-wise chunks run along its 8 rows (position 8*hpos + u, the same
+// sign for every column of row u).
 __device__ __forceinline__ void rht_pair_signs(uint32_t sign_mask, int hpos_row, int hpos_col,
                                                uint32_t row_m[4], uint32_t col_m[8])
 {
     const uint32_t sr = sign_mask >> (8 * hpos_row), sc = sign_mask >> (8 * hpos_col);
+    const uint32_t nrow = hpos_row ? 0x80008000u : 0u, ncol = hpos_col ? 0x80008000u : 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        row_m[k] = (((sr >> (2 * k)) & 1u) << 15) | (((sr >> (2 * k + 1)) & 1u) << 31);
+        row_m[k] = ((((sr >> (2 * k)) & 1u) << 15) | (((sr >> (2 * k + 1)) & 1u) << 31)) ^ nrow;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) col_m[u] = ((sc >> u) & 1u) * 0x80008000u;
+    for (int u = 0; u < 8; ++u) col_m[u] = (((sc >> u) & 1u) * 0x80008000u) ^ ncol;
 }
 
 __device__ __forceinline__ uint4 xor4(const uint4& v, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
@@ -151,26 +157,68 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a)
            (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
-// E2M1 magnitude code of a in [0, 6] by stochastic rounding with word r: the
-// lower neighbour lo <= a, plus one iff (r >> 8) < p * 2^24 with
-// p = (a - lo) / (hi - lo).  Two exact forms, selected on a:
-//  * a >= 1 (FP32 bits b): the grid {1, 1.5, 2, 3, 4, 6} keeps one mantissa
-//    bit, so lo's code is (b >> 22) - 252 and p * 2^24 = (b mod 2^22) * 4,
-//    an integer; (r >> 8) < p * 2^24 is then the unsigned r < (b << 10).
-//  * a < 1 (grid {0, 0.5, 1}): u = 2a is exact, lo's code is [u >= 1] and
-//    p = u - floor(u) (exact); the comparison is taken in FP32, where both
-//    (r >> 8) and p * 2^24 are exact.
-// Equal to the segment-by-segment rule for every FP32 a in [0, 6], checked
-// on the host at each a's decision threshold (and one either side) plus
-// random words: 1.3e10 pairs.
-__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r)
+// Stochastic E2M1 codes of 8 values (element 2k in the low nibble of byte
+// k, 2k + 1 in the high nibble) from v_cvt_scalef32_sr_pk_fp4_f32 at unit
+// scale.  The instruction converts a pair (lo slot, hi slot) into one byte;
+// the lo slot rounds up iff (s >> 10) + floor(p * 2^22) >= 2^22 for its
+// random operand s, the hi slot the same with rotl(s, 1), and both keep the
+// sign (so -0 gives code 8) and saturate at 6.  With s = ~r the lo slot
+// rounds up iff (r >> 10) < floor(p * 2^22), the rule above; the hi slot
+// gets it with s = rotr(~r, 1).  Each pair is therefore converted twice,
+// once with the even element's operand and once with the odd one's, and
+// the nibbles are merged with a bitfield insert: every element rounds with
+// its own word.  Checked on gfx950 against the rule in integer arithmetic
+// for every FP32 magnitude in [0, 6], both signs, with words at and beside
+// each decision boundary, in every one of the 8 positions.  Written as
+// inline assembly because the compiler builtin does not tie its old-value
+// operand to the destination, which the byte select relies on to keep the
+// other three bytes.  nr holds ~r for the 8 values.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ void cvt_sr_fp4_byte(uint32_t& w, f32x2 v, uint32_t s)
 {
-    const uint32_t b = as_u32(a);
-    const uint32_t hi = (b >> 22) - 252u + (r < (b << 10) ? 1u : 0u);
-    const float u = a * 2.0f;
-    const float p = __builtin_amdgcn_fractf(u);
-    const uint32_t lo = (u >= 1.0f ? 1u : 0u) + ((float)(r >> 8) < p * 16777216.0f ? 1u : 0u);
-    return a >= 1.0f ? hi : lo;
+    if constexpr (SEL == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(v), "v"(s));
+    else if constexpr (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(w) : "v"(v), "v"(s));
+    else if constexpr (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(v), "v"(s));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(w) : "v"(v), "v"(s));
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float v[8], const uint32_t nr[8])
+{
+    uint32_t ev, od;       // every byte is written by the four calls below
+    asm("" : "=v"(ev));
+    asm("" : "=v"(od));
+    cvt_sr_fp4_byte<0>(ev, f32x2{v[0], v[1]}, nr[0]);
+    cvt_sr_fp4_byte<0>(od, f32x2{v[0], v[1]}, __builtin_amdgcn_alignbit(nr[1], nr[1], 1));
+    cvt_sr_fp4_byte<1>(ev, f32x2{v[2], v[3]}, nr[2]);
+    cvt_sr_fp4_byte<1>(od, f32x2{v[2], v[3]}, __builtin_amdgcn_alignbit(nr[3], nr[3], 1));
+    cvt_sr_fp4_byte<2>(ev, f32x2{v[4], v[5]}, nr[4]);
+    cvt_sr_fp4_byte<2>(od, f32x2{v[4], v[5]}, __builtin_amdgcn_alignbit(nr[5], nr[5], 1));
+    cvt_sr_fp4_byte<3>(ev, f32x2{v[6], v[7]}, nr[6]);
+    cvt_sr_fp4_byte<3>(od, f32x2{v[6], v[7]}, __builtin_amdgcn_alignbit(nr[7], nr[7], 1));
+    return (ev & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
+}
+
+// E2M1 codes of 8 quotients, packed: stochastic from e2m1_sr_pack8, or RNE
+// from v_cvt_scalef32_pk_fp4_f32 (unit scale), which equals the RNE encoder
+// with the sign of the input for every FP32 value in [-6, 6] and saturates
+// at 6 beyond (both checked exhaustively on gfx950).
+template <bool SR>
+__device__ __forceinline__ uint32_t e2m1_pack8(const float v[8], const uint32_t nr[8])
+{
+    if constexpr (SR) {
+        return e2m1_sr_pack8(v, nr);
+    } else {
+        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+        return w;
+    }
 }
 
 struct TensorScale {
@@ -208,11 +256,12 @@ __device__ __forceinline__ float div_rn(float a, float d, float r)
 // (so -0 gives the negative-zero code 0x8) and saturated at 6.  A block with
 // amax_b < 2^-30 divides y * 2^64 by d * 2^64 (both exact), which keeps every
 // residual normal; in other blocks an element below 2^-90 has a quotient
-// below 2^-57, where RNE gives 0 and stochastic rounding makes the same
-// choice for every positive value, so its rounding cannot change a code.
-// RNE codes come from the hardware converter v_cvt_scalef32_pk_fp4_f32
-// (unit scale), which equals the RNE encoder above with the sign of the
-// input for every FP32 value in [-6, 6] (checked exhaustively on gfx950).
+// below 2^-57, where RNE gives 0 and stochastic rounding never rounds up
+// (floor(p * 2^22) = 0), so its rounding cannot change a code.  RNE codes
+// come from the hardware converter v_cvt_scalef32_pk_fp4_f32 (unit scale),
+// which equals the RNE encoder above with the sign of the input for every
+// FP32 value in [-6, 6] (checked exhaustively on gfx950); stochastic codes
+// from e2m1_sr_pack8, with nr the complements ~r of the elements' words.
 //
 // y = z / zscale: z is either the value itself (zscale 1) or four times the
 // transformed value (zscale 4, see rht16x4); amax_b is the amax of y.  The
@@ -220,7 +269,7 @@ __device__ __forceinline__ float div_rn(float a, float d, float r)
 // is exact (d <= 448 * 2^128 / 2688 leaves room for the factor 4).
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b, const TensorScale& ts,
-                                              const uint32_t rw[8], uint32_t& sb_out, float zscale)
+                                              const uint32_t nr[8], uint32_t& sb_out, float zscale)
 {
     // fl32(amax_b / (6 s_t)) by the same correction as the elements (the
     // residual is normal for amax_b >= 2^-90; smaller block maxima take IEEE
@@ -228,6 +277,27 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
     // 448 (1 + 2^-23) because amax_b <= amax_t, and the med3 clamp to 448
     // makes the cast saturate exactly as the encoder does.
     const float amb = as_f32(amax_b);
+    // Wave-uniform fast path: every lane's block has a finite amax of at
+    // least 2^-30 and a nonzero, finite d.  Then the scale quotient takes
+    // the correction, no element needs the 2^64 pre-scale, the quotients
+    // are taken on the signed values (div_by_scale: sign-symmetric and
+    // equal to div_rn on |y|, -0 kept) and the converters saturate beyond 6
+    // by themselves (checked on gfx950 for every FP32 magnitude above 6).
+    {
+        const float qs = div_rn(amb, ts.six_st, ts.r6);
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(qs, 448.0f), 0.0f, 0, false) & 0xFFu;
+        const float d = e4m3_value(sb) * ts.st;
+        const bool ok = amax_b >= 0x30800000u && amax_b < 0x7F800000u && d > 0.0f;
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+            sb_out = sb;
+            const float dk = d * zscale;
+            const float r = 1.0f / dk;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = div_by_scale(y[i], dk, r);
+            return e2m1_pack8<SR>(v, nr);
+        }
+    }
     float qs;
     if (__builtin_expect(amb >= 0x1p-90f, 1)) qs = div_rn(amb, ts.six_st, ts.r6);
     else qs = amb / ts.six_st;
@@ -250,21 +320,10 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
         q[i] = __builtin_fminf(div_rn(a, dk, r), 6.0f);
         sg[i] = as_u32(y[i]) & 0x80000000u;
     }
-    if constexpr (SR) {
-        uint32_t packed = 0;
+    float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) packed |= (e2m1_sr(q[i], rw[i]) | ((sg[i] >> 31) << 3)) << (4 * i);
-        return packed;
-    } else {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = as_f32(as_u32(q[i]) | sg[i]);
-        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
-        return w;
-    }
+    for (int i = 0; i < 8; ++i) v[i] = as_f32(as_u32(q[i]) | sg[i]);
+    return e2m1_pack8<SR>(v, nr);
 }
 
 // The counter hash's last round: r = fmix32(lo32(i) ^ mid) with
@@ -324,7 +383,7 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(
     const int64_t nbc = (cols + TB - 1) / TB, nblk = ((rows + TB - 1) / TB) * nbc;
     uint32_t row_m[4], col_m[8];
     rht_pair_signs(sign_mask, cg & 1, (l >> 4) & 1, row_m, col_m);
-    const float sgn_row = (cg & 1) ? -1.0f : 1.0f, sgn_col = ((l >> 4) & 1) ? -1.0f : 1.0f;
+    const float sgn_row = (cg & 1) ? 1.0f : -1.0f, sgn_col = ((l >> 4) & 1) ? 1.0f : -1.0f;
     const bool rht_row = rht_mask & 1, rht_col = rht_mask & 2;
 
     uint32_t plain = 0, mrow4 = 0, mcol4 = 0;     // mrow4 / mcol4: amax of 4 x the transform
@@ -422,7 +481,8 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     const TensorScale ts_col = tensor_scale_from(max(max(s_red[1][0], s_red[1][1]), max(s_red[1][2], s_red[1][3])));
     // SR: the random word of an element does not depend on the
     // orientation: hash each of the thread's 64 elements once for both
-    // outputs (the seed rounds once per row of the thread)
+    // outputs (the seed rounds once per row of the thread), kept as ~r, the
+    // converter's operand
     uint32_t W[8][8];
     if constexpr (SR) {
 #pragma unroll
@@ -430,7 +490,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
             const uint64_t i0 = (uint64_t)((r0 + 8 * rg + u) * cols + col);
             const uint32_t base = (uint32_t)i0 ^ sr_mid(seed_lo, seed_hi, i0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) W[u][j] = sr_word_at(base, j);
+            for (int j = 0; j < 8; ++j) W[u][j] = ~sr_word_at(base, j);
         }
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
@@ -445,7 +505,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
     if (q) {
         const int64_t qcols = cols / 2, nsc = cols / 16;
         const bool rht = rht_mask & 1;
-        const float sgn = (cg & 1) ? -1.0f : 1.0f, zscale = rht ? 4.0f : 1.0f;
+        const float sgn = (cg & 1) ? 1.0f : -1.0f, zscale = rht ? 4.0f : 1.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             float z[8];
@@ -477,7 +537,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(
         const int64_t nscT = rows / 16;
         const int hpos = (l >> 4) & 1;
         const bool rht = rht_mask & 2;
-        const float sgn = hpos ? -1.0f : 1.0f, zscale = rht ? 4.0f : 1.0f;
+        const float sgn = hpos ? 1.0f : -1.0f, zscale = rht ? 4.0f : 1.0f;
         if (rht) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = xor4(v[u], col_m[u], col_m[u], col_m[u], col_m[u]);
