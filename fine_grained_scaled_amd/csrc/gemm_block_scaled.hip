@@ -354,8 +354,11 @@ enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
 // the MFMA, MX scales are applied by the instruction, and the 1x128 / 128x128
 // promotion stays as above.  The instruction's own sum is not exact (see the
 // header), so its results are bounded more loosely than the default path's.
+// Four-wave workgroups (the MoE tile) run two to a CU: declaring it caps them
+// at 256 VGPRs, which puts their MFMA results in VGPRs rather than AGPRs, so
+// the promotion reads the partial sums without a copy out of the AGPRs.
 template <class S, int AMODE, int BMODE, bool OUT_BF16, int GROUP, int ELEMS = 0, bool MMA8 = false>
-__global__ __launch_bounds__(64 * S::NWM * S::NWN) void gemm_block_scaled_kernel(GemmParams p)
+__global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1) void gemm_block_scaled_kernel(GemmParams p)
 {
     constexpr int NWM = S::NWM, NWN = S::NWN;
     constexpr int NW = NWM * NWN;        // waves
