@@ -98,6 +98,45 @@ def test_nvfp4_special_values(fgs):
     _check(fgs, synth.f32_to_bf16_bits(tiny), 3, False)
 
 
+def _mixed_class_tensor():
+    """BF16 bits of a 256 x 256 tensor with amax near 2^-12 whose ordinary
+    blocks sit beside blocks of the kernel's careful path: row blocks and
+    16 x 16 squares (careful in both orientations) with amax just under
+    2^-30 (nonzero scale byte, pre-scaled quotient), scales that round to
+    zero, and zeros."""
+    g = np.random.default_rng(77)
+    f = (g.standard_normal((256, 256)) * 2.0 ** -14).astype(np.float32)
+    for r, c, lg in [(3, 16, -31.5), (3, 48, -31.0), (40, 0, -33.0), (77, 112, None), (130, 32, -31.2),
+                     (200, 240, -29.5), (255, 128, -45.0)]:
+        f[r, c:c + 16] = 0.0 if lg is None else g.standard_normal(16) * 2.0 ** lg
+    for r, c, lg in [(96, 64, -31.3), (16, 208, -40.0), (160, 160, None)]:
+        f[r:r + 16, c:c + 16] = 0.0 if lg is None else g.standard_normal((16, 16)) * 2.0 ** lg
+    return synth.f32_to_bf16_bits(f)
+
+
+def test_nvfp4_mixed_block_classes_are_covered():
+    """The fixture really holds blocks with amax below 2^-30 and a nonzero
+    scale byte, blocks whose scale byte is 0 with a nonzero amax, and
+    ordinary blocks, in the same 128 x 128 tiles (oracle, no transform)."""
+    bits = _mixed_class_tensor()
+    f = oracle.bf16_bits_to_f32(bits)
+    _, s, _ = oracle.quant_nvfp4(bits, colwise=False, rht=False, rht_seed=RHT_SEED, stochastic=False,
+                                 sr_seed=SR_SEED)
+    amax = np.abs(f).reshape(256, 16, 16).max(axis=2)
+    assert np.any((amax < 2.0 ** -30) & (amax > 0) & (s != 0))
+    assert np.any((amax > 0) & (s == 0))
+    assert np.sum(amax >= 2.0 ** -30) > 3000
+
+
+@pytest.mark.parametrize("rht_mask", [0, 3])
+@pytest.mark.parametrize("stochastic", [False, True])
+def test_nvfp4_mixed_block_classes(fgs, rht_mask, stochastic):
+    """Waves that hold one careful-path block take the careful path for all
+    their blocks, the other waves the fast one: codes, scale bytes and
+    tensor scales stay bit-exact in both orientations."""
+    _check(fgs, _mixed_class_tensor(), rht_mask, stochastic)
+
+
 def test_nvfp4_determinism(fgs):
     bits = synth.gradients(512, 512, seed=46)
     x = synth.to_torch_bf16(bits).to("cuda")
