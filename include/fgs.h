@@ -198,8 +198,10 @@ int fgs_quantize_mx(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *   rht_seed) along the quantized dimension of the row-wise output; bit 1:
  *   same for the column-wise output.  The transform precedes the amax.
  * round    FGS_ROUND_RNE or FGS_ROUND_STOCHASTIC (applies to both outputs);
- *   the SR word of an element hashes sr_seed with its linear index
- *   row * cols + col in x.
+ *   the SR word r of an element hashes sr_seed with its linear index
+ *   row * cols + col in x, and |y| between neighbours lo < hi rounds up iff
+ *   (r >> 10) < floor(p * 2^22), p = (|y| - lo) / (hi - lo): the stochastic
+ *   rounding is resolved to 22 bits.
  * Row-wise (needs cols % 16 == 0): q [rows x cols/2], scales u8 [rows][cols/16].
  * Column-wise (needs rows % 128 == 0): qT [cols x rows/2], scalesT u8
  *   [cols][rows/16].
