@@ -456,39 +456,59 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
             }
             return cnt;
         };
-        int my_tiles = 0;
-        for (int g = t; g < p.G; g += NT) my_tiles += m_tiles(g);
-        s_scan[t] = my_tiles;
-        __syncthreads();
-        for (int d = NT / 2; d > 0; d >>= 1) {
-            if (t < d) s_scan[t] += s_scan[t + d];
+        // Prefix sums of the groups' tile counts, NT groups at a time: an
+        // inclusive scan inside each wave (shuffles, no barrier), then the
+        // wave totals through LDS (two barriers per chunk of groups).
+        // Returns the chunk's total; cnt and excl are this thread's group's
+        // count and exclusive prefix within the chunk.
+        auto chunk_scan = [&](int chunk, int& cnt, int& excl) -> int {
+            cnt = m_tiles(chunk + t);
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d);
+                if (l >= d) incl += y;
+            }
+            if (l == 63) s_scan[w] = incl;
             __syncthreads();
+            int before = 0, all = 0;
+            for (int i = 0; i < NW; ++i) {
+                const int c = s_scan[i];
+                all += c;
+                if (i < w) before += c;
+            }
+            __syncthreads();                          // s_scan is written again by the next chunk
+            excl = before + incl - cnt;
+            return all;
+        };
+        if (t == 0) s_sel[0] = -1;                    // ordered before any pick by the scan's barriers
+        int total_tiles = 0, cnt0 = 0, excl0 = 0, all0 = 0;
+        for (int chunk = 0; chunk < p.G; chunk += NT) {
+            int cnt, excl;
+            const int all = chunk_scan(chunk, cnt, excl);
+            if (chunk == 0) {
+                cnt0 = cnt;
+                excl0 = excl;
+                all0 = all;
+            }
+            total_tiles += all;
         }
-        const int64_t total = (int64_t)s_scan[0] * p.tiles_n;
-        __syncthreads();
+        const int64_t total = (int64_t)total_tiles * p.tiles_n;
         if ((int64_t)blockIdx.x >= total) return;                  // beyond the last tile
         const int64_t vb = (int64_t)blockIdx.x >> 3, vbase = ((vb >> 1) << 3) + (blockIdx.x & 7);
         const int64_t v = (vb & 1) ? total - 1 - vbase : vbase;
+        // the group that holds tile v (exactly one thread finds it); the
+        // first chunk's scan is reused, later chunks are scanned again
         int running = 0;
-        if (t == 0) s_sel[0] = -1;
         for (int chunk = 0; chunk < p.G; chunk += NT) {
-            const int g = chunk + t;
-            const int cnt = m_tiles(g);
-            s_scan[t] = cnt;
-            __syncthreads();
-            for (int d = 1; d < NT; d <<= 1) {
-                const int add = (t >= d) ? s_scan[t - d] : 0;
-                __syncthreads();
-                s_scan[t] += add;
-                __syncthreads();
+            int cnt = cnt0, excl = excl0, all = all0;
+            if (chunk > 0) all = chunk_scan(chunk, cnt, excl);
+            const int ex = running + excl;
+            if (cnt > 0 && v >= (int64_t)ex * p.tiles_n && v < (int64_t)(ex + cnt) * p.tiles_n) {
+                s_sel[0] = chunk + t;
+                s_sel[1] = ex;
             }
-            const int excl = running + s_scan[t] - cnt;
-            if (cnt > 0 && v >= (int64_t)excl * p.tiles_n && v < (int64_t)(excl + cnt) * p.tiles_n) {
-                s_sel[0] = g;
-                s_sel[1] = excl;
-            }
-            running += s_scan[NT - 1];
-            __syncthreads();
+            running += all;
         }
         __syncthreads();
         const int g = s_sel[0];
