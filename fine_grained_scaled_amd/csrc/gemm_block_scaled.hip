@@ -419,6 +419,9 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
     const uint8_t* Bp = p.B;
     const float* sBp = p.sB;
     int64_t nkb = p.K / BK;
+    // contraction groups: tokens of the group's last K block (1 .. BK); the
+    // k-steps past them multiply zero codes and are skipped
+    int kv_last = BK;
     int64_t c_off = 0;                    // elements from C to this tile's C matrix
     if constexpr (GROUP == GROUP_NONE) {
         int id = blockIdx.x;
@@ -547,6 +550,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
         const bool ok = o0 >= 0 && o1 >= o0 && (int64_t)o1 <= p.T;
         const int64_t kb0 = ok ? (int64_t)(o0 >> 7) + g : 0;
         nkb = ok ? (o1 - o0 + BK - 1) / BK : 0;
+        if (nkb > 0) kv_last = (int)((o1 - o0) - (nkb - 1) * BK);
         Ap = p.A + kb0 * BK;
         Bp = p.B + kb0 * BK;
         sAp = p.sA + kb0 * p.M;
@@ -1126,6 +1130,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
                 constexpr int FB = (ELEMS & 2) ? 1 : 0, FA = (ELEMS & 1) ? 1 : 0;
     #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
+                    if (GROUP == GROUP_K && kb == nkb - 1 && 64 * s2 >= kv_last) continue;
                     const int c0 = ((4 * s2 + half) ^ swz) << 4, c1 = ((4 * s2 + 2 + half) ^ swz) << 4;
                     i32x8 af[TI], bf[TJ];
                     int ea8[TI], eb8[TJ];
@@ -1156,6 +1161,7 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
             } else
     #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
+                if (GROUP == GROUP_K && kb == nkb - 1 && 32 * ks >= kv_last) continue;
                 const int co = ((2 * ks + half) ^ swz) << 4;
                 if constexpr (MX) {
                     // k-steps 2ks, 2ks+1 are MX block ks of this 128-K block
