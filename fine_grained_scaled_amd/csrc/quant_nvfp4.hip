@@ -252,8 +252,9 @@ __device__ __forceinline__ float div_rn(float a, float d, float r)
 
 // Codes of 8 values of one 16-block whose (two-lane) amax bits are amax_b.
 // Returns the 8 nibbles packed (element 2j in the low nibble) and the scale
-// byte.  The quotient y / d is taken on |y| with the sign put back bitwise
-// (so -0 gives the negative-zero code 0x8) and saturated at 6.  A block with
+// byte.  Waves whose blocks are all ordinary take the fast path below; on
+// the careful path the quotient y / d is taken on |y| with the sign put back
+// bitwise (so -0 gives the negative-zero code 0x8) and saturated at 6.  A block with
 // amax_b < 2^-30 divides y * 2^64 by d * 2^64 (both exact), which keeps every
 // residual normal; in other blocks an element below 2^-90 has a quotient
 // below 2^-57, where RNE gives 0 and stochastic rounding never rounds up
@@ -274,8 +275,8 @@ __device__ __forceinline__ uint32_t nv_block8(const float y[8], uint32_t amax_b,
     // fl32(amax_b / (6 s_t)) by the same correction as the elements (the
     // residual is normal for amax_b >= 2^-90; smaller block maxima take IEEE
     // division), then the hardware E4M3 cast: the quotient is at most
-    // 448 (1 + 2^-23) because amax_b <= amax_t, and the med3 clamp to 448
-    // makes the cast saturate exactly as the encoder does.
+    // 448 (1 + 2^-23) because amax_b <= amax_t, and the min with 448 makes
+    // the cast saturate exactly as the encoder does.
     const float amb = as_f32(amax_b);
     // Wave-uniform fast path: every lane's block has a finite amax of at
     // least 2^-30 and a nonzero, finite d.  Then the scale quotient takes
