@@ -61,6 +61,19 @@ __device__ __forceinline__ uint32_t e5m2_code_abs(float a)
     return c < 0x7Bu ? c : 0x7Bu;
 }
 
+// Four E5M2 codes by the hardware converter v_cvt_pk_bf8_f32 (OCP E5M2 on
+// gfx950, round to nearest even), a in the lowest byte.  For every FP32
+// magnitude in [0, 57344], of either sign, it equals e5m2_code_abs with the
+// sign bit put back (checked exhaustively on gfx950), so after a clamp to
+// +-57344 it is the saturating encoder.  The first conversion's old value
+// is overwritten by the second, so a's own bits serve.
+__device__ __forceinline__ uint32_t e5m2_pack4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)as_u32(a), false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // Code of one element (FP32 bits of a BF16 value) under scale s.  The
 // quotient is the IEEE FP32 division: unlike the online scales, s need not
 // come from this tensor's amax, so the quotient may lie anywhere.
@@ -107,12 +120,9 @@ __device__ __forceinline__ uint2 delayed_code8_fast(const uint32_t xb[8], float 
         y[j] = __builtin_fmaf(-e, r, q0);
     }
     if constexpr (E5M2) {
-        uint32_t c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            c[j] = ((as_u32(y[j]) >> 24) & 0x80u) | e5m2_code_abs(__builtin_fminf(__builtin_fabsf(y[j]), 57344.0f));
-        return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                          c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], -57344.0f, 57344.0f);
+        return make_uint2(e5m2_pack4(y[0], y[1], y[2], y[3]), e5m2_pack4(y[4], y[5], y[6], y[7]));
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(y[j], -448.0f, 448.0f);
