@@ -136,25 +136,11 @@ __device__ __forceinline__ uint32_t amax8(const float z[8])
     return m;
 }
 
-// E4M3 code of a non-negative FP32 value (RNE, saturating; NaN -> 0x7F)
-__device__ __forceinline__ uint32_t e4m3_code_f32(float a)
-{
-    if (a != a) return 0x7Fu;
-    return e4m3_code_abs(a < 448.0f ? a : 448.0f);
-}
-
 __device__ __forceinline__ float e4m3_value(uint32_t c)
 {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
     return v[0];
-}
-
-// E2M1 magnitude code of a in [0, 6]: nearest, ties to the even code
-__device__ __forceinline__ uint32_t e2m1_rne(float a)
-{
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-           (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
 // Stochastic E2M1 codes of 8 values (element 2k in the low nibble of byte
@@ -204,9 +190,10 @@ __device__ __forceinline__ uint32_t e2m1_sr_pack8(const float v[8], const uint32
 }
 
 // E2M1 codes of 8 quotients, packed: stochastic from e2m1_sr_pack8, or RNE
-// from v_cvt_scalef32_pk_fp4_f32 (unit scale), which equals the RNE encoder
-// with the sign of the input for every FP32 value in [-6, 6] and saturates
-// at 6 beyond (both checked exhaustively on gfx950).
+// from v_cvt_scalef32_pk_fp4_f32 (unit scale), which for every FP32 value in
+// [-6, 6] gives the nearest magnitude of {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties
+// to the even code) with the sign of the input, and saturates at 6 beyond
+// (both checked exhaustively on gfx950).
 template <bool SR>
 __device__ __forceinline__ uint32_t e2m1_pack8(const float v[8], const uint32_t nr[8])
 {
@@ -259,10 +246,8 @@ __device__ __forceinline__ float div_rn(float a, float d, float r)
 // residual normal; in other blocks an element below 2^-90 has a quotient
 // below 2^-57, where RNE gives 0 and stochastic rounding never rounds up
 // (floor(p * 2^22) = 0), so its rounding cannot change a code.  RNE codes
-// come from the hardware converter v_cvt_scalef32_pk_fp4_f32 (unit scale),
-// which equals the RNE encoder above with the sign of the input for every
-// FP32 value in [-6, 6] (checked exhaustively on gfx950); stochastic codes
-// from e2m1_sr_pack8, with nr the complements ~r of the elements' words.
+// come from e2m1_pack8 (the hardware converters), with nr the complements
+// ~r of the elements' words for stochastic rounding.
 //
 // y = z / zscale: z is either the value itself (zscale 1) or four times the
 // transformed value (zscale 4, see rht16x4); amax_b is the amax of y.  The
