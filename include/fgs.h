@@ -244,7 +244,8 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  * The products of the decoded operands are exact and the sums are FP32
  * (the matrix unit's own FP8 path rounds inside each group of 8 products,
  * which the bound below does not allow).
- * K must be a multiple of 128.  M, N >= 0 arbitrary.
+ * K must be a positive multiple of 128 (K = 0 with M, N > 0 returns
+ *   FGS_ERR_UNSUPPORTED); M, N >= 0 arbitrary, and M or N = 0 launches nothing.
  * C: FP32 or BF16 (RNE) [M x N], row stride ldc >= N (elements).
  * Accuracy: |C - C_ref| <= 1e-5 * sum_k |a_k b_k| + 1e-6 for FP32 output,
  * C_ref the exact product of the dequantized operands.

@@ -95,6 +95,7 @@ def test_gemm_validation(lib):
     a, b = _op(mode=1), _op(mode=2)
     r = ctypes.byref
     assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # K % 128
+    assert g(r(a), r(b), 128, 128, 0, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED        # K = 0
     assert g(r(a), r(b), -1, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_INVALID_ARG
     assert g(r(a), r(b), 128, 128, 256, FAKE, 64, 0, S) == _lib.FGS_ERR_INVALID_ARG       # ldc < N
     assert g(r(a), r(b), 128, 128, 256, FAKE, 128, 5, S) == _lib.FGS_ERR_INVALID_ARG      # out dtype
@@ -315,6 +316,7 @@ def test_gemm_fp8mma_validation(lib):
     r = ctypes.byref
     a, b = _op(mode=1), _op(mode=2)
     assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED      # K % 128
+    assert g(r(a), r(b), 128, 128, 0, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED        # K = 0
     assert g(r(a), r(b), 128, 128, 256, FAKE, 64, 0, S) == _lib.FGS_ERR_INVALID_ARG       # ldc < N
     assert g(r(_op(mode=2)), r(b), 128, 128, 256, FAKE, 128, 0, S) == _lib.FGS_ERR_UNSUPPORTED   # A block
     an, bn = _op(elem=1, mode=4, ts=FAKE), _op(elem=1, mode=4, ts=FAKE)
