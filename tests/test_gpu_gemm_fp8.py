@@ -128,6 +128,29 @@ def test_gemm_row_stride_and_ldc(fgs):
     assert np.all(c[:, N:] == 7.0)
 
 
+@pytest.mark.parametrize("tile", ["narrow", "wide"])
+def test_gemm_row_stride_at_the_limit(fgs, tile):
+    """A row stride of 2^24 - 16 bytes, the largest the 32-bit lane offsets
+    (row within the tile x stride) admit: a 256-row A spans 4 GiB, and its
+    last row's offset lands just under 2^32."""
+    M, N, K = 256, 256, 256
+    ld = (1 << 24) - 16
+    a_bits = synth.activations(M, K, seed=11)
+    b_bits = synth.weights(N, K, seed=12)
+    A, ah = oracle_operand(fgs, a_bits, "tile")
+    B, bh = oracle_operand(fgs, b_bits, "block")
+    wide = torch.zeros((M, ld), dtype=torch.uint8, device="cuda")
+    wide[:, :K] = A.data
+    A2 = fgs.Operand(wide, A.scales, A.scale_mode)
+    assert A2.c_struct().ld == ld
+    c = fgs.gemm_block_scaled(A2, B, torch.float32, K=K, tile=tile)
+    torch.cuda.synchronize()
+    del wide
+    cref, sref = oracle.gemm_ref(ah, bh)
+    ok, worst = gemm_within_fp32_bound(c.cpu().numpy().astype(np.float64), cref, sref)
+    assert ok, worst
+
+
 def test_gemm_adversarial_promotion(fgs):
     """Each 128-K block of A has its own scale spanning 2^-20 .. 2^20, so an
     accumulator without per-block FP32 promotion of the scale would fail."""
