@@ -6,7 +6,8 @@ element offsets and the stochastic-rounding index need all 64 bits.
 hashes its linear index, whose upper 32 bits are nonzero past 2^32
 elements); "Can you explain the role of FP8 precision in DeepSeek-V3
 training", section "Fine-grained quantization" (1x128 tiles, both
-orientations).  The inputs are drawn on the GPU in chunks (seeded, bounded
+orientations); "Accelerating FP8 training performance with the NVIDIA NeMo
+framework" (MXFP8, one E8M0 scale per 32 values).  The inputs are drawn on the GPU in chunks (seeded, bounded
 to (-1, 1)), so the tensor amax of the NVFP4 case is fixed by one planted
 value and sampled rows and columns are checked against the oracle.
 """
@@ -85,5 +86,26 @@ def test_e4m3_tile_dual_output_past_2_31_elements(fgs):
     qt, st = oracle.quant_e4m3(np.ascontiguousarray(_bits(x[:, torch.from_numpy(cs).cuda()])), "tile", colwise=True)
     assert np.array_equal(r.qT[torch.from_numpy(cs).cuda()].cpu().numpy(), qt)
     assert np.array_equal(r.scalesT[:, torch.from_numpy(cs).cuda()].cpu().numpy().T, st)
+    del r, x
+    torch.cuda.empty_cache()
+
+
+def test_mx_dual_output_past_2_31_elements(fgs):
+    """65664 x 32768 MXFP8, row-wise and column-wise: the same 64-bit
+    offsets (the scale bytes of the last rows and columns, too)."""
+    rows, cols = 65664, 32768
+    x = _uniform_bf16(rows, cols, seed=7)
+    r = fgs.quantize_mx(x, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    rs = np.array([0, 65535, 65536, 65663])
+    idx = torch.from_numpy(rs).cuda()
+    q, s = oracle.quant_mx(_bits(x[idx]))
+    assert np.array_equal(r.q[idx].cpu().numpy(), q)
+    assert np.array_equal(r.scales[idx].cpu().numpy(), s)
+    cs = np.array([0, 16383, 32767])
+    cidx = torch.from_numpy(cs).cuda()
+    qt, st = oracle.quant_mx(np.ascontiguousarray(_bits(x[:, cidx])), colwise=True)
+    assert np.array_equal(r.qT[cidx].cpu().numpy(), qt)
+    assert np.array_equal(r.scalesT[cidx].cpu().numpy(), st)
     del r, x
     torch.cuda.empty_cache()
