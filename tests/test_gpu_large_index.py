@@ -7,7 +7,8 @@ hashes its linear index, whose upper 32 bits are nonzero past 2^32
 elements); "Can you explain the role of FP8 precision in DeepSeek-V3
 training", section "Fine-grained quantization" (1x128 tiles, both
 orientations); "Accelerating FP8 training performance with the NVIDIA NeMo
-framework" (MXFP8, one E8M0 scale per 32 values).  The inputs are drawn on the GPU in chunks (seeded, bounded
+framework" (MXFP8, one E8M0 scale per 32 values); and the block-scaled GEMM
+("Mixed precision framework") on an operand past 2^31 bytes.  The inputs are drawn on the GPU in chunks (seeded, bounded
 to (-1, 1)), so the tensor amax of the NVFP4 case is fixed by one planted
 value and sampled rows and columns are checked against the oracle.
 """
@@ -17,6 +18,8 @@ import torch
 
 import oracle
 from fine_grained_scaled_amd import synth
+
+from _helpers import gemm_within_fp32_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -108,4 +111,39 @@ def test_mx_dual_output_past_2_31_elements(fgs):
     assert np.array_equal(r.qT[cidx].cpu().numpy(), qt)
     assert np.array_equal(r.scalesT[cidx].cpu().numpy(), st)
     del r, x
+    torch.cuda.empty_cache()
+
+
+def _e4m3_codes(rows, cols, seed):
+    """Random finite E4M3 codes (every byte but 0x7F and 0xFF) on the GPU."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    r = torch.randint(0, 254, (rows, cols), generator=g, device="cuda", dtype=torch.int16)
+    return (r + (r >= 127).to(torch.int16)).to(torch.uint8)
+
+
+def test_gemm_operand_past_2_31_bytes(fgs):
+    """A 65664 x 32768 operand (2^31 + 2^22 code bytes) with 1x128 scales
+    against a 256 x 32768 operand with 128x128 scales, FP32 out: rows past
+    65536 are checked against the oracle's product of the dequantized
+    operands.  Codes and power-of-two-spread scales are drawn on the GPU."""
+    M, N, K = 65664, 256, 32768
+    qa = _e4m3_codes(M, K, seed=8)
+    qb = _e4m3_codes(N, K, seed=9)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(10)
+    sa = torch.exp2(torch.randint(-6, 7, (K // 128, M), generator=g, device="cuda").float()) * 0.75
+    sb = torch.exp2(torch.randint(-6, 7, (N // 128, K // 128), generator=g, device="cuda").float()) * 1.25
+    A = fgs.Operand(qa, sa, 1)
+    B = fgs.Operand(qb, sb, 2)
+    c = fgs.gemm_block_scaled(A, B, torch.float32)
+    torch.cuda.synchronize()
+    rs = np.array([0, 65535, 65536, 65600, 65663])
+    idx = torch.from_numpy(rs).cuda()
+    a_hat = oracle.dequant_e4m3(qa[idx].cpu().numpy(), np.ascontiguousarray(sa[:, idx].cpu().numpy().T), "tile")
+    b_hat = oracle.dequant_e4m3(qb.cpu().numpy(), sb.cpu().numpy(), "block")
+    cref, sref = oracle.gemm_ref(a_hat, b_hat)
+    ok, worst = gemm_within_fp32_bound(c[idx].cpu().numpy().astype(np.float64), cref, sref)
+    assert ok, worst
+    del c, qa, qb
     torch.cuda.empty_cache()
