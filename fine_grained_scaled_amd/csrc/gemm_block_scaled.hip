@@ -329,7 +329,9 @@ struct Shape {
 using ShapeDense = Shape<4, 2, 2>;      // 256 x 128, promoted modes
 using ShapeWide = Shape<2, 4, 4>;       // 256 x 256, modes without promotion
 using ShapeGrouped = Shape<2, 2, 2>;    // 128 x 128, MoE groups
+using ShapeShort = Shape<2, 2, 1>;      // 64 x 128, MoE groups below kShortRows rows
 constexpr int32_t kWideRows = 256;      // row groups this long take ShapeWide (exact path)
+constexpr int32_t kShortRows = 64;      // row groups this short take ShapeShort
 
 // SCW: scale words per tile row and K block staged with the codes (MX: the
 // four E8M0 bytes; NVFP4: the eight E4M3 bytes as two words); word h of tile
@@ -1593,19 +1595,25 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
         p.sb_group_stride = ((a.N + 127) / 128) * (a.K / BK);
         if (a.A.scale_mode == FGS_SCALE_TILE_1x128 && a.B.scale_mode == FGS_SCALE_BLOCK_128x128) {
             // Groups of at least kWideRows rows take the 256 x 256 tile with
-            // 16x16 output tiles, the smaller ones the 128 x 128 tile: two
-            // launches on the stream, each one's device schedule skipping the
-            // other's groups.  Measured per tile: long groups 1.11-1.16 PF
+            // 16x16 output tiles, groups below kShortRows the 64 x 128 tile
+            // (three workgroups per CU keep more weight bytes in flight for
+            // the groups that only stream weights), the rest the 128 x 128
+            // tile: three launches on the stream, each one's device schedule
+            // skipping the others' groups.  Measured per tile: long groups 1.11-1.16 PF
             // on the 256 x 256 tile against 0.93-0.98 on the 128 x 128 one;
             // groups of 16-64 rows stream their weights at 4.0-4.3 TB/s on
             // the 128 x 128 tile, 3.3-3.4 on the 256 x 256 one.
             // The FP8 matrix instructions take the same split.
-            GemmParams ps = p, pl = p;
+            GemmParams pt = p, ps = p, pl = p;
+            pt.grp_hi = kShortRows;
+            ps.grp_lo = kShortRows;
             ps.grp_hi = kWideRows;
             pl.grp_lo = kWideRows;
             auto split = [&](auto mma8) -> hipError_t {
                 constexpr bool M8 = decltype(mma8)::value;
-                const hipError_t e = launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(ps, a, bf16, stream);
+                hipError_t e = launch_modes<ShapeShort, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(pt, a, bf16, stream);
+                if (e != hipSuccess) return e;
+                e = launch_modes<ShapeGrouped, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(ps, a, bf16, stream);
                 if (e != hipSuccess) return e;
                 return launch_modes<ShapeWide, FGS_SCALE_TILE_1x128, FGS_SCALE_BLOCK_128x128, GROUP_M, 0, M8>(pl, a, bf16, stream);
             };
