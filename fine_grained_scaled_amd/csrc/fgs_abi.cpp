@@ -39,6 +39,9 @@ int hip_status(hipError_t e, const char* what)
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int64_t kMaxRowBlocks = 65535;   // grid.y limit of the 128x128 quant kernels
+// the grouped quantizers launch the column blocks along grid.x and the
+// token blocks along grid.y
+constexpr int64_t kMaxColBlocks = 0x7FFFFFFF;
 
 int check_bf16_source(const void* x, int64_t rows, int64_t cols, int64_t ldx)
 {
@@ -424,8 +427,6 @@ int fgs_quantize_grouped_colwise(const void* x, int64_t rows, int64_t cols, int6
     if (row_index) {
         if (src_rows < 0) return fail(FGS_ERR_INVALID_ARG, "src_rows must be >= 0");
         st = check_bf16_source(x, src_rows, cols, ldx);
-        if (st == FGS_OK && (rows + 127) / 128 > kMaxRowBlocks)
-            st = fail(FGS_ERR_UNSUPPORTED, "rows too large (%lld)", (long long)rows);
     } else {
         st = check_bf16_source(x, rows, cols, ldx);
     }
@@ -435,8 +436,10 @@ int fgs_quantize_grouped_colwise(const void* x, int64_t rows, int64_t cols, int6
     if (row_index && src_rows > 0 && !x) return fail(FGS_ERR_INVALID_ARG, "x is NULL");
     if (qT && !scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
     const int64_t blocks = fgs_grouped_colwise_blocks(rows, G);
-    if (blocks > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many token blocks");
-    if ((cols + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "cols too large (%lld)", (long long)cols);
+    if (blocks > kMaxRowBlocks)
+        return fail(FGS_ERR_UNSUPPORTED, "rows / 128 + G = %lld token blocks (at most %lld)", (long long)blocks,
+                    (long long)kMaxRowBlocks);
+    if ((cols + 127) / 128 > kMaxColBlocks) return fail(FGS_ERR_UNSUPPORTED, "cols too large (%lld)", (long long)cols);
     if (qT) {
         if (ldqT < 128 * blocks)
             return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,
@@ -469,8 +472,10 @@ int fgs_swiglu_quantize_grouped(const void* gate_up, int64_t rows, int64_t inter
     if (h && !aligned(h, 16)) return fail(FGS_ERR_UNSUPPORTED, "h must be 16-byte aligned");
     if (qT && !scalesT) return fail(FGS_ERR_INVALID_ARG, "scalesT is NULL while qT is given");
     const int64_t blocks = fgs_grouped_colwise_blocks(rows, G);
-    if (blocks > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many token blocks");
-    if ((inter + 127) / 128 > kMaxRowBlocks) return fail(FGS_ERR_UNSUPPORTED, "inter too large (%lld)", (long long)inter);
+    if (blocks > kMaxRowBlocks)
+        return fail(FGS_ERR_UNSUPPORTED, "rows / 128 + G = %lld token blocks (at most %lld)", (long long)blocks,
+                    (long long)kMaxRowBlocks);
+    if ((inter + 127) / 128 > kMaxColBlocks) return fail(FGS_ERR_UNSUPPORTED, "inter too large (%lld)", (long long)inter);
     if (qT) {
         if (ldqT < 128 * blocks)
             return fail(FGS_ERR_INVALID_ARG, "ldqT (%lld) < 128 * (rows / 128 + G) = %lld", (long long)ldqT,

@@ -128,9 +128,11 @@ __device__ __forceinline__ uint4 swiglu8(const uint4& g, const uint4& u)
 // blocks kb_g = floor(offsets[g] / 128) + g .. kb_g + ceil(M_g / 128) - 1 of
 // qT (row stride ldqT) and the same rows of scalesT; those blocks never
 // overlap for non-decreasing offsets, so no scan over the groups is needed.
-// Workgroup (blockIdx.x = block j, blockIdx.y = column block) finds the group
+// Workgroup (blockIdx.x = column block, blockIdx.y = block j) finds the group
 // that owns block j; rows past the group's end read as zero (zero codes in
-// qT, no effect on the amax).  With row_index, logical row t is source row
+// qT, no effect on the amax).  The column blocks of one row block are
+// launched side by side, so the 256-byte segments of a row are read together
+// (measured 2-10% faster than row blocks side by side).  With row_index, logical row t is source row
 // row_index[t] of x (the MoE dispatch gather, fused so the permuted BF16
 // copy is never written); an index outside [0, src_rows) reads as zeros.
 // SWIGLU (GROUPED only): x holds a gate/up GEMM output [rows x 2*cols] and
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256, GROUPED ? 5 : 6) void quant_e4m3_kernel(
         tb = blockIdx.y;
         ldt = rows;
     } else {
-        const int64_t j = blockIdx.x;
+        const int64_t j = blockIdx.y;
         if (t == 0) s_group = -1;
         __syncthreads();
         for (int g = t; g < G; g += 256) {
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256, GROUPED ? 5 : 6) void quant_e4m3_kernel(
         if (g < 0) return;                       // a block no group owns
         const int32_t o0 = offsets[g], o1 = offsets[g + 1];
         r0 = (int64_t)o0 + (j - ((int64_t)(o0 >> 7) + g)) * TB;
-        c0 = (int64_t)blockIdx.y * TB;
+        c0 = (int64_t)blockIdx.x * TB;
         live = (int64_t)o1 - r0;
         tc = j * TB;
         tb = j;
@@ -287,7 +289,8 @@ __global__ __launch_bounds__(256, GROUPED ? 5 : 6) void quant_e4m3_kernel(
                 if (col_ok && 8 * rg + u < live) {
                     uint8_t* dst = q_base + u * cols;
                     // non-temporal stores measured faster for the grouped
-                    // (MoE) layout and slower for the dense one
+                    // (MoE) layout (plain stores there cost the next GEMM
+                    // more than they save) and slower for the dense one
                     if constexpr (GROUPED) store_nt8(dst, codes);
                     else *reinterpret_cast<uint2*>(dst) = codes;
                 }
@@ -522,7 +525,7 @@ hipError_t launch_quant_grouped_colwise(const QuantGroupedArgs& a, hipStream_t s
     // every group owns at most floor(rows / 128) + G blocks in total
     const int64_t nblk = a.rows / TB + a.G, nbc = (a.cols + TB - 1) / TB;
     if (a.G == 0 || a.rows == 0 || nbc == 0) return hipSuccess;
-    const dim3 grid((unsigned)nblk, (unsigned)nbc);
+    const dim3 grid((unsigned)nbc, (unsigned)nblk);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (a.swiglu)
         hipLaunchKernelGGL((quant_e4m3_kernel<FGS_SCALE_TILE_1x128, true, true>), grid, dim3(256), 0, stream,

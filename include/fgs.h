@@ -342,7 +342,8 @@ int fgs_grouped_gemm_block_scaled_fp8mma(const fgs_operand *A, const fgs_operand
  *   kb_g .. kb_g + ceil(M_g/128) - 1 with kb_g = floor(offsets[g]/128) + g,
  *   so the layout needs no scan and no host synchronisation; blocks no group
  *   owns are not written.  There are at most
- *   fgs_grouped_colwise_blocks(rows, G) = floor(rows/128) + G blocks.
+ *   fgs_grouped_colwise_blocks(rows, G) = floor(rows/128) + G blocks; more
+ *   than 65535 returns FGS_ERR_UNSUPPORTED.
  *   qT       E4M3 [cols x ldqT], ldqT >= 128 * fgs_grouped_colwise_blocks,
  *            ldqT % 16 == 0.
  *   scalesT  FP32 [fgs_grouped_colwise_blocks][cols] (the TILE_1x128 layout

@@ -240,6 +240,11 @@ def test_grouped_colwise_validation(lib):
     assert call(idx=FAKE, src=-1) == _lib.FGS_ERR_INVALID_ARG
     assert call(idx=FAKE, src=100, ldx=100) == _lib.FGS_ERR_INVALID_ARG           # ldx < cols
     assert call(x=NULL, idx=FAKE, src=100) == _lib.FGS_ERR_INVALID_ARG
+    # the token blocks (floor(rows / 128) + G) run along grid.y: at most 65535
+    big_ld = 128 * 65536
+    assert call(rows=128 * 65535, G=1, ldq=big_ld) == _lib.FGS_ERR_UNSUPPORTED
+    assert b"token blocks" in lib.fgs_last_error()
+    assert call(rows=128 * 65534, idx=FAKE, src=100, G=2, ldq=big_ld) == _lib.FGS_ERR_UNSUPPORTED
 
 
 def test_swiglu_quantize_validation(lib):
@@ -256,6 +261,7 @@ def test_swiglu_quantize_validation(lib):
     assert call(ldq=128 * 5) == _lib.FGS_ERR_INVALID_ARG
     assert call(q=NULL, s=NULL, qT=NULL, sT=NULL) == _lib.FGS_OK        # nothing to write
     assert call(G=0) == _lib.FGS_OK
+    assert call(rows=128 * 65000, G=600, ldq=128 * 65600) == _lib.FGS_ERR_UNSUPPORTED   # token blocks
 
 
 def test_grouped_wgrad_validation(lib):
