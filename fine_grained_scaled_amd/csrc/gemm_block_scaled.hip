@@ -534,18 +534,19 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
         // g * M * ldc.  Workgroups run group by group; within a group of
         // per % 8 == 0 tiles, the eight XCDs (dealt workgroups round-robin)
         // each take a contiguous eighth of the tile order.  The order runs
-        // down GM m-tiles, then to the next n-tile: for a C of 32 or more
-        // n-tiles GM = 1, so the tiles in flight on an XCD cover whole
-        // 128-row bands of C (on DeepSeek-V3, gate/up dW [4096 x 7168]: 7.61-
-        // 7.71 ms against 7.94-8.11 with GM = 8); below that GM = 8 (down dW
-        // [7168 x 2048]: 3.52-3.59 ms against 4.52-4.55 with GM = 1).  A group
-        // without tokens, or with offsets out of order or range, runs no K
-        // block and writes zeros.
+        // down GM m-tiles, then to the next n-tile, and sets the shape of the
+        // region of C that an XCD's tiles in flight write.  Measured on
+        // DeepSeek-V3, same box: gate/up dW [4096 x 7168] (56 n-tiles) 7.45-
+        // 7.47 ms with GM = 2, 7.62-7.67 with 1, 7.94-8.11 with 8; down dW
+        // [7168 x 2048] (16 n-tiles) 3.56-3.61 ms with GM = 16, 3.57 with 8,
+        // 3.76 with 4, 4.22 with 2, 4.53 with 1.  A group without tokens, or
+        // with offsets out of order or range, runs no K block and writes
+        // zeros.
         const int64_t per = (int64_t)p.tiles_m * p.tiles_n;
         const int g = (int)(blockIdx.x / per);
         int id = (int)(blockIdx.x % per);
         if ((per & 7) == 0) id = (id & 7) * (int)(per >> 3) + (id >> 3);
-        const int GM = p.tiles_n >= 32 ? 1 : 8;
+        const int GM = p.tiles_n >= 32 ? 2 : 8;
         const int group = id / (GM * p.tiles_n);
         const int first_m = group * GM;
         const int gsz = min(p.tiles_m - first_m, GM);
