@@ -447,11 +447,17 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
         n0 = (int64_t)tn * BN;
     } else if constexpr (GROUP == GROUP_M) {
         // Device-side schedule over the tiles of all groups in canonical
-        // order u (group, then n-tile, then m-tile fastest).  Workgroup v
-        // takes u from the front for even runs of 8 and from the back for odd
-        // runs, so short (HBM-bound) and long (MFMA-bound) groups run side by
-        // side whatever order the groups come in.  v -> u is a bijection on
-        // [0, T): the front takes [0, F) and the back [T - B, T) with F + B = T.
+        // order u (group, then n-tile, then m-tile fastest).  Workgroups are
+        // taken in blocks of 64, from the front of the order for even blocks
+        // and from the back for odd ones, so short (HBM-bound) and long
+        // (MFMA-bound) groups run side by side whatever order the groups come
+        // in.  Within a full block, workgroup 8 r + x (dealt to XCD x) takes
+        // the block's tile 8 x + r: an XCD gets 8 consecutive tiles, the
+        // m-tiles of one n-tile, which read the same weight rows through its
+        // L2 (8 XCDs each fetching them measured 5x the weight bytes on the
+        // DeepSeek-V3 long groups).  The last, partial block keeps the plain
+        // order.  v -> u is a bijection on [0, T): the front takes [0, F) and
+        // the back [T - B, T) with F + B = T.
         auto m_tiles = [&](int g) {
             int cnt = 0;
             if (g < p.G) {
@@ -500,8 +506,10 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
         }
         const int64_t total = (int64_t)total_tiles * p.tiles_n;
         if ((int64_t)blockIdx.x >= total) return;                  // beyond the last tile
-        const int64_t vb = (int64_t)blockIdx.x >> 3, vbase = ((vb >> 1) << 3) + (blockIdx.x & 7);
-        const int64_t v = (vb & 1) ? total - 1 - vbase : vbase;
+        const int64_t bx = blockIdx.x, blk = bx >> 6;
+        const int64_t inner = (blk + 1) * 64 <= total ? 8 * (bx & 7) + ((bx >> 3) & 7) : (bx & 63);
+        const int64_t vbase = ((blk >> 1) << 6) + inner;
+        const int64_t v = (blk & 1) ? total - 1 - vbase : vbase;
         // the group that holds tile v (exactly one thread finds it); the
         // first chunk's scan is reused, later chunks are scanned again
         int running = 0;
