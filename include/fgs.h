@@ -233,7 +233,10 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *     (e_A - E_A) + (e_B - E_B) >= -108 (each decoded code a BF16 number,
  *     each product a normal FP32 number); a pair further apart adds less
  *     than 2^-90 * 2^(E_A + E_B - 254) per product; a NaN scale byte makes
- *     its A row or B column of C NaN;
+ *     its A row or B column of C NaN.  The rows' largest exponents are
+ *     formed by a pass of their own enqueued before the GEMM, in a 2 (M + N)
+ *     byte stream-ordered allocation (hipMallocAsync) released on the same
+ *     stream after it;
  *   E4M3 or E5M2 on each side with TENSOR on both (the delayed-scaling
  *     recipes; E5M2 gradients against E4M3 weights or activations): every
  *     E5M2 code is exactly the FP16 number with the code as its upper byte,
