@@ -237,6 +237,15 @@ def test_grouped_many_groups(fgs):
     _grouped_case(fgs, counts, N=128, K=128, seed=5)
 
 
+def test_grouped_long_groups_every_output(fgs):
+    """Groups of 256 rows or more (the 256 x 256 tile's launch) over 2048
+    columns: 4 + 3 + 6 + 4 m-tiles x 8 n-tiles = 136 tiles, so the device
+    schedule deals two full blocks of 64 workgroups (each XCD taking 8
+    consecutive tiles, blocks alternating between the two ends of the tile
+    order) and a partial one; every output is checked."""
+    _grouped_case(fgs, [1000, 700, 1300, 1000], N=2048, K=256, out=torch.bfloat16, seed=9)
+
+
 # ------------------------------------------------------- full-size layer --
 @pytest.mark.parametrize("orient", ["fwd", "dgrad", "wgrad"])
 def test_llama8b_qkv_layer_sampled(fgs, orient):
