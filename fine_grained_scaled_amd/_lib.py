@@ -34,6 +34,7 @@ EXPORTS = (
     "fgs_swiglu_quantize_grouped",
     "fgs_grouped_wgrad_block_scaled",
     "fgs_workspace_bytes",
+    "fgs_gemm_workspace_bytes",
     "fgs_last_error",
     "fgs_version",
 )
@@ -56,6 +57,8 @@ class FgsGemmOptions(ctypes.Structure):
         ("fp8_mma", ctypes.c_int32),
         ("q_out", ctypes.c_void_p),
         ("scales_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -101,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.fgs_grouped_wgrad_block_scaled_fp8mma.argtypes = [OP, OP, P, ctypes.c_int32, I64, I64, I64, P, I64, I32, P]
     lib.fgs_workspace_bytes.argtypes = [I64, I64]
     lib.fgs_workspace_bytes.restype = SZ
+    lib.fgs_gemm_workspace_bytes.argtypes = [I32, I64, I64]
+    lib.fgs_gemm_workspace_bytes.restype = SZ
     lib.fgs_last_error.restype = ctypes.c_char_p
     lib.fgs_version.restype = ctypes.c_char_p
     for name in ("fgs_quantize_blockwise", "fgs_quantize_blockwise_noalloc", "fgs_quantize_delayed", "fgs_quantize_mx", "fgs_quantize_nvfp4",

@@ -103,6 +103,12 @@ const char* fgs_version(void) { return "fgs 0.1.0 (gfx950)"; }
 // The tensor-amax passes keep one partial per amax workgroup (4 bytes for
 // TENSOR mode, 8 for NVFP4's two orientations), up to two workgroups per
 // compute unit: 4 KiB covers 256 compute units at full speed.
+size_t fgs_gemm_workspace_bytes(int a_scale_mode, int64_t M, int64_t N)
+{
+    if (a_scale_mode != FGS_SCALE_MX32_E8M0 || M < 0 || N < 0) return 0;
+    return (size_t)(2 * (M + N));
+}
+
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols)
 {
     (void)rows;
@@ -292,8 +298,17 @@ static int gemm_impl(const fgs_operand* A, const fgs_operand* B, int64_t M, int6
     if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(FGS_ERR_UNSUPPORTED, "M or N too large");
     // the launch numbers its workgroup tiles (256 x 128 at the finest) in 32 bits
     if (((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF) return fail(FGS_ERR_UNSUPPORTED, "too many tiles");
+    void* ws = nullptr;
+    if (o.workspace || o.workspace_bytes) {
+        const size_t need = fgs_gemm_workspace_bytes(A->scale_mode, M, N);
+        if (!o.workspace || o.workspace_bytes < need)
+            return fail(FGS_ERR_INVALID_ARG, "workspace_bytes (%zu) < fgs_gemm_workspace_bytes (%zu), or workspace is NULL",
+                        o.workspace_bytes, need);
+        if (!aligned(o.workspace, 16)) return fail(FGS_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        if (need > 0) ws = o.workspace;
+    }
     fgs::GemmArgs a{*A, *B, M, N, K, C, ldc, out_dtype == FGS_OUT_BF16, nullptr, 0, 0, 0, q_out, s_out, o.fp8_mma,
-                    o.tile, name, name_len};
+                    o.tile, name, name_len, ws};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (o.fp8_mma && (A->elem == FGS_ELEM_E2M1 || B->elem == FGS_ELEM_E2M1))
         return fail(FGS_ERR_UNSUPPORTED, "the FP8 matrix-instruction GEMM takes E4M3 / E5M2 operands only");

@@ -104,6 +104,7 @@ struct GemmArgs {
     int tile;                       // dense only: FGS_TILE_AUTO | FGS_TILE_NARROW | FGS_TILE_WIDE
     char* name_out;                 // non-null: write the kernel instantiation's name instead of launching
     size_t name_len;
+    void* workspace;                // MXFP8 exact path: 2 (M + N) bytes for the rows' references, or nullptr
 };
 // Compute units of the current device (cached per device; 256 if the
 // query fails).

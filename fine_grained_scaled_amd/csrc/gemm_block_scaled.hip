@@ -709,19 +709,72 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
     uint32_t ea[TI], eb = 0;
     if constexpr (MX && !MMA8) {
         // the tile's rows: A rows 0 .. BM-1, then B rows (rows past the end
-        // clamped; they only feed outputs that are never stored), their
-        // references formed once per launch by mx_row_ref_kernel
+        // clamped; they only feed outputs that are never stored): their
+        // references formed once per launch by mx_row_ref_kernel when the
+        // caller brought a workspace, else scanned here, one row per thread
         if (t == 0) s_mx_eb = 0;
         __syncthreads();
+        const uint8_t* const sA8 = reinterpret_cast<const uint8_t*>(p.sA);
+        const uint8_t* const sB8 = reinterpret_cast<const uint8_t*>(sBp);
+        const int64_t ksc = p.K / 32;                 // scale bytes of a row
+        // 16 bytes per load where the rows allow it, eight loads in flight
+        // before any is scanned (the eight 405B MXFP8 GEMMs, same box: 7%
+        // less time than 4-byte loads each waited for before the next; the
+        // per-launch pass saves 10%)
+        const bool wide_rows = (ksc & 15) == 0 && (reinterpret_cast<uintptr_t>(sA8) & 15) == 0 &&
+                               (reinterpret_cast<uintptr_t>(sB8) & 15) == 0;
         for (int rr = t; rr < BM + BN; rr += NT) {
             const bool is_a = rr < BM;
             int64_t row = is_a ? m0 + rr : n0 + (rr - BM);
             const int64_t lim = is_a ? m_end : p.N;
             row = row < lim ? row : lim - 1;
-            const uint32_t v = p.mx_ref[is_a ? row : p.M + row];
-            s_mx_ref[rr] = (uint8_t)(v & 0xFFu);
-            s_mx_nan[rr] = (uint8_t)(v >> 8);
-            if (!is_a) atomicMax(&s_mx_eb, v & 0xFFu);
+            uint32_t mref = 0, nan = 0;
+            if (p.mx_ref) {
+                const uint32_t v = p.mx_ref[is_a ? row : p.M + row];
+                mref = v & 0xFFu;
+                nan = v >> 8;
+            } else {
+                auto scan_word = [&](uint32_t w4) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t v = (w4 >> (8 * b)) & 0xFFu;
+                        nan |= v == 0xFFu;
+                        mref = max(mref, v == 0xFFu ? 0u : v);
+                    }
+                };
+                const uint8_t* const rowp = (is_a ? sA8 : sB8) + row * ksc;
+                if (wide_rows) {
+                    constexpr int BATCH = 8;
+                    const uint4* src = reinterpret_cast<const uint4*>(rowp);
+                    const int64_t n16 = ksc / 16;
+                    int64_t c = 0;
+                    for (; c + BATCH <= n16; c += BATCH) {
+                        uint4 q[BATCH];
+#pragma unroll
+                        for (int k = 0; k < BATCH; ++k) q[k] = src[c + k];
+#pragma unroll
+                        for (int k = 0; k < BATCH; ++k) {
+                            scan_word(q[k].x);
+                            scan_word(q[k].y);
+                            scan_word(q[k].z);
+                            scan_word(q[k].w);
+                        }
+                    }
+                    for (; c < n16; ++c) {
+                        const uint4 q = src[c];
+                        scan_word(q.x);
+                        scan_word(q.y);
+                        scan_word(q.z);
+                        scan_word(q.w);
+                    }
+                } else {
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(rowp);
+                    for (int64_t c = 0; c < ksc / 4; ++c) scan_word(src[c]);
+                }
+            }
+            s_mx_ref[rr] = (uint8_t)mref;
+            s_mx_nan[rr] = (uint8_t)nan;
+            if (!is_a) atomicMax(&s_mx_eb, mref);
         }
         __syncthreads();
 #pragma unroll
@@ -1435,8 +1488,8 @@ __global__ __launch_bounds__(64 * S::NWM * S::NWN, S::NWM * S::NWN == 4 ? 2 : 1)
 // none), with bit 8 set when the row holds a NaN byte.  One wave per row,
 // each lane reading 16 bytes at a time where the rows allow it (4 where they
 // do not), the lanes' results met by lane exchange.  Formed once per launch
-// instead of by every tile that reads the row: on the 405B MXFP8 layers the
-// per-tile scan took 17-20% of the GEMM time.
+// instead of by every tile that reads the row (each B row is otherwise
+// scanned again by every m-tile).
 __global__ __launch_bounds__(256) void mx_row_ref_kernel(const uint8_t* __restrict__ sA, int64_t M,
                                                           const uint8_t* __restrict__ sB, int64_t N,
                                                           int64_t ksc, uint16_t* __restrict__ out)
@@ -1668,23 +1721,16 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t stream)
         return hipErrorInvalidValue;
     }
     if (a.fp8_mma) return dispatch_dense<true>(p, a, bf16, stream);
-    if (a.A.scale_mode == FGS_SCALE_MX32_E8M0 && !a.name_out) {
-        // the rows' reference bytes, in a stream-ordered allocation that is
-        // released on the stream after the GEMM
+    if (a.A.scale_mode == FGS_SCALE_MX32_E8M0 && a.workspace && !a.name_out) {
+        // the rows' reference bytes, once, into the caller's workspace
         const int64_t rows = a.M + a.N;
-        uint16_t* ref = nullptr;
-        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ref), (size_t)rows * sizeof(uint16_t), stream);
-        if (e != hipSuccess) return e;
+        uint16_t* ref = static_cast<uint16_t*>(a.workspace);
         hipLaunchKernelGGL(mx_row_ref_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
                            reinterpret_cast<const uint8_t*>(a.A.scales), a.M, reinterpret_cast<const uint8_t*>(a.B.scales),
                            a.N, a.K / 32, ref);
-        e = hipGetLastError();
-        if (e == hipSuccess) {
-            p.mx_ref = ref;
-            e = dispatch_dense<false>(p, a, bf16, stream);
-        }
-        const hipError_t f = hipFreeAsync(ref, stream);
-        return e != hipSuccess ? e : f;
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.mx_ref = ref;
     }
     return dispatch_dense<false>(p, a, bf16, stream);
 }

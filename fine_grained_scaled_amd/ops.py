@@ -237,13 +237,16 @@ def _out_code(out_dtype):
 
 def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
                       out: Optional[torch.Tensor] = None, K: Optional[int] = None,
-                      fp8_mma: bool = False, tile: str = "auto") -> torch.Tensor:
+                      fp8_mma: bool = False, tile: str = "auto", workspace: bool = True) -> torch.Tensor:
     """C[M x N] = sum_k A^[m, k] * B^[n, k] over scaled low-precision operands.
     fp8_mma=True runs the FP8 matrix instructions with promotion per 128-K
     block (FP8 operands only; a looser error bound than the exact default).
     tile: "auto" (chosen per problem), "narrow" (256 x 128 outputs per
-    workgroup) or "wide" (256 x 256).  The defaults call
-    fgs_gemm_block_scaled / fgs_gemm_block_scaled_fp8mma, a forced tile
+    workgroup) or "wide" (256 x 256).  workspace: for MXFP8 on the exact
+    path, hand the library fgs_gemm_workspace_bytes of torch-allocated
+    scratch (same bits, faster); False makes every tile scan its rows' scale
+    bytes.  The defaults call fgs_gemm_block_scaled /
+    fgs_gemm_block_scaled_fp8mma; a forced tile or a workspace
     fgs_gemm_block_scaled_ex."""
     _need_gpu(A.data, B.data, A.scales, B.scales)
     M, N = A.data.shape[0], B.data.shape[0]
@@ -259,11 +262,16 @@ def gemm_block_scaled(A: Operand, B: Operand, out_dtype=torch.float32,
         raise ValueError("out must be a [M x N] tensor of out_dtype with unit column stride")
     a, b = A.c_struct(), B.c_struct()
     lib = _lib.load()
-    if tcode == _lib.TILE_AUTO:
+    # MXFP8 on the exact path: a workspace for the rows' reference exponents
+    # (formed once per launch instead of by every tile)
+    ws_bytes = 0 if fp8_mma else lib.fgs_gemm_workspace_bytes(A.scale_mode, M, N) if workspace else 0
+    if tcode == _lib.TILE_AUTO and ws_bytes == 0:
         fn = lib.fgs_gemm_block_scaled_fp8mma if fp8_mma else lib.fgs_gemm_block_scaled
         check(fn(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0), code, _stream()))
     else:
-        opt = _lib.FgsGemmOptions(tcode, 1 if fp8_mma else 0, None, None)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=A.data.device) if ws_bytes else None
+        opt = _lib.FgsGemmOptions(tcode, 1 if fp8_mma else 0, None, None,
+                                  ws.data_ptr() if ws is not None else None, ws_bytes)
         check(lib.fgs_gemm_block_scaled_ex(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0),
                                            code, ctypes.byref(opt), _stream()))
     return out

@@ -233,10 +233,7 @@ int fgs_quantize_nvfp4(const void *x, int64_t rows, int64_t cols, int64_t ldx,
  *     (e_A - E_A) + (e_B - E_B) >= -108 (each decoded code a BF16 number,
  *     each product a normal FP32 number); a pair further apart adds less
  *     than 2^-90 * 2^(E_A + E_B - 254) per product; a NaN scale byte makes
- *     its A row or B column of C NaN.  The rows' largest exponents are
- *     formed by a pass of their own enqueued before the GEMM, in a 2 (M + N)
- *     byte stream-ordered allocation (hipMallocAsync) released on the same
- *     stream after it;
+ *     its A row or B column of C NaN;
  *   E4M3 or E5M2 on each side with TENSOR on both (the delayed-scaling
  *     recipes; E5M2 gradients against E4M3 weights or activations): every
  *     E5M2 code is exactly the FP16 number with the code as its upper byte,
@@ -470,6 +467,17 @@ int fgs_grouped_gemm_block_scaled_fp8out(const fgs_operand *A, const fgs_operand
  *               fgs_gemm_block_scaled_fp8out (then out_dtype must be
  *               FGS_OUT_BF16, C may be NULL, N % 128 == 0, and fp8_mma must
  *               be 0).
+ *   workspace, workspace_bytes  NULL / 0, or DEVICE scratch (16-byte
+ *               aligned, owned by the caller, not read before it is
+ *               written) of at least fgs_gemm_workspace_bytes(A->scale_mode,
+ *               M, N) bytes.  MXFP8 on the exact path then forms each row's
+ *               largest scale exponent once, in a pass of its own enqueued
+ *               before the GEMM; without it every workgroup tile scans the
+ *               scale bytes of its own rows (slower: on the Llama-3.1-405B
+ *               MXFP8 layers, about 3% of the GEMM time more).  The results
+ *               are the same bits either way.  Other modes ignore it.  A
+ *               workspace given with fewer bytes than required, or
+ *               misaligned, returns FGS_ERR_INVALID_ARG.
  * Other arguments, layouts, ownership and errors as fgs_gemm_block_scaled;
  * an unknown tile or fp8_mma value returns FGS_ERR_INVALID_ARG.  The library
  * keeps no state between calls: every choice is made from the arguments.
@@ -480,6 +488,8 @@ typedef struct {
     int32_t fp8_mma;       /* 0 or 1                                          */
     uint8_t *q_out;        /* device E4M3 [M x N] or NULL                     */
     float *scales_out;     /* device FP32 [N/128][M] or NULL                  */
+    void *workspace;       /* device scratch or NULL                          */
+    size_t workspace_bytes;
 } fgs_gemm_options;
 int fgs_gemm_block_scaled_ex(const fgs_operand *A, const fgs_operand *B,
                              int64_t M, int64_t N, int64_t K, void *C, int64_t ldc,
@@ -503,6 +513,12 @@ int fgs_gemm_kernel_name(const fgs_operand *A, const fgs_operand *B, int64_t M, 
 
 /* Device workspace needed by TENSOR-mode and NVFP4 quantization (bytes). */
 size_t fgs_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Device workspace the GEMM options can bring for an M x N product whose A
+ * operand has scale mode a_scale_mode: 2 (M + N) bytes for
+ * FGS_SCALE_MX32_E8M0 (one reference byte and one NaN flag per row of A and
+ * of B), 0 for the other modes and for negative sizes. */
+size_t fgs_gemm_workspace_bytes(int a_scale_mode, int64_t M, int64_t N);
 
 /* Message for the last error on this thread ("" if none); never NULL. */
 const char *fgs_last_error(void);

@@ -144,6 +144,22 @@ def test_gemm_ex_options_validation(lib):
         assert g(r(a), r(b), 128, 128, 200, FAKE, 128, 0, r(O(tile, 0, None, None)), S) == _lib.FGS_ERR_UNSUPPORTED
     # nothing to do: M = 0 succeeds with any valid option and launches nothing
     assert g(r(a), r(b), 0, 128, 256, FAKE, 128, 0, r(O(2, 1, None, None)), S) == _lib.FGS_OK
+    # the workspace: 2 (M + N) bytes for MX32 A scales, none otherwise; one
+    # given too small, without a pointer, or misaligned is refused
+    wsb = lib.fgs_gemm_workspace_bytes
+    assert wsb(3, 300, 200) == 1000 and wsb(1, 300, 200) == 0 and wsb(4, 300, 200) == 0 and wsb(3, -1, 5) == 0
+    am, bm = _op(mode=3), _op(mode=3)
+    need = wsb(3, 128, 128)
+    assert g(r(am), r(bm), 128, 128, 256, FAKE, 128, 0, r(O(0, 0, None, None, 0x10000, need - 1)), S) == \
+        _lib.FGS_ERR_INVALID_ARG
+    assert b"workspace" in lib.fgs_last_error()
+    assert g(r(am), r(bm), 128, 128, 256, FAKE, 128, 0, r(O(0, 0, None, None, None, need)), S) == \
+        _lib.FGS_ERR_INVALID_ARG
+    assert g(r(am), r(bm), 128, 128, 256, FAKE, 128, 0, r(O(0, 0, None, None, 0x10008, need)), S) == \
+        _lib.FGS_ERR_INVALID_ARG
+    # the argument checks come first: a valid workspace with a K error still reports K
+    assert g(r(am), r(bm), 128, 128, 200, FAKE, 128, 0, r(O(0, 0, None, None, 0x10000, need)), S) == \
+        _lib.FGS_ERR_UNSUPPORTED
 
 
 def test_gemm_kernel_name(lib):

@@ -55,6 +55,38 @@ def test_mx_gemm_ragged(fgs, M, N, K, out):
     _check(fgs, A, B, ah, bh, out)
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 130, 384), (300, 520, 1024), (256, 264, 4096), (130, 600, 16896)])
+@pytest.mark.parametrize("tile", ["narrow", "wide"])
+def test_mx_gemm_workspace_same_bits(fgs, M, N, K, tile):
+    """With a workspace the rows' reference exponents come from a pass of
+    their own; without one every tile scans its rows' scale bytes (4 bytes
+    at a time for K = 384, 16 at a time from K = 512 on, in batches of 8
+    from K = 4096).  Both give the same references, so the same bits, here
+    with a NaN scale byte planted in one A row and one B row; the result is
+    checked against the oracle too."""
+    a_bits = synth.activations(M, K, seed=M + 40, outliers=False)
+    b_bits = synth.weights(N, K, seed=N + 41)
+    qa, sa = oracle.quant_mx(a_bits)
+    qb, sb = oracle.quant_mx(b_bits)
+    sa[M // 3, K // 64] = 0xFF
+    sb[N - 2, 1] = 0xFF
+    A = fgs.Operand(torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(), fgs.SCALE_MX32_E8M0)
+    B = fgs.Operand(torch.from_numpy(qb).cuda(), torch.from_numpy(sb).cuda(), fgs.SCALE_MX32_E8M0)
+    c_ws = fgs.gemm_block_scaled(A, B, torch.float32, tile=tile)
+    c_scan = fgs.gemm_block_scaled(A, B, torch.float32, tile=tile, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c_ws.view(torch.int32), c_scan.view(torch.int32))
+    c = c_ws.cpu().numpy().astype(np.float64)
+    assert np.isnan(c[M // 3]).all() and np.isnan(c[:, N - 2]).all()
+    keep_r = np.setdiff1d(np.arange(M), [M // 3])
+    keep_c = np.setdiff1d(np.arange(N), [N - 2])
+    ah = oracle.dequant_mx(qa[keep_r], sa[keep_r])
+    bh = oracle.dequant_mx(qb[keep_c], sb[keep_c])
+    cref, sref = oracle.gemm_ref(ah, bh)
+    ok, worst = gemm_within_fp32_bound(c[np.ix_(keep_r, keep_c)], cref, sref)
+    assert ok, f"worst err/bound = {worst}"
+
+
 def test_mx_gemm_exponent_spread(fgs):
     """Every 32-block of both operands scaled by its own power of two in
     2^-40 .. 2^40, so the E8M0 exponents inside one 128-K block and across
