@@ -43,8 +43,10 @@
 // partial sums, so their waves can own 128 x 64 (2 x 4 waves, tile
 // 256 x 256): each decoded fragment feeds more MFMAs and each staged byte
 // more FLOPs; a launch takes this tile unless its last round of workgroups
-// would be poorly filled (see prefer_wide).  The grouped (MoE) kernel uses 2 x 2 waves of
-// 64 x 64 (tile 128 x 128; groups are short).  K advances in
+// would be poorly filled (see prefer_wide).  The MoE row groups take one of
+// three tiles by size (64 x 128 below 64 rows, 128 x 128 below 256, the
+// 256 x 256 one above), the MoE weight gradients 2 x 2 waves of 64 x 64
+// (tile 128 x 128).  K advances in
 // 128-deep blocks staged in LDS as code bytes (128 bytes per row for E4M3,
 // 64 for E2M1), double-buffered, by direct global->LDS loads
 // (global_load_lds_dwordx4: lane i of a wave-instruction fills bytes
