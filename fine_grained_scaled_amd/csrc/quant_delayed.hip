@@ -20,6 +20,8 @@
 // 128 x 128 blocks (the thread layout of the E4M3 quantizer: 8 x 8 values
 // per thread, 16 lanes over one 256-byte row segment) and atomically maxes
 // the block amax into the slot.
+#include <algorithm>
+
 #include "fgs_device.h"
 #include "fgs_internal.h"
 
@@ -157,94 +159,110 @@ __global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ 
     }
 }
 
-template <bool E5M2>
-__global__ __launch_bounds__(256) void quant_delayed_kernel(
+// Workgroup (blockIdx.x, blockIdx.y) quantizes column tiles
+// blockIdx.x * tpw .. + tpw - 1 of row tile blockIdx.y, one after another,
+// and adds its amax to the history slot with one atomic: same-address
+// atomics are served one at a time (measured on the Llama-3-8B hybrid step,
+// one per 128 x 128 tile: 15-25% of these kernels' time).  Addresses are a
+// tile's uniform base plus per-lane offsets below 2^31 (Off = int32_t when
+// 128 rows of every array fit, which the host checks), so the loop keeps
+// few per-lane registers live.
+template <bool E5M2, typename Off>
+__global__ __launch_bounds__(256, 4) void quant_delayed_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     const float* __restrict__ scale, uint32_t* __restrict__ amax_slot,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ qT)
+    uint8_t* __restrict__ q, uint8_t* __restrict__ qT, int tpw)
 {
     __shared__ uint32_t red[4];
     __shared__ __align__(16) uint8_t tbuf[TB][TB + TPAD];
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int cg = l & 15, rg = 4 * w + (l >> 4);
-    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
-    const int64_t col = c0 + 8 * cg;
-    const bool col_ok = col < cols;
-
-    uint4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int64_t row = r0 + 8 * rg + u;
-        v[u] = (col_ok && row < rows) ? load_nt16(x + row * ldx + col)
-                                      : make_uint4(0, 0, 0, 0);
-    }
+    const int64_t r0 = (int64_t)blockIdx.y * TB;
+    const int64_t nbc = (cols + TB - 1) / TB;
     const float s = scale[0];
+    const int lrow = 8 * rg;           // the thread's first row of the tile
+    uint32_t mrun = 0;                 // the wave's amax over its tiles
 
-    // amax of the block (|BF16| bits order like the values, NaN on top)
-    uint32_t m = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = max(m, abs_max8_bf16(v[u]));
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
-    if (l == 0) red[w] = m;
+    for (int k = 0; k < tpw; ++k) {
+        const int64_t cb = (int64_t)blockIdx.x * tpw + k;
+        if (cb >= nbc) break;                         // uniform
+        const int64_t c0 = cb * TB;
+        const bool col_ok = c0 + 8 * cg < cols;
+        const uint16_t* const xt = x + r0 * ldx + c0;
 
-    // the codes of the thread's 8 x 8 values, computed once: row u is c[u]
-    // (byte j = column j); the column-wise output is their byte transpose.
-    // m is the wave's amax: the branch is uniform across the wave.
-    uint2 c[8];
-    if (s >= 0x1p-60f && s <= 0x1p60f && m < 0x7F80u) {
-        const float r = 1.0f / s;                        // IEEE division, once
-        const float t = (E5M2 ? 2.0f * 57344.0f : 2.0f * 448.0f) * s;
+        uint4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            uint32_t xb[8];
+        for (int u = 0; u < 8; ++u)
+            v[u] = (col_ok && r0 + lrow + u < rows) ? load_nt16(xt + ((Off)(lrow + u) * (Off)ldx + 8 * cg))
+                                                    : make_uint4(0, 0, 0, 0);
+
+        // amax of the tile (|BF16| bits order like the values, NaN on top)
+        uint32_t m = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
-            c[u] = delayed_code8_fast<E5M2>(xb, s, r, t);
-        }
-    } else {
+        for (int u = 0; u < 8; ++u) m = max(m, abs_max8_bf16(v[u]));
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            uint32_t xb[8];
+        for (int d = 32; d > 0; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+        mrun = max(mrun, m);
+
+        // the codes of the thread's 8 x 8 values, computed once: row u is
+        // c[u] (byte j = column j); the column-wise output is their byte
+        // transpose.  m is the wave's amax: the branch is uniform across it.
+        uint2 c[8];
+        if (s >= 0x1p-60f && s <= 0x1p60f && m < 0x7F80u) {
+            const float r = 1.0f / s;                        // IEEE division, once
+            const float tt = (E5M2 ? 2.0f * 57344.0f : 2.0f * 448.0f) * s;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
-            c[u] = delayed_code8<E5M2>(xb, s);
-        }
-    }
-    if (q) {
+            for (int u = 0; u < 8; ++u) {
+                uint32_t xb[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t row = r0 + 8 * rg + u;
-            if (col_ok && row < rows) *reinterpret_cast<uint2*>(q + row * cols + col) = c[u];
-        }
-    }
-    if (qT) {
-        // column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+                for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+                c[u] = delayed_code8_fast<E5M2>(xb, s, r, tt);
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t b[8];
+            for (int u = 0; u < 8; ++u) {
+                uint32_t xb[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) b[u] = (((j < 4) ? c[u].x : c[u].y) >> (8 * (j & 3))) & 0xFFu;
-            *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][8 * rg]) =
-                make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
-        }
-    }
-    __syncthreads();
-    if (t == 0) {
-        m = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(amax_slot, m << 16);               // FP32 bits of the BF16 amax
-    }
-    if (qT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int trow = 32 * i + (t >> 3), chunk = t & 7;
-            const int64_t orow = c0 + trow;
-            if (orow < cols) {
-                const uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
-                *reinterpret_cast<uint4*>(qT + orow * rows + r0 + 16 * chunk) = d;
+                for (int j = 0; j < 8; ++j) xb[j] = bf16_elem_bits(v[u], j);
+                c[u] = delayed_code8<E5M2>(xb, s);
             }
         }
+        if (q) {
+            uint8_t* const qt = q + r0 * cols + c0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (col_ok && r0 + lrow + u < rows)
+                    *reinterpret_cast<uint2*>(qt + ((Off)(lrow + u) * (Off)cols + 8 * cg)) = c[u];
+        }
+        if (qT) {
+            // column j, rows 8*rg .. 8*rg+7 -> 8 contiguous bytes of qT
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t b[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) b[u] = (((j < 4) ? c[u].x : c[u].y) >> (8 * (j & 3))) & 0xFFu;
+                *reinterpret_cast<uint2*>(&tbuf[8 * cg + j][lrow]) =
+                    make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+            }
+            __syncthreads();
+            uint8_t* const qTt = qT + c0 * rows + r0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int trow = 32 * i + (t >> 3), chunk = t & 7;
+                if (c0 + trow < cols) {
+                    const uint4 d = *reinterpret_cast<const uint4*>(&tbuf[trow][16 * chunk]);
+                    *reinterpret_cast<uint4*>(qTt + ((Off)trow * (Off)rows + 16 * chunk)) = d;
+                }
+            }
+            __syncthreads();                          // tbuf is written again by the next tile
+        }
+    }
+    if (l == 0) red[w] = mrun;
+    __syncthreads();
+    if (t == 0) {
+        const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(amax_slot, m << 16);               // FP32 bits of the BF16 amax
     }
 }
 
@@ -257,15 +275,18 @@ hipError_t launch_quant_delayed(const QuantDelayedArgs& a, hipStream_t stream)
                        a.history, a.history_len, a.slot, e5 ? 57344.0f : 448.0f, a.scale);
     const int64_t nbr = (a.rows + TB - 1) / TB, nbc = (a.cols + TB - 1) / TB;
     if (nbr > 0 && nbc > 0) {
-        const dim3 grid((unsigned)nbc, (unsigned)nbr);
+        // 32-bit offsets when 128 rows of every array stay below 2^31
+        // elements (bytes for the codes); then tiles per workgroup for about
+        // eight workgroups per CU in all, at most 8
+        const bool small = (int64_t)TB * std::max({a.ldx, a.cols, a.rows}) < ((int64_t)1 << 31);
+        int64_t tpw = small ? nbr * nbc / (8 * (int64_t)device_cus()) : 1;
+        tpw = std::max<int64_t>(1, std::min<int64_t>({tpw, 8, nbc}));
+        const dim3 grid((unsigned)((nbc + tpw - 1) / tpw), (unsigned)nbr);
         const uint16_t* x = static_cast<const uint16_t*>(a.x);
         uint32_t* slot = reinterpret_cast<uint32_t*>(a.history + a.slot);
-        if (e5)
-            hipLaunchKernelGGL(quant_delayed_kernel<true>, grid, dim3(256), 0, stream,
-                               x, a.rows, a.cols, a.ldx, a.scale, slot, a.q, a.qT);
-        else
-            hipLaunchKernelGGL(quant_delayed_kernel<false>, grid, dim3(256), 0, stream,
-                               x, a.rows, a.cols, a.ldx, a.scale, slot, a.q, a.qT);
+        auto k = e5 ? (small ? quant_delayed_kernel<true, int32_t> : quant_delayed_kernel<true, int64_t>)
+                    : (small ? quant_delayed_kernel<false, int32_t> : quant_delayed_kernel<false, int64_t>);
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, x, a.rows, a.cols, a.ldx, a.scale, slot, a.q, a.qT, (int)tpw);
     }
     return hipGetLastError();
 }

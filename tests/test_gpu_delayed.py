@@ -58,6 +58,29 @@ def _check(fgs, x_bits, elem, hist, slot, rowwise=True, colwise=True):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+def test_delayed_quant_wide_row_stride(fgs, elem):
+    """A row stride of 2^24 + 8 elements, so 128 rows of it pass 2^31: the
+    kernel then takes 64-bit offsets and one tile per workgroup (below that,
+    32-bit offsets and several tiles per workgroup).  Row-wise codes, scale
+    and the recorded amax against the oracle."""
+    rows, cols, ldx = 2, 384, (1 << 24) + 8
+    xb = synth.gradients(rows, cols, seed=77) if elem == "e5m2" else synth.activations(rows, cols, seed=77)
+    big = torch.empty((rows, ldx), dtype=torch.bfloat16, device="cuda")
+    big[:, :cols] = synth.to_torch_bf16(xb).cuda()
+    x = big[:, :cols]
+    amax = F32(np.abs(oracle.bf16_bits_to_f32(xb)).max())
+    hist = [amax / F32(2.0), F32(0.0)]
+    h = torch.from_numpy(np.asarray(hist, F32).copy()).cuda()
+    qq = fgs.quantize_delayed(x, h, 1, elem, rowwise=True, colwise=False)
+    torch.cuda.synchronize()
+    oq, os_, oam = oracle.quant_delayed(xb, elem, hist)
+    assert np.array_equal(qq.q.cpu().numpy(), oq)
+    assert np.float32(qq.scales.cpu().numpy()[0]).tobytes() == np.float32(os_).tobytes()
+    assert h.cpu().numpy()[1] == oam
+    del big
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("rows,cols,colwise", [(256, 384, True), (128, 200, True), (300, 256, False), (1, 8, False)])
 def test_delayed_quant_ragged_with_saturation(fgs, elem, rows, cols, colwise):
     """The history's max is a quarter of this tensor's amax, so the largest
