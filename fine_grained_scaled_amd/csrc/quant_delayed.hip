@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ 
 }
 
 // Workgroup (blockIdx.x, blockIdx.y) quantizes column tiles
-// blockIdx.x * tpw .. + tpw - 1 of row tile blockIdx.y, one after another,
+// blockIdx.x * tpw .. + tpw - 1 of row tile blockIdx.y (up to 32), one after another,
 // and adds its amax to the history slot with one atomic: same-address
 // atomics are served one at a time (measured on the Llama-3-8B hybrid step,
 // one per 128 x 128 tile: 15-25% of these kernels' time).  Addresses are a
@@ -277,10 +277,12 @@ hipError_t launch_quant_delayed(const QuantDelayedArgs& a, hipStream_t stream)
     if (nbr > 0 && nbc > 0) {
         // 32-bit offsets when 128 rows of every array stay below 2^31
         // elements (bytes for the codes); then tiles per workgroup for about
-        // eight workgroups per CU in all, at most 8
+        // two workgroups per CU in all, at most 32 (hybrid step, same box:
+        // 734 us with this, 763 with eight workgroups per CU, 802 with eight
+        // per CU and at most 8 tiles)
         const bool small = (int64_t)TB * std::max({a.ldx, a.cols, a.rows}) < ((int64_t)1 << 31);
-        int64_t tpw = small ? nbr * nbc / (8 * (int64_t)device_cus()) : 1;
-        tpw = std::max<int64_t>(1, std::min<int64_t>({tpw, 8, nbc}));
+        int64_t tpw = small ? nbr * nbc / (2 * (int64_t)device_cus()) : 1;
+        tpw = std::max<int64_t>(1, std::min<int64_t>({tpw, 32, nbc}));
         const dim3 grid((unsigned)((nbc + tpw - 1) / tpw), (unsigned)nbr);
         const uint16_t* x = static_cast<const uint16_t*>(a.x);
         uint32_t* slot = reinterpret_cast<uint32_t*>(a.history + a.slot);
